@@ -1,0 +1,140 @@
+"""fp64 CPU oracle for attention over a TPA factor cache.
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import it.  The library
+(``factorized_kv_cache_tpa_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``tpa_oracle.c`` (plain C, fp64, OpenMP over heads):
+materialize K and V from the factors, apply standard RoPE to the full key and
+query rows, run textbook two-pass softmax attention.  This wrapper only
+marshals numpy arrays and maps decode / prefill onto that one routine:
+
+* decode (one query row per sequence at position N, sees all N cached tokens);
+* causal chunked prefill (chunk row j at position ctx + j sees tokens
+  0 .. ctx + j, including the chunk's own earlier tokens and itself).
+
+The reading of the pages these follow is spelled out in ``tpa_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tpa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP, -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        D = ctypes.POINTER(ctypes.c_double)
+        I64 = ctypes.POINTER(ctypes.c_int64)
+        lib.tpa_oracle_rope_row.argtypes = [D, ctypes.c_int, ctypes.c_double, ctypes.c_double]
+        lib.tpa_oracle_rope_row.restype = None
+        lib.tpa_oracle_attention.argtypes = [ctypes.c_int] * 4 + [ctypes.c_int64] + [D] * 5 + [
+            ctypes.c_int64, D, D, I64, ctypes.c_double, ctypes.c_double, D, ctypes.c_int]
+        lib.tpa_oracle_attention.restype = ctypes.c_int
+        lib.tpa_oracle_factor_elems_per_token.argtypes = [ctypes.c_int] * 4
+        lib.tpa_oracle_factor_elems_per_token.restype = ctypes.c_int64
+        lib.tpa_oracle_dense_elems_per_token.argtypes = [ctypes.c_int] * 2
+        lib.tpa_oracle_dense_elems_per_token.restype = ctypes.c_int64
+        lib.tpa_oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _dp(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def max_threads() -> int:
+    return int(_load().tpa_oracle_max_threads())
+
+
+def rope_rows(x: np.ndarray, pos: float, base: float) -> np.ndarray:
+    """Standard RoPE of every last-axis row of x (even length) at one position; returns a copy."""
+    y = _f64(x).copy()
+    flat = y.reshape(-1, y.shape[-1])
+    lib = _load()
+    for r in range(flat.shape[0]):
+        row = np.ascontiguousarray(flat[r])
+        lib.tpa_oracle_rope_row(_dp(row), int(row.shape[0]), float(pos), float(base))
+        flat[r] = row
+    return y
+
+
+def attention(A_K, B_K, A_V, B_V, kv_pos, q, q_pos, q_nvis, base: float, scale: Optional[float] = None,
+              threads: Optional[int] = None) -> np.ndarray:
+    """out[n][h][d] for query rows q[n][h][d] over cached factors (all float64-convertible)."""
+    A_K, B_K, A_V, B_V = _f64(A_K), _f64(B_K), _f64(A_V), _f64(B_V)
+    q = _f64(q)
+    n_kv, RK, h = A_K.shape
+    RV = A_V.shape[1]
+    d = B_K.shape[2]
+    n_q = q.shape[0]
+    assert B_K.shape == (n_kv, RK, d) and A_V.shape == (n_kv, RV, h) and B_V.shape == (n_kv, RV, d)
+    assert q.shape == (n_q, h, d)
+    kv_pos = _f64(kv_pos).reshape(n_kv)
+    q_pos = _f64(q_pos).reshape(n_q)
+    q_nvis = np.ascontiguousarray(q_nvis, dtype=np.int64).reshape(n_q)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((n_q, h, d), dtype=np.float64)
+    nt = threads if threads is not None else max_threads()
+    rc = _load().tpa_oracle_attention(
+        h, d, RK, RV, n_kv, _dp(A_K), _dp(B_K), _dp(A_V), _dp(B_V), _dp(kv_pos), n_q, _dp(q), _dp(q_pos),
+        q_nvis.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), float(base), float(scale), _dp(out), int(nt))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out
+
+
+def decode(A_K, B_K, A_V, B_V, q, base: float, scale: Optional[float] = None, n_cached: Optional[int] = None,
+           threads: Optional[int] = None) -> np.ndarray:
+    """One query row q[h][d] at position N over N cached tokens at positions 0..N-1 -> [h][d]."""
+    n = int(np.shape(A_K)[0]) if n_cached is None else int(n_cached)
+    q = _f64(q).reshape((1,) + np.shape(q)[-2:])
+    return attention(A_K, B_K, A_V, B_V, np.arange(np.shape(A_K)[0]), q, [n], [n], base, scale, threads)[0]
+
+
+def prefill(A_K, B_K, A_V, B_V, q, ctx: int, base: float, scale: Optional[float] = None,
+            rows: Optional[np.ndarray] = None, threads: Optional[int] = None) -> np.ndarray:
+    """Causal chunk: query row j at position ctx+j sees tokens 0..ctx+j -> [n_rows][h][d].
+
+    ``rows`` selects a subset of chunk rows (sampled checks); default all rows of q.
+    """
+    q = _f64(q)
+    j = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    return attention(A_K, B_K, A_V, B_V, np.arange(np.shape(A_K)[0]), q[j], ctx + j, ctx + j + 1, base,
+                     scale, threads)
+
+
+def factor_elems_per_token(h: int, d: int, RK: int, RV: int) -> int:
+    return int(_load().tpa_oracle_factor_elems_per_token(h, d, RK, RV))
+
+
+def dense_elems_per_token(h: int, d: int) -> int:
+    return int(_load().tpa_oracle_dense_elems_per_token(h, d))
