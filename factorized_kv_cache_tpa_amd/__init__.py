@@ -1,0 +1,205 @@
+"""Python binding of libtpa: attention over a TPA factor cache on MI355X.
+
+Thin ctypes marshalling of the C ABI in ``include/tpa.h``; the functions
+carry the same names.  Every step of the computation runs in the HIP kernels
+of ``libtpa.so``; this module only turns torch tensors into device pointers
+and the current HIP stream into a ``hipStream_t``.  There is no fallback: if
+the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "TPAError", "Dims", "load", "library_path", "tpa_abi_version", "tpa_status_string", "tpa_supported",
+    "tpa_block_tokens", "tpa_cache_bytes", "tpa_cache_append", "tpa_cache_read", "tpa_decode_workspace_bytes",
+    "tpa_decode", "tpa_prefill_chunk", "TPA_F32", "TPA_BF16",
+]
+
+TPA_F32 = 0
+TPA_BF16 = 1
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libtpa.so")
+_lib = None
+
+_EXPORTS = {
+    "tpa_abi_version": ([], ctypes.c_int32),
+    "tpa_status_string": ([ctypes.c_int32], ctypes.c_char_p),
+    "tpa_supported": ([ctypes.c_void_p], ctypes.c_int32),
+    "tpa_block_tokens": ([ctypes.c_void_p], ctypes.c_int32),
+    "tpa_cache_bytes": ([ctypes.c_void_p, ctypes.c_int64], ctypes.c_int64),
+    "tpa_cache_append": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                          ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int32),
+    "tpa_cache_read": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p],
+                       ctypes.c_int32),
+    "tpa_decode_workspace_bytes": ([ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32],
+                                   ctypes.c_int64),
+    "tpa_decode": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                    ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p], ctypes.c_int32),
+    "tpa_prefill_chunk": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                           ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
+                           ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int32),
+}
+
+
+class TPAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {tpa_status_string(status)} (status {status})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    """tpa_dims: h, d_h, R_K, R_V, dtype (TPA_F32 / TPA_BF16), rope_base."""
+    _fields_ = [("h", ctypes.c_int32), ("d_h", ctypes.c_int32), ("R_K", ctypes.c_int32), ("R_V", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32), ("rope_base", ctypes.c_double)]
+
+    def __init__(self, h: int, d_h: int, R_K: int, R_V: int, dtype="bf16", rope_base: float = 1e4):
+        if isinstance(dtype, str):
+            dtype = {"bf16": TPA_BF16, "f32": TPA_F32}[dtype]
+        elif isinstance(dtype, torch.dtype):
+            dtype = {torch.bfloat16: TPA_BF16, torch.float32: TPA_F32}[dtype]
+        super().__init__(int(h), int(d_h), int(R_K), int(R_V), int(dtype), 0, float(rope_base))
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == TPA_BF16 else torch.float32
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libtpa.so (built in-tree by ``__graft_entry__.build()``); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"libtpa.so is not built ({_LIB_PATH}); run __graft_entry__.build()")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (args, res) in _EXPORTS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+    return _lib
+
+
+def _ref(d: Dims):
+    return ctypes.byref(d)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype] = None, name: str = "tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise TPAError(status, where)
+
+
+def tpa_abi_version() -> int:
+    return int(load().tpa_abi_version())
+
+
+def tpa_status_string(status: int) -> str:
+    return load().tpa_status_string(int(status)).decode()
+
+
+def tpa_supported(dims: Dims) -> bool:
+    return bool(load().tpa_supported(_ref(dims)))
+
+
+def tpa_block_tokens(dims: Dims) -> int:
+    return int(load().tpa_block_tokens(_ref(dims)))
+
+
+def tpa_cache_bytes(dims: Dims, capacity_tokens: int) -> int:
+    return int(load().tpa_cache_bytes(_ref(dims), int(capacity_tokens)))
+
+
+def tpa_decode_workspace_bytes(dims: Dims, batch: int, max_len: int, split_tokens: int = 0) -> int:
+    return int(load().tpa_decode_workspace_bytes(_ref(dims), int(batch), int(max_len), int(split_tokens)))
+
+
+def tpa_cache_append(dims: Dims, cache: torch.Tensor, capacity_tokens: int, slot: torch.Tensor,
+                     kv_pos: torch.Tensor, A_K: torch.Tensor, B_K: torch.Tensor, A_V: torch.Tensor,
+                     B_V: torch.Tensor, slot_hi: Optional[int] = None, q_pos: Optional[torch.Tensor] = None,
+                     q_in: Optional[torch.Tensor] = None, q_out: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    """Append factors of slot.numel() tokens (B_K rotated by kv_pos) and rotate optional query rows.
+
+    A_K [n][R_K][h], B_K [n][R_K][d_h], A_V [n][R_V][h], B_V [n][R_V][d_h]; q_in/q_out [n_q][rows][d_h].
+    ``slot_hi`` is a host-side bound on max(slot)+1 (default: capacity_tokens).
+    """
+    dt = dims.torch_dtype
+    n_kv = slot.numel()
+    n_q = 0 if q_pos is None else q_pos.numel()
+    q_rows = 0
+    if n_q:
+        if q_in is None:
+            raise ValueError("q_in is required with q_pos")
+        q_out = q_in if q_out is None else q_out
+        q_rows = q_in.numel() // (n_q * dims.d_h)
+    lib = load()
+    st = lib.tpa_cache_append(
+        _ref(dims), _ptr(cache, name="cache"), int(capacity_tokens), n_kv, _ptr(slot, torch.int64, "slot"),
+        _ptr(kv_pos, torch.int32, "kv_pos"), int(capacity_tokens if slot_hi is None else slot_hi),
+        _ptr(A_K, dt, "A_K"), _ptr(B_K, dt, "B_K"), _ptr(A_V, dt, "A_V"), _ptr(B_V, dt, "B_V"), n_q, q_rows,
+        _ptr(q_pos, torch.int32, "q_pos") if n_q else None, _ptr(q_in, dt, "q_in") if n_q else None,
+        _ptr(q_out, dt, "q_out") if n_q else None, _stream(stream))
+    _check(st, "tpa_cache_append")
+
+
+def tpa_cache_read(dims: Dims, cache: torch.Tensor, capacity_tokens: int, slot: torch.Tensor,
+                   A_K: torch.Tensor, B_K: torch.Tensor, A_V: torch.Tensor, B_V: torch.Tensor, stream=None) -> None:
+    dt = dims.torch_dtype
+    st = load().tpa_cache_read(_ref(dims), _ptr(cache, name="cache"), int(capacity_tokens), slot.numel(),
+                               _ptr(slot, torch.int64, "slot"), _ptr(A_K, dt, "A_K"), _ptr(B_K, dt, "B_K"),
+                               _ptr(A_V, dt, "A_V"), _ptr(B_V, dt, "B_V"), _stream(stream))
+    _check(st, "tpa_cache_read")
+
+
+def tpa_decode(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_start: torch.Tensor,
+               seq_len: torch.Tensor, max_len: int, q_rot: torch.Tensor, out: torch.Tensor,
+               workspace: torch.Tensor, scale: float = 0.0, split_tokens: int = 0, stream=None) -> None:
+    """out[b][h][d_h] (fp32) = attention of q_rot[b] over the seq_len[b] cached tokens of sequence b."""
+    st = load().tpa_decode(
+        _ref(dims), _ptr(cache, name="cache"), int(capacity_tokens), seq_start.numel(),
+        _ptr(seq_start, torch.int64, "seq_start"), _ptr(seq_len, torch.int32, "seq_len"), int(max_len),
+        _ptr(q_rot, dims.torch_dtype, "q_rot"), float(scale), _ptr(out, torch.float32, "out"), int(split_tokens),
+        _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "tpa_decode")
+
+
+def tpa_prefill_chunk(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_start: torch.Tensor,
+                      ctx_len: torch.Tensor, max_ctx: int, chunk_len: int, q_rot: torch.Tensor, out: torch.Tensor,
+                      scale: float = 0.0, stream=None) -> None:
+    """out[b][j][h][d_h] (fp32): causal attention of chunk row j over slots 0 .. ctx_len[b] + j."""
+    st = load().tpa_prefill_chunk(
+        _ref(dims), _ptr(cache, name="cache"), int(capacity_tokens), seq_start.numel(),
+        _ptr(seq_start, torch.int64, "seq_start"), _ptr(ctx_len, torch.int32, "ctx_len"), int(max_ctx),
+        int(chunk_len), _ptr(q_rot, dims.torch_dtype, "q_rot"), float(scale), _ptr(out, torch.float32, "out"),
+        _stream(stream))
+    _check(st, "tpa_prefill_chunk")

@@ -1,0 +1,217 @@
+// C ABI of libtpa: argument checks, launch planning and dispatch.
+// Every check runs on the host before any HIP call, so a rejected call has no
+// side effect and the checks work on a machine without a GPU.
+#include <math.h>
+
+#include "../../include/tpa.h"
+#include "common.h"
+
+namespace {
+
+using tpa::Layout;
+
+// Decode work-groups the planner aims for when it picks the split size: two
+// per compute unit of an MI355X (256 CUs), so every CU streams from the start.
+constexpr int64_t kTargetSplitGroups = 512;
+constexpr int kDecodeWaves = 4;
+
+bool dims_valid(const tpa_dims *d) {
+    if (!d) return false;
+    if (d->h < 1 || d->h > 64) return false;
+    if (d->d_h < 2 || d->d_h > 256 || (d->d_h & 1)) return false;
+    if (d->R_K < 1 || d->R_K > 4 || d->R_V < 1 || d->R_V > 4) return false;
+    if (d->dtype != TPA_F32 && d->dtype != TPA_BF16) return false;
+    if (d->reserved != 0) return false;
+    if (!(d->rope_base > 0.0) || !isfinite(d->rope_base)) return false;
+    return true;
+}
+
+Layout layout_of(const tpa_dims *d) { return tpa::make_layout(d->h, d->d_h, d->R_K, d->R_V, d->dtype); }
+
+int32_t check_dims(const tpa_dims *d) {
+    if (!dims_valid(d)) return TPA_ERR_ARG;
+    if (!tpa::decode_supported(layout_of(d))) return TPA_ERR_UNSUPPORTED;
+    return TPA_OK;
+}
+
+struct DecodePlan {
+    int split_blocks = 1;
+    int n_split = 1;
+    int64_t off_ml = 0;
+    int64_t bytes = 0;
+};
+
+DecodePlan plan_decode(const Layout &L, int32_t batch, int32_t max_len, int32_t split_tokens) {
+    DecodePlan P;
+    const int TOK = L.tok_per_block();
+    const int64_t nblk_max = (int64_t(max_len) + TOK - 1) / TOK;
+    int64_t sb;
+    if (split_tokens > 0) {
+        sb = (int64_t(split_tokens) + TOK - 1) / TOK;
+    } else {
+        const int64_t total = int64_t(batch) * nblk_max;
+        sb = (total + kTargetSplitGroups - 1) / kTargetSplitGroups;
+        sb = (sb + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
+        if (sb < kDecodeWaves) sb = kDecodeWaves;
+    }
+    if (sb < 1) sb = 1;
+    int64_t ns = (nblk_max + sb - 1) / sb;
+    if (ns < 1) ns = 1;
+    P.split_blocks = int(sb > (1 << 30) ? (1 << 30) : sb);
+    P.n_split = int(ns);
+    const int64_t parts = int64_t(batch) * ns;
+    const int64_t o_bytes = parts * L.HP * L.DP * 4;
+    P.off_ml = (o_bytes + 255) / 256 * 256;
+    P.bytes = P.off_ml + (parts * L.HP * 2 * 4 + 255) / 256 * 256;
+    return P;
+}
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+float resolve_scale(float scale, int d_h) { return scale > 0.f ? scale : float(1.0 / sqrt(double(d_h))); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t tpa_abi_version(void) { return TPA_ABI_VERSION; }
+
+const char *tpa_status_string(int32_t status) {
+    switch (status) {
+        case TPA_OK: return "TPA_OK";
+        case TPA_ERR_ARG: return "TPA_ERR_ARG: invalid argument";
+        case TPA_ERR_UNSUPPORTED: return "TPA_ERR_UNSUPPORTED: no kernel compiled for these dims";
+        case TPA_ERR_CAPACITY: return "TPA_ERR_CAPACITY: slot beyond cache capacity";
+        case TPA_ERR_WORKSPACE: return "TPA_ERR_WORKSPACE: workspace missing or too small";
+        case TPA_ERR_HIP: return "TPA_ERR_HIP: kernel launch failed";
+    }
+    return "TPA_ERR_UNKNOWN";
+}
+
+int32_t tpa_supported(const tpa_dims *dims) { return check_dims(dims) == TPA_OK ? 1 : 0; }
+
+int32_t tpa_block_tokens(const tpa_dims *dims) {
+    if (!dims_valid(dims)) return -1;
+    return layout_of(dims).tok_per_block();
+}
+
+int64_t tpa_cache_bytes(const tpa_dims *dims, int64_t capacity_tokens) {
+    if (!dims_valid(dims) || capacity_tokens < 0) return -1;
+    const Layout L = layout_of(dims);
+    const int64_t blocks = (capacity_tokens + L.tok_per_block() - 1) / L.tok_per_block();
+    return blocks * L.block_elems() * L.es;
+}
+
+int32_t tpa_cache_append(const tpa_dims *dims, void *cache, int64_t capacity_tokens, int64_t n_kv,
+                         const int64_t *slot, const int32_t *kv_pos, int64_t slot_hi, const void *A_K,
+                         const void *B_K, const void *A_V, const void *B_V, int64_t n_q, int32_t q_rows,
+                         const int32_t *q_pos, const void *q_in, void *q_out, void *stream) {
+    int32_t st = check_dims(dims);
+    if (st != TPA_OK) return st;
+    if (capacity_tokens < 0 || n_kv < 0 || n_q < 0) return TPA_ERR_ARG;
+    if (n_kv + n_q > int64_t(0x7fffffff)) return TPA_ERR_ARG;
+    if (n_kv > 0) {
+        if (!cache || !slot || !kv_pos || !A_K || !B_K || !A_V || !B_V) return TPA_ERR_ARG;
+        if (slot_hi < 0) return TPA_ERR_ARG;
+        if (slot_hi > capacity_tokens) return TPA_ERR_CAPACITY;
+    }
+    if (n_q > 0) {
+        if (q_rows < 1 || !q_pos || !q_in || !q_out) return TPA_ERR_ARG;
+        if (int64_t(q_rows) * dims->d_h > int64_t(1) << 24) return TPA_ERR_ARG;
+    }
+    if (n_kv == 0 && n_q == 0) return TPA_OK;
+    const hipError_t e = tpa::launch_append(layout_of(dims), dims->h, dims->d_h, dims->R_K, dims->R_V,
+                                            dims->rope_base, cache, capacity_tokens, n_kv, slot, kv_pos, A_K, B_K,
+                                            A_V, B_V, n_q, q_rows, q_pos, q_in, q_out, as_stream(stream));
+    return e == hipSuccess ? TPA_OK : TPA_ERR_HIP;
+}
+
+int32_t tpa_cache_read(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int64_t n,
+                       const int64_t *slot, void *A_K, void *B_K, void *A_V, void *B_V, void *stream) {
+    int32_t st = check_dims(dims);
+    if (st != TPA_OK) return st;
+    if (capacity_tokens < 0 || n < 0 || n > int64_t(0x7fffffff)) return TPA_ERR_ARG;
+    if (n == 0) return TPA_OK;
+    if (!cache || !slot || !A_K || !B_K || !A_V || !B_V) return TPA_ERR_ARG;
+    const hipError_t e = tpa::launch_read(layout_of(dims), dims->h, dims->d_h, dims->R_K, dims->R_V, cache,
+                                          capacity_tokens, n, slot, A_K, B_K, A_V, B_V, as_stream(stream));
+    return e == hipSuccess ? TPA_OK : TPA_ERR_HIP;
+}
+
+int64_t tpa_decode_workspace_bytes(const tpa_dims *dims, int32_t batch, int32_t max_len, int32_t split_tokens) {
+    if (!dims_valid(dims) || batch < 0 || max_len < 0 || split_tokens < 0) return -1;
+    return plan_decode(layout_of(dims), batch, max_len, split_tokens).bytes;
+}
+
+int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
+                   const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *q_rot,
+                   float scale, float *out, int32_t split_tokens, void *workspace, int64_t workspace_bytes,
+                   void *stream) {
+    int32_t st = check_dims(dims);
+    if (st != TPA_OK) return st;
+    if (batch < 0 || batch > 65535 || max_len < 0 || split_tokens < 0 || capacity_tokens < 0)
+        return TPA_ERR_ARG;
+    if (batch == 0) return TPA_OK;
+    if (!cache || !seq_start || !seq_len || !q_rot || !out) return TPA_ERR_ARG;
+    if (!isfinite(scale)) return TPA_ERR_ARG;
+    if (int64_t(max_len) > capacity_tokens) return TPA_ERR_CAPACITY;
+    const Layout L = layout_of(dims);
+    const DecodePlan P = plan_decode(L, batch, max_len, split_tokens);
+    if (!workspace || workspace_bytes < P.bytes) return TPA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TPA_ERR_WORKSPACE;
+    if (P.n_split > 65535) return TPA_ERR_ARG;
+
+    tpa::DecodeParams p;
+    p.cache = cache;
+    p.seq_start = seq_start;
+    p.seq_len = seq_len;
+    p.q = q_rot;
+    p.out = out;
+    p.ws_o = reinterpret_cast<float *>(workspace);
+    p.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + P.off_ml);
+    p.h = dims->h;
+    p.d_h = dims->d_h;
+    p.RK = dims->R_K;
+    p.RV = dims->R_V;
+    p.batch = batch;
+    p.max_len = max_len;
+    p.split_blocks = P.split_blocks;
+    p.n_split = P.n_split;
+    p.score_mul = float(double(resolve_scale(scale, dims->d_h)) * M_LOG2E / dims->R_K);
+    p.out_mul = float(1.0 / dims->R_V);
+    const hipError_t e = tpa::launch_decode(L, p, as_stream(stream));
+    return e == hipSuccess ? TPA_OK : TPA_ERR_HIP;
+}
+
+int32_t tpa_prefill_chunk(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
+                          const int64_t *seq_start, const int32_t *ctx_len, int32_t max_ctx, int32_t chunk_len,
+                          const void *q_rot, float scale, float *out, void *stream) {
+    int32_t st = check_dims(dims);
+    if (st != TPA_OK) return st;
+    if (batch < 0 || batch > 65535 || max_ctx < 0 || chunk_len < 0 || capacity_tokens < 0) return TPA_ERR_ARG;
+    if (batch == 0 || chunk_len == 0) return TPA_OK;
+    if (!cache || !seq_start || !ctx_len || !q_rot || !out) return TPA_ERR_ARG;
+    if (!isfinite(scale)) return TPA_ERR_ARG;
+    if (int64_t(max_ctx) + chunk_len > capacity_tokens) return TPA_ERR_CAPACITY;
+    const Layout L = layout_of(dims);
+    if (!tpa::prefill_supported(L)) return TPA_ERR_UNSUPPORTED;
+    tpa::PrefillParams p;
+    p.cache = cache;
+    p.seq_start = seq_start;
+    p.ctx_len = ctx_len;
+    p.q = q_rot;
+    p.out = out;
+    p.h = dims->h;
+    p.d_h = dims->d_h;
+    p.RK = dims->R_K;
+    p.RV = dims->R_V;
+    p.batch = batch;
+    p.chunk = chunk_len;
+    p.max_ctx = max_ctx;
+    p.score_mul = float(double(resolve_scale(scale, dims->d_h)) * M_LOG2E / dims->R_K);
+    p.out_mul = float(1.0 / dims->R_V);
+    const hipError_t e = tpa::launch_prefill(L, p, as_stream(stream));
+    return e == hipSuccess ? TPA_OK : TPA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// Internal definitions shared by the libtpa kernels and the C ABI layer.
+//
+// Cache block layout.  A block holds kRows = 32 factor rows; a row is one
+// (token, rank) pair and a token owns RH consecutive rows, where RH is the
+// rank padded to 1, 2 or 4 (rows r >= R_K or r >= R_V are stored as zeros).
+// A block therefore holds 32 / RH tokens.  Heads are padded to HP (a
+// multiple of 16) and the head dimension to DP; padding is stored as zeros.
+//
+// The decode kernel runs two matrix-core contractions per block with the
+// 16x16 MFMA shapes (bf16 16x16x32: E = 8 k-values per lane; fp32 16x16x4:
+// E = 1):
+//   scores  U^T[row][head] = B~_K[row][:] . q~[head][:]   (A operand: B~_K rows)
+//   values  O^T[d][head]  += B_V[:][d]^T . W[:][head]      (A operand: B_V columns)
+// and applies the head factors A_K, A_V as per-(row, head) gates on the
+// score accumulators.  Each region of a block is stored exactly in the
+// per-lane order of the operand or accumulator it feeds, so one wave-wide
+// load of 16 (or 8) bytes per lane reads a contiguous 1 KiB (512 B) span:
+//   A_K, A_V gates : [mblk 2][NB][lane 64][4]     row = 16 mblk + 4 (lane/16) + v,
+//                                                 head = 16 nb + lane%16
+//   B~_K           : [mblk 2][KBS][lane 64][E]    row = 16 mblk + lane%16,
+//                                                 d = 4E kb + E (lane/16) + e
+//   B_V            : [MBV][KBV][lane 64][E]        d = 16 mv + lane%16,
+//                                                 row = score row of slot t = E q + e:
+//                                                 16 (t/4) + 4 (lane/16) + t%4
+// so the score accumulator a lane holds (rows 4(lane/16)+v of both score
+// row blocks, one head) is exactly the k-slice it must supply to the value
+// contraction: no data moves between lanes between the two contractions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpa {
+
+constexpr int kRows = 32;  // factor rows per cache block
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// Runtime description of one cache layout (host and device).
+struct Layout {
+    int HP, DP, RH, E;  // padded heads, padded head dim, padded rank, k-values per lane
+    int es;             // element size in bytes
+
+    __host__ __device__ int tok_per_block() const { return kRows / RH; }
+    __host__ __device__ int NB() const { return HP / 16; }
+    __host__ __device__ int KBS() const { return DP / (4 * E); }
+    __host__ __device__ int MBV() const { return DP / 16; }
+    __host__ __device__ int KBV() const { return kRows / (4 * E); }
+    __host__ __device__ int64_t block_elems() const { return 2LL * kRows * (HP + DP); }
+    __host__ __device__ int off_ak() const { return 0; }
+    __host__ __device__ int off_av() const { return kRows * HP; }
+    __host__ __device__ int off_bk() const { return 2 * kRows * HP; }
+    __host__ __device__ int off_bv() const { return 2 * kRows * HP + kRows * DP; }
+
+    // element offsets inside a block region
+    __host__ __device__ int gate(int row, int head) const {
+        int mb = row >> 4, nb = head >> 4, lane = 16 * ((row & 15) >> 2) + (head & 15), v = row & 3;
+        return ((mb * NB() + nb) * kWave + lane) * 4 + v;
+    }
+    __host__ __device__ int bk(int row, int d) const {
+        int mb = row >> 4, kb = d / (4 * E), lane = 16 * ((d % (4 * E)) / E) + (row & 15), e = d % E;
+        return ((mb * KBS() + kb) * kWave + lane) * E + e;
+    }
+    __host__ __device__ int bv(int row, int d) const {
+        int t = 4 * (row >> 4) + (row & 3), g = (row & 15) >> 2;
+        int q = t / E, e = t % E, mv = d >> 4, lane = 16 * g + (d & 15);
+        return ((mv * KBV() + q) * kWave + lane) * E + e;
+    }
+};
+
+__host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Padded rank: 1, 2 or 4 rows per token.
+__host__ __device__ inline int padded_rank(int RK, int RV) {
+    int r = RK > RV ? RK : RV;
+    return r <= 1 ? 1 : (r <= 2 ? 2 : 4);
+}
+
+__host__ __device__ inline Layout make_layout(int h, int d_h, int RK, int RV, int dtype) {
+    Layout L;
+    L.E = dtype == 1 ? 8 : 1;
+    L.es = dtype == 1 ? 2 : 4;
+    L.HP = round_up(h, 16);
+    L.DP = round_up(d_h, dtype == 1 ? 32 : 16);
+    L.RH = padded_rank(RK, RV);
+    return L;
+}
+
+// bf16 <-> fp32 (bit level; bf16 is the upper half of an fp32).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+    static constexpr int dtype = 0;
+    __device__ static float load(const float *p, int64_t i) { return p[i]; }
+    __device__ static float to_f32(float x) { return x; }
+    __device__ static float from_f64(double x) { return float(x); }
+};
+template <>
+struct Elem<uint16_t> {
+    static constexpr int dtype = 1;
+    __device__ static float to_f32(uint16_t x) { return bf16_to_f32(x); }
+    __device__ static uint16_t from_f64(double x) { return f32_to_bf16_rne(float(x)); }
+};
+
+// Parameters of one decode call, shared by the split and merge kernels.
+struct DecodeParams {
+    const void *cache;
+    const int64_t *seq_start;
+    const int32_t *seq_len;
+    const void *q;  // [batch][h][d_h]
+    float *out;     // [batch][h][d_h]
+    float *ws_o;    // [batch][n_split][HP][DP]
+    float *ws_ml;   // [batch][n_split][HP][2]
+    int h, d_h, RK, RV;
+    int batch, max_len, split_blocks, n_split;
+    float score_mul;  // scale * log2(e) / R_K
+    float out_mul;    // 1 / R_V
+};
+
+struct PrefillParams {
+    const void *cache;
+    const int64_t *seq_start;
+    const int32_t *ctx_len;
+    const void *q;  // [batch][chunk][h][d_h]
+    float *out;     // [batch][chunk][h][d_h]
+    int h, d_h, RK, RV;
+    int batch, chunk, max_ctx;
+    float score_mul;  // scale * log2(e) / R_K
+    float out_mul;    // 1 / R_V
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_append(const Layout &L, int h, int d_h, int RK, int RV, double base, void *cache,
+                         int64_t capacity, int64_t n_kv, const int64_t *slot, const int32_t *kv_pos,
+                         const void *A_K, const void *B_K, const void *A_V, const void *B_V, int64_t n_q,
+                         int q_rows, const int32_t *q_pos, const void *q_in, void *q_out, hipStream_t s);
+hipError_t launch_read(const Layout &L, int h, int d_h, int RK, int RV, const void *cache, int64_t capacity,
+                       int64_t n, const int64_t *slot, void *A_K, void *B_K, void *A_V, void *B_V,
+                       hipStream_t s);
+bool decode_supported(const Layout &L);
+hipError_t launch_decode(const Layout &L, const DecodeParams &p, hipStream_t s);
+bool prefill_supported(const Layout &L);
+hipError_t launch_prefill(const Layout &L, const PrefillParams &p, hipStream_t s);
+
+}  // namespace tpa

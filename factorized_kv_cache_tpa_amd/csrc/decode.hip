@@ -1,0 +1,421 @@
+// Split-sequence decode over a TPA factor cache.
+//
+// TPA notes page, Key design: K_s = (1/R_K) A_K[s]^T B_K[s] and V_s likewise;
+// FlashTPA: attention is evaluated from the factors, never from a built K/V.
+// For one query row q~ (already rotated) and head i:
+//   z_s,i = scale * q~_i . K~_s[i,:] = (scale/R_K) sum_r A_K[s,r,i] (B~_K[s,r,:] . q~_i)
+//   out_i = sum_s softmax_s(z_s,i) V_s[i,:]
+//         = (1/R_V) sum_s sum_r (p_s,i A_V[s,r,i]) B_V[s,r,:] / sum_s p_s,i
+// Both inner sums are matrix-core contractions with the heads as the N
+// dimension:
+//   1. U^T[(s,r), i] = B~_K[(s,r), :] . q~^T[:, i]   (M = token rows, K = d_h)
+//   2. gate: z[s, i] = sum_r A_K[s,r,i] U^T[(s,r), i]  (in-lane: a lane's four
+//      accumulator rows hold whole tokens because the padded rank is 1, 2 or 4)
+//   3. online softmax per head (running max in log2 units, running sum)
+//   4. W[(s,r), i] = p[s,i] A_V[s,r,i], rounded once to the element type
+//   5. O^T[:, i] += B_V[(s,r), :]^T W[(s,r), i]     (M = d_h, K = token rows)
+// The cache block layout (common.h) makes the score accumulator of a lane
+// exactly the k-slice it feeds to step 5, so no data crosses lanes between
+// the contractions.  Each work-group (4 waves) handles one split of one
+// sequence, the waves taking interleaved blocks; the waves merge in LDS and
+// write one partial (max, sum, unnormalized output) per split; a second
+// kernel merges the splits of each sequence:
+//   M = max_j m_j,  out = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j.
+#include "common.h"
+
+namespace tpa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<uint16_t> {  // bf16 in, fp32 accumulate: v_mfma_f32_16x16x32_bf16
+    static constexpr int E = 8;
+    typedef bf16x8 Frag;
+    __device__ static Frag load(const uint16_t *p) {
+        uint4 v = *reinterpret_cast<const uint4 *>(p);
+        return __builtin_bit_cast(Frag, v);
+    }
+    __device__ static Frag pack(const float *x) {
+        uint4 v;
+        v.x = uint32_t(f32_to_bf16_rne(x[0])) | (uint32_t(f32_to_bf16_rne(x[1])) << 16);
+        v.y = uint32_t(f32_to_bf16_rne(x[2])) | (uint32_t(f32_to_bf16_rne(x[3])) << 16);
+        v.z = uint32_t(f32_to_bf16_rne(x[4])) | (uint32_t(f32_to_bf16_rne(x[5])) << 16);
+        v.w = uint32_t(f32_to_bf16_rne(x[6])) | (uint32_t(f32_to_bf16_rne(x[7])) << 16);
+        return __builtin_bit_cast(Frag, v);
+    }
+    // zero the slots whose flag bit is set
+    __device__ static Frag mask(Frag f, unsigned zero_bits) {
+        uint4 v = __builtin_bit_cast(uint4, f);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (zero_bits & (1u << e)) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        v.x = w[0];
+        v.y = w[1];
+        v.z = w[2];
+        v.w = w[3];
+        return __builtin_bit_cast(Frag, v);
+    }
+    __device__ static void load_gates(const uint16_t *p, float *g) {
+        uint2 v = *reinterpret_cast<const uint2 *>(p);
+        g[0] = __uint_as_float(v.x << 16);
+        g[1] = __uint_as_float(v.x & 0xffff0000u);
+        g[2] = __uint_as_float(v.y << 16);
+        g[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+    __device__ static float q_elem(const uint16_t *p, int64_t i) { return bf16_to_f32(p[i]); }
+    __device__ static floatx4 mma(Frag a, Frag b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mfma<float> {  // fp32 in, fp32 accumulate: v_mfma_f32_16x16x4_f32
+    static constexpr int E = 1;
+    typedef float Frag;
+    __device__ static Frag load(const float *p) { return *p; }
+    __device__ static Frag pack(const float *x) { return x[0]; }
+    __device__ static Frag mask(Frag f, unsigned zero_bits) { return (zero_bits & 1u) ? 0.0f : f; }
+    __device__ static void load_gates(const float *p, float *g) {
+        float4 v = *reinterpret_cast<const float4 *>(p);
+        g[0] = v.x;
+        g[1] = v.y;
+        g[2] = v.z;
+        g[3] = v.w;
+    }
+    __device__ static float q_elem(const float *p, int64_t i) { return p[i]; }
+    __device__ static floatx4 mma(Frag a, Frag b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+__device__ __forceinline__ float wave_max_across_groups(float x) {
+    // lanes l, l^16, l^32, l^48 hold the same head
+    x = fmaxf(x, __shfl_xor(x, 16, kWave));
+    x = fmaxf(x, __shfl_xor(x, 32, kWave));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum_across_groups(float x) {
+    x += __shfl_xor(x, 16, kWave);
+    x += __shfl_xor(x, 32, kWave);
+    return x;
+}
+
+template <typename T, int HP, int DP, int RH>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
+    using M = Mfma<T>;
+    constexpr int E = M::E;
+    constexpr int NB = HP / 16;           // head blocks (MFMA N)
+    constexpr int KBS = DP / (4 * E);     // score K blocks
+    constexpr int MBV = DP / 16;          // value M blocks
+    constexpr int KBV = kRows / (4 * E);  // value K blocks
+    constexpr int TOK = kRows / RH;       // tokens per cache block
+    constexpr int TPL = 4 / RH;           // tokens per lane per score row block
+    constexpr int ES = int(sizeof(T));
+    const Layout L = {HP, DP, RH, E, ES};
+    constexpr int64_t BLK = 2LL * kRows * (HP + DP);
+
+    __shared__ float sm_m[kWaves][HP];
+    __shared__ float sm_l[kWaves][HP];
+    __shared__ float sm_o[HP][DP + 4];
+
+    const int b = blockIdx.y;
+    const int split = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const int g = lane >> 4, c = lane & 15;
+
+    int len = p.seq_len[b];
+    len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
+    const int nblk = (len + TOK - 1) / TOK;
+    const int blk_begin = split * p.split_blocks;
+    if (blk_begin >= nblk) return;
+    const int blk_end = min(nblk, blk_begin + p.split_blocks);
+    const int64_t start = p.seq_start[b];
+    if (start < 0 || start % TOK != 0) return;  // the merge kernel reports it as NaN
+    const T *seq = reinterpret_cast<const T *>(p.cache) + (start / TOK) * BLK;
+
+    // query operand (B of the score contraction): lane holds q~[16 nb + c][4E kb + E g + e]
+    typename M::Frag qf[KBS][NB];
+    {
+        const T *qb = reinterpret_cast<const T *>(p.q) + int64_t(b) * p.h * p.d_h;
+#pragma unroll
+        for (int kb = 0; kb < KBS; ++kb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                float x[E];
+                const int head = 16 * nb + c;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int d = 4 * E * kb + E * g + e;
+                    x[e] = (head < p.h && d < p.d_h) ? M::q_elem(qb, int64_t(head) * p.d_h + d) : 0.0f;
+                }
+                qf[kb][nb] = M::pack(x);
+            }
+    }
+
+    floatx4 acc[MBV][NB];
+#pragma unroll
+    for (int mv = 0; mv < MBV; ++mv)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mv][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float run_m[NB], run_l[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        run_m[nb] = -INFINITY;
+        run_l[nb] = 0.f;
+    }
+
+    for (int blk = blk_begin + w; blk < blk_end; blk += kWaves) {
+        const T *bp = seq + int64_t(blk) * BLK;
+        // ---- loads (one contiguous wave-wide span each)
+        float ak[2][NB][4], av[2][NB][4];
+        typename M::Frag bk[2][KBS], bv[MBV][KBV];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                M::load_gates(bp + L.off_ak() + ((mb * NB + nb) * kWave + lane) * 4, ak[mb][nb]);
+                M::load_gates(bp + L.off_av() + ((mb * NB + nb) * kWave + lane) * 4, av[mb][nb]);
+            }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int kb = 0; kb < KBS; ++kb) bk[mb][kb] = M::load(bp + L.off_bk() + ((mb * KBS + kb) * kWave + lane) * E);
+#pragma unroll
+        for (int mv = 0; mv < MBV; ++mv)
+#pragma unroll
+            for (int q = 0; q < KBV; ++q) bv[mv][q] = M::load(bp + L.off_bv() + ((mv * KBV + q) * kWave + lane) * E);
+
+        const int valid = min(TOK, len - blk * TOK);  // tokens of this block inside the sequence
+
+        // ---- 1. score contraction
+        floatx4 u[2][NB];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                floatx4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < KBS; ++kb) a = M::mma(bk[mb][kb], qf[kb][nb], a);
+                u[mb][nb] = a;
+            }
+
+        // ---- 2.-4. gates, online softmax, value weights
+        float wv[2][NB][4];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            float z[2][TPL];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int t = 0; t < TPL; ++t) {
+                    float s = 0.f;
+#pragma unroll
+                    for (int r = 0; r < RH; ++r) s += ak[mb][nb][t * RH + r] * u[mb][nb][t * RH + r];
+                    const int tok = (16 * mb + 4 * g) / RH + t;
+                    z[mb][t] = tok < valid ? s * p.score_mul : -INFINITY;
+                    mx = fmaxf(mx, z[mb][t]);
+                }
+            mx = wave_max_across_groups(mx);
+            const float mn = fmaxf(run_m[nb], mx);
+            const float alpha = exp2f(run_m[nb] - mn);
+            run_m[nb] = mn;
+            run_l[nb] *= alpha;
+#pragma unroll
+            for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int t = 0; t < TPL; ++t) {
+                    const int tok = (16 * mb + 4 * g) / RH + t;
+                    const float pr = exp2f(z[mb][t] - mn);
+                    run_l[nb] += pr;
+#pragma unroll
+                    for (int r = 0; r < RH; ++r) wv[mb][nb][t * RH + r] = tok < valid ? pr * av[mb][nb][t * RH + r] : 0.f;
+                }
+        }
+
+        // rows beyond the sequence: their stored B_V may be anything, zero them
+        if (valid < TOK) {
+#pragma unroll
+            for (int q = 0; q < KBV; ++q) {
+                unsigned bits = 0;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int t = E * q + e;
+                    const int row = 16 * (t / 4) + 4 * g + (t % 4);
+                    if (row / RH >= valid) bits |= 1u << e;
+                }
+#pragma unroll
+                for (int mv = 0; mv < MBV; ++mv) bv[mv][q] = M::mask(bv[mv][q], bits);
+            }
+        }
+
+        // ---- 5. value contraction
+#pragma unroll
+        for (int q = 0; q < KBV; ++q)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                float x[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int t = E * q + e;
+                    x[e] = wv[t / 4][nb][t % 4];
+                }
+                const typename M::Frag wf = M::pack(x);
+#pragma unroll
+                for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] = M::mma(bv[mv][q], wf, acc[mv][nb]);
+            }
+    }
+
+    // ---- merge the waves of this work-group
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) run_l[nb] = wave_sum_across_groups(run_l[nb]);
+    if (g == 0) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            sm_m[w][16 * nb + c] = run_m[nb];
+            sm_l[w][16 * nb + c] = run_l[nb];
+        }
+    }
+    __syncthreads();
+    float wscale[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int head = 16 * nb + c;
+        float mm = sm_m[0][head];
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][head]);
+        wscale[nb] = run_m[nb] == -INFINITY ? 0.f : exp2f(run_m[nb] - mm);
+    }
+    for (int ww = 0; ww < kWaves; ++ww) {
+        if (w == ww) {
+#pragma unroll
+            for (int mv = 0; mv < MBV; ++mv)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float *dst = &sm_o[16 * nb + c][16 * mv + 4 * g + v];
+                        const float val = acc[mv][nb][v] * wscale[nb];
+                        *dst = ww == 0 ? val : *dst + val;
+                    }
+        }
+        __syncthreads();
+    }
+    // write the split's partial: O [HP][DP], (max, sum) [HP]
+    const int64_t part = int64_t(b) * p.n_split + split;
+    float *wo = p.ws_o + part * HP * DP;
+    for (int idx = threadIdx.x; idx < HP * DP / 4; idx += kThreads) {
+        const int head = idx / (DP / 4), d4 = idx % (DP / 4);
+        const float *src = &sm_o[head][4 * d4];
+        *reinterpret_cast<float4 *>(wo + head * DP + 4 * d4) = make_float4(src[0], src[1], src[2], src[3]);
+    }
+    for (int head = threadIdx.x; head < HP; head += kThreads) {
+        float mm = sm_m[0][head];
+        for (int ww = 1; ww < kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][head]);
+        float ll = 0.f;
+        for (int ww = 0; ww < kWaves; ++ww)
+            ll += sm_m[ww][head] == -INFINITY ? 0.f : sm_l[ww][head] * exp2f(sm_m[ww][head] - mm);
+        p.ws_ml[(part * HP + head) * 2 + 0] = mm;
+        p.ws_ml[(part * HP + head) * 2 + 1] = ll;
+    }
+}
+
+// Second pass: merge the per-split partials of one sequence.
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int HP, int DP, int TOK) {
+    const int b = blockIdx.x;
+    int len = p.seq_len[b];
+    len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
+    const int nblk = (len + TOK - 1) / TOK;
+    const int n_valid = (nblk + p.split_blocks - 1) / p.split_blocks;
+    const int64_t start = p.seq_start[b];
+    const bool misaligned = start < 0 || start % TOK != 0;
+    float *out = p.out + int64_t(b) * p.h * p.d_h;
+    const int D4 = (p.d_h + 3) / 4;
+    for (int idx = threadIdx.x; idx < p.h * D4; idx += blockDim.x) {
+        const int head = idx / D4, d0 = 4 * (idx % D4);
+        float o[4] = {0.f, 0.f, 0.f, 0.f};
+        if (misaligned) {
+            o[0] = o[1] = o[2] = o[3] = __builtin_nanf("");
+        } else if (n_valid > 0) {
+            float mm = -INFINITY;
+            for (int j = 0; j < n_valid; ++j)
+                mm = fmaxf(mm, p.ws_ml[((int64_t(b) * p.n_split + j) * HP + head) * 2]);
+            float ll = 0.f;
+            for (int j = 0; j < n_valid; ++j) {
+                const int64_t part = int64_t(b) * p.n_split + j;
+                const float mj = p.ws_ml[(part * HP + head) * 2];
+                const float sj = mj == -INFINITY ? 0.f : exp2f(mj - mm);
+                ll += sj * p.ws_ml[(part * HP + head) * 2 + 1];
+                const float4 v = *reinterpret_cast<const float4 *>(p.ws_o + (part * HP + head) * DP + d0);
+                o[0] += sj * v.x;
+                o[1] += sj * v.y;
+                o[2] += sj * v.z;
+                o[3] += sj * v.w;
+            }
+            const float inv = p.out_mul / ll;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] *= inv;
+        }
+        for (int k = 0; k < 4 && d0 + k < p.d_h; ++k) out[head * p.d_h + d0 + k] = o[k];
+    }
+}
+
+template <typename T, int HP, int DP, int RH>
+hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
+    hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH>), dim3(p.n_split, p.batch), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename T, int HP, int DP>
+hipError_t launch_split_rank(int RH, const DecodeParams &p, hipStream_t s) {
+    switch (RH) {
+        case 1: return launch_split<T, HP, DP, 1>(p, s);
+        case 2: return launch_split<T, HP, DP, 2>(p, s);
+        case 4: return launch_split<T, HP, DP, 4>(p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Compiled (element type, padded heads, padded head dim) combinations.
+#define TPA_DECODE_SHAPES(X)                                                                            \
+    X(uint16_t, 2, 16, 32) X(uint16_t, 2, 16, 64) X(uint16_t, 2, 16, 128) X(uint16_t, 2, 32, 32)     \
+        X(uint16_t, 2, 32, 64) X(uint16_t, 2, 32, 128) X(uint16_t, 2, 64, 32) X(uint16_t, 2, 64, 64) \
+            X(float, 4, 16, 16) X(float, 4, 16, 32) X(float, 4, 16, 64) X(float, 4, 16, 128)         \
+                X(float, 4, 32, 32) X(float, 4, 32, 64) X(float, 4, 32, 128)
+
+}  // namespace
+
+bool decode_supported(const Layout &L) {
+#define X(T, ES, HP_, DP_) \
+    if (L.es == ES && L.HP == HP_ && L.DP == DP_) return true;
+    TPA_DECODE_SHAPES(X)
+#undef X
+    return false;
+}
+
+hipError_t launch_decode(const Layout &L, const DecodeParams &p, hipStream_t s) {
+    hipError_t e = hipErrorInvalidValue;
+    bool found = false;
+#define X(T, ES, HP_, DP_)                                         \
+    if (!found && L.es == ES && L.HP == HP_ && L.DP == DP_) {       \
+        found = true;                                              \
+        e = launch_split_rank<T, HP_, DP_>(L.RH, p, s);            \
+    }
+    TPA_DECODE_SHAPES(X)
+#undef X
+    if (!found || e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(p.batch), dim3(256), 0, s, p, L.HP, L.DP, L.tok_per_block());
+    return hipGetLastError();
+}
+
+}  // namespace tpa

@@ -1,0 +1,171 @@
+/*
+ * tpa.h -- C ABI of libtpa: attention evaluated directly over a factorized
+ * KV cache in Tensor Product Attention (TPA) form, on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method ("Tensor Product Attention Is All You Need", paper notes page):
+ *   - Key design, tensor product decomposition: each token's key is
+ *     K_t = (1/R_K) A_K(x_t)^T B_K(x_t) with a head factor A_K in R^{R_K x h}
+ *     and a feature factor B_K in R^{R_K x d_h}; V likewise with R_V.  The
+ *     cache keeps only A_K, B_K, A_V, B_V: (R_K + R_V)(h + d_h) elements per
+ *     token instead of 2 h d_h.
+ *   - Key design, RoPE compatibility (Theorem 3.1): rotating only the B
+ *     factors by position keeps RoPE's relative-position property,
+ *     Q~_t K~_s^T = Q_t T_{t-s} K_s^T.
+ *   - Key design, FlashTPA: attention is computed from the factors without
+ *     ever building the full K or V.
+ * Readings where the pages are silent: RoPE uses RoFormer pairs (2j, 2j+1)
+ * with theta_j = rope_base^(-2j/d_h) over all d_h features; the softmax
+ * scale defaults to 1/sqrt(d_h) and 1/R_K, 1/R_V are applied inside.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked [host].  Element arrays hold
+ *     `dims->dtype` elements (fp32 or bf16); outputs are fp32.
+ *   - The caller owns every buffer (allocate with hipMalloc or a framework
+ *     allocator).  The library allocates nothing, keeps no mutable global
+ *     state, never synchronizes, and enqueues its kernels on `stream`
+ *     (a hipStream_t; NULL = the null stream).  Completion is asynchronous.
+ *   - Every call returns a tpa_status.  All argument checks run on the host
+ *     before any HIP call; a rejected call launches nothing.  TPA_ERR_HIP
+ *     reports a failed launch (hipGetLastError).  Values held in device
+ *     memory (slots, lengths) cannot be checked on the host; what the
+ *     kernels do with bad ones is stated per entry point.
+ *
+ * Cache layout (opaque; written by tpa_cache_append, read back by
+ * tpa_cache_read).  Tokens are grouped into blocks of tpa_block_tokens()
+ * consecutive slots; inside a block the factors are stored in the order the
+ * decode kernel's matrix-core operands consume them, so every load is a
+ * contiguous 1 KiB wave read.  A sequence occupies consecutive slots
+ * starting at a block boundary; slot order is position order.
+ */
+#ifndef TPA_H
+#define TPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TPA_ABI_VERSION 1
+
+typedef enum tpa_status {
+    TPA_OK = 0,
+    TPA_ERR_ARG = 1,         /* null pointer, bad dimension or count, misaligned size */
+    TPA_ERR_UNSUPPORTED = 2, /* valid shape with no compiled kernel (see tpa_supported) */
+    TPA_ERR_CAPACITY = 3,    /* a slot at or beyond the cache capacity */
+    TPA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than tpa_decode_workspace_bytes */
+    TPA_ERR_HIP = 5          /* a kernel launch failed */
+} tpa_status;
+
+typedef enum tpa_dtype { TPA_F32 = 0, TPA_BF16 = 1 } tpa_dtype;
+
+/* Problem statement of one attention layer (TPA notes page, tensor product
+ * decomposition and RoPE compatibility):
+ *   h          number of heads, 1..64
+ *   d_h        head dimension, even, 2..256
+ *   R_K, R_V   factor ranks of K and V, 1..4
+ *   dtype      element type of factors, queries and the cache
+ *   rope_base  RoPE base (theta_j = rope_base^(-2j/d_h)), > 0 */
+typedef struct tpa_dims {
+    int32_t h;
+    int32_t d_h;
+    int32_t R_K;
+    int32_t R_V;
+    int32_t dtype;
+    int32_t reserved; /* must be 0 */
+    double rope_base;
+} tpa_dims;
+
+int32_t tpa_abi_version(void);
+
+/* Human-readable name of a status code.  Never NULL. */
+const char *tpa_status_string(int32_t status);
+
+/* 1 if kernels exist for these dims, 0 if not (also 0 for invalid dims). */
+int32_t tpa_supported(const tpa_dims *dims);
+
+/* Tokens per cache block: sequences must start at a multiple of it.  <= 0 on bad dims. */
+int32_t tpa_block_tokens(const tpa_dims *dims);
+
+/* Bytes of device memory a cache of capacity_tokens slots needs (capacity is
+ * rounded up to whole blocks).  For h a multiple of 16 and d_h a multiple of
+ * 32 (bf16) or 16 (fp32), and R_K = R_V in {1, 2, 4}, this is exactly
+ * capacity * (R_K + R_V)(h + d_h) * sizeof(element): the factor-only size of
+ * the tensor product decomposition paragraph.  Other shapes are padded.
+ * -1 on bad dims or a negative capacity. */
+int64_t tpa_cache_bytes(const tpa_dims *dims, int64_t capacity_tokens);
+
+/* Write factors of n_kv tokens into the cache and, optionally, rotate query rows.
+ * (TPA notes page: the cache holds only A_K, B_K, A_V, B_V; RoPE compatibility:
+ * B_K is rotated by the token's position, and so are query rows.)
+ *   cache, capacity_tokens   the cache (tpa_cache_bytes(dims, capacity_tokens) bytes)
+ *   slot[n_kv]     int64, cache slot of each token; a slot < 0 or >= capacity is skipped
+ *   kv_pos[n_kv]   int32, position of each token (>= 0)
+ *   slot_hi        [host] an upper bound on max(slot)+1; must be <= capacity_tokens
+ *   A_K [n_kv][R_K][h], B_K [n_kv][R_K][d_h], A_V [n_kv][R_V][h], B_V [n_kv][R_V][d_h]
+ *                  unrotated factors, contiguous; B_K is rotated on the way in
+ *   n_q            number of query tokens to rotate (0: none; q pointers may then be NULL)
+ *   q_rows         rows per query token: h for a full query, or R_Q for a B_Q factor
+ *   q_pos[n_q]     int32 positions
+ *   q_in, q_out    [n_q][q_rows][d_h]; q_out = RoPE(q_in); q_out may equal q_in
+ * Angles are computed in fp64, rotations in fp64, rounded once to dtype. */
+int32_t tpa_cache_append(const tpa_dims *dims, void *cache, int64_t capacity_tokens, int64_t n_kv,
+                         const int64_t *slot, const int32_t *kv_pos, int64_t slot_hi, const void *A_K,
+                         const void *B_K, const void *A_V, const void *B_V, int64_t n_q, int32_t q_rows,
+                         const int32_t *q_pos, const void *q_in, void *q_out, void *stream);
+
+/* Read n tokens back out of the cache in natural layout (B_K as stored, i.e.
+ * rotated).  Same array shapes as tpa_cache_append; slots out of range read as
+ * zeros.  For tests and cache export. */
+int32_t tpa_cache_read(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int64_t n,
+                       const int64_t *slot, void *A_K, void *B_K, void *A_V, void *B_V, void *stream);
+
+/* Workspace bytes tpa_decode needs for (batch, max_len, split_tokens).  -1 on bad arguments. */
+int64_t tpa_decode_workspace_bytes(const tpa_dims *dims, int32_t batch, int32_t max_len, int32_t split_tokens);
+
+/* Split-sequence decode: one query row per sequence attends to all of its
+ * cached tokens, computed from the factors (TPA notes page, FlashTPA: no full
+ * K/V is built).  Per sequence b and head i:
+ *     out[b][i] = sum_s softmax_s(scale * q~_b,i . K~_s[i,:]) V_s[i,:]
+ * over s = 0 .. seq_len[b]-1, with K~_s, V_s from the cached factors.
+ *   seq_start[batch]  int64 first slot of each sequence; must be a multiple of
+ *                     tpa_block_tokens() (a misaligned sequence gets NaN output)
+ *   seq_len[batch]    int32 cached tokens of each sequence (0 gives a zero output;
+ *                     values above max_len are clamped to max_len)
+ *   max_len           [host] >= every seq_len; sizes the launch
+ *   q_rot [batch][h][d_h]  queries already rotated to their positions (tpa_cache_append)
+ *   scale             softmax scale; <= 0 selects 1/sqrt(d_h)
+ *   out [batch][h][d_h]    fp32
+ *   split_tokens      tokens per split work unit; 0 lets the library choose
+ *   workspace         >= tpa_decode_workspace_bytes(dims, batch, max_len, split_tokens)
+ *                     bytes of device memory, 256-byte aligned; holds per-split partials
+ *                     (running max, sum, unnormalized output) between the two passes.
+ * Slots of a sequence must lie inside the cache (seq_start + max_len <= capacity). */
+int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
+                   const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *q_rot,
+                   float scale, float *out, int32_t split_tokens, void *workspace, int64_t workspace_bytes,
+                   void *stream);
+
+/* Causal chunked prefill: chunk_len query rows per sequence attend to the
+ * sequence's cached context and to the chunk's own tokens up to and including
+ * their own (the chunk's factors must already be in the cache, appended at
+ * slots seq_start[b] + ctx_len[b] + j).  Row j of sequence b sees slots
+ * seq_start[b] + 0 .. seq_start[b] + ctx_len[b] + j.  K~ and V for one head
+ * are rebuilt from the factors on chip, never in device memory.
+ *   ctx_len[batch]   int32 cached tokens before the chunk (<= max_ctx)
+ *   max_ctx          [host] >= every ctx_len
+ *   chunk_len        [host] rows per sequence
+ *   q_rot [batch][chunk_len][h][d_h]  rotated query rows (row j at position ctx_len[b] + j)
+ *   out   [batch][chunk_len][h][d_h]  fp32
+ * Currently bf16 only (TPA_ERR_UNSUPPORTED for fp32). */
+int32_t tpa_prefill_chunk(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
+                          const int64_t *seq_start, const int32_t *ctx_len, int32_t max_ctx, int32_t chunk_len,
+                          const void *q_rot, float scale, float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPA_H */

@@ -1,0 +1,207 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/tpa.h, sizes caches and workspaces as documented, and
+rejects bad arguments on the host before any HIP call.
+
+Every call here is one the host checks reject, so nothing is ever launched,
+even if this file runs on a machine with a GPU.
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import factorized_kv_cache_tpa_amd as tpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpa.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tpa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tpa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("tpa_cache_append", "tpa_decode", "tpa_prefill_chunk"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_covers_every_declared_symbol():
+    for name in declared_functions():
+        assert hasattr(tpa, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    assert tpa.tpa_abi_version() == 1
+    for code, word in [(0, "TPA_OK"), (1, "ARG"), (2, "UNSUPPORTED"), (3, "CAPACITY"), (4, "WORKSPACE"),
+                       (5, "HIP")]:
+        assert word in tpa.tpa_status_string(code)
+    assert "UNKNOWN" in tpa.tpa_status_string(99)
+
+
+def _d(**kw):
+    base = dict(h=32, d_h=128, R_K=1, R_V=1, dtype="bf16", rope_base=1e4)
+    base.update(kw)
+    return tpa.Dims(**base)
+
+
+def test_page_example_cache_size_is_factor_only():
+    """R_K=R_V=1, h=32, d_h=128: 320 elements per token (TPA notes page), i.e. 640 bytes in bf16."""
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "cache_size_page.json")))
+    d = _d(h=g["h"], d_h=g["d_h"], R_K=g["R_K"], R_V=g["R_V"])
+    tok = tpa.tpa_block_tokens(d)
+    assert tpa.tpa_cache_bytes(d, tok) == tok * g["tpa_elements_per_token"] * 2
+    assert tpa.tpa_cache_bytes(d, 4096) == 4096 * 640
+
+
+@pytest.mark.parametrize("h,d,R,dtype,per_token_bytes", [
+    (32, 128, 1, "bf16", 640), (16, 64, 2, "bf16", 640), (32, 128, 2, "bf16", 1280), (32, 128, 4, "bf16", 2560),
+    (16, 16, 1, "f32", 256), (32, 64, 2, "f32", 1536)])
+def test_cache_bytes_exact_for_unpadded_shapes(h, d, R, dtype, per_token_bytes):
+    dims = _d(h=h, d_h=d, R_K=R, R_V=R, dtype=dtype)
+    es = 2 if dtype == "bf16" else 4
+    assert per_token_bytes == (R + R) * (h + d) * es
+    tok = tpa.tpa_block_tokens(dims)
+    assert tok == 32 // R
+    assert tpa.tpa_cache_bytes(dims, 10 * tok) == 10 * tok * per_token_bytes
+    # capacity rounds up to whole blocks
+    assert tpa.tpa_cache_bytes(dims, 10 * tok + 1) == 11 * tok * per_token_bytes
+
+
+def test_padded_shapes_round_heads_and_dims():
+    # h=4 pads to 16 heads; fp32 d_h=16 needs no padding; R=1 -> 32 tokens per block
+    d = _d(h=4, d_h=16, dtype="f32")
+    assert tpa.tpa_cache_bytes(d, 64) == 64 * 2 * (16 + 16) * 4
+    # R_K=1, R_V=3 pads both ranks to 4
+    d = _d(R_K=1, R_V=3)
+    assert tpa.tpa_block_tokens(d) == 8
+    assert tpa.tpa_cache_bytes(d, 8) == 8 * 2 * 4 * (32 + 128) * 2
+
+
+def test_supported_set():
+    assert tpa.tpa_supported(_d())
+    assert tpa.tpa_supported(_d(h=16, d_h=64, R_K=2, R_V=2))
+    assert tpa.tpa_supported(_d(R_K=4, R_V=4))
+    assert tpa.tpa_supported(_d(h=4, d_h=16, dtype="f32"))
+    assert not tpa.tpa_supported(_d(h=64, d_h=256))  # valid but not compiled
+    assert not tpa.tpa_supported(_d(d_h=7))           # invalid
+
+
+@pytest.mark.parametrize("kw", [dict(h=0), dict(h=65), dict(d_h=0), dict(d_h=7), dict(d_h=258), dict(R_K=0),
+                                dict(R_V=5), dict(dtype=7), dict(rope_base=0.0), dict(rope_base=-1.0),
+                                dict(rope_base=float("inf"))])
+def test_bad_dims_rejected(lib, kw):
+    d = _d(**{k: v for k, v in kw.items() if k != "dtype"})
+    if "dtype" in kw:
+        d.dtype = kw["dtype"]
+    assert lib.tpa_block_tokens(ctypes.byref(d)) <= 0
+    assert lib.tpa_cache_bytes(ctypes.byref(d), 64) == -1
+    assert lib.tpa_decode_workspace_bytes(ctypes.byref(d), 1, 64, 0) == -1
+    st = lib.tpa_decode(ctypes.byref(d), FAKE, 64, 1, FAKE, FAKE, 64, FAKE, 0.0, FAKE, 0, FAKE, 1 << 20, None)
+    assert st == 1
+
+
+def test_reserved_field_must_be_zero(lib):
+    d = _d()
+    d.reserved = 1
+    assert lib.tpa_supported(ctypes.byref(d)) == 0
+
+
+def test_null_dims_rejected(lib):
+    assert lib.tpa_cache_bytes(None, 10) == -1
+    assert lib.tpa_decode(None, FAKE, 64, 1, FAKE, FAKE, 64, FAKE, 0.0, FAKE, 0, FAKE, 1 << 20, None) == 1
+
+
+def test_unsupported_dims_status(lib):
+    d = _d(h=64, d_h=256)
+    st = lib.tpa_decode(ctypes.byref(d), FAKE, 64, 1, FAKE, FAKE, 64, FAKE, 0.0, FAKE, 0, FAKE, 1 << 20, None)
+    assert st == 2
+    st = lib.tpa_cache_append(ctypes.byref(d), FAKE, 64, 1, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 0, 0, None,
+                              None, None, None)
+    assert st == 2
+
+
+def test_append_argument_checks(lib):
+    d = _d()
+    ref = ctypes.byref(d)
+    # slot_hi beyond capacity
+    assert lib.tpa_cache_append(ref, FAKE, 64, 1, FAKE, FAKE, 65, FAKE, FAKE, FAKE, FAKE, 0, 0, None, None, None,
+                                None) == 3
+    # null factor pointer
+    assert lib.tpa_cache_append(ref, FAKE, 64, 1, FAKE, FAKE, 1, None, FAKE, FAKE, FAKE, 0, 0, None, None, None,
+                                None) == 1
+    # negative counts
+    assert lib.tpa_cache_append(ref, FAKE, 64, -1, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 0, 0, None, None, None,
+                                None) == 1
+    # queries without rows / pointers
+    assert lib.tpa_cache_append(ref, FAKE, 64, 0, None, None, 0, None, None, None, None, 2, 0, FAKE, FAKE, FAKE,
+                                None) == 1
+    assert lib.tpa_cache_append(ref, FAKE, 64, 0, None, None, 0, None, None, None, None, 2, 32, None, FAKE, FAKE,
+                                None) == 1
+    # nothing to do is OK and launches nothing
+    assert lib.tpa_cache_append(ref, None, 0, 0, None, None, 0, None, None, None, None, 0, 0, None, None, None,
+                                None) == 0
+
+
+def test_decode_argument_checks(lib):
+    d = _d()
+    ref = ctypes.byref(d)
+    need = lib.tpa_decode_workspace_bytes(ref, 16, 4096, 0)
+    assert need > 0
+    # batch 0 is a no-op
+    assert lib.tpa_decode(ref, None, 0, 0, None, None, 0, None, 0.0, None, 0, None, 0, None) == 0
+    # null pointers
+    assert lib.tpa_decode(ref, None, 8192, 16, FAKE, FAKE, 4096, FAKE, 0.0, FAKE, 0, FAKE, need, None) == 1
+    assert lib.tpa_decode(ref, FAKE, 8192, 16, FAKE, FAKE, 4096, FAKE, 0.0, None, 0, FAKE, need, None) == 1
+    # max_len beyond capacity
+    assert lib.tpa_decode(ref, FAKE, 1024, 16, FAKE, FAKE, 4096, FAKE, 0.0, FAKE, 0, FAKE, need, None) == 3
+    # workspace too small / missing / misaligned
+    assert lib.tpa_decode(ref, FAKE, 8192, 16, FAKE, FAKE, 4096, FAKE, 0.0, FAKE, 0, FAKE, need - 1, None) == 4
+    assert lib.tpa_decode(ref, FAKE, 8192, 16, FAKE, FAKE, 4096, FAKE, 0.0, FAKE, 0, None, need, None) == 4
+    assert lib.tpa_decode(ref, FAKE, 8192, 16, FAKE, FAKE, 4096, FAKE, 0.0, FAKE, 0, ctypes.c_void_p(0x1008),
+                          need, None) == 4
+    # bad batch / lengths / split / scale
+    assert lib.tpa_decode(ref, FAKE, 8192, -1, FAKE, FAKE, 4096, FAKE, 0.0, FAKE, 0, FAKE, need, None) == 1
+    assert lib.tpa_decode(ref, FAKE, 8192, 16, FAKE, FAKE, -5, FAKE, 0.0, FAKE, 0, FAKE, need, None) == 1
+    assert lib.tpa_decode(ref, FAKE, 8192, 16, FAKE, FAKE, 4096, FAKE, 0.0, FAKE, -3, FAKE, need, None) == 1
+    assert lib.tpa_decode(ref, FAKE, 8192, 16, FAKE, FAKE, 4096, FAKE, float("nan"), FAKE, 0, FAKE, need,
+                          None) == 1
+
+
+def test_workspace_grows_with_splits(lib):
+    d = _d(R_K=2, R_V=2)
+    ref = ctypes.byref(d)
+    a = lib.tpa_decode_workspace_bytes(ref, 4, 131072, 4096)
+    b = lib.tpa_decode_workspace_bytes(ref, 4, 131072, 1024)
+    assert 0 < a < b
+    # per split: 32 heads x (128 outputs + max + sum) fp32, 256-byte aligned regions
+    n_split = 131072 // 1024
+    assert b >= 4 * n_split * 32 * (128 + 2) * 4
+    assert lib.tpa_decode_workspace_bytes(ref, -1, 10, 0) == -1
+
+
+def test_prefill_argument_checks(lib):
+    d = _d(R_K=4, R_V=4)
+    ref = ctypes.byref(d)
+    assert lib.tpa_prefill_chunk(ref, None, 0, 0, None, None, 0, 0, None, 0.0, None, None) == 0
+    assert lib.tpa_prefill_chunk(ref, FAKE, 4096, 8, FAKE, FAKE, 2048, 512, None, 0.0, FAKE, None) == 1
+    assert lib.tpa_prefill_chunk(ref, FAKE, 2048, 8, FAKE, FAKE, 2048, 512, FAKE, 0.0, FAKE, None) == 3
+    assert lib.tpa_prefill_chunk(ref, FAKE, 4096, 8, FAKE, FAKE, -1, 512, FAKE, 0.0, FAKE, None) == 1
+    f32 = _d(h=32, d_h=128, R_K=1, R_V=1, dtype="f32")
+    assert lib.tpa_prefill_chunk(ctypes.byref(f32), FAKE, 4096, 8, FAKE, FAKE, 2048, 512, FAKE, 0.0, FAKE,
+                                 None) == 2

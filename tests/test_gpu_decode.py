@@ -1,0 +1,122 @@
+"""GPU parity of tpa_decode against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tpa_inputs as ti
+from tests.gpu_cases import DecodeSetup, assert_close, case_workload, f64, random_sequences, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_all(setup: DecodeSetup, out: np.ndarray, what: str, scale=None):
+    ref = np.stack([setup.oracle(b, scale) for b in range(setup.batch)])
+    assert_close(out, ref, setup.w.dtype, what)
+
+
+def test_tiny_fp32_workload():
+    """h=4, d_h=16, R=1, 64 cached tokens, query at position 64, fp32: tolerance 1e-5."""
+    w = ti.get("c1")
+    say("case: tiny fp32 decode workload")
+    s = DecodeSetup(w, ti.decode_batch(w))
+    _check_all(s, s.run(), "tiny fp32")
+
+
+@pytest.mark.parametrize("h,d_h,R_K,R_V,dtype", [
+    (32, 128, 1, 1, ti.BF16), (32, 128, 2, 2, ti.BF16), (32, 128, 4, 4, ti.BF16), (16, 64, 2, 2, ti.BF16),
+    (16, 64, 1, 1, ti.BF16), (32, 64, 1, 3, ti.BF16), (4, 16, 1, 1, ti.F32), (16, 32, 2, 2, ti.F32),
+    (32, 128, 3, 1, ti.F32), (20, 48, 2, 2, ti.BF16), (6, 40, 1, 2, ti.F32)])
+@pytest.mark.parametrize("q_scale", [1.0, 12.0])
+def test_small_shapes_ragged(h, d_h, R_K, R_V, dtype, q_scale):
+    """Several blocks per split and a ragged tail; q_scale 12 sharpens the softmax."""
+    w = case_workload(h, d_h, R_K, R_V, dtype)
+    lens = [1, 7, 33, 100, 257, 600]
+    say(f"case: decode h={h} d_h={d_h} R_K={R_K} R_V={R_V} {dtype} q_scale={q_scale}")
+    s = DecodeSetup(w, random_sequences(w, lens, q_scale=q_scale, seed=h * 31 + d_h))
+    for split in (0, 16, 64):
+        _check_all(s, s.run(split_tokens=split), f"split_tokens={split}")
+
+
+def test_split_size_invariance_and_determinism():
+    w = case_workload(32, 128, 2, 2)
+    s = DecodeSetup(w, random_sequences(w, [3000, 1234, 17], q_scale=8.0, seed=5))
+    outs = {split: s.run(split_tokens=split) for split in (0, 16, 32, 128, 512, 4096)}
+    ref = outs[0]
+    for split, o in outs.items():
+        np.testing.assert_allclose(o, ref, rtol=0, atol=2e-6, err_msg=f"split {split}")
+    again = s.run(split_tokens=0)
+    assert np.array_equal(again, ref), "two identical calls differ"
+
+
+def test_explicit_scale():
+    w = case_workload(16, 64, 1, 1)
+    s = DecodeSetup(w, random_sequences(w, [77, 300], q_scale=2.0, seed=9))
+    _check_all(s, s.run(scale=0.3), "scale=0.3", scale=0.3)
+
+
+def test_empty_sequence_and_clamped_length():
+    w = case_workload(32, 128, 1, 1)
+    seqs = random_sequences(w, [0, 50, 64], seed=11)
+    s = DecodeSetup(w, seqs)
+    out = s.run()
+    assert np.all(out[0] == 0.0)
+    assert_close(out[1:], np.stack([s.oracle(1), s.oracle(2)]), w.dtype, "non-empty rows")
+
+
+def test_misaligned_start_gives_nan():
+    w = case_workload(32, 128, 1, 1)
+    s = DecodeSetup(w, random_sequences(w, [40, 40], seed=12))
+    bad = s.cache.seq_start.clone()
+    bad[1] += 1
+    out = s.run(seq_start=bad)
+    assert np.all(np.isnan(out[1]))
+    assert_close(out[0], s.oracle(0), w.dtype, "aligned row")
+
+
+def test_cache_tail_garbage_is_ignored():
+    """The cache is pre-filled with NaN bit patterns; tokens past seq_len in a block must not leak in."""
+    w = case_workload(32, 128, 4, 4)
+    seqs = random_sequences(w, [13, 29], seed=13)
+    s = DecodeSetup(w, seqs)
+    # attend to fewer tokens than were appended: rows after seq_len hold real data, rows after that NaN
+    short = torch.tensor([5, 21], dtype=torch.int32, device="cuda")
+    out = s.run(seq_len=short)
+    for b, n in enumerate([5, 21]):
+        sq = seqs[b]
+        sub = ti.Sequence(sq.A_K[:n], sq.B_K[:n], sq.A_V[:n], sq.B_V[:n], sq.q)
+        # the query was rotated at the appended length, so the oracle places it there too
+        ref = oracle.attention(f64(sub.A_K, w.dtype), f64(sub.B_K, w.dtype), f64(sub.A_V, w.dtype),
+                               f64(sub.B_V, w.dtype), np.arange(n), f64(sq.q, w.dtype), [len(sq.A_K)], [n],
+                               w.rope_base)[0]
+        assert_close(out[b], ref, w.dtype, f"seq {b} first {n} tokens")
+
+
+# ---- the measured workloads at full size ------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_full_size_decode_all_sequences(name):
+    w = ti.get(name)
+    say(f"case: full-size {w.name}")
+    s = DecodeSetup(w, ti.decode_batch(w))
+    _check_all(s, s.run(), w.name)
+
+
+def test_full_size_long_context():
+    w = ti.get("c4")
+    say(f"case: full-size {w.name}")
+    s = DecodeSetup(w, ti.decode_batch(w))
+    _check_all(s, s.run(), w.name)
+
+
+def test_full_size_ragged_decode_sampled():
+    """128 ragged sequences on the GPU in the benchmark's launch configuration; 8 checked by the oracle."""
+    w = ti.get("c5")
+    say(f"case: full-size ragged decode {w.name}")
+    lens = ti.decode_lengths(w)
+    s = DecodeSetup(w, ti.decode_batch(w))
+    out = s.run()
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 1, 63, 64, 126, 127})
+    ref = np.stack([s.oracle(b) for b in pick])
+    assert_close(out[pick], ref, w.dtype, f"sampled sequences {pick}")
+    assert np.all(np.isfinite(out))

@@ -1,0 +1,47 @@
+"""GPU parity of tpa_prefill_chunk (causal chunk over a factor cache) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import tpa_inputs as ti
+from tests.gpu_cases import (DecodeSetup, PrefillSetup, assert_close, case_workload, random_sequences, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("h,d_h,R", [(32, 128, 4), (32, 128, 1), (16, 64, 2), (20, 48, 3)])
+@pytest.mark.parametrize("ctx,chunk", [([0, 45, 300], 70), ([64, 2], 160), ([257], 129)])
+@pytest.mark.parametrize("q_scale", [1.0, 10.0])
+def test_small_chunks(h, d_h, R, ctx, chunk, q_scale):
+    w = case_workload(h, d_h, R, R)
+    say(f"case: prefill h={h} d_h={d_h} R={R} ctx={ctx} chunk={chunk} q_scale={q_scale}")
+    seqs = random_sequences(w, [c + chunk for c in ctx], n_q=chunk, q_scale=q_scale, seed=h + chunk)
+    s = PrefillSetup(w, seqs, ctx)
+    out = s.run()
+    ref = np.stack([s.oracle(b) for b in range(len(seqs))])
+    assert_close(out, ref, w.dtype, "all rows")
+
+
+def test_prefill_rows_match_gpu_decode():
+    """Chunk row j equals a decode over the first ctx + j + 1 tokens with the query at position ctx + j."""
+    w = case_workload(32, 128, 2, 2)
+    ctx, chunk = 90, 40
+    (seq,) = random_sequences(w, [ctx + chunk], n_q=chunk, q_scale=6.0, seed=21)
+    pre = PrefillSetup(w, [seq], [ctx]).run()[0]
+    rows = [0, 1, 17, 39]
+    subs = [ti.Sequence(seq.A_K[:ctx + j + 1], seq.B_K[:ctx + j + 1], seq.A_V[:ctx + j + 1],
+                        seq.B_V[:ctx + j + 1], seq.q[j:j + 1]) for j in rows]
+    dec = DecodeSetup(w, subs, q_positions=[ctx + j for j in rows]).run()
+    assert_close(pre[rows], dec, w.dtype, "prefill rows vs decodes")
+
+
+def test_full_size_prefill_sampled_rows():
+    """8 sequences x (2048 cached + 512-row causal chunk), h=32, d_h=128, R=4; oracle on sampled rows."""
+    w = ti.get("c5")
+    say(f"case: full-size prefill of {w.name}")
+    seqs = ti.prefill_batch(w)
+    s = PrefillSetup(w, seqs, [w.prefill_ctx] * w.prefill_batch)
+    out = s.run()
+    assert np.all(np.isfinite(out))
+    rows = np.array([0, 1, 31, 32, 127, 128, 255, 256, 383, 384, 510, 511])
+    for b in (0, 3, 7):
+        assert_close(out[b][rows], s.oracle(b, rows=rows), w.dtype, f"seq {b} rows")
