@@ -1,0 +1,274 @@
+"""Benchmark of decode over a TPA factor cache on one MI355X.
+
+One step = one decode step of the whole hot path for a batch:
+  tpa_cache_append  (the step's new token per sequence: B_K rotated and stored;
+                     the step's query rows rotated)
+  tpa_decode        (split-sequence attention over the cached factors + merge)
+on the workload "decode_b16_h32_d128_r1_n4096": 16 sequences x 4096 cached
+tokens, h=32, d_h=128, R_K=R_V=1, bf16 factors, RoPE base 10000, synthetic
+seeded inputs.  The cache is replicated and the replicas are visited in turn so
+every step streams its factors from HBM rather than from the 256 MB
+last-level cache.
+
+Printed: one JSON line with the metric (cached tokens/s), the decode kernel's
+achieved HBM bandwidth against the 8 TB/s peak, the other measured workloads
+(decode shapes and the causal prefill chunk against the bf16 matrix-core
+peak), and the fp64 CPU oracle timed on the host as a reference baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
+MALL_BYTES = 256 << 20
+MAIN = "c2"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def decode_bytes(w, lens) -> int:
+    """Algorithmic bytes of one decode: the factor stream plus the query read and the fp32 output write."""
+    es = 2 if w.dtype == "bf16" else 4
+    per_tok = (w.R_K + w.R_V) * (w.h + w.d_h) * es
+    return int(np.sum(lens)) * per_tok + len(lens) * w.h * w.d_h * (es + 4)
+
+
+class DecodeBench:
+    """Cache replicas + per-step buffers for one decode workload."""
+
+    def __init__(self, name: str, min_bytes: int):
+        import torch
+        import factorized_kv_cache_tpa_amd as tpa
+        import tpa_inputs as ti
+        from factorized_kv_cache_tpa_amd.cache import FactorCache, to_device
+
+        self.torch, self.tpa = torch, tpa
+        w = self.w = ti.get(name)
+        self.dims = tpa.Dims(w.h, w.d_h, w.R_K, w.R_V, w.dtype, w.rope_base)
+        t0 = time.time()
+        seqs = ti.decode_batch(w)
+        self.lens = ti.decode_lengths(w)
+        log(f"[{w.name}] inputs generated in {time.time() - t0:.1f}s")
+        self.batch = w.batch
+        one = tpa.tpa_cache_bytes(self.dims, int(np.sum(self.lens + tpa.tpa_block_tokens(self.dims))))
+        self.n_rep = max(1, -(-min_bytes // one))
+        caps = [int(n) + 1 for n in self.lens] * self.n_rep  # +1: the step's new token
+        t0 = time.time()
+        self.cache = FactorCache(self.dims, caps)
+        for b, s in enumerate(seqs):
+            dev = [to_device(x, self.dims) for x in (s.A_K, s.B_K, s.A_V, s.B_V)]
+            for r in range(self.n_rep):
+                self.cache.append(r * self.batch + b, *dev)
+            del dev
+        torch.cuda.synchronize()
+        log(f"[{w.name}] {self.n_rep} cache replica(s), {self.cache.nbytes / 1e9:.2f} GB, built in "
+            f"{time.time() - t0:.1f}s")
+        # the step's new token (factors at position N) and its query, as the producer would hand them over
+        rng = np.random.default_rng(w.seed)
+        mk = lambda shape, sig: to_device(ti.to_storage(rng.standard_normal(shape, dtype=np.float32) * sig,
+                                                        w.dtype), self.dims)
+        self.new_AK = mk((self.batch, w.R_K, w.h), 1 / np.sqrt(w.R_K))
+        self.new_BK = mk((self.batch, w.R_K, w.d_h), 1 / np.sqrt(w.R_K))
+        self.new_AV = mk((self.batch, w.R_V, w.h), 1 / np.sqrt(w.R_V))
+        self.new_BV = mk((self.batch, w.R_V, w.d_h), 1 / np.sqrt(w.R_V))
+        self.q = to_device(np.stack([s.q[0] for s in seqs]), self.dims)
+        self.q_rot = torch.empty_like(self.q)
+        self.pos = torch.tensor(self.lens, dtype=torch.int32, device="cuda")
+        starts = self.cache.seq_start.view(self.n_rep, self.batch)
+        self.rep_start = [starts[r].contiguous() for r in range(self.n_rep)]
+        self.rep_slot = [(starts[r] + self.pos.to(torch.int64)).contiguous() for r in range(self.n_rep)]
+        self.seq_len = torch.tensor(self.lens, dtype=torch.int32, device="cuda")
+        self.max_len = int(np.max(self.lens))
+        ws = tpa.tpa_decode_workspace_bytes(self.dims, self.batch, self.max_len)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
+        self.out = torch.empty(self.batch, w.h, w.d_h, dtype=torch.float32, device="cuda")
+        self.bytes = decode_bytes(w, self.lens)
+
+    def step(self, i: int, ev=None):
+        tpa, r = self.tpa, i % self.n_rep
+        tpa.tpa_cache_append(self.dims, self.cache.buf, self.cache.capacity, self.rep_slot[r], self.pos,
+                             self.new_AK, self.new_BK, self.new_AV, self.new_BV, q_pos=self.pos, q_in=self.q,
+                             q_out=self.q_rot)
+        if ev is not None:
+            ev[0].record()
+        tpa.tpa_decode(self.dims, self.cache.buf, self.cache.capacity, self.rep_start[r], self.seq_len,
+                       self.max_len, self.q_rot, self.out, self.ws)
+        if ev is not None:
+            ev[1].record()
+
+    def run(self, steps: int, warmup: int):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t_start.record()
+        for i in range(steps):
+            self.step(warmup + i, evs[i])
+        t_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms_step = t_start.elapsed_time(t_end) / steps
+        ms_dec = sum(a.elapsed_time(b) for a, b in evs) / steps
+        toks = float(np.sum(self.lens))
+        return dict(ms_per_step=ms_step, decode_ms=ms_dec, wall_s=wall, tokens_per_s=toks / (ms_step / 1e3),
+                    decode_tokens_per_s=toks / (ms_dec / 1e3), bytes=self.bytes,
+                    decode_GBps=self.bytes / (ms_dec / 1e3) / 1e9)
+
+
+def prefill_bench(steps: int, warmup: int):
+    """Causal chunk: 8 sequences x (2048 cached + 512 chunk rows), h=32, d_h=128, R=4, bf16."""
+    import torch
+    import factorized_kv_cache_tpa_amd as tpa
+    import tpa_inputs as ti
+    from factorized_kv_cache_tpa_amd.cache import FactorCache, to_device
+
+    w = ti.get("c5")
+    dims = tpa.Dims(w.h, w.d_h, w.R_K, w.R_V, w.dtype, w.rope_base)
+    seqs = ti.prefill_batch(w)
+    B, ctx, chunk = w.prefill_batch, w.prefill_ctx, w.prefill_chunk
+    cache = FactorCache(dims, [ctx + chunk] * B)
+    for b, s in enumerate(seqs):
+        cache.append_host(b, s.A_K, s.B_K, s.A_V, s.B_V)
+    q = to_device(np.stack([s.q for s in seqs]), dims).reshape(B * chunk, w.h, w.d_h)
+    q_pos = torch.arange(ctx, ctx + chunk, dtype=torch.int32, device="cuda").repeat(B)
+    q_rot = cache.rotate_queries(q, q_pos).reshape(B, chunk, w.h, w.d_h)
+    ctx_len = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, chunk, w.h, w.d_h, dtype=torch.float32, device="cuda")
+
+    def call():
+        tpa.tpa_prefill_chunk(dims, cache.buf, cache.capacity, cache.seq_start, ctx_len, ctx, chunk, q_rot, out)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    pairs = B * sum(ctx + j + 1 for j in range(chunk))
+    flops = 4.0 * w.d_h * w.h * pairs
+    tf = flops / (ms / 1e3) / 1e12
+    return dict(workload=f"prefill_b{B}_ctx{ctx}_chunk{chunk}_h{w.h}_d{w.d_h}_r{w.R_K}_causal", ms=ms,
+                gflop=flops / 1e9, tflops=tf, mfma_frac=tf / MFMA_BF16_PEAK_TFLOPS)
+
+
+def cpu_baseline(name: str, budget_s: float = 12.0):
+    """The fp64 oracle on the host's cores over whole sequences of the same workload (bounded)."""
+    import oracle
+    import tpa_inputs as ti
+
+    w = ti.get(name)
+    seqs = ti.decode_batch(w)
+    f = lambda a: ti.to_f64(a, w.dtype)
+    conv = [(f(s.A_K), f(s.B_K), f(s.A_V), f(s.B_V), f(s.q[0])) for s in seqs]
+    threads = oracle.max_threads()
+    done_tokens, n_seq = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        for args in conv:
+            oracle.decode(*args, w.rope_base, threads=threads)
+            done_tokens += args[0].shape[0]
+            n_seq += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=done_tokens / dt, unit="cached-tokens/s", cores=threads, kind="oracle",
+                sample=f"{n_seq} decode sequences of {w.name} (4096 cached tokens each), fp64, "
+                       f"{dt:.1f}s wall")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extras", action="store_true", help="time only the main workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the library runs on a "
+              f"single MI355X; see the sharding notes in the design document)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import factorized_kv_cache_tpa_amd as tpa
+    tpa.load()  # fails loudly when the HIP library is missing
+    torch.cuda.set_device(0)
+
+    main_b = DecodeBench(MAIN, min_bytes=4 * MALL_BYTES)
+    res = main_b.run(args.steps, args.warmup)
+    log(f"[{main_b.w.name}] step {res['ms_per_step'] * 1e3:.2f} us, decode {res['decode_ms'] * 1e3:.2f} us, "
+        f"{res['decode_GBps']:.0f} GB/s")
+    extras = {}
+    if not args.no_extras:
+        for name in ("c3", "c4", "c5"):
+            b = DecodeBench(name, min_bytes=4 * MALL_BYTES)
+            r = b.run(max(10, args.steps // 4), max(3, args.warmup // 4))
+            extras[b.w.name] = dict(decode_us=round(r["decode_ms"] * 1e3, 2),
+                                    step_us=round(r["ms_per_step"] * 1e3, 2),
+                                    cached_tokens_per_s=round(r["decode_tokens_per_s"], 1),
+                                    GBps=round(r["decode_GBps"], 1),
+                                    hbm_frac=round(r["decode_GBps"] / HBM_PEAK_GBS, 4))
+            log(f"[{b.w.name}] decode {r['decode_ms'] * 1e3:.2f} us, {r['decode_GBps']:.0f} GB/s")
+            del b
+            torch.cuda.empty_cache()
+        p = prefill_bench(max(5, args.steps // 10), 3)
+        pname = p.pop("workload")
+        extras[pname] = {k: round(v, 4) for k, v in p.items()}
+        log(f"[prefill] {p['ms'] * 1e3:.1f} us, {p['tflops']:.1f} TFLOP/s, {100 * p['mfma_frac']:.1f}% MFMA")
+
+    achieved = res["decode_GBps"]
+    line = {
+        "metric": "factor-cache decode cached-tokens/s + HBM GB/s (% of roofline); prefill % MFMA",
+        "value": round(res["tokens_per_s"], 1),
+        "unit": "cached-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian factors; no dataset)",
+        "config": {"workload": main_b.w.name, "batch": main_b.batch, "cached_tokens_per_seq": main_b.max_len,
+                   "h": main_b.w.h, "d_h": main_b.w.d_h, "R_K": main_b.w.R_K, "R_V": main_b.w.R_V,
+                   "rope_base": main_b.w.rope_base, "cache_replicas": main_b.n_rep,
+                   "step": "tpa_cache_append (new token + query RoPE) + tpa_decode"},
+        "roofline": {"kernel": "tpa_decode (split + merge kernels)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": main_b.bytes,
+                     "avg_launch_us": round(res["decode_ms"] * 1e3, 3)},
+        "extras": extras,
+    }
+    del main_b
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(MAIN)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

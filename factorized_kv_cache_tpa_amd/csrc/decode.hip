@@ -330,44 +330,91 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     }
 }
 
-// Second pass: merge the per-split partials of one sequence.
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int HP, int DP, int TOK) {
-    const int b = blockIdx.x;
+// Second pass: merge the per-split partials.  One work-group per (head, sequence);
+// thread t owns output columns 4 (t % C4) .. +3 and the splits j = t / C4 (mod JL),
+// where C4 = DP / 4 and JL = 256 / C4.  Each thread folds its splits with the
+// same rescaling rule, loads issued eight at a time, and the JL lanes of a column
+// group are folded once more through LDS.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeUnroll = 8;
+
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p, int HP, int DP, int TOK) {
+    __shared__ float sm[kMergeThreads][6];
+    const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int C4 = DP / 4, JL = kMergeThreads / C4;
+    const int c4 = tid % C4, jl = tid / C4;
     int len = p.seq_len[b];
     len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
     const int nblk = (len + TOK - 1) / TOK;
     const int n_valid = (nblk + p.split_blocks - 1) / p.split_blocks;
     const int64_t start = p.seq_start[b];
     const bool misaligned = start < 0 || start % TOK != 0;
-    float *out = p.out + int64_t(b) * p.h * p.d_h;
-    const int D4 = (p.d_h + 3) / 4;
-    for (int idx = threadIdx.x; idx < p.h * D4; idx += blockDim.x) {
-        const int head = idx / D4, d0 = 4 * (idx % D4);
-        float o[4] = {0.f, 0.f, 0.f, 0.f};
-        if (misaligned) {
-            o[0] = o[1] = o[2] = o[3] = __builtin_nanf("");
-        } else if (n_valid > 0) {
-            float mm = -INFINITY;
-            for (int j = 0; j < n_valid; ++j)
-                mm = fmaxf(mm, p.ws_ml[((int64_t(b) * p.n_split + j) * HP + head) * 2]);
-            float ll = 0.f;
-            for (int j = 0; j < n_valid; ++j) {
-                const int64_t part = int64_t(b) * p.n_split + j;
-                const float mj = p.ws_ml[(part * HP + head) * 2];
-                const float sj = mj == -INFINITY ? 0.f : exp2f(mj - mm);
-                ll += sj * p.ws_ml[(part * HP + head) * 2 + 1];
-                const float4 v = *reinterpret_cast<const float4 *>(p.ws_o + (part * HP + head) * DP + d0);
-                o[0] += sj * v.x;
-                o[1] += sj * v.y;
-                o[2] += sj * v.z;
-                o[3] += sj * v.w;
-            }
-            const float inv = p.out_mul / ll;
+
+    float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    const int64_t base = int64_t(b) * p.n_split;
+    for (int j0 = jl; j0 < n_valid; j0 += JL * kMergeUnroll) {
+        float mj[kMergeUnroll], lj[kMergeUnroll];
+        float4 oj[kMergeUnroll];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) o[k] *= inv;
+        for (int u = 0; u < kMergeUnroll; ++u) {
+            const int j = j0 + u * JL;
+            if (j < n_valid) {
+                const int64_t part = base + j;
+                const float2 ml = *reinterpret_cast<const float2 *>(p.ws_ml + (part * HP + head) * 2);
+                mj[u] = ml.x;
+                lj[u] = ml.y;
+                oj[u] = *reinterpret_cast<const float4 *>(p.ws_o + (part * HP + head) * DP + 4 * c4);
+            } else {
+                mj[u] = -INFINITY;
+                lj[u] = 0.f;
+                oj[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
-        for (int k = 0; k < 4 && d0 + k < p.d_h; ++k) out[head * p.d_h + d0 + k] = o[k];
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) {
+            if (mj[u] == -INFINITY) continue;
+            const float Mn = fmaxf(M, mj[u]);
+            const float a = exp2f(M - Mn), c = exp2f(mj[u] - Mn);
+            L = L * a + lj[u] * c;
+            o0 = o0 * a + oj[u].x * c;
+            o1 = o1 * a + oj[u].y * c;
+            o2 = o2 * a + oj[u].z * c;
+            o3 = o3 * a + oj[u].w * c;
+            M = Mn;
+        }
     }
+    sm[tid][0] = M;
+    sm[tid][1] = L;
+    sm[tid][2] = o0;
+    sm[tid][3] = o1;
+    sm[tid][4] = o2;
+    sm[tid][5] = o3;
+    __syncthreads();
+    if (jl != 0 || head >= p.h || 4 * c4 >= p.d_h) return;
+    for (int k = 1; k < JL; ++k) {
+        const float *r = sm[tid + k * C4];
+        if (r[0] == -INFINITY) continue;
+        const float Mn = fmaxf(M, r[0]);
+        const float a = exp2f(M - Mn), c = exp2f(r[0] - Mn);
+        L = L * a + r[1] * c;
+        o0 = o0 * a + r[2] * c;
+        o1 = o1 * a + r[3] * c;
+        o2 = o2 * a + r[4] * c;
+        o3 = o3 * a + r[5] * c;
+        M = Mn;
+    }
+    float o[4] = {o0, o1, o2, o3};
+    if (misaligned) {
+        o[0] = o[1] = o[2] = o[3] = __builtin_nanf("");
+    } else if (n_valid == 0 || L == 0.f) {
+        o[0] = o[1] = o[2] = o[3] = 0.f;
+    } else {
+        const float inv = p.out_mul / L;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] *= inv;
+    }
+    float *out = p.out + (int64_t(b) * p.h + head) * p.d_h;
+    for (int k = 0; k < 4 && 4 * c4 + k < p.d_h; ++k) out[4 * c4 + k] = o[k];
 }
 
 template <typename T, int HP, int DP, int RH>
@@ -414,7 +461,8 @@ hipError_t launch_decode(const Layout &L, const DecodeParams &p, hipStream_t s) 
     TPA_DECODE_SHAPES(X)
 #undef X
     if (!found || e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(p.batch), dim3(256), 0, s, p, L.HP, L.DP, L.tok_per_block());
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(L.HP, p.batch), dim3(kMergeThreads), 0, s, p, L.HP, L.DP,
+                       L.tok_per_block());
     return hipGetLastError();
 }
 

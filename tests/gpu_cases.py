@@ -2,8 +2,13 @@
 from seeded inputs, run decode / prefill, and compare with the fp64 oracle.
 
 Tolerances (element-wise over the whole output tensor):
-  bf16 factors, fp32 accumulation: max-abs <= 1e-2 and rel-L2 <= 5e-3
-  fp32 inputs:                     max-abs <= 1e-5 and rel-L2 <= 1e-5
+  bf16 factors, fp32 accumulation: max-abs <= 1e-2 * M and rel-L2 <= 5e-3
+  fp32 inputs:                     max-abs <= 1e-5 * M and rel-L2 <= 1e-5
+with M = max(1, max|oracle|).  For the five measured workloads the outputs are
+below 0.1 in magnitude, so M = 1 and these are the plain absolute bounds.  Small
+stress cases (few tokens, rank 1, sharpened softmax) reach outputs of 3..10,
+where a bf16 value itself is only defined to +-0.03; there the absolute bound
+scales with the output magnitude, i.e. the same relative precision.
 """
 from __future__ import annotations
 
@@ -42,7 +47,9 @@ def assert_close(gpu, ref, dtype: str, what: str = ""):
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
     max_abs, rel = errors(gpu, ref)
     tol_abs, tol_rel = TOL[dtype]
-    say(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    mag = max(1.0, float(np.abs(ref).max())) if np.size(ref) else 1.0
+    tol_abs *= mag
+    say(f"  {what}: max_abs={max_abs:.3e} (bound {tol_abs:.1e}) rel_l2={rel:.3e}")
     assert max_abs <= tol_abs and rel <= tol_rel, f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}"
 
 

@@ -26,7 +26,7 @@ def test_tiny_fp32_workload():
 @pytest.mark.parametrize("h,d_h,R_K,R_V,dtype", [
     (32, 128, 1, 1, ti.BF16), (32, 128, 2, 2, ti.BF16), (32, 128, 4, 4, ti.BF16), (16, 64, 2, 2, ti.BF16),
     (16, 64, 1, 1, ti.BF16), (32, 64, 1, 3, ti.BF16), (4, 16, 1, 1, ti.F32), (16, 32, 2, 2, ti.F32),
-    (32, 128, 3, 1, ti.F32), (20, 48, 2, 2, ti.BF16), (6, 40, 1, 2, ti.F32)])
+    (32, 128, 3, 1, ti.F32), (20, 48, 2, 2, ti.BF16), (6, 30, 1, 2, ti.F32)])
 @pytest.mark.parametrize("q_scale", [1.0, 12.0])
 def test_small_shapes_ragged(h, d_h, R_K, R_V, dtype, q_scale):
     """Several blocks per split and a ragged tail; q_scale 12 sharpens the softmax."""
@@ -39,12 +39,17 @@ def test_small_shapes_ragged(h, d_h, R_K, R_V, dtype, q_scale):
 
 
 def test_split_size_invariance_and_determinism():
+    """Every split size meets the oracle bound; splits agree with each other to the bf16 rounding of the
+    value weights (the running max, and so the rounding of p * A_V, depends on the split); a repeated
+    call with the same split is bitwise identical."""
     w = case_workload(32, 128, 2, 2)
     s = DecodeSetup(w, random_sequences(w, [3000, 1234, 17], q_scale=8.0, seed=5))
     outs = {split: s.run(split_tokens=split) for split in (0, 16, 32, 128, 512, 4096)}
     ref = outs[0]
+    _check_all(s, ref, "split auto")
     for split, o in outs.items():
-        np.testing.assert_allclose(o, ref, rtol=0, atol=2e-6, err_msg=f"split {split}")
+        _check_all(s, o, f"split {split}")
+        np.testing.assert_allclose(o, ref, rtol=0, atol=2.0 ** -7 * np.abs(ref).max(), err_msg=f"split {split}")
     again = s.run(split_tokens=0)
     assert np.array_equal(again, ref), "two identical calls differ"
 
