@@ -39,6 +39,31 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_bytes_decode_b16_h32_d128_r1_n4096.json")
+
+
+def decode_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("decode.hip", "common.h"):
+        with open(os.path.join(ROOT, "factorized_kv_cache_tpa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def decode_traffic():
+    """HBM bytes per tpa_decode call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by a
+    plain copy of known size); None when that summary is missing or the decode kernels changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != decode_source_hash():
+        return None
+    return int(round(d["decode_call_traffic_bytes"]))
+
+
 def decode_bytes(w, lens) -> int:
     """Algorithmic bytes of one decode: the factor stream plus the query read and the fp32 output write."""
     es = 2 if w.dtype == "bf16" else 4
@@ -93,39 +118,74 @@ class DecodeBench:
         self.seq_len = torch.tensor(self.lens, dtype=torch.int32, device="cuda")
         self.max_len = int(np.max(self.lens))
         ws = tpa.tpa_decode_workspace_bytes(self.dims, self.batch, self.max_len)
-        self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
+        self.ws = torch.zeros(ws, dtype=torch.uint8, device="cuda")
         self.out = torch.empty(self.batch, w.h, w.d_h, dtype=torch.float32, device="cuda")
         self.bytes = decode_bytes(w, self.lens)
 
-    def step(self, i: int, ev=None):
+    def step(self, i: int):
+        """One decode step on cache replica i % n_rep: append the new token + rotate the query, decode."""
         tpa, r = self.tpa, i % self.n_rep
         tpa.tpa_cache_append(self.dims, self.cache.buf, self.cache.capacity, self.rep_slot[r], self.pos,
                              self.new_AK, self.new_BK, self.new_AV, self.new_BV, q_pos=self.pos, q_in=self.q,
                              q_out=self.q_rot)
-        if ev is not None:
-            ev[0].record()
-        tpa.tpa_decode(self.dims, self.cache.buf, self.cache.capacity, self.rep_start[r], self.seq_len,
-                       self.max_len, self.q_rot, self.out, self.ws)
-        if ev is not None:
-            ev[1].record()
+        self.decode(r)
+
+    def decode(self, r: int, out=None):
+        self.tpa.tpa_decode(self.dims, self.cache.buf, self.cache.capacity, self.rep_start[r], self.seq_len,
+                            self.max_len, self.q_rot, self.out if out is None else out, self.ws)
+
+    def _capture(self, fn, n: int):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.cap_stream):
+            for i in range(n):
+                fn(i)
+        return g
 
     def run(self, steps: int, warmup: int):
+        """Time exactly `steps` steps.  The steps are recorded once into HIP graphs (a pass over all
+        cache replicas per graph) so the GPU is never waiting on the Python launch path."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        self.cap_stream = torch.cuda.Stream()
+        full = self._capture(self.step, self.n_rep)
+        rem = steps % self.n_rep
+        part = self._capture(self.step, rem) if rem else None
+        dec = self._capture(self.decode, self.n_rep)
+        full.replay()
+        dec.replay()
+        torch.cuda.synchronize()
+
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        a, b, c, d = ev(), ev(), ev(), ev()
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
-        t_start.record()
-        for i in range(steps):
-            self.step(warmup + i, evs[i])
-        t_end.record()
+        a.record()
+        for _ in range(steps // self.n_rep):
+            full.replay()
+        if part is not None:
+            part.replay()
+        b.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
-        ms_step = t_start.elapsed_time(t_end) / steps
-        ms_dec = sum(a.elapsed_time(b) for a, b in evs) / steps
+        # the decode kernels alone, back to back over the replicas, same stream
+        n_dec = max(1, -(-steps // self.n_rep))
+        c.record()
+        for _ in range(n_dec):
+            dec.replay()
+        d.record()
+        torch.cuda.synchronize()
+        ms_step = a.elapsed_time(b) / steps
+        ms_dec = c.elapsed_time(d) / (n_dec * self.n_rep)
+        # replays must reproduce the eager result bit for bit (decode is deterministic)
+        got = self.out.clone()
+        ref = torch.empty_like(self.out)
+        self.decode(self.n_rep - 1, out=ref)
+        torch.cuda.synchronize()
+        if not torch.equal(got, ref):
+            raise RuntimeError("graph replay of tpa_decode differs from the eager call")
         toks = float(np.sum(self.lens))
         return dict(ms_per_step=ms_step, decode_ms=ms_dec, wall_s=wall, tokens_per_s=toks / (ms_step / 1e3),
                     decode_tokens_per_s=toks / (ms_dec / 1e3), bytes=self.bytes,
@@ -158,10 +218,15 @@ def prefill_bench(steps: int, warmup: int):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        for _ in range(steps):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
-    for _ in range(steps):
-        call()
+    g.replay()
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / steps
@@ -206,6 +271,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extras", action="store_true", help="time only the main workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run a plain 64 MiB device copy three times (scale reference for the HBM byte "
+                         "counters of a profiled run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the library runs on a "
@@ -257,14 +325,20 @@ def main():
                    "h": main_b.w.h, "d_h": main_b.w.d_h, "R_K": main_b.w.R_K, "R_V": main_b.w.R_V,
                    "rope_base": main_b.w.rope_base, "cache_replicas": main_b.n_rep,
                    "step": "tpa_cache_append (new token + query RoPE) + tpa_decode"},
-        "roofline": {"kernel": "tpa_decode (split + merge kernels)", "bound": "hbm",
+        "roofline": {"kernel": "tpa_decode (split + merge kernels, timed back to back in a graph)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
                      "algorithmic_bytes_per_launch": main_b.bytes,
                      "avg_launch_us": round(res["decode_ms"] * 1e3, 3)},
         "extras": extras,
     }
     del main_b
+    if args.calibration_copy:
+        src = torch.empty(64 << 20, dtype=torch.uint8, device="cuda").fill_(7)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(MAIN)
     print(json.dumps(line), flush=True)

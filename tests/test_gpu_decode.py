@@ -125,3 +125,31 @@ def test_full_size_ragged_decode_sampled():
     ref = np.stack([s.oracle(b) for b in pick])
     assert_close(out[pick], ref, w.dtype, f"sampled sequences {pick}")
     assert np.all(np.isfinite(out))
+
+
+def test_graph_replay_matches_eager():
+    """Append (query RoPE) + decode recorded in a HIP graph: every replay equals the eager result bit for bit."""
+    import factorized_kv_cache_tpa_amd as tpa
+    from factorized_kv_cache_tpa_amd.cache import to_device
+    w = case_workload(32, 128, 1, 1)
+    seqs = random_sequences(w, [500, 77, 1000], q_scale=4.0, seed=31)
+    s = DecodeSetup(w, seqs)
+    eager = s.run()
+    q = to_device(np.stack([x.q[0] for x in seqs]), s.dims)
+    q_rot = torch.empty_like(q)
+    q_pos = torch.tensor(s.lens, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(tpa.tpa_decode_workspace_bytes(s.dims, s.batch, s.max_len), dtype=torch.uint8, device="cuda")
+    out = torch.empty(s.batch, w.h, w.d_h, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        s.cache.rotate_queries(q, q_pos, q_out=q_rot)
+        tpa.tpa_decode(s.dims, s.cache.buf, s.cache.capacity, s.cache.seq_start, s.seq_len, s.max_len, q_rot,
+                       out, ws)
+    for k in range(3):
+        out.fill_(float("nan"))
+        q_rot.zero_()
+        _ = (torch.randn(1000, device="cuda") * 2).sum().item()  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager), f"replay {k}"
