@@ -28,14 +28,14 @@ constexpr int kPrefillWaves = 8;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
 constexpr int kQT = 32 * kPrefillWaves;  // query rows per work-group
 constexpr int kKT = 64;                  // keys per tile
+constexpr float kLazyPrefill = 8.0f;     // headroom of the lazy reference max, log2 units
+constexpr int kXcds = 8;                 // MI355X: 8 XCDs, 32 CUs and one L2 each
 
 __device__ __forceinline__ floatx16 mma32(bf16x8 a, bf16x8 b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return uint32_t(f32_to_bf16_rne(a)) | (uint32_t(f32_to_bf16_rne(b)) << 16);
-}
+__device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
 
 __device__ __forceinline__ bf16x8 pack8(const float *x) {
     const uint4 v = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
@@ -55,6 +55,8 @@ __device__ __forceinline__ void unpack4(uint2 raw, float *x) {
     x[3] = __uint_as_float(raw.y & 0xffff0000u);
 }
 
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
 // LDS position of tile key k inside the value contraction's key order
 __device__ __forceinline__ int vpos(int k) { return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3); }
 
@@ -68,19 +70,36 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     constexpr int TOK = kRows / RH;
     constexpr int SKS = DP + 8;   // LDS row stride of K~ (bf16 elements)
     constexpr int SVS = kKT + 8;  // LDS row stride of V^T
-    constexpr int64_t BLK = 2LL * kRows * (HP + DP);
+    constexpr int BLK = 2 * kRows * (HP + DP);
     constexpr int OFF_AV = kRows * HP, OFF_BK = 2 * kRows * HP, OFF_BV = 2 * kRows * HP + kRows * DP;
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKT * SKS];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][DP * SVS];
 
-    const int head = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 31, hi = lane >> 5;
-    const int j0 = blockIdx.x * kQT;
+    // Work-groups are dispatched round-robin over the 8 XCDs (linear id mod 8), each with its own L2.
+    // When the batch is a multiple of 8, the linear id is mapped so that all work-groups of a sequence
+    // (every head and query tile: they all read the same B factors) land on one XCD and share its L2.
+    const int n_qt = (p.chunk + kQT - 1) / kQT;
+    const int L = blockIdx.x;
+    int b, head, qt;
+    if (p.batch % kXcds == 0) {
+        const int per_seq = p.h * n_qt;
+        b = L % kXcds + kXcds * (L / (kXcds * per_seq));
+        const int r = (L / kXcds) % per_seq;
+        head = r / n_qt;
+        qt = r % n_qt;
+    } else {
+        qt = L % n_qt;
+        head = (L / n_qt) % p.h;
+        b = L / (n_qt * p.h);
+    }
+    const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hi = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j0 = qt * kQT;
     const int jw = j0 + 32 * w;  // first query row of this wave
     const int jq = jw + col;     // query row of this lane's accumulator column
     int ctx = p.ctx_len[b];
-    ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
     const int64_t start = p.seq_start[b];
+    ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
     float *out = p.out + int64_t(b) * p.chunk * p.h * p.d_h;
 
     if (start < 0 || start % TOK != 0) {  // misaligned sequence: report NaN
@@ -90,88 +109,162 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         }
         return;
     }
-    const uint16_t *seq = reinterpret_cast<const uint16_t *>(p.cache) + (start / TOK) * BLK;
+    const uint16_t *seq = reinterpret_cast<const uint16_t *>(p.cache) + (start / TOK) * int64_t(BLK);
     const int j_last = min(p.chunk, j0 + kQT) - 1;
     const int n_keys = ctx + j_last + 1;  // keys any row of this work-group sees (all appended)
     const int n_kt = (n_keys + kKT - 1) / kKT;
     const int gate_lane = head & 15, gate_nb = head >> 4;
 
-    // ---- rebuild K~_i and V_i^T of tile kt into LDS buffer `buf`
-    auto rebuild = [&](int kt, int buf) {
+    // ---- rebuild of K~_i and V_i^T for one tile.  Each thread owns fixed items; since a tile starts
+    // at a block boundary, every load address is the tile's first block plus a per-thread constant
+    // (computed once here) plus a compile-time step per item.  All loads of a tile are issued before
+    // any arithmetic; products are bf16 pairs fed to v_dot2_f32_bf16 (fp32 accumulation).
+    constexpr int C8 = DP / 8;                                    // 8-feature chunks per key row
+    constexpr int K_ITEMS = kKT * C8 / kPrefillThreads;           // (key, 8 features) per thread
+    constexpr int K_STEP = kPrefillThreads / C8;                  // keys between a thread's items
+    // V items: the 8 wave-rows of the group split over the tile's blocks; a thread takes one block and
+    // one chunk lane, and V_ITEMS feature groups of that block, so it needs one pair of gate loads
+    constexpr int BPT = kKT / TOK;                                // cache blocks per tile
+    constexpr int MVG = kPrefillWaves / BPT;                      // thread rows sharing one block
+    constexpr int V_ITEMS = MBV / MVG;                            // 16-feature groups per thread
+    static_assert(K_ITEMS * kPrefillThreads == kKT * C8 && K_STEP % TOK == 0, "K items must tile the group");
+    static_assert(MVG * BPT == kPrefillWaves && V_ITEMS * MVG == MBV, "V items must tile the group");
+    const int kk = tid / C8, c8 = tid % C8;    // key of item 0, its feature chunk
+    const int krow0 = (kk % TOK) * RH;         // the key's first factor row in its block
+    const int kv0 = krow0 & 3;                 // its first gate inside a 4-gate chunk
+    // byte offsets from the tile's first block (unsigned 32-bit: scalar base + vector offset addressing)
+    const uint32_t k_off_blk = uint32_t((kk / TOK) * BLK) * 2u;  // block of item 0 inside the tile
+    const uint32_t k_off_gate =
+        k_off_blk + uint32_t((((krow0 >> 4) * NB + gate_nb) * kWave + 16 * ((krow0 & 15) >> 2) + gate_lane) * 4) * 2u;
+    uint32_t k_off_b[RH];
+#pragma unroll
+    for (int r = 0; r < RH; ++r) {
+        const int row = krow0 + r, d0 = 8 * c8;
+        k_off_b[r] = k_off_blk +
+                     uint32_t(OFF_BK + (((row >> 4) * KBS + (d0 >> 5)) * kWave + 16 * ((d0 & 31) >> 3) + (row & 15)) * 8) * 2u;
+    }
+    const int vrow = tid / kWave, vcl = tid % kWave, vg4 = vcl >> 4;
+    const int vbi = vrow % BPT, vmv0 = (vrow / BPT) * V_ITEMS;  // block inside the tile, first feature group
+    // feature of item u: 16 (vmv0 + u) + vcl % 16; chunk of item u: (vmv0 + u) * 64 + vcl
+    const uint32_t v_off = uint32_t(vbi * BLK + OFF_BV + (vmv0 * kWave + vcl) * 8) * 2u;
+    const uint32_t v_off_gate = uint32_t(vbi * BLK + OFF_AV + (gate_nb * kWave + 16 * vg4 + gate_lane) * 4) * 2u;
+
+    // raw factor data of one tile, in registers between its loads and its rebuild
+    struct Raw {
+        uint2 kg[K_ITEMS];
+        uint4 kb_raw[K_ITEMS][RH];
+        uint4 vx[V_ITEMS];
+        uint2 vg[2];
+    };
+    auto fetch = [&](Raw &raw, int kt) {
+        const int key0 = kt * kKT;
+        const char *tb = reinterpret_cast<const char *>(seq + int64_t(key0 / TOK) * BLK);  // tile's first block
+        const bool whole = key0 + kKT <= n_keys;  // uniform; only the last tile may reach past n_keys
+        // past n_keys the addresses are clamped to the last live key
+        auto &kg = raw.kg;
+        auto &kb_raw = raw.kb_raw;
+        auto &vx = raw.vx;
+        auto &vg = raw.vg;
+        const int last_blk = (n_keys - 1) / TOK - key0 / TOK;  // last block with live keys, tile-relative
+#pragma unroll
+        for (int u = 0; u < K_ITEMS; ++u) {
+            // item u's block, tile-relative, in bytes past item 0's (clamped to the last live block)
+            uint32_t delta = uint32_t(u * (K_STEP / TOK) * BLK) * 2u;
+            if (!whole)
+                delta = uint32_t(min(kk / TOK + u * (K_STEP / TOK), last_blk) * BLK) * 2u - k_off_blk;
+            kg[u] = *reinterpret_cast<const uint2 *>(tb + (k_off_gate + delta));
+#pragma unroll
+            for (int r = 0; r < RH; ++r) kb_raw[u][r] = *reinterpret_cast<const uint4 *>(tb + (k_off_b[r] + delta));
+        }
+        {
+            // a block past the last live one: read the last live block instead (its keys are zeroed below)
+            const uint32_t delta = whole ? 0u : uint32_t((min(vbi, last_blk) - vbi) * BLK) * 2u;
+#pragma unroll
+            for (int u = 0; u < V_ITEMS; ++u)
+                vx[u] = *reinterpret_cast<const uint4 *>(tb + (v_off + uint32_t(u * kWave * 8 * 2) + delta));
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                vg[m] = *reinterpret_cast<const uint2 *>(tb + (v_off_gate + uint32_t(m * NB * kWave * 4 * 2) + delta));
+        }
+    };
+    auto rebuild = [&](Raw &raw, int kt, int buf) {
         const int key0 = kt * kKT;
         uint16_t *dK = sK[buf];
         uint16_t *dV = sV[buf];
-        // K~ rows: item = (key, 8 features)
-        for (int it = tid; it < kKT * (DP / 8); it += kPrefillThreads) {
-            const int k = it / (DP / 8), c8 = it % (DP / 8);
-            const int key = key0 + k;
+        const bool whole = key0 + kKT <= n_keys;
+        auto &kg = raw.kg;
+        auto &kb_raw = raw.kb_raw;
+        auto &vx = raw.vx;
+        auto &vg = raw.vg;
+        // -- K~ rows: K~[key][d] = sum_r A_K[key][r] B~_K[key][r][d]
+#pragma unroll
+        for (int u = 0; u < K_ITEMS; ++u) {
+            const int k = kk + u * K_STEP;
+            const uint32_t gw[2] = {kg[u].x, kg[u].y};
             float kv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) kv[e] = 0.f;
-            if (key < n_keys) {
-                const uint16_t *blk = seq + int64_t(key / TOK) * BLK;
-                const int row0 = (key % TOK) * RH;
-                const int mb = row0 >> 4, g4 = (row0 & 15) >> 2, v0 = row0 & 3;
-                float a[4];
-                unpack4(*reinterpret_cast<const uint2 *>(blk + ((mb * NB + gate_nb) * kWave + 16 * g4 + gate_lane) * 4),
-                        a);
-                const int d0 = 8 * c8, kb = d0 >> 5, lsub = (d0 & 31) >> 3;
+            for (int w2 = 0; w2 < 4; ++w2) {  // feature pairs (2 w2, 2 w2 + 1)
+                if (RH == 1) {
+                    const uint32_t a = (kv0 & 1) ? (gw[kv0 >> 1] >> 16) : (gw[kv0 >> 1] & 0xffffu);
+                    const uint32_t bw = (&kb_raw[u][0].x)[w2];
+                    kv[2 * w2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(bw & 0xffffu), 0.f, false);
+                    kv[2 * w2 + 1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(bw >> 16), 0.f, false);
+                } else {
+                    kv[2 * w2] = kv[2 * w2 + 1] = 0.f;
 #pragma unroll
-                for (int r = 0; r < RH; ++r) {
-                    const int row = row0 + r;
-                    float bk[8];
-                    unpack8(*reinterpret_cast<const uint4 *>(
-                                blk + OFF_BK + (((row >> 4) * KBS + kb) * kWave + 16 * lsub + (row & 15)) * 8),
-                            bk);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) kv[e] += a[v0 + r] * bk[e];
+                    for (int rp = 0; rp < RH / 2; ++rp) {  // rank pairs (2 rp, 2 rp + 1)
+                        const uint32_t a = gw[(kv0 >> 1) + rp];
+                        const uint32_t b0 = (&kb_raw[u][2 * rp].x)[w2], b1 = (&kb_raw[u][2 * rp + 1].x)[w2];
+                        const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x05040100u);  // (b0[d], b1[d])
+                        const uint32_t hi2 = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // (b0[d+1], b1[d+1])
+                        kv[2 * w2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(lo), kv[2 * w2], false);
+                        kv[2 * w2 + 1] =
+                            __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(hi2), kv[2 * w2 + 1], false);
+                    }
                 }
             }
-            *reinterpret_cast<bf16x8 *>(&dK[k * SKS + 8 * c8]) = pack8(kv);
+            uint4 packed = make_uint4(pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3]), pack_bf16x2(kv[4], kv[5]),
+                                      pack_bf16x2(kv[6], kv[7]));
+            if (!whole && key0 + k >= n_keys) packed = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(&dK[k * SKS + 8 * c8]) = packed;
         }
-        // V^T columns: item = (block of the tile, 16-feature group, lane of the cache chunk); the
-        // 16-byte chunk holds 8 factor rows (whole tokens) of one feature
-        constexpr int BPT = kKT / TOK;  // cache blocks per tile
-        for (int it = tid; it < BPT * MBV * kWave; it += kPrefillThreads) {
-            const int bi = it / (MBV * kWave), rem = it % (MBV * kWave);
-            const int mv = rem / kWave, cl = rem % kWave;
-            const int g4 = cl >> 4, d = 16 * mv + (cl & 15);
-            const int kbase = bi * TOK;  // tile-relative key of the block's first token
-            const bool live = key0 + kbase < n_keys;
-            float x[8], ga[2][4];
-            if (live) {
-                const uint16_t *blk = seq + int64_t((key0 + kbase) / TOK) * BLK;
-                unpack8(*reinterpret_cast<const uint4 *>(blk + OFF_BV + (mv * kWave + cl) * 8), x);
+        // -- V^T columns: a 16-byte chunk holds 8 factor rows (whole tokens) of feature vd
+        const int kbase = vbi * TOK;  // tile-relative key of the block's first token
 #pragma unroll
-                for (int m = 0; m < 2; ++m)
-                    unpack4(*reinterpret_cast<const uint2 *>(
-                                blk + OFF_AV + ((m * NB + gate_nb) * kWave + 16 * g4 + gate_lane) * 4),
-                            ga[m]);
-            }
+        for (int u = 0; u < V_ITEMS; ++u) {
+            const int vd = 16 * (vmv0 + u) + (vcl & 15);  // the feature this chunk holds
+            const uint32_t xw[4] = {vx[u].x, vx[u].y, vx[u].z, vx[u].w};
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                // rows 16 m + 4 g4 + 0..3 of the block: 4 / RH whole tokens
+                // rows 16 m + 4 vg4 + 0..3 of the block: 4 / RH whole tokens
                 constexpr int TPH = 4 / RH;
+                const uint32_t gw[2] = {vg[m].x, vg[m].y};
                 float vt[TPH];
 #pragma unroll
                 for (int tl = 0; tl < TPH; ++tl) {
                     float acc = 0.f;
-                    if (live) {
+                    if (RH == 1) {
+                        const uint32_t a = (tl & 1) ? (gw[tl >> 1] >> 16) : (gw[tl >> 1] & 0xffffu);
+                        const uint32_t x = (tl & 1) ? (xw[2 * m + (tl >> 1)] >> 16) : (xw[2 * m + (tl >> 1)] & 0xffffu);
+                        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(x), 0.f, false);
+                    } else {
 #pragma unroll
-                        for (int r = 0; r < RH; ++r) acc += ga[m][tl * RH + r] * x[4 * m + tl * RH + r];
+                        for (int rp = 0; rp < RH / 2; ++rp)
+                            acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(gw[(tl * RH) / 2 + rp]),
+                                                                  as_bf16x2(xw[2 * m + (tl * RH) / 2 + rp]), acc,
+                                                                  false);
                     }
-                    const int key = kbase + (16 * m + 4 * g4) / RH + tl;
-                    vt[tl] = key0 + key < n_keys ? acc : 0.f;
+                    vt[tl] = acc;
+                    if (!whole && key0 + kbase + (16 * m + 4 * vg4) / RH + tl >= n_keys) vt[tl] = 0.f;
                 }
-                const int k0 = kbase + (16 * m + 4 * g4) / RH;
-                uint16_t *dst = &dV[d * SVS + vpos(k0)];
+                uint16_t *dst = &dV[vd * SVS + vpos(kbase + (16 * m + 4 * vg4) / RH)];
                 if (TPH == 4) {
-                    *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2(vt[0], vt[TPH > 1 ? 1 : 0]),
-                                                                 pack2(vt[TPH > 2 ? 2 : 0], vt[TPH > 3 ? 3 : 0]));
+                    *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(vt[0], vt[TPH > 1 ? 1 : 0]),
+                                                                 pack_bf16x2(vt[TPH > 2 ? 2 : 0], vt[TPH > 3 ? 3 : 0]));
                 } else if (TPH == 2) {
-                    *reinterpret_cast<uint32_t *>(dst) = pack2(vt[0], vt[TPH > 1 ? 1 : 0]);
+                    *reinterpret_cast<uint32_t *>(dst) = pack_bf16x2(vt[0], vt[TPH > 1 ? 1 : 0]);
                 } else {
-                    *dst = f32_to_bf16_rne(vt[0]);
+                    *dst = uint16_t(pack_bf16x2(vt[0], 0.f) & 0xffffu);
                 }
             }
         }
@@ -201,16 +294,24 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[mb][v] = 0.f;
-    float run_m = -INFINITY, run_l = 0.f;
+    // raw scores (the scale goes inside the exponent); lazy reference max as in decode
+    const float sm = p.score_mul, lazy_raw = kLazyPrefill / sm;
+    float run_m = -INFINITY, neg_ms = INFINITY, run_l = 0.f;
     const int wave_last = min(p.chunk - 1, jw + 31);
+    const bool wave_live = jw < p.chunk;
+    const int jq_vis = jq < p.chunk ? ctx + jq : -1;  // last key this lane's query sees (-1: none)
 
-    rebuild(0, 0);
+    // software pipeline: tile t+1's factor loads are in flight while the matrix cores work on tile t,
+    // then the waves rebuild tile t+1 into the other LDS buffer
+    Raw raw;
+    fetch(raw, 0);
+    rebuild(raw, 0, 0);
     __syncthreads();
     for (int kt = 0; kt < n_kt; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < n_kt) rebuild(kt + 1, buf ^ 1);
+        if (kt + 1 < n_kt) fetch(raw, kt + 1);
         const int key0 = kt * kKT;
-        if (jw < p.chunk && key0 <= ctx + wave_last) {
+        if (wave_live && key0 <= ctx + wave_last) {
             const uint16_t *cK = sK[buf];
             const uint16_t *cV = sV[buf];
             // ---- S^T = K~ Q~^T for two 32-key blocks
@@ -225,40 +326,47 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
                     s[kb2] = mma32(a, qf[ks], s[kb2]);
                 }
             }
-            // ---- causal mask, online softmax (log2 units)
+            // ---- causal mask only where the tile crosses the diagonal (or past the chunk's end)
+            if (key0 + kKT - 1 > ctx + jw || wave_last < jw + 31) {
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int key = key0 + 32 * kb2 + 8 * (v >> 2) + 4 * hi + (v & 3);
+                        s[kb2][v] = key <= jq_vis ? s[kb2][v] : -INFINITY;
+                    }
+            }
             float mx = -INFINITY;
-            const bool full = key0 + kKT - 1 <= ctx + jw;  // no key of the tile is beyond any row of the wave
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int key = key0 + 32 * kb2 + 8 * (v >> 2) + 4 * hi + (v & 3);
-                    const bool vis = jq < p.chunk && (full || key <= ctx + jq);
-                    s[kb2][v] = vis ? s[kb2][v] * p.score_mul : -INFINITY;
-                    mx = fmaxf(mx, s[kb2][v]);
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb2][v]);
+            if (__any(mx > run_m + lazy_raw)) {
+                const float mn = fmaxf(run_m, fmaxf(mx, __shfl_xor(mx, 32, kWave)));
+                if (mn != -INFINITY) {
+                    const float alpha = __builtin_amdgcn_exp2f((run_m - mn) * sm);
+                    run_m = mn;
+                    neg_ms = -mn * sm;
+                    run_l *= alpha;
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-            const float mn = fmaxf(run_m, mx);
-            const float m_use = mn == -INFINITY ? 0.f : mn;
-            const float alpha = exp2f(run_m - m_use);
-            run_m = mn;
-            run_l *= alpha;
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
+            }
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    s[kb2][v] = exp2f(s[kb2][v] - m_use);
+                    s[kb2][v] = __builtin_amdgcn_exp2f(fmaf(s[kb2][v], sm, neg_ms));
                     run_l += s[kb2][v];
                 }
             // ---- O^T += V^T P^T over four 16-key steps
 #pragma unroll
             for (int ks4 = 0; ks4 < 4; ++ks4) {
-                float x[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = s[ks4 >> 1][8 * (ks4 & 1) + e];
-                const bf16x8 pf = pack8(x);
+                const floatx16 &sv = s[ks4 >> 1];
+                const int o8 = 8 * (ks4 & 1);
+                const uint4 pw = make_uint4(pack_bf16x2(sv[o8], sv[o8 + 1]), pack_bf16x2(sv[o8 + 2], sv[o8 + 3]),
+                                            pack_bf16x2(sv[o8 + 4], sv[o8 + 5]), pack_bf16x2(sv[o8 + 6], sv[o8 + 7]));
+                const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
                     const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&cV[(32 * mb + col) * SVS + 16 * ks4 + 8 * hi]);
@@ -266,6 +374,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
                 }
             }
         }
+        if (kt + 1 < n_kt) rebuild(raw, kt + 1, buf ^ 1);
         __syncthreads();
     }
 
@@ -292,7 +401,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
 
 template <int HP, int DP, int RH>
 hipError_t launch_one(const PrefillParams &p, hipStream_t s) {
-    const dim3 grid((p.chunk + kQT - 1) / kQT, p.h, p.batch);
+    const dim3 grid(unsigned(((p.chunk + kQT - 1) / kQT) * p.h * p.batch));
     hipLaunchKernelGGL((prefill_kernel<HP, DP, RH>), grid, dim3(kPrefillThreads), 0, s, p);
     return hipGetLastError();
 }
