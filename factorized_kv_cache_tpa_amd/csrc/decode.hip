@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 
     __shared__ float sm_m[kWaves][HP];
     __shared__ float sm_l[kWaves][HP];
-    __shared__ float sm_o[HP][DP + 4];
+    __shared__ __attribute__((aligned(16))) float sm_o[kWaves][HP][DP + 4];
 
     const int b = blockIdx.y;
     const int split = blockIdx.x;
@@ -188,17 +188,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             for (int q = 0; q < KBV; ++q) st.bv[mv][q] = M::stream(op + OFF_BV + (mv * KBV + q) * kWave * E);
     };
 
-    // Two register stages (the next block's loads in flight while one is consumed) wherever they
-    // fit in the register file; wide fp32 operands use one stage.
-    constexpr bool kTwoStages = sizeof(T) == 2 || HP * DP <= 1024;
-    Stage s0, s1;
-    int blk = blk_begin + w;
-    if (kTwoStages) {  // start streaming the first two blocks before anything else
-        if (blk < full_end) load(s0, blk);
-        if (blk + kWaves < full_end) load(s1, blk + kWaves);
-    }
-
-    // query operand (B of the score contraction): lane holds q~[16 nb + c][4E kb + E g + e]
+    // query operand (B of the score contraction; loaded first: memory returns in order, so the first
+    // block can start as soon as its own loads land): lane holds q~[16 nb + c][4E kb + E g + e]
     Frag qf[KBS][NB];
     {
         const T *qb = reinterpret_cast<const T *>(p.q) + int64_t(b) * p.h * p.d_h;
@@ -211,6 +202,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                 qf[kb][nb] = M::load_q(qb, head, d0, p.h, p.d_h);
             }
     }
+
+    // Two register stages (the next block's loads in flight while one is consumed) wherever they
+    // fit in the register file; wide fp32 operands use one stage.
+    constexpr bool kTwoStages = sizeof(T) == 2 || HP * DP <= 1024;
+    Stage s0, s1;
+    int blk = blk_begin + w;
+    if (kTwoStages) {  // start streaming the first two blocks before anything else
+        if (blk < full_end) load(s0, blk);
+        if (blk + kWaves < full_end) load(s1, blk + kWaves);
+    }
+
 
     floatx4 acc[MBV][NB];
 #pragma unroll
@@ -377,30 +379,31 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         for (int ww = 1; ww < kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][head]);
         wscale[nb] = run_m[nb] == -INFINITY ? 0.f : exp2f(run_m[nb] - mm);
     }
-    for (int ww = 0; ww < kWaves; ++ww) {
-        if (w == ww) {
+    // every wave writes its rescaled accumulators to its own LDS slice; after one barrier all threads
+    // sum the slices column by column straight into the split's partial
 #pragma unroll
-            for (int mv = 0; mv < MBV; ++mv)
+    for (int mv = 0; mv < MBV; ++mv)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    float4 *dst = reinterpret_cast<float4 *>(&sm_o[16 * nb + c][16 * mv + 4 * g]);
-                    const floatx4 a = acc[mv][nb] * wscale[nb];
-                    if (ww == 0) {
-                        *dst = make_float4(a[0], a[1], a[2], a[3]);
-                    } else {
-                        const float4 o = *dst;
-                        *dst = make_float4(o.x + a[0], o.y + a[1], o.z + a[2], o.w + a[3]);
-                    }
-                }
+        for (int nb = 0; nb < NB; ++nb) {
+            const floatx4 a = acc[mv][nb] * wscale[nb];
+            *reinterpret_cast<float4 *>(&sm_o[w][16 * nb + c][16 * mv + 4 * g]) = make_float4(a[0], a[1], a[2], a[3]);
         }
-        __syncthreads();
-    }
+    __syncthreads();
     // write the split's partial: O [HP][DP], (max, sum) [HP]
     const int64_t part = int64_t(b) * p.n_split + split;
     float *wo = p.ws_o + part * HP * DP;
     for (int idx = threadIdx.x; idx < HP * DP / 4; idx += kThreads) {
-        const int head = idx / (DP / 4), d4 = idx % (DP / 4);
-        *reinterpret_cast<float4 *>(wo + head * DP + 4 * d4) = *reinterpret_cast<const float4 *>(&sm_o[head][4 * d4]);
+        const int hh = idx / (DP / 4), d4 = idx % (DP / 4);
+        float4 o = *reinterpret_cast<const float4 *>(&sm_o[0][hh][4 * d4]);
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) {
+            const float4 x = *reinterpret_cast<const float4 *>(&sm_o[ww][hh][4 * d4]);
+            o.x += x.x;
+            o.y += x.y;
+            o.z += x.z;
+            o.w += x.w;
+        }
+        *reinterpret_cast<float4 *>(wo + hh * DP + 4 * d4) = o;
     }
     for (int head = threadIdx.x; head < HP; head += kThreads) {
         float mm = sm_m[0][head];
