@@ -74,6 +74,7 @@ DecodePlan plan_decode(const Layout &L, int32_t batch, int32_t max_len, int32_t 
 }
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool aligned16(const void *ptr) { return reinterpret_cast<uintptr_t>(ptr) % 16 == 0; }
 
 float resolve_scale(float scale, int d_h) { return scale > 0.f ? scale : float(1.0 / sqrt(double(d_h))); }
 
@@ -116,16 +117,24 @@ int32_t tpa_cache_append(const tpa_dims *dims, void *cache, int64_t capacity_tok
     int32_t st = check_dims(dims);
     if (st != TPA_OK) return st;
     if (capacity_tokens < 0 || n_kv < 0 || n_q < 0) return TPA_ERR_ARG;
-    if (n_kv + n_q > int64_t(0x7fffffff)) return TPA_ERR_ARG;
+    if (n_kv > int64_t(0x7fffffff) || n_q > int64_t(0x7fffffff)) return TPA_ERR_ARG;
+    const uintptr_t pair_bytes = 2u * uintptr_t(dims->dtype == TPA_BF16 ? 2 : 4);
+    auto pair_aligned = [&](const void *ptr) { return reinterpret_cast<uintptr_t>(ptr) % pair_bytes == 0; };
     if (n_kv > 0) {
         if (!cache || !slot || !kv_pos || !A_K || !B_K || !A_V || !B_V) return TPA_ERR_ARG;
+        if (!pair_aligned(B_K) || !pair_aligned(B_V) || !aligned16(cache))
+            return TPA_ERR_ARG;
         if (slot_hi < 0) return TPA_ERR_ARG;
         if (slot_hi > capacity_tokens) return TPA_ERR_CAPACITY;
     }
     if (n_q > 0) {
         if (q_rows < 1 || !q_pos || !q_in || !q_out) return TPA_ERR_ARG;
+        if (!pair_aligned(q_in) || !pair_aligned(q_out)) return TPA_ERR_ARG;
         if (int64_t(q_rows) * dims->d_h > int64_t(1) << 24) return TPA_ERR_ARG;
     }
+    // one work-group per cache token and append_q_groups per query token
+    if (n_kv + (n_q > 0 ? n_q * tpa::append_q_groups(q_rows, dims->d_h) : 0) > int64_t(0x7fffffff))
+        return TPA_ERR_ARG;
     if (n_kv == 0 && n_q == 0) return TPA_OK;
     const hipError_t e = tpa::launch_append(layout_of(dims), dims->h, dims->d_h, dims->R_K, dims->R_V,
                                             dims->rope_base, cache, capacity_tokens, n_kv, slot, kv_pos, A_K, B_K,
@@ -160,6 +169,7 @@ int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
         return TPA_ERR_ARG;
     if (batch == 0) return TPA_OK;
     if (!cache || !seq_start || !seq_len || !q_rot || !out) return TPA_ERR_ARG;
+    if (!aligned16(cache) || !aligned16(q_rot)) return TPA_ERR_ARG;
     if (!isfinite(scale)) return TPA_ERR_ARG;
     if (int64_t(max_len) > capacity_tokens) return TPA_ERR_CAPACITY;
     const Layout L = layout_of(dims);
@@ -198,6 +208,7 @@ int32_t tpa_prefill_chunk(const tpa_dims *dims, const void *cache, int64_t capac
     if (batch < 0 || batch > 65535 || max_ctx < 0 || chunk_len < 0 || capacity_tokens < 0) return TPA_ERR_ARG;
     if (batch == 0 || chunk_len == 0) return TPA_OK;
     if (!cache || !seq_start || !ctx_len || !q_rot || !out) return TPA_ERR_ARG;
+    if (!aligned16(cache) || !aligned16(q_rot) || !aligned16(out)) return TPA_ERR_ARG;
     if (!isfinite(scale)) return TPA_ERR_ARG;
     if (int64_t(max_ctx) + chunk_len > capacity_tokens) return TPA_ERR_CAPACITY;
     const Layout L = layout_of(dims);

@@ -8,10 +8,11 @@
 //
 // Rotation: RoFormer pairs (2j, 2j+1), theta_j = base^(-2j/d_h),
 // (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a), a = pos * theta_j.
-// The angle and the rotation are computed in fp64 (positions reach 131072
-// and beyond, where an fp32 angle is off by milliradians) and the result is
-// rounded once to the storage type.  This is an HBM copy, not on the
-// per-token hot loop.
+// The angle is formed and reduced in fp64; the precision of the rest is
+// described at RopeMath.  The result is rounded once to the storage type.
+// This is an HBM copy of one token per sequence per decode step; its cost is
+// latency (a position load, the angle table, the stores), so every input
+// load is issued first and query rows are spread over several work-groups.
 #include "common.h"
 
 namespace tpa {
@@ -19,91 +20,183 @@ namespace {
 
 constexpr int kAppendThreads = 128;
 
-// cos and sin of pos * theta_j for the d_h/2 pairs of one position, fp64, shared by the work-group.
-// The angle is reduced modulo 2 pi first (Cody-Waite with 2 pi split in two doubles; positions are
-// int32, so |angle| < 2^31 and the two-part split keeps r exact to ~1e-15), so sincos sees |r| <= pi.
-__device__ inline void rope_table(double *cs, int d_h, double pos, const RopeTable &rt) {
+// Arithmetic of the rotation.  The angle pos * theta_j is always formed and reduced modulo 2 pi in
+// fp64 (positions reach 131072 and beyond, where an fp32 angle is off by milliradians).  For bf16
+// storage, cos/sin of the reduced angle (|r| <= pi) and the rotation itself are then fp32: their error,
+// ~1e-7 relative, is far below half a bf16 unit, so the stored value is the correctly rounded rotation
+// except within 1e-7 of a rounding tie (at most one unit off).  fp32 storage keeps fp64 throughout.
+template <typename T>
+struct RopeMath {
+    using F = double;
+    __device__ static void sincos_reduced(double r, F *s, F *c) { sincos(r, s, c); }
+};
+template <>
+struct RopeMath<uint16_t> {
+    using F = float;
+    __device__ static void sincos_reduced(double r, F *s, F *c) { sincosf(float(r), s, c); }
+};
+
+// cos and sin of pos * theta_j for the d_h/2 pairs of one position, shared by the work-group.
+// theta is this thread's theta_j (j = threadIdx.x < d_h/2; d_h/2 <= kAppendThreads), loaded up front.
+// The reduction is Cody-Waite with 2 pi split in two doubles; positions are int32, so |angle| < 2^31
+// and the two-part split keeps r exact to ~1e-15 before sincos sees |r| <= pi.
+template <typename T>
+__device__ inline void rope_table(typename RopeMath<T>::F *cs, int d_h, double pos, double theta) {
     constexpr double kTwoPiHi = 6.283185307179586232;    // nearest double to 2 pi
     constexpr double kTwoPiLo = 2.4492935982947064e-16;  // 2 pi - kTwoPiHi
     constexpr double kInvTwoPi = 0.15915494309189535;
-    for (int j = threadIdx.x; j < d_h / 2; j += blockDim.x) {
-        const double phi = pos * rt.theta[j];
+    const int j = threadIdx.x;
+    if (j < d_h / 2) {
+        const double phi = pos * theta;
         const double k = rint(phi * kInvTwoPi);
         const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, phi));
-        double sn, cn;
-        sincos(r, &sn, &cn);
+        typename RopeMath<T>::F sn, cn;
+        RopeMath<T>::sincos_reduced(r, &sn, &cn);
         cs[2 * j] = cn;
         cs[2 * j + 1] = sn;
     }
     __syncthreads();
 }
 
+// Two adjacent elements (a rotary pair) moved as one load or store.
 template <typename T>
-__device__ inline void rope_pair(T x0, T x1, const double *cs, int j, T &y0, T &y1) {
-    const double c = cs[2 * j], s = cs[2 * j + 1];
-    const double a = double(Elem<T>::to_f32(x0)), b = double(Elem<T>::to_f32(x1));
-    y0 = Elem<T>::from_f64(a * c - b * s);
-    y1 = Elem<T>::from_f64(a * s + b * c);
+struct Pair;
+template <>
+struct Pair<uint16_t> {
+    using V = uint32_t;
+    __device__ static V zero() { return 0u; }
+    __device__ static float lo(V v) { return bf16_to_f32(uint16_t(v & 0xffffu)); }
+    __device__ static float hi(V v) { return bf16_to_f32(uint16_t(v >> 16)); }
+    __device__ static V make(float a, float b) { return pack_bf16x2(a, b); }
+    __device__ static uint16_t first(V v) { return uint16_t(v & 0xffffu); }
+    __device__ static uint16_t second(V v) { return uint16_t(v >> 16); }
+};
+template <>
+struct Pair<float> {
+    using V = float2;
+    __device__ static V zero() { return make_float2(0.f, 0.f); }
+    __device__ static double lo(V v) { return double(v.x); }
+    __device__ static double hi(V v) { return double(v.y); }
+    __device__ static V make(double a, double b) { return make_float2(float(a), float(b)); }
+    __device__ static float first(V v) { return v.x; }
+    __device__ static float second(V v) { return v.y; }
+};
+
+// (x0, x1) rotated by the angle whose cos, sin sit at cs[2j], cs[2j+1]; one rounding to T at the end.
+template <typename T>
+__device__ inline typename Pair<T>::V rope_pair(typename Pair<T>::V x, const typename RopeMath<T>::F *cs, int j) {
+    using P = Pair<T>;
+    const auto c = cs[2 * j], s = cs[2 * j + 1];
+    const auto a = P::lo(x), b = P::hi(x);
+    return P::make(fma(a, c, -(b * s)), fma(a, s, b * c));
 }
 
 template <typename T>
 __device__ inline T zero_of() { return T(0); }
 
+// Per-thread register budget of one work-group.  A token's factors span at most RH * DP / 2 <= 512
+// rotary pairs and RH * HP <= 256 head-factor values.  Query rows are split over work-groups of
+// kQPairs pairs per thread.  Every load is issued before the angle table is built, so the memory
+// latency of the inputs overlaps the table instead of following it.
+constexpr int kKvPairs = 4;
+constexpr int kKvGates = 2;
+constexpr int kQPairs = 4;
+
+}  // namespace
+
+int64_t append_q_groups(int q_rows, int d_h) {
+    const int64_t per_group = int64_t(kAppendThreads) * kQPairs;
+    return (int64_t(q_rows) * (d_h / 2) + per_group - 1) / per_group;
+}
+
+namespace {
+
+// Grid: one work-group per cache token (n < n_kv), then append_q_groups(q_rows, d_h) work-groups per
+// query token, each rotating kAppendThreads * kQPairs consecutive pairs of that token's rows.
 template <typename T>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     Layout L, int h, int d_h, int RK, int RV, RopeTable rt, T *__restrict__ cache, int64_t capacity, int64_t n_kv,
     const int64_t *__restrict__ slot, const int32_t *__restrict__ kv_pos, const T *__restrict__ A_K,
     const T *__restrict__ B_K, const T *__restrict__ A_V, const T *__restrict__ B_V, int64_t n_q, int q_rows,
-    const int32_t *__restrict__ q_pos, const T *q_in, T *q_out) {
-    __shared__ double cs[256];  // cos, sin per rotary pair (d_h <= 256)
+    int q_groups, const int32_t *__restrict__ q_pos, const T *q_in, T *q_out) {
+    using P = Pair<T>;
+    using V = typename P::V;
+    using F = typename RopeMath<T>::F;
+    __shared__ F cs[256];  // cos, sin per rotary pair (d_h <= 256)
     const int64_t n = blockIdx.x;
     const int tid = threadIdx.x;
+    const double theta = tid < d_h / 2 ? rt.theta[tid] : 0.0;
     if (n < n_kv) {
         const int64_t s = slot[n];
-        if (s < 0 || s >= capacity) return;
+        const double pos = double(kv_pos[n]);
+        const int HD = L.DP / 2;  // pairs per padded feature row
+        V kx[kKvPairs], vx[kKvPairs];
+        T ga[kKvGates], gv[kKvGates];
+#pragma unroll
+        for (int k = 0; k < kKvPairs; ++k) {
+            const int idx = tid + k * kAppendThreads, r = idx / HD, d = 2 * (idx % HD);
+            const bool in = idx < L.RH * HD && d < d_h;
+            kx[k] = in && r < RK ? *reinterpret_cast<const V *>(B_K + (n * RK + r) * d_h + d) : P::zero();
+            vx[k] = in && r < RV ? *reinterpret_cast<const V *>(B_V + (n * RV + r) * d_h + d) : P::zero();
+        }
+#pragma unroll
+        for (int k = 0; k < kKvGates; ++k) {
+            const int idx = tid + k * kAppendThreads, r = idx / L.HP, i = idx % L.HP;
+            const bool in = idx < L.RH * L.HP && i < h;
+            ga[k] = in && r < RK ? A_K[(n * RK + r) * h + i] : zero_of<T>();
+            gv[k] = in && r < RV ? A_V[(n * RV + r) * h + i] : zero_of<T>();
+        }
+        rope_table<T>(cs, d_h, pos, theta);
+        if (s < 0 || s >= capacity) return;  // uniform over the work-group, after the barrier
         const int TOK = L.tok_per_block();
         T *blk = cache + (s / TOK) * L.block_elems();
         const int row0 = int(s % TOK) * L.RH;
-        rope_table(cs, d_h, double(kv_pos[n]), rt);
-        // head factors: gates stored per (row, head)
-        for (int idx = tid; idx < L.RH * L.HP; idx += kAppendThreads) {
-            const int r = idx / L.HP, i = idx % L.HP;
-            const int off = L.gate(row0 + r, i);
-            blk[L.off_ak() + off] = (r < RK && i < h) ? A_K[(n * RK + r) * h + i] : zero_of<T>();
-            blk[L.off_av() + off] = (r < RV && i < h) ? A_V[(n * RV + r) * h + i] : zero_of<T>();
+#pragma unroll
+        for (int k = 0; k < kKvGates; ++k) {
+            const int idx = tid + k * kAppendThreads, r = idx / L.HP, i = idx % L.HP;
+            if (idx < L.RH * L.HP) {
+                const int off = L.gate(row0 + r, i);
+                blk[L.off_ak() + off] = ga[k];
+                blk[L.off_av() + off] = gv[k];
+            }
         }
-        // feature factors: B_K rotated pairwise, B_V copied
-        const int HD = L.DP / 2;
-        for (int idx = tid; idx < L.RH * HD; idx += kAppendThreads) {
-            const int r = idx / HD, j = idx % HD, d = 2 * j;
-            T k0 = zero_of<T>(), k1 = zero_of<T>(), v0 = zero_of<T>(), v1 = zero_of<T>();
-            if (r < RK && d < d_h) {
-                const T *src = B_K + (n * RK + r) * d_h + d;
-                rope_pair<T>(src[0], src[1], cs, j, k0, k1);
+#pragma unroll
+        for (int k = 0; k < kKvPairs; ++k) {
+            const int idx = tid + k * kAppendThreads, r = idx / HD, j = idx % HD, d = 2 * j;
+            if (idx < L.RH * HD) {
+                const V y = r < RK && d < d_h ? rope_pair<T>(kx[k], cs, j) : P::zero();
+                T *pk = blk + L.off_bk() + L.bk(row0 + r, d);
+                if constexpr (sizeof(T) == 2) {
+                    *reinterpret_cast<V *>(pk) = y;  // bf16: d even, so d, d+1 share one lane's 8-value k-run
+                } else {
+                    pk[0] = P::first(y);
+                    blk[L.off_bk() + L.bk(row0 + r, d + 1)] = P::second(y);
+                }
+                blk[L.off_bv() + L.bv(row0 + r, d)] = P::first(vx[k]);
+                blk[L.off_bv() + L.bv(row0 + r, d + 1)] = P::second(vx[k]);
             }
-            if (r < RV && d < d_h) {
-                const T *src = B_V + (n * RV + r) * d_h + d;
-                v0 = src[0];
-                v1 = src[1];
-            }
-            blk[L.off_bk() + L.bk(row0 + r, d)] = k0;
-            blk[L.off_bk() + L.bk(row0 + r, d + 1)] = k1;
-            blk[L.off_bv() + L.bv(row0 + r, d)] = v0;
-            blk[L.off_bv() + L.bv(row0 + r, d + 1)] = v1;
         }
     } else {
-        const int64_t nq = n - n_kv;
-        if (nq >= n_q) return;
-        rope_table(cs, d_h, double(q_pos[nq]), rt);
+        const int64_t g = n - n_kv;
+        const int64_t nq = g / q_groups;
+        if (nq >= n_q) return;  // uniform over the work-group
+        const double pos = double(q_pos[nq]);
         const int HD = d_h / 2;
-        for (int idx = tid; idx < q_rows * HD; idx += kAppendThreads) {
-            const int row = idx / HD, j = idx % HD;
-            const int64_t o = (nq * q_rows + row) * d_h + 2 * j;
-            const T x0 = q_in[o], x1 = q_in[o + 1];
-            T y0, y1;
-            rope_pair<T>(x0, x1, cs, j, y0, y1);
-            q_out[o] = y0;
-            q_out[o + 1] = y1;
+        const int items = q_rows * HD;  // pair idx = row * HD + j sits at element 2 * idx of the token
+        const int first = int(g % q_groups) * (kAppendThreads * kQPairs);
+        const V *src = reinterpret_cast<const V *>(q_in + nq * q_rows * d_h);
+        V *dst = reinterpret_cast<V *>(q_out + nq * q_rows * d_h);
+        V x[kQPairs];
+#pragma unroll
+        for (int k = 0; k < kQPairs; ++k) {
+            const int idx = first + k * kAppendThreads + tid;
+            x[k] = idx < items ? src[idx] : P::zero();
+        }
+        rope_table<T>(cs, d_h, pos, theta);
+#pragma unroll
+        for (int k = 0; k < kQPairs; ++k) {
+            const int idx = first + k * kAppendThreads + tid;
+            if (idx < items) dst[idx] = rope_pair<T>(x[k], cs, idx % HD);
         }
     }
 }
@@ -144,20 +237,25 @@ hipError_t launch_append(const Layout &L, int h, int d_h, int RK, int RV, double
                          int64_t capacity, int64_t n_kv, const int64_t *slot, const int32_t *kv_pos,
                          const void *A_K, const void *B_K, const void *A_V, const void *B_V, int64_t n_q,
                          int q_rows, const int32_t *q_pos, const void *q_in, void *q_out, hipStream_t s) {
-    const int64_t grid = n_kv + n_q;
+    if (L.RH * L.DP / 2 > kKvPairs * kAppendThreads || L.RH * L.HP > kKvGates * kAppendThreads ||
+        d_h / 2 > kAppendThreads)
+        return hipErrorInvalidValue;  // outside the validated dimension range
+    const int64_t q_groups = n_q > 0 ? append_q_groups(q_rows, d_h) : 1;
+    const int64_t grid = n_kv + n_q * q_groups;
     if (grid == 0) return hipSuccess;
+    if (grid > int64_t(0x7fffffff)) return hipErrorInvalidConfiguration;
     RopeTable rt;
     for (int j = 0; j < 128; ++j) rt.theta[j] = j < d_h / 2 ? pow(base, -2.0 * double(j) / double(d_h)) : 0.0;
     if (L.es == 2) {
         using T = uint16_t;
         hipLaunchKernelGGL(append_kernel<T>, dim3(unsigned(grid)), dim3(kAppendThreads), 0, s, L, h, d_h, RK, RV,
                            rt, (T *)cache, capacity, n_kv, slot, kv_pos, (const T *)A_K, (const T *)B_K,
-                           (const T *)A_V, (const T *)B_V, n_q, q_rows, q_pos, (const T *)q_in, (T *)q_out);
+                           (const T *)A_V, (const T *)B_V, n_q, q_rows, int(q_groups), q_pos, (const T *)q_in, (T *)q_out);
     } else {
         using T = float;
         hipLaunchKernelGGL(append_kernel<T>, dim3(unsigned(grid)), dim3(kAppendThreads), 0, s, L, h, d_h, RK, RV,
                            rt, (T *)cache, capacity, n_kv, slot, kv_pos, (const T *)A_K, (const T *)B_K,
-                           (const T *)A_V, (const T *)B_V, n_q, q_rows, q_pos, (const T *)q_in, (T *)q_out);
+                           (const T *)A_V, (const T *)B_V, n_q, q_rows, int(q_groups), q_pos, (const T *)q_in, (T *)q_out);
     }
     return hipGetLastError();
 }

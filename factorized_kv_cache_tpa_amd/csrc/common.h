@@ -169,6 +169,9 @@ struct RopeTable {
     double theta[128];
 };
 
+// Work-groups of tpa_cache_append per query token of q_rows rows.
+int64_t append_q_groups(int q_rows, int d_h);
+
 // Launchers (return hipError_t of the launch).
 hipError_t launch_append(const Layout &L, int h, int d_h, int RK, int RV, double base, void *cache,
                          int64_t capacity, int64_t n_kv, const int64_t *slot, const int32_t *kv_pos,

@@ -25,6 +25,8 @@
  *     allocator).  The library allocates nothing, keeps no mutable global
  *     state, never synchronizes, and enqueues its kernels on `stream`
  *     (a hipStream_t; NULL = the null stream).  Completion is asynchronous.
+ *   - The cache, q_rot and prefill's out must be 16-byte aligned (wide vector
+ *     loads and stores); hipMalloc and framework allocators give 256 bytes.
  *   - Every call returns a tpa_status.  All argument checks run on the host
  *     before any HIP call; a rejected call launches nothing.  TPA_ERR_HIP
  *     reports a failed launch (hipGetLastError).  Values held in device
@@ -110,6 +112,8 @@ int64_t tpa_cache_bytes(const tpa_dims *dims, int64_t capacity_tokens);
  *   q_rows         rows per query token: h for a full query, or R_Q for a B_Q factor
  *   q_pos[n_q]     int32 positions
  *   q_in, q_out    [n_q][q_rows][d_h]; q_out = RoPE(q_in); q_out may equal q_in
+ *   B_K, B_V, q_in and q_out must be aligned to two elements (rotary pairs are
+ *   moved as one word) and the cache to 16 bytes; TPA_ERR_ARG otherwise.
  * Angles are computed in fp64, rotations in fp64, rounded once to dtype. */
 int32_t tpa_cache_append(const tpa_dims *dims, void *cache, int64_t capacity_tokens, int64_t n_kv,
                          const int64_t *slot, const int32_t *kv_pos, int64_t slot_hi, const void *A_K,

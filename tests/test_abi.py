@@ -205,3 +205,28 @@ def test_prefill_argument_checks(lib):
     f32 = _d(h=32, d_h=128, R_K=1, R_V=1, dtype="f32")
     assert lib.tpa_prefill_chunk(ctypes.byref(f32), FAKE, 4096, 8, FAKE, FAKE, 2048, 512, FAKE, 0.0, FAKE,
                                  None) == 2
+
+
+def test_misaligned_pointers_rejected(lib):
+    """Rotary pairs move as one word and cache / query tiles as 16-byte vectors: misaligned
+    pointers are refused on the host."""
+    d = _d()
+    ref = ctypes.byref(d)
+    odd2 = ctypes.c_void_p(0x1002)  # bf16-aligned but not pair-aligned
+    odd8 = ctypes.c_void_p(0x1008)  # pair-aligned but not 16-byte aligned
+    # B_K, B_V not pair-aligned; cache not 16-byte aligned
+    for bk, bv, cache in [(odd2, FAKE, FAKE), (FAKE, odd2, FAKE), (FAKE, FAKE, odd8)]:
+        assert lib.tpa_cache_append(ref, cache, 64, 1, FAKE, FAKE, 1, FAKE, bk, FAKE, bv, 0, 0, None, None, None,
+                                    None) == 1
+    # query rows not pair-aligned
+    assert lib.tpa_cache_append(ref, None, 0, 0, None, None, 0, None, None, None, None, 1, 32, FAKE, odd2, FAKE,
+                                None) == 1
+    assert lib.tpa_cache_append(ref, None, 0, 0, None, None, 0, None, None, None, None, 1, 32, FAKE, FAKE, odd2,
+                                None) == 1
+    need = lib.tpa_decode_workspace_bytes(ref, 16, 4096, 0)
+    assert lib.tpa_decode(ref, odd8, 8192, 16, FAKE, FAKE, 4096, FAKE, 0.0, FAKE, 0, FAKE, need, None) == 1
+    assert lib.tpa_decode(ref, FAKE, 8192, 16, FAKE, FAKE, 4096, odd8, 0.0, FAKE, 0, FAKE, need, None) == 1
+    d4 = _d(R_K=4, R_V=4)
+    r4 = ctypes.byref(d4)
+    for cache, q, out in [(odd8, FAKE, FAKE), (FAKE, odd8, FAKE), (FAKE, FAKE, odd8)]:
+        assert lib.tpa_prefill_chunk(r4, cache, 8192, 1, FAKE, FAKE, 1024, 64, q, 0.0, out, None) == 1
