@@ -14,11 +14,13 @@
 //     O^T += V_i^T P^T  (M = d_h, N = queries, K = keys)
 // A work-group owns 256 query rows of one head (8 waves x 32), so every
 // (key, head) pair is rebuilt at most twice per chunk of 512 rows.  The LDS
-// tiles are double-buffered: the waves rebuild tile t+1 while their matrix
-// cores work on tile t.  The key order inside the value contraction is
+// tiles are double-buffered: the factor loads of tile t+1 are issued between
+// the matrix-core instructions of tile t, then the waves rebuild tile t+1.  The key order inside the value contraction is
 // permuted (bits 2 and 3 of the key index swapped within each group of 16)
 // so that the score accumulator a lane holds is exactly its slice of P^T and
 // its slice of V^T is one 16-byte LDS read.
+#include <type_traits>
+
 #include "common.h"
 
 namespace tpa {
@@ -40,19 +42,6 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2
 __device__ __forceinline__ bf16x8 pack8(const float *x) {
     const uint4 v = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
     return __builtin_bit_cast(bf16x8, v);
-}
-
-__device__ __forceinline__ void unpack8(uint4 raw, float *x) {
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
-}
-
-__device__ __forceinline__ void unpack4(uint2 raw, float *x) {
-    x[0] = __uint_as_float(raw.x << 16);
-    x[1] = __uint_as_float(raw.x & 0xffff0000u);
-    x[2] = __uint_as_float(raw.y << 16);
-    x[3] = __uint_as_float(raw.y & 0xffff0000u);
 }
 
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
@@ -156,42 +145,46 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         uint4 vx[V_ITEMS];
         uint2 vg[2];
     };
-    auto fetch = [&](Raw &raw, int kt) {
+    // Loads of one tile, in two halves (the K~ inputs, the V inputs) so that each half can be issued
+    // between the matrix-core instructions of one phase.  Only the last tile may reach past n_keys:
+    // there a block past the last live one is replaced by that block (its keys are zeroed in the
+    // rebuild), so no address leaves the sequence's slots.  No branches: the selects keep each half in
+    // the basic block it is placed in.
+    auto tile_base = [&](int kt) {
+        return reinterpret_cast<const char *>(seq + int64_t((kt * kKT) / TOK) * BLK);  // tile's first block
+    };
+    auto tile_last_blk = [&](int kt) {  // last block with live keys, tile-relative (large if the tile is whole)
         const int key0 = kt * kKT;
-        const char *tb = reinterpret_cast<const char *>(seq + int64_t(key0 / TOK) * BLK);  // tile's first block
-        const bool whole = key0 + kKT <= n_keys;  // uniform; only the last tile may reach past n_keys
-        // past n_keys the addresses are clamped to the last live key
-        auto &kg = raw.kg;
-        auto &kb_raw = raw.kb_raw;
-        auto &vx = raw.vx;
-        auto &vg = raw.vg;
-        const int last_blk = (n_keys - 1) / TOK - key0 / TOK;  // last block with live keys, tile-relative
+        return key0 + kKT <= n_keys ? 1 << 20 : (n_keys - 1) / TOK - key0 / TOK;
+    };
+    auto fetch_k = [&](Raw &raw, int kt) {
+        const char *tb = tile_base(kt);
+        const int last_blk = tile_last_blk(kt);
 #pragma unroll
         for (int u = 0; u < K_ITEMS; ++u) {
-            // item u's block, tile-relative, in bytes past item 0's (clamped to the last live block)
-            uint32_t delta = uint32_t(u * (K_STEP / TOK) * BLK) * 2u;
-            if (!whole)
-                delta = uint32_t(min(kk / TOK + u * (K_STEP / TOK), last_blk) * BLK) * 2u - k_off_blk;
-            kg[u] = *reinterpret_cast<const uint2 *>(tb + (k_off_gate + delta));
+            // item u's block lies u * (K_STEP / TOK) blocks past item 0's
+            const uint32_t delta = uint32_t(min(kk / TOK + u * (K_STEP / TOK), last_blk) * BLK) * 2u - k_off_blk;
+            raw.kg[u] = *reinterpret_cast<const uint2 *>(tb + (k_off_gate + delta));
 #pragma unroll
-            for (int r = 0; r < RH; ++r) kb_raw[u][r] = *reinterpret_cast<const uint4 *>(tb + (k_off_b[r] + delta));
-        }
-        {
-            // a block past the last live one: read the last live block instead (its keys are zeroed below)
-            const uint32_t delta = whole ? 0u : uint32_t((min(vbi, last_blk) - vbi) * BLK) * 2u;
-#pragma unroll
-            for (int u = 0; u < V_ITEMS; ++u)
-                vx[u] = *reinterpret_cast<const uint4 *>(tb + (v_off + uint32_t(u * kWave * 8 * 2) + delta));
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-                vg[m] = *reinterpret_cast<const uint2 *>(tb + (v_off_gate + uint32_t(m * NB * kWave * 4 * 2) + delta));
+            for (int r = 0; r < RH; ++r) raw.kb_raw[u][r] = *reinterpret_cast<const uint4 *>(tb + (k_off_b[r] + delta));
         }
     };
-    auto rebuild = [&](Raw &raw, int kt, int buf) {
+    auto fetch_v = [&](Raw &raw, int kt) {
+        const char *tb = tile_base(kt);
+        const uint32_t delta = uint32_t((min(vbi, tile_last_blk(kt)) - vbi) * BLK) * 2u;
+#pragma unroll
+        for (int u = 0; u < V_ITEMS; ++u)
+            raw.vx[u] = *reinterpret_cast<const uint4 *>(tb + (v_off + uint32_t(u * kWave * 8 * 2) + delta));
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            raw.vg[m] = *reinterpret_cast<const uint2 *>(tb + (v_off_gate + uint32_t(m * NB * kWave * 4 * 2) + delta));
+    };
+    // Partial: true only for a tile that reaches past n_keys (its dead keys are written as zeros).
+    auto rebuild = [&](Raw &raw, int kt, int buf, auto partial_tag) {
+        constexpr bool kPartial = decltype(partial_tag)::value;
         const int key0 = kt * kKT;
         uint16_t *dK = sK[buf];
         uint16_t *dV = sV[buf];
-        const bool whole = key0 + kKT <= n_keys;
         auto &kg = raw.kg;
         auto &kb_raw = raw.kb_raw;
         auto &vx = raw.vx;
@@ -225,19 +218,20 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
             }
             uint4 packed = make_uint4(pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3]), pack_bf16x2(kv[4], kv[5]),
                                       pack_bf16x2(kv[6], kv[7]));
-            if (!whole && key0 + k >= n_keys) packed = make_uint4(0, 0, 0, 0);
+            if (kPartial && key0 + k >= n_keys) packed = make_uint4(0, 0, 0, 0);
             *reinterpret_cast<uint4 *>(&dK[k * SKS + 8 * c8]) = packed;
         }
         // -- V^T columns: a 16-byte chunk holds 8 factor rows (whole tokens) of feature vd
         const int kbase = vbi * TOK;  // tile-relative key of the block's first token
+        constexpr int TPH = 4 / RH;  // tokens in each 4-row half of a chunk
 #pragma unroll
         for (int u = 0; u < V_ITEMS; ++u) {
             const int vd = 16 * (vmv0 + u) + (vcl & 15);  // the feature this chunk holds
             const uint32_t xw[4] = {vx[u].x, vx[u].y, vx[u].z, vx[u].w};
+            float v_one[2];  // RH == 4: the one token of each half, packed together below
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                // rows 16 m + 4 vg4 + 0..3 of the block: 4 / RH whole tokens
-                constexpr int TPH = 4 / RH;
+                // rows 16 m + 4 vg4 + 0..3 of the block: TPH whole tokens
                 const uint32_t gw[2] = {vg[m].x, vg[m].y};
                 float vt[TPH];
 #pragma unroll
@@ -255,17 +249,21 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
                                                                   false);
                     }
                     vt[tl] = acc;
-                    if (!whole && key0 + kbase + (16 * m + 4 * vg4) / RH + tl >= n_keys) vt[tl] = 0.f;
+                    if (kPartial && key0 + kbase + (16 * m + 4 * vg4) / RH + tl >= n_keys) vt[tl] = 0.f;
                 }
                 uint16_t *dst = &dV[vd * SVS + vpos(kbase + (16 * m + 4 * vg4) / RH)];
-                if (TPH == 4) {
-                    *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(vt[0], vt[TPH > 1 ? 1 : 0]),
-                                                                 pack_bf16x2(vt[TPH > 2 ? 2 : 0], vt[TPH > 3 ? 3 : 0]));
-                } else if (TPH == 2) {
-                    *reinterpret_cast<uint32_t *>(dst) = pack_bf16x2(vt[0], vt[TPH > 1 ? 1 : 0]);
+                if constexpr (TPH == 4) {
+                    *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(vt[0], vt[1]), pack_bf16x2(vt[2], vt[3]));
+                } else if constexpr (TPH == 2) {
+                    *reinterpret_cast<uint32_t *>(dst) = pack_bf16x2(vt[0], vt[1]);
                 } else {
-                    *dst = uint16_t(pack_bf16x2(vt[0], 0.f) & 0xffffu);
+                    v_one[m] = vt[0];
                 }
+            }
+            if constexpr (TPH == 1) {
+                const uint32_t pk = pack_bf16x2(v_one[0], v_one[1]);
+                dV[vd * SVS + vpos(kbase + vg4)] = uint16_t(pk & 0xffffu);
+                dV[vd * SVS + vpos(kbase + 4 + vg4)] = uint16_t(pk >> 16);
             }
         }
     };
@@ -298,33 +296,54 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     const float sm = p.score_mul, lazy_raw = kLazyPrefill / sm;
     float run_m = -INFINITY, neg_ms = INFINITY, run_l = 0.f;
     const int wave_last = min(p.chunk - 1, jw + 31);
-    const bool wave_live = jw < p.chunk;
     const int jq_vis = jq < p.chunk ? ctx + jq : -1;  // last key this lane's query sees (-1: none)
 
-    // software pipeline: tile t+1's factor loads are in flight while the matrix cores work on tile t,
-    // then the waves rebuild tile t+1 into the other LDS buffer
+    const bf16x2 ones2 = as_bf16x2(0x3F803F80u);  // (1, 1) in bf16
+    auto rebuild_tile = [&](Raw &raw, int kt, int buf) {
+        if (kt * kKT + kKT <= n_keys)
+            rebuild(raw, kt, buf, std::false_type{});
+        else
+            rebuild(raw, kt, buf, std::true_type{});
+    };
+
+    // Software pipeline, one barrier per tile: the loads of tile t+1 are issued in two halves between
+    // the matrix-core instructions of tile t (so the waves do not stall on a full memory queue before
+    // their first MFMA), then the waves rebuild tile t+1 into the other LDS buffer.  The last iteration
+    // reloads the last tile (in bounds, unused) so that the loads need no branch.  Every wave runs every
+    // tile: a tile past a wave's diagonal (or a wave past the chunk's end) is fully masked, its P is
+    // zero, and skipping it would put the loads behind a branch, which costs more registers than the
+    // few masked tiles cost matrix-core time.
     Raw raw;
-    fetch(raw, 0);
-    rebuild(raw, 0, 0);
+    fetch_k(raw, 0);
+    fetch_v(raw, 0);
+    rebuild_tile(raw, 0, 0);
     __syncthreads();
     for (int kt = 0; kt < n_kt; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < n_kt) fetch(raw, kt + 1);
+        const int kn = min(kt + 1, n_kt - 1);  // tile whose loads are issued now
         const int key0 = kt * kKT;
-        if (wave_live && key0 <= ctx + wave_last) {
+        {
             const uint16_t *cK = sK[buf];
             const uint16_t *cV = sV[buf];
-            // ---- S^T = K~ Q~^T for two 32-key blocks
+            // ---- S^T = K~ Q~^T for two 32-key blocks, with the K~ inputs of the next tile issued
             floatx16 s[2];
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) {
+            for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) s[kb2][v] = 0.f;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2) {
                     const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&cK[(32 * kb2 + col) * SKS + 16 * ks + 8 * hi]);
                     s[kb2] = mma32(a, qf[ks], s[kb2]);
                 }
+            fetch_k(raw, kn);
+#pragma unroll
+            for (int i = 0; i < KS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // global loads
             }
             // ---- causal mask only where the tile crosses the diagonal (or past the chunk's end)
             if (key0 + kKT - 1 > ctx + jw || wave_last < jw + 31) {
@@ -355,26 +374,34 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    s[kb2][v] = __builtin_amdgcn_exp2f(fmaf(s[kb2][v], sm, neg_ms));
-                    run_l += s[kb2][v];
-                }
-            // ---- O^T += V^T P^T over four 16-key steps
+                for (int v = 0; v < 16; ++v) s[kb2][v] = __builtin_amdgcn_exp2f(fmaf(s[kb2][v], sm, neg_ms));
+            // ---- O^T += V^T P^T over four 16-key steps, with the V inputs of the next tile issued; the
+            // row sum takes the same bf16-rounded P the matrix cores use, two values per v_dot2 against (1, 1)
 #pragma unroll
             for (int ks4 = 0; ks4 < 4; ++ks4) {
                 const floatx16 &sv = s[ks4 >> 1];
                 const int o8 = 8 * (ks4 & 1);
-                const uint4 pw = make_uint4(pack_bf16x2(sv[o8], sv[o8 + 1]), pack_bf16x2(sv[o8 + 2], sv[o8 + 3]),
-                                            pack_bf16x2(sv[o8 + 4], sv[o8 + 5]), pack_bf16x2(sv[o8 + 6], sv[o8 + 7]));
-                const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+                const uint32_t pw[4] = {pack_bf16x2(sv[o8], sv[o8 + 1]), pack_bf16x2(sv[o8 + 2], sv[o8 + 3]),
+                                        pack_bf16x2(sv[o8 + 4], sv[o8 + 5]), pack_bf16x2(sv[o8 + 6], sv[o8 + 7])};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    run_l = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw[i]), ones2, run_l, false);
+                const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
                     const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&cV[(32 * mb + col) * SVS + 16 * ks4 + 8 * hi]);
                     acc[mb] = mma32(a, pf, acc[mb]);
                 }
             }
+            fetch_v(raw, kn);
+#pragma unroll
+            for (int i = 0; i < 4 * MB / 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // global loads
+            }
         }
-        if (kt + 1 < n_kt) rebuild(raw, kt + 1, buf ^ 1);
+        if (kt + 1 < n_kt) rebuild_tile(raw, kt + 1, buf ^ 1);
         __syncthreads();
     }
 
