@@ -151,10 +151,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     const int64_t start = p.seq_start[b];
     len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
     const int nblk = (len + TOK - 1) / TOK;
-    // no partials for an empty or misaligned sequence: the merge kernel writes zeros / NaN
-    if (start < 0 || start % TOK != 0 || nblk == 0) return;
     const int blk_begin = split * p.split_blocks;
-    if (blk_begin >= nblk) return;
+    if (start < 0 || start % TOK != 0 || blk_begin >= nblk) {
+        // A split with no tokens (past the sequence's end, or the sequence is empty or misaligned) marks
+        // its partial empty (max -inf, sum 0), so the merge kernel can read every split without first
+        // reading the sequence lengths; the merge writes zeros (empty) or NaN (misaligned).
+        const int64_t part = int64_t(b) * p.n_split + split;
+        for (int head = threadIdx.x; head < HP; head += kThreads)
+            *reinterpret_cast<float2 *>(p.ws_ml + (part * HP + head) * 2) = make_float2(-INFINITY, 0.f);
+        return;
+    }
     const int blk_end = min(nblk, blk_begin + p.split_blocks);
     const int full_end = min(blk_end, len / TOK);  // blocks [blk_begin, full_end) hold TOK valid tokens
     const T *seq = reinterpret_cast<const T *>(p.cache) + (start / TOK) * BLK;
@@ -429,12 +435,11 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
     const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int C4 = DP / 4, JL = kMergeThreads / C4;
     const int c4 = tid % C4, jl = tid / C4;
-    int len = p.seq_len[b];
-    len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
-    const int nblk = (len + TOK - 1) / TOK;
-    const int n_valid = (nblk + p.split_blocks - 1) / p.split_blocks;
+    // Every split wrote a partial (an empty one has max -inf), so the loads below do not wait on the
+    // sequence's length; only its start is read, for the misaligned case.
     const int64_t start = p.seq_start[b];
     const bool misaligned = start < 0 || start % TOK != 0;
+    const int n_valid = p.n_split;
 
     float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
     const int64_t base = int64_t(b) * p.n_split;
@@ -492,7 +497,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
     float o[4] = {o0, o1, o2, o3};
     if (misaligned) {
         o[0] = o[1] = o[2] = o[3] = __builtin_nanf("");
-    } else if (n_valid == 0 || L == 0.f) {
+    } else if (L == 0.f) {  // no tokens
         o[0] = o[1] = o[2] = o[3] = 0.f;
     } else {
         const float inv = p.out_mul / L;
