@@ -1,19 +1,20 @@
 """Benchmark of decode over a TPA factor cache on one MI355X.
 
-One step = one decode step of the whole hot path for a batch:
-  tpa_cache_append  (the step's new token per sequence: B_K rotated and stored;
-                     the step's query rows rotated)
-  tpa_decode        (split-sequence attention over the cached factors + merge)
+One step = one decode step of the whole hot path for a batch, in one call:
+  tpa_decode_step  (per sequence: the step's new token is appended -- B_K rotated
+                    and stored --, the query is rotated, and the query attends over
+                    the cached tokens and the new one; split + merge kernels)
 on the workload "decode_b16_h32_d128_r1_n4096": 16 sequences x 4096 cached
 tokens, h=32, d_h=128, R_K=R_V=1, bf16 factors, RoPE base 10000, synthetic
 seeded inputs.  The cache is replicated and the replicas are visited in turn so
 every step streams its factors from HBM rather than from the 256 MB
-last-level cache.
+last-level cache.  The same step as two calls (tpa_cache_append, then
+tpa_decode over the cached tokens) and tpa_decode alone are timed beside it.
 
-Printed: one JSON line with the metric (cached tokens/s), the decode kernel's
-achieved HBM bandwidth against the 8 TB/s peak, the other measured workloads
-(decode shapes and the causal prefill chunk against the bf16 matrix-core
-peak), and the fp64 CPU oracle timed on the host as a reference baseline.
+Printed: one JSON line with the metric (cached tokens/s), the step's achieved
+HBM bandwidth against the 8 TB/s peak, the other measured workloads (decode
+shapes and the causal prefill chunk against the bf16 matrix-core peak), and the
+fp64 CPU oracle timed on the host as a reference baseline.
 """
 from __future__ import annotations
 
@@ -52,8 +53,8 @@ def decode_source_hash() -> str:
 
 
 def decode_traffic():
-    """HBM bytes per tpa_decode call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by a
-    plain copy of known size); None when that summary is missing or the decode kernels changed since."""
+    """HBM bytes per tpa_decode_step call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by
+    a plain copy of known size); None when that summary is missing or the decode kernels changed since."""
     try:
         with open(TRAFFIC_FILE) as fh:
             d = json.load(fh)
@@ -61,7 +62,9 @@ def decode_traffic():
         return None
     if d.get("source_hash") != decode_source_hash():
         return None
-    return int(round(d["decode_call_traffic_bytes"]))
+    if "step_call_traffic_bytes" not in d:
+        return None
+    return int(round(d["step_call_traffic_bytes"]))
 
 
 def decode_bytes(w, lens) -> int:
@@ -69,6 +72,14 @@ def decode_bytes(w, lens) -> int:
     es = 2 if w.dtype == "bf16" else 4
     per_tok = (w.R_K + w.R_V) * (w.h + w.d_h) * es
     return int(np.sum(lens)) * per_tok + len(lens) * w.h * w.d_h * (es + 4)
+
+
+def step_bytes(w, lens) -> int:
+    """Algorithmic bytes of one fused step: the decode's, plus each new token's factors read and its record
+    written."""
+    es = 2 if w.dtype == "bf16" else 4
+    per_tok = (w.R_K + w.R_V) * (w.h + w.d_h) * es
+    return decode_bytes(w, lens) + 2 * len(lens) * per_tok
 
 
 class DecodeBench:
@@ -121,9 +132,17 @@ class DecodeBench:
         self.ws = torch.zeros(ws, dtype=torch.uint8, device="cuda")
         self.out = torch.empty(self.batch, w.h, w.d_h, dtype=torch.float32, device="cuda")
         self.bytes = decode_bytes(w, self.lens)
+        self.step_bytes = step_bytes(w, self.lens)
 
-    def step(self, i: int):
-        """One decode step on cache replica i % n_rep: append the new token + rotate the query, decode."""
+    def step(self, i: int, out=None):
+        """One fused decode step on cache replica i % n_rep (tpa_decode_step)."""
+        r = i % self.n_rep
+        self.tpa.tpa_decode_step(self.dims, self.cache.buf, self.cache.capacity, self.rep_start[r], self.seq_len,
+                                 self.max_len, self.new_AK, self.new_BK, self.new_AV, self.new_BV, self.q,
+                                 self.out if out is None else out, self.ws)
+
+    def step_two_call(self, i: int):
+        """The same step as two calls: append the new token + rotate the query, then decode the cached tokens."""
         tpa, r = self.tpa, i % self.n_rep
         tpa.tpa_cache_append(self.dims, self.cache.buf, self.cache.capacity, self.rep_slot[r], self.pos,
                              self.new_AK, self.new_BK, self.new_AV, self.new_BV, q_pos=self.pos, q_in=self.q,
@@ -142,9 +161,21 @@ class DecodeBench:
                 fn(i)
         return g
 
-    def run(self, steps: int, warmup: int):
-        """Time exactly `steps` steps.  The steps are recorded once into HIP graphs (a pass over all
-        cache replicas per graph) so the GPU is never waiting on the Python launch path."""
+    def _time(self, graph, n_calls: int, reps: int) -> float:
+        """Milliseconds per call over `reps` back-to-back replays of a graph of `n_calls` calls."""
+        torch = self.torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * n_calls)
+
+    def run(self, steps: int, warmup: int, step_only: bool = False):
+        """Time exactly `steps` fused steps.  The calls are recorded once into HIP graphs (a pass over all cache
+        replicas per graph) so the GPU is never waiting on the Python launch path."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
@@ -153,13 +184,10 @@ class DecodeBench:
         full = self._capture(self.step, self.n_rep)
         rem = steps % self.n_rep
         part = self._capture(self.step, rem) if rem else None
-        dec = self._capture(self.decode, self.n_rep)
         full.replay()
-        dec.replay()
         torch.cuda.synchronize()
 
-        ev = lambda: torch.cuda.Event(enable_timing=True)
-        a, b, c, d = ev(), ev(), ev(), ev()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
         a.record()
@@ -170,26 +198,31 @@ class DecodeBench:
         b.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
-        # the decode kernels alone, back to back over the replicas, same stream
-        n_dec = max(1, -(-steps // self.n_rep))
-        c.record()
-        for _ in range(n_dec):
-            dec.replay()
-        d.record()
-        torch.cuda.synchronize()
         ms_step = a.elapsed_time(b) / steps
-        ms_dec = c.elapsed_time(d) / (n_dec * self.n_rep)
-        # replays must reproduce the eager result bit for bit (decode is deterministic)
+        # a replay must reproduce the eager result bit for bit (the step is deterministic and rewrites the
+        # same record)
         got = self.out.clone()
         ref = torch.empty_like(self.out)
-        self.decode(self.n_rep - 1, out=ref)
+        self.step((steps - 1) % self.n_rep, out=ref)
         torch.cuda.synchronize()
         if not torch.equal(got, ref):
-            raise RuntimeError("graph replay of tpa_decode differs from the eager call")
+            raise RuntimeError("graph replay of tpa_decode_step differs from the eager call")
         toks = float(np.sum(self.lens))
-        return dict(ms_per_step=ms_step, decode_ms=ms_dec, wall_s=wall, tokens_per_s=toks / (ms_step / 1e3),
-                    decode_tokens_per_s=toks / (ms_dec / 1e3), bytes=self.bytes,
-                    decode_GBps=self.bytes / (ms_dec / 1e3) / 1e9)
+        res = dict(ms_per_step=ms_step, wall_s=wall, tokens_per_s=toks / (ms_step / 1e3), bytes=self.step_bytes,
+                   step_GBps=self.step_bytes / (ms_step / 1e3) / 1e9)
+        if step_only:
+            return res
+        # the two-call step and tpa_decode alone, each a pass over the replicas per graph, same stream
+        reps = max(1, -(-steps // self.n_rep))
+        two = self._capture(self.step_two_call, self.n_rep)
+        dec = self._capture(self.decode, self.n_rep)
+        two.replay()
+        dec.replay()
+        ms_two = self._time(two, self.n_rep, reps)
+        ms_dec = self._time(dec, self.n_rep, reps)
+        res.update(two_call_ms=ms_two, decode_ms=ms_dec, decode_tokens_per_s=toks / (ms_dec / 1e3),
+                   decode_GBps=self.bytes / (ms_dec / 1e3) / 1e9)
+        return res
 
 
 def prefill_bench(steps: int, warmup: int):
@@ -271,6 +304,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extras", action="store_true", help="time only the main workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time only the fused step of the main workload (for profiled runs)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 64 MiB device copy three times (scale reference for the HBM byte "
                          "counters of a profiled run)")
@@ -286,20 +321,28 @@ def main():
     torch.cuda.set_device(0)
 
     main_b = DecodeBench(MAIN, min_bytes=4 * MALL_BYTES)
-    res = main_b.run(args.steps, args.warmup)
-    log(f"[{main_b.w.name}] step {res['ms_per_step'] * 1e3:.2f} us, decode {res['decode_ms'] * 1e3:.2f} us, "
-        f"{res['decode_GBps']:.0f} GB/s")
+    res = main_b.run(args.steps, args.warmup, step_only=args.step_only)
+    log(f"[{main_b.w.name}] fused step {res['ms_per_step'] * 1e3:.2f} us, {res['step_GBps']:.0f} GB/s")
     extras = {}
-    if not args.no_extras:
+    if not args.step_only:
+        log(f"[{main_b.w.name}] two-call step {res['two_call_ms'] * 1e3:.2f} us, decode alone "
+            f"{res['decode_ms'] * 1e3:.2f} us, {res['decode_GBps']:.0f} GB/s")
+        extras[main_b.w.name] = dict(two_call_step_us=round(res["two_call_ms"] * 1e3, 2),
+                                     decode_us=round(res["decode_ms"] * 1e3, 2),
+                                     decode_GBps=round(res["decode_GBps"], 1),
+                                     decode_hbm_frac=round(res["decode_GBps"] / HBM_PEAK_GBS, 4))
+    if not args.no_extras and not args.step_only:
         for name in ("c3", "c4", "c5"):
             b = DecodeBench(name, min_bytes=4 * MALL_BYTES)
             r = b.run(max(10, args.steps // 4), max(3, args.warmup // 4))
             extras[b.w.name] = dict(decode_us=round(r["decode_ms"] * 1e3, 2),
                                     step_us=round(r["ms_per_step"] * 1e3, 2),
+                                    two_call_step_us=round(r["two_call_ms"] * 1e3, 2),
                                     cached_tokens_per_s=round(r["decode_tokens_per_s"], 1),
                                     GBps=round(r["decode_GBps"], 1),
                                     hbm_frac=round(r["decode_GBps"] / HBM_PEAK_GBS, 4))
-            log(f"[{b.w.name}] decode {r['decode_ms'] * 1e3:.2f} us, {r['decode_GBps']:.0f} GB/s")
+            log(f"[{b.w.name}] decode {r['decode_ms'] * 1e3:.2f} us, {r['decode_GBps']:.0f} GB/s, fused step "
+                f"{r['ms_per_step'] * 1e3:.2f} us")
             del b
             torch.cuda.empty_cache()
         p = prefill_bench(max(5, args.steps // 10), 3)
@@ -307,7 +350,7 @@ def main():
         extras[pname] = {k: round(v, 4) for k, v in p.items()}
         log(f"[prefill] {p['ms'] * 1e3:.1f} us, {p['tflops']:.1f} TFLOP/s, {100 * p['mfma_frac']:.1f}% MFMA")
 
-    achieved = res["decode_GBps"]
+    achieved = res["step_GBps"]
     line = {
         "metric": "factor-cache decode cached-tokens/s + HBM GB/s (% of roofline); prefill % MFMA",
         "value": round(res["tokens_per_s"], 1),
@@ -324,12 +367,12 @@ def main():
         "config": {"workload": main_b.w.name, "batch": main_b.batch, "cached_tokens_per_seq": main_b.max_len,
                    "h": main_b.w.h, "d_h": main_b.w.d_h, "R_K": main_b.w.R_K, "R_V": main_b.w.R_V,
                    "rope_base": main_b.w.rope_base, "cache_replicas": main_b.n_rep,
-                   "step": "tpa_cache_append (new token + query RoPE) + tpa_decode"},
-        "roofline": {"kernel": "tpa_decode (split + merge kernels, timed back to back in a graph)", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "step": "tpa_decode_step: append the new token, rotate the query, attend (split + merge)"},
+        "roofline": {"kernel": "tpa_decode_step (split + merge kernels, timed back to back in a graph)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
-                     "algorithmic_bytes_per_launch": main_b.bytes,
-                     "avg_launch_us": round(res["decode_ms"] * 1e3, 3)},
+                     "algorithmic_bytes_per_launch": main_b.step_bytes,
+                     "avg_launch_us": round(res["ms_per_step"] * 1e3, 3)},
         "extras": extras,
     }
     del main_b

@@ -44,6 +44,10 @@ _EXPORTS = {
     "tpa_decode": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                     ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p], ctypes.c_int32),
+    "tpa_decode_step": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_int32,
+                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p], ctypes.c_int32),
     "tpa_prefill_chunk": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
                            ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int32),
@@ -191,6 +195,22 @@ def tpa_decode(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_start:
         _ptr(q_rot, dims.torch_dtype, "q_rot"), float(scale), _ptr(out, torch.float32, "out"), int(split_tokens),
         _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "tpa_decode")
+
+
+def tpa_decode_step(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_start: torch.Tensor,
+                    seq_len: torch.Tensor, max_len: int, A_K: torch.Tensor, B_K: torch.Tensor, A_V: torch.Tensor,
+                    B_V: torch.Tensor, q: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                    scale: float = 0.0, split_tokens: int = 0, stream=None) -> None:
+    """One fused decode step: append each sequence's new token at slot seq_start[b] + seq_len[b] (B_K rotated
+    there), rotate q[b] at position seq_len[b], and write out[b] = attention over the seq_len[b] + 1 tokens."""
+    dt = dims.torch_dtype
+    st = load().tpa_decode_step(
+        _ref(dims), _ptr(cache, name="cache"), int(capacity_tokens), seq_start.numel(),
+        _ptr(seq_start, torch.int64, "seq_start"), _ptr(seq_len, torch.int32, "seq_len"), int(max_len),
+        _ptr(A_K, dt, "A_K"), _ptr(B_K, dt, "B_K"), _ptr(A_V, dt, "A_V"), _ptr(B_V, dt, "B_V"), _ptr(q, dt, "q"),
+        float(scale), _ptr(out, torch.float32, "out"), int(split_tokens), _ptr(workspace, name="workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "tpa_decode_step")
 
 
 def tpa_prefill_chunk(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_start: torch.Tensor,

@@ -78,6 +78,55 @@ inline bool aligned16(const void *ptr) { return reinterpret_cast<uintptr_t>(ptr)
 
 float resolve_scale(float scale, int d_h) { return scale > 0.f ? scale : float(1.0 / sqrt(double(d_h))); }
 
+// tpa_decode and tpa_decode_step: host checks, the split plan, then the split and merge kernels.
+// `step` is null for a plain decode over rotated queries.
+int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
+                   const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *q, float scale,
+                   float *out, int32_t split_tokens, void *workspace, int64_t workspace_bytes, void *stream,
+                   const tpa::StepInputs *step) {
+    int32_t st = check_dims(dims);
+    if (st != TPA_OK) return st;
+    if (batch < 0 || batch > 65535 || max_len < 0 || split_tokens < 0 || capacity_tokens < 0)
+        return TPA_ERR_ARG;
+    if (batch == 0) return TPA_OK;
+    if (!cache || !seq_start || !seq_len || !q || !out) return TPA_ERR_ARG;
+    if (!aligned16(cache) || !aligned16(q)) return TPA_ERR_ARG;
+    if (!isfinite(scale)) return TPA_ERR_ARG;
+    // a step also writes slot seq_start + seq_len, so its last possible slot must exist too
+    if (int64_t(max_len) + (step ? 1 : 0) > capacity_tokens) return TPA_ERR_CAPACITY;
+    const Layout L = layout_of(dims);
+    const DecodePlan P = plan_decode(L, batch, max_len, split_tokens);
+    if (!workspace || workspace_bytes < P.bytes) return TPA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TPA_ERR_WORKSPACE;
+    if (P.n_split > 65535) return TPA_ERR_ARG;
+
+    tpa::DecodeParams p{};
+    p.cache = cache;
+    p.seq_start = seq_start;
+    p.seq_len = seq_len;
+    p.q = q;
+    p.out = out;
+    p.ws_o = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + P.off_o);
+    p.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + P.off_ml);
+    p.h = dims->h;
+    p.d_h = dims->d_h;
+    p.RK = dims->R_K;
+    p.RV = dims->R_V;
+    p.batch = batch;
+    p.max_len = max_len;
+    p.split_blocks = P.split_blocks;
+    p.n_split = P.n_split;
+    p.score_mul = float(double(resolve_scale(scale, dims->d_h)) * M_LOG2E / dims->R_K);
+    p.out_mul = float(1.0 / dims->R_V);
+    if (step) {
+        p.step = 1;
+        p.st = *step;
+        p.rope = tpa::make_rope_table(dims->d_h, dims->rope_base);
+    }
+    const hipError_t e = tpa::launch_decode(L, p, as_stream(stream));
+    return e == hipSuccess ? TPA_OK : TPA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -163,41 +212,26 @@ int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
                    const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *q_rot,
                    float scale, float *out, int32_t split_tokens, void *workspace, int64_t workspace_bytes,
                    void *stream) {
-    int32_t st = check_dims(dims);
-    if (st != TPA_OK) return st;
-    if (batch < 0 || batch > 65535 || max_len < 0 || split_tokens < 0 || capacity_tokens < 0)
-        return TPA_ERR_ARG;
-    if (batch == 0) return TPA_OK;
-    if (!cache || !seq_start || !seq_len || !q_rot || !out) return TPA_ERR_ARG;
-    if (!aligned16(cache) || !aligned16(q_rot)) return TPA_ERR_ARG;
-    if (!isfinite(scale)) return TPA_ERR_ARG;
-    if (int64_t(max_len) > capacity_tokens) return TPA_ERR_CAPACITY;
-    const Layout L = layout_of(dims);
-    const DecodePlan P = plan_decode(L, batch, max_len, split_tokens);
-    if (!workspace || workspace_bytes < P.bytes) return TPA_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TPA_ERR_WORKSPACE;
-    if (P.n_split > 65535) return TPA_ERR_ARG;
+    return run_decode(dims, cache, capacity_tokens, batch, seq_start, seq_len, max_len, q_rot, scale, out,
+                      split_tokens, workspace, workspace_bytes, stream, nullptr);
+}
 
-    tpa::DecodeParams p;
-    p.cache = cache;
-    p.seq_start = seq_start;
-    p.seq_len = seq_len;
-    p.q = q_rot;
-    p.out = out;
-    p.ws_o = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + P.off_o);
-    p.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + P.off_ml);
-    p.h = dims->h;
-    p.d_h = dims->d_h;
-    p.RK = dims->R_K;
-    p.RV = dims->R_V;
-    p.batch = batch;
-    p.max_len = max_len;
-    p.split_blocks = P.split_blocks;
-    p.n_split = P.n_split;
-    p.score_mul = float(double(resolve_scale(scale, dims->d_h)) * M_LOG2E / dims->R_K);
-    p.out_mul = float(1.0 / dims->R_V);
-    const hipError_t e = tpa::launch_decode(L, p, as_stream(stream));
-    return e == hipSuccess ? TPA_OK : TPA_ERR_HIP;
+int32_t tpa_decode_step(const tpa_dims *dims, void *cache, int64_t capacity_tokens, int32_t batch,
+                        const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *A_K,
+                        const void *B_K, const void *A_V, const void *B_V, const void *q, float scale, float *out,
+                        int32_t split_tokens, void *workspace, int64_t workspace_bytes, void *stream) {
+    const int32_t st = check_dims(dims);
+    if (st != TPA_OK) return st;
+    if (batch > 0 && (!A_K || !B_K || !A_V || !B_V)) return TPA_ERR_ARG;
+    tpa::StepInputs step;
+    step.A_K = A_K;
+    step.B_K = B_K;
+    step.A_V = A_V;
+    step.B_V = B_V;
+    step.cache = cache;
+    step.capacity = capacity_tokens;
+    return run_decode(dims, cache, capacity_tokens, batch, seq_start, seq_len, max_len, q, scale, out, split_tokens,
+                      workspace, workspace_bytes, stream, &step);
 }
 
 int32_t tpa_prefill_chunk(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,

@@ -20,41 +20,12 @@ namespace {
 
 constexpr int kAppendThreads = 128;
 
-// Arithmetic of the rotation.  The angle pos * theta_j is always formed and reduced modulo 2 pi in
-// fp64 (positions reach 131072 and beyond, where an fp32 angle is off by milliradians).  For bf16
-// storage, cos/sin of the reduced angle (|r| <= pi) and the rotation itself are then fp32: their error,
-// ~1e-7 relative, is far below half a bf16 unit, so the stored value is the correctly rounded rotation
-// except within 1e-7 of a rounding tie (at most one unit off).  fp32 storage keeps fp64 throughout.
-template <typename T>
-struct RopeMath {
-    using F = double;
-    __device__ static void sincos_reduced(double r, F *s, F *c) { sincos(r, s, c); }
-};
-template <>
-struct RopeMath<uint16_t> {
-    using F = float;
-    __device__ static void sincos_reduced(double r, F *s, F *c) { sincosf(float(r), s, c); }
-};
-
 // cos and sin of pos * theta_j for the d_h/2 pairs of one position, shared by the work-group.
 // theta is this thread's theta_j (j = threadIdx.x < d_h/2; d_h/2 <= kAppendThreads), loaded up front.
-// The reduction is Cody-Waite with 2 pi split in two doubles; positions are int32, so |angle| < 2^31
-// and the two-part split keeps r exact to ~1e-15 before sincos sees |r| <= pi.
 template <typename T>
 __device__ inline void rope_table(typename RopeMath<T>::F *cs, int d_h, double pos, double theta) {
-    constexpr double kTwoPiHi = 6.283185307179586232;    // nearest double to 2 pi
-    constexpr double kTwoPiLo = 2.4492935982947064e-16;  // 2 pi - kTwoPiHi
-    constexpr double kInvTwoPi = 0.15915494309189535;
     const int j = threadIdx.x;
-    if (j < d_h / 2) {
-        const double phi = pos * theta;
-        const double k = rint(phi * kInvTwoPi);
-        const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, phi));
-        typename RopeMath<T>::F sn, cn;
-        RopeMath<T>::sincos_reduced(r, &sn, &cn);
-        cs[2 * j] = cn;
-        cs[2 * j + 1] = sn;
-    }
+    if (j < d_h / 2) rope_cos_sin<T>(cs + 2 * j, pos, theta);
     __syncthreads();
 }
 
@@ -86,9 +57,9 @@ struct Pair<float> {
 template <typename T>
 __device__ inline typename Pair<T>::V rope_pair(typename Pair<T>::V x, const typename RopeMath<T>::F *cs, int j) {
     using P = Pair<T>;
-    const auto c = cs[2 * j], s = cs[2 * j + 1];
-    const auto a = P::lo(x), b = P::hi(x);
-    return P::make(fma(a, c, -(b * s)), fma(a, s, b * c));
+    typename RopeMath<T>::F y0, y1;
+    rope_rotate(P::lo(x), P::hi(x), cs[2 * j], cs[2 * j + 1], y0, y1);
+    return P::make(y0, y1);
 }
 
 template <typename T>
@@ -233,6 +204,12 @@ __global__ __launch_bounds__(kAppendThreads) void read_kernel(Layout L, int h, i
 
 }  // namespace
 
+RopeTable make_rope_table(int d_h, double base) {
+    RopeTable rt;
+    for (int j = 0; j < 128; ++j) rt.theta[j] = j < d_h / 2 ? pow(base, -2.0 * double(j) / double(d_h)) : 0.0;
+    return rt;
+}
+
 hipError_t launch_append(const Layout &L, int h, int d_h, int RK, int RV, double base, void *cache,
                          int64_t capacity, int64_t n_kv, const int64_t *slot, const int32_t *kv_pos,
                          const void *A_K, const void *B_K, const void *A_V, const void *B_V, int64_t n_q,
@@ -244,8 +221,7 @@ hipError_t launch_append(const Layout &L, int h, int d_h, int RK, int RV, double
     const int64_t grid = n_kv + n_q * q_groups;
     if (grid == 0) return hipSuccess;
     if (grid > int64_t(0x7fffffff)) return hipErrorInvalidConfiguration;
-    RopeTable rt;
-    for (int j = 0; j < 128; ++j) rt.theta[j] = j < d_h / 2 ? pow(base, -2.0 * double(j) / double(d_h)) : 0.0;
+    const RopeTable rt = make_rope_table(d_h, base);
     if (L.es == 2) {
         using T = uint16_t;
         hipLaunchKernelGGL(append_kernel<T>, dim3(unsigned(grid)), dim3(kAppendThreads), 0, s, L, h, d_h, RK, RV,

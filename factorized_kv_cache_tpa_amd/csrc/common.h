@@ -136,6 +136,58 @@ struct Elem<uint16_t> {
     __device__ static uint16_t from_f64(double x) { return f32_to_bf16_rne(float(x)); }
 };
 
+// ---- RoPE (TPA notes page, Key design, RoPE compatibility): RoFormer pairs (2j, 2j+1),
+// theta_j = base^(-2j/d_h), (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a), a = pos * theta_j.
+// Shared by the cache append and the fused decode step, so both write bit-identical records.
+
+// Frequencies theta_j, j < d_h/2, computed once per call on the host in fp64 and passed by value.
+struct RopeTable {
+    double theta[128];
+};
+
+// Arithmetic of the rotation.  The angle pos * theta_j is always formed and reduced modulo 2 pi in
+// fp64 (positions reach 131072 and beyond, where an fp32 angle is off by milliradians).  For bf16
+// storage, cos/sin of the reduced angle and the rotation itself are then fp32: their error, ~1e-7
+// relative, is far below half a bf16 unit, so the stored value is the correctly rounded rotation
+// except within 1e-7 of a rounding tie (at most one unit off).  fp32 storage keeps fp64 throughout.
+template <typename T>
+struct RopeMath {
+    using F = double;
+    __device__ static void sincos_reduced(double r, F *s, F *c) { sincos(r, s, c); }
+};
+template <>
+struct RopeMath<uint16_t> {
+    using F = float;
+    __device__ static void sincos_reduced(double r, F *s, F *c) { sincosf(float(r), s, c); }
+};
+
+// cos and sin of pos * theta into cs[0], cs[1].  The reduction is Cody-Waite with 2 pi split in two
+// doubles; positions are int32, so |angle| < 2^31 and r is exact to ~1e-15 before sincos sees |r| <= pi.
+template <typename T>
+__device__ inline void rope_cos_sin(typename RopeMath<T>::F *cs, double pos, double theta) {
+    constexpr double kTwoPiHi = 6.283185307179586232;    // nearest double to 2 pi
+    constexpr double kTwoPiLo = 2.4492935982947064e-16;  // 2 pi - kTwoPiHi
+    constexpr double kInvTwoPi = 0.15915494309189535;
+    const double phi = pos * theta;
+    const double k = rint(phi * kInvTwoPi);
+    const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, phi));
+    RopeMath<T>::sincos_reduced(r, &cs[1], &cs[0]);
+}
+
+// (a, b) rotated by the angle whose cos, sin are c, s, in the precision F; the caller rounds once to T.
+template <typename F>
+__device__ inline void rope_rotate(F a, F b, F c, F s, F &y0, F &y1) {
+    y0 = fma(a, c, -(b * s));
+    y1 = fma(a, s, b * c);
+}
+
+// New token of a fused decode step (tpa_decode_step): unrotated factors [batch][R][h | d_h].
+struct StepInputs {
+    const void *A_K, *B_K, *A_V, *B_V;
+    void *cache;       // the cache, written at slot seq_start[b] + seq_len[b]
+    int64_t capacity;  // slots in the cache
+};
+
 // Parameters of one decode call, shared by the split and merge kernels.
 struct DecodeParams {
     const void *cache;
@@ -149,6 +201,11 @@ struct DecodeParams {
     int batch, max_len, split_blocks, n_split;
     float score_mul;  // scale * log2(e) / R_K
     float out_mul;    // 1 / R_V
+    // Fused step (tpa_decode_step) when nonzero: q is unrotated and sits at position seq_len[b]; the
+    // split kernel rotates it, the merge kernel folds in the new token and writes its record.
+    int step;
+    StepInputs st;
+    RopeTable rope;
 };
 
 struct PrefillParams {
@@ -163,11 +220,8 @@ struct PrefillParams {
     float out_mul;    // 1 / R_V
 };
 
-// RoPE frequencies theta_j = base^(-2j/d_h), j < d_h/2, computed once per call on the host in fp64
-// and passed to the kernel by value.
-struct RopeTable {
-    double theta[128];
-};
+// Host: theta_j = base^(-2j/d_h) in fp64 (zeros past d_h/2).
+RopeTable make_rope_table(int d_h, double base);
 
 // Work-groups of tpa_cache_append per query token of q_rows rows.
 int64_t append_q_groups(int q_rows, int d_h);

@@ -80,6 +80,26 @@ struct Mfma<uint16_t> {  // bf16 in, fp32 accumulate: v_mfma_f32_16x16x32_bf16
         for (int e = 0; e < 8; ++e) x[e] = d0 + e < d_h ? bf16_to_f32(src[e]) : 0.f;
         return pack(x);
     }
+    __device__ static float value(Frag f, int e) {
+        const uint4 v = __builtin_bit_cast(uint4, f);
+        const uint32_t w = e < 2 ? v.x : (e < 4 ? v.y : (e < 6 ? v.z : v.w));
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+    // RoPE of a loaded fragment q[head][d0 .. d0+7] (d0 even: four whole pairs), cs = cos/sin table
+    __device__ static Frag rotate_q(Frag f, int d0, const float *cs) {
+        const uint4 v = __builtin_bit_cast(uint4, f);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int j = (d0 >> 1) + k;
+            float y0, y1;
+            rope_rotate(bf16_to_f32(uint16_t(w[k] & 0xffffu)), bf16_to_f32(uint16_t(w[k] >> 16)), cs[2 * j],
+                        cs[2 * j + 1], y0, y1);
+            o[k] = pack_bf16x2(y0, y1);
+        }
+        return __builtin_bit_cast(Frag, make_uint4(o[0], o[1], o[2], o[3]));
+    }
     __device__ static floatx4 mma(Frag a, Frag b, floatx4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
@@ -104,6 +124,16 @@ struct Mfma<float> {  // fp32 in, fp32 accumulate: v_mfma_f32_16x16x4_f32
     __device__ static Frag load_q(const float *qb, int head, int d0, int h, int d_h) {
         return (head < h && d0 < d_h) ? qb[int64_t(head) * d_h + d0] : 0.f;
     }
+    __device__ static float value(Frag f, int) { return f; }
+    // RoPE of q[head][d0]: its pair partner d0 ^ 1 sits in the lane 16 apart (g ^ 1, same head)
+    __device__ static Frag rotate_q(Frag f, int d0, const double *cs) {
+        const float partner = __shfl_xor(f, 16, kWave);
+        const int j = d0 >> 1;
+        const double a = (d0 & 1) ? partner : f, b = (d0 & 1) ? f : partner;
+        double y0, y1;
+        rope_rotate(a, b, cs[2 * j], cs[2 * j + 1], y0, y1);
+        return float((d0 & 1) ? y1 : y0);
+    }
     __device__ static floatx4 mma(Frag a, Frag b, floatx4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
@@ -122,7 +152,8 @@ __device__ __forceinline__ float wave_sum_across_groups(float x) {
     return x;
 }
 
-template <typename T, int HP, int DP, int RH>
+// kStep: a fused step (tpa_decode_step), a separate instantiation so the plain decode carries none of it.
+template <typename T, int HP, int DP, int RH, bool kStep>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
     using M = Mfma<T>;
     using Frag = typename M::Frag;
@@ -137,9 +168,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     constexpr int64_t BLK = 2LL * kRows * (HP + DP);
     constexpr int OFF_AV = kRows * HP, OFF_BK = 2 * kRows * HP, OFF_BV = 2 * kRows * HP + kRows * DP;
 
-    __shared__ float sm_m[kWaves][HP];
-    __shared__ float sm_l[kWaves][HP];
+    using F = typename RopeMath<T>::F;
+    // per-wave (max, sum); row kWaves holds a fused step's new token (split 0), else (-inf, 0)
+    __shared__ float sm_m[kWaves + 1][HP];
+    __shared__ float sm_l[kWaves + 1][HP];
     __shared__ __attribute__((aligned(16))) float sm_o[kWaves][HP][DP + 4];
+    constexpr int SH = kStep ? HP : 1, SD = kStep ? DP : 2;
+    __shared__ F sm_cs[SD];             // fused step: cos/sin of the query's position
+    __shared__ float sm_na[2][RH][SH];  // fused step, split 0: the new token's A_K, A_V
+    __shared__ float sm_nb[2][RH][SD];  // ... and its B~_K (rotated, rounded as stored), B_V
+    static_assert(RH * HP <= kThreads && RH * DP / 2 <= kThreads && DP / 2 <= kThreads,
+                  "one new-token item and one RoPE pair per thread");
 
     const int b = blockIdx.y;
     const int split = blockIdx.x;
@@ -152,7 +191,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
     const int nblk = (len + TOK - 1) / TOK;
     const int blk_begin = split * p.split_blocks;
-    if (start < 0 || start % TOK != 0 || blk_begin >= nblk) {
+    const bool misaligned = start < 0 || start % TOK != 0;
+    // A fused step's split 0 carries the step's new token (even over an empty sequence): it writes the
+    // token's record and folds the token's own score and value into its partial.
+    const bool new_tok = kStep && split == 0 && !misaligned;
+    if (misaligned || (blk_begin >= nblk && !new_tok)) {
         // A split with no tokens (past the sequence's end, or the sequence is empty or misaligned) marks
         // its partial empty (max -inf, sum 0), so the merge kernel can read every split without first
         // reading the sequence lengths; the merge writes zeros (empty) or NaN (misaligned).
@@ -194,6 +237,35 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             for (int q = 0; q < KBV; ++q) st.bv[mv][q] = M::stream(op + OFF_BV + (mv * KBV + q) * kWave * E);
     };
 
+    // Fused step, split 0: this thread's item of the new token (one head-factor pair (A_K, A_V) of row
+    // r, head i, and one feature pair (d, d+1) of B_K and B_V of row r), loaded before everything else:
+    // memory returns in order, so these must not queue behind the factor stream.
+    const int tid = threadIdx.x;
+    const int na_r = tid / HP, na_i = tid % HP, nb_r = tid / (DP / 2), nb_d = 2 * (tid % (DP / 2));
+    T nak = T(0), nav = T(0), nbk0 = T(0), nbk1 = T(0), nbv0 = T(0), nbv1 = T(0);
+    if (kStep && new_tok) {
+        const T *AK = reinterpret_cast<const T *>(p.st.A_K) + int64_t(b) * p.RK * p.h;
+        const T *AV = reinterpret_cast<const T *>(p.st.A_V) + int64_t(b) * p.RV * p.h;
+        const T *BK = reinterpret_cast<const T *>(p.st.B_K) + int64_t(b) * p.RK * p.d_h;
+        const T *BV = reinterpret_cast<const T *>(p.st.B_V) + int64_t(b) * p.RV * p.d_h;
+        if (na_r < p.RK && na_i < p.h) nak = AK[na_r * p.h + na_i];
+        if (na_r < p.RV && na_i < p.h) nav = AV[na_r * p.h + na_i];
+        if (nb_r < p.RK && nb_d < p.d_h) {
+            nbk0 = BK[nb_r * p.d_h + nb_d];
+            nbk1 = BK[nb_r * p.d_h + nb_d + 1];
+        }
+        if (nb_r < p.RV && nb_d < p.d_h) {
+            nbv0 = BV[nb_r * p.d_h + nb_d];
+            nbv1 = BV[nb_r * p.d_h + nb_d + 1];
+        }
+    }
+    for (int head = tid; head < HP; head += kThreads) {
+        sm_m[kWaves][head] = -INFINITY;
+        sm_l[kWaves][head] = 0.f;
+    }
+    // fused step: this thread's RoPE frequency (pair j = tid), read now for the same reason
+    const double theta_j = kStep && tid < DP / 2 ? p.rope.theta[tid] : 0.0;
+
     // query operand (B of the score contraction; loaded first: memory returns in order, so the first
     // block can start as soon as its own loads land): lane holds q~[16 nb + c][4E kb + E g + e]
     Frag qf[KBS][NB];
@@ -208,15 +280,101 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                 qf[kb][nb] = M::load_q(qb, head, d0, p.h, p.d_h);
             }
     }
-
     // Two register stages (the next block's loads in flight while one is consumed) wherever they
     // fit in the register file; wide fp32 operands use one stage.
     constexpr bool kTwoStages = sizeof(T) == 2 || HP * DP <= 1024;
     Stage s0, s1;
     int blk = blk_begin + w;
-    if (kTwoStages) {  // start streaming the first two blocks before anything else
+    if (kTwoStages) {  // start streaming the first two blocks before anything else (a fused step issues
+                       // the second after its own set-up: a wave cannot pass its loads' issue until most of
+                       // them have landed, so work placed behind both stages would wait for the stream)
         if (blk < full_end) load(s0, blk);
-        if (blk + kWaves < full_end) load(s1, blk + kWaves);
+        if (!kStep && blk + kWaves < full_end) load(s1, blk + kWaves);
+    }
+    if constexpr (kStep) {
+        // Fused step, while the first blocks stream in: q arrives unrotated and sits at position len (the
+        // number of cached tokens); rotate it in registers.  The table covers every padded pair (theta is
+        // zero past d_h / 2: an identity rotation of zeros).  Split 0 also writes the new token's record at
+        // slot len: no work-group of this kernel reads that slot's rows (a partly filled last block masks
+        // every row at or past len), and the next call sees it.
+        if (tid < DP / 2) rope_cos_sin<T>(sm_cs + 2 * tid, double(len), theta_j);
+        __syncthreads();
+#pragma unroll
+        for (int kb = 0; kb < KBS; ++kb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) qf[kb][nb] = M::rotate_q(qf[kb][nb], 4 * E * kb + E * g, sm_cs);
+        if (new_tok) {
+            // the record, rotated and rounded exactly as tpa_cache_append stores it
+            T k0 = nbk0, k1 = nbk1;
+            if (nb_r < p.RK && nb_d < p.d_h) {
+                F y0, y1;
+                rope_rotate(F(Elem<T>::to_f32(nbk0)), F(Elem<T>::to_f32(nbk1)), sm_cs[nb_d], sm_cs[nb_d + 1], y0, y1);
+                if constexpr (sizeof(T) == 2) {
+                    const uint32_t pk = pack_bf16x2(y0, y1);
+                    k0 = T(pk & 0xffffu);
+                    k1 = T(pk >> 16);
+                } else {
+                    k0 = T(y0);
+                    k1 = T(y1);
+                }
+            }
+            const int64_t slot = start + len;
+            if (slot < p.st.capacity) {
+                T *rec = reinterpret_cast<T *>(p.st.cache) + (slot / TOK) * BLK;
+                const int row0 = int(slot % TOK) * RH;
+                const Layout Lay = make_layout(p.h, p.d_h, p.RK, p.RV, Elem<T>::dtype);
+                if (na_r < RH) {
+                    rec[Lay.gate(row0 + na_r, na_i)] = nak;
+                    rec[OFF_AV + Lay.gate(row0 + na_r, na_i)] = nav;
+                }
+                if (nb_r < RH) {
+                    rec[OFF_BK + Lay.bk(row0 + nb_r, nb_d)] = k0;
+                    rec[OFF_BK + Lay.bk(row0 + nb_r, nb_d + 1)] = k1;
+                    rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d)] = nbv0;
+                    rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d + 1)] = nbv1;
+                }
+            }
+            // the token's factors in LDS for its score and value row
+            if (na_r < RH) {
+                sm_na[0][na_r][na_i] = Elem<T>::to_f32(nak);
+                sm_na[1][na_r][na_i] = Elem<T>::to_f32(nav);
+            }
+            if (nb_r < RH) {
+                sm_nb[0][nb_r][nb_d] = Elem<T>::to_f32(k0);
+                sm_nb[0][nb_r][nb_d + 1] = Elem<T>::to_f32(k1);
+                sm_nb[1][nb_r][nb_d] = Elem<T>::to_f32(nbv0);
+                sm_nb[1][nb_r][nb_d + 1] = Elem<T>::to_f32(nbv1);
+            }
+            __syncthreads();
+            // its score per head, from the rotated query fragments: a lane sums its d-values, the four
+            // lane groups of a head are summed across (the same contraction as the cached tokens')
+            if (w == 0) {
+                float dot[NB][RH];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int r = 0; r < RH; ++r) {
+                        float x = 0.f;
+#pragma unroll
+                        for (int kb = 0; kb < KBS; ++kb)
+#pragma unroll
+                            for (int e = 0; e < E; ++e)
+                                x = fmaf(M::value(qf[kb][nb], e), sm_nb[0][r][4 * E * kb + E * g + e], x);
+                        dot[nb][r] = wave_sum_across_groups(x);
+                    }
+                if (g == 0)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const int head = 16 * nb + c;
+                        float z = 0.f;
+#pragma unroll
+                        for (int r = 0; r < RH; ++r) z = fmaf(sm_na[0][r][head], dot[nb][r], z);
+                        sm_m[kWaves][head] = head < p.h ? z * p.score_mul : -INFINITY;
+                        sm_l[kWaves][head] = head < p.h ? 1.f : 0.f;
+                    }
+            }
+        }
+        if (kTwoStages && blk + kWaves < full_end) load(s1, blk + kWaves);
     }
 
 
@@ -382,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         const int head = 16 * nb + c;
         float mm = sm_m[0][head];
 #pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][head]);
+        for (int ww = 1; ww <= kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][head]);
         wscale[nb] = run_m[nb] == -INFINITY ? 0.f : exp2f(run_m[nb] - mm);
     }
     // every wave writes its rescaled accumulators to its own LDS slice; after one barrier all threads
@@ -409,13 +567,28 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             o.z += x.z;
             o.w += x.w;
         }
+        if constexpr (kStep) {
+            if (new_tok && sm_m[kWaves][hh] != -INFINITY) {  // the new token's value row, at its own weight
+                float mm = sm_m[0][hh];
+                for (int ww = 1; ww <= kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][hh]);
+                const float wt = exp2f(sm_m[kWaves][hh] - mm);
+                float v[4] = {0.f, 0.f, 0.f, 0.f};
+                for (int r = 0; r < RH; ++r)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) v[k] = fmaf(sm_na[1][r][hh], sm_nb[1][r][4 * d4 + k], v[k]);
+                o.x = fmaf(v[0], wt, o.x);
+                o.y = fmaf(v[1], wt, o.y);
+                o.z = fmaf(v[2], wt, o.z);
+                o.w = fmaf(v[3], wt, o.w);
+            }
+        }
         *reinterpret_cast<float4 *>(wo + hh * DP + 4 * d4) = o;
     }
     for (int head = threadIdx.x; head < HP; head += kThreads) {
         float mm = sm_m[0][head];
-        for (int ww = 1; ww < kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][head]);
+        for (int ww = 1; ww <= kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][head]);
         float ll = 0.f;
-        for (int ww = 0; ww < kWaves; ++ww)
+        for (int ww = 0; ww <= kWaves; ++ww)
             ll += sm_m[ww][head] == -INFINITY ? 0.f : sm_l[ww][head] * exp2f(sm_m[ww][head] - mm);
         *reinterpret_cast<float2 *>(p.ws_ml + (part * HP + head) * 2) = make_float2(mm, ll);
     }
@@ -426,7 +599,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 // thread t owns output columns 4 (t % C4) .. +3 and the splits j = t / C4 (mod JL),
 // where C4 = DP / 4 and JL = 256 / C4.  Each thread folds its splits with the
 // same rescaling rule, loads issued eight at a time, and the JL lanes of a column
-// group are folded once more through LDS.
+// group are folded once more through LDS.  (A fused step's new token is already part
+// of split 0's partial.)
 constexpr int kMergeThreads = 256;
 constexpr int kMergeUnroll = 8;
 
@@ -510,7 +684,12 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
 
 template <typename T, int HP, int DP, int RH>
 hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH>), dim3(p.n_split, p.batch), dim3(kThreads), 0, s, p);
+    if (p.step)
+        hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, true>), dim3(p.n_split, p.batch), dim3(kThreads), 0,
+                           s, p);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, false>), dim3(p.n_split, p.batch), dim3(kThreads), 0,
+                           s, p);
     return hipGetLastError();
 }
 

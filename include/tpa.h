@@ -154,6 +154,26 @@ int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
                    float scale, float *out, int32_t split_tokens, void *workspace, int64_t workspace_bytes,
                    void *stream);
 
+/* Fused single decode step (one new token per sequence): for each sequence b with N = seq_len[b] cached
+ * tokens, write the new token's factors into slot seq_start[b] + N (B_K rotated at position N, exactly as
+ * tpa_cache_append writes it), rotate the query at position N, and attend over the N cached tokens and
+ * the new one (the one-query decode of the TPA notes page, FlashTPA; RoPE compatibility, Theorem 3.1):
+ *     out[b][i] = sum_{s <= N} softmax_s(scale * q~_b,i . K~_s[i,:]) V_s[i,:]
+ * Two kernel launches (split, merge) and no separate append: the split kernel rotates the query in
+ * registers, the merge kernel folds in the new token's own score and value (query and token share a
+ * position, so RoPE cancels in that score) and writes its record.
+ *   A_K [batch][R_K][h], B_K [batch][R_K][d_h], A_V [batch][R_V][h], B_V [batch][R_V][d_h]
+ *                     the new token's factors, unrotated
+ *   q [batch][h][d_h]  the step's query, unrotated (16-byte aligned)
+ *   seq_len[batch]     cached tokens before the step; not modified (the caller advances it)
+ *   max_len [host]     >= every seq_len; max_len + 1 <= capacity_tokens (TPA_ERR_CAPACITY otherwise)
+ * Other arguments, the workspace (tpa_decode_workspace_bytes(dims, batch, max_len, split_tokens)) and the
+ * error behaviour are those of tpa_decode; a slot at or past the capacity is not written. */
+int32_t tpa_decode_step(const tpa_dims *dims, void *cache, int64_t capacity_tokens, int32_t batch,
+                        const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *A_K,
+                        const void *B_K, const void *A_V, const void *B_V, const void *q, float scale, float *out,
+                        int32_t split_tokens, void *workspace, int64_t workspace_bytes, void *stream);
+
 /* Causal chunked prefill: chunk_len query rows per sequence attend to the
  * sequence's cached context and to the chunk's own tokens up to and including
  * their own (the chunk's factors must already be in the cache, appended at

@@ -230,3 +230,29 @@ def test_misaligned_pointers_rejected(lib):
     r4 = ctypes.byref(d4)
     for cache, q, out in [(odd8, FAKE, FAKE), (FAKE, odd8, FAKE), (FAKE, FAKE, odd8)]:
         assert lib.tpa_prefill_chunk(r4, cache, 8192, 1, FAKE, FAKE, 1024, 64, q, 0.0, out, None) == 1
+
+
+def test_decode_step_argument_checks(lib):
+    d = _d()
+    ref = ctypes.byref(d)
+    need = lib.tpa_decode_workspace_bytes(ref, 16, 4096, 0)
+    ok = dict(cache=FAKE, cap=8192, batch=16, start=FAKE, lens=FAKE, max_len=4096, f=[FAKE] * 4, q=FAKE,
+              out=FAKE, ws=FAKE, ws_bytes=need)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.tpa_decode_step(ref, a["cache"], a["cap"], a["batch"], a["start"], a["lens"], a["max_len"],
+                                   *a["f"], a["q"], 0.0, a["out"], 0, a["ws"], a["ws_bytes"], None)
+    # batch 0 is a no-op; null factors / query / output; the new slot must fit (max_len + 1 <= capacity)
+    assert lib.tpa_decode_step(ref, None, 0, 0, None, None, 0, None, None, None, None, None, 0.0, None, 0, None,
+                               0, None) == 0
+    assert call(f=[FAKE, None, FAKE, FAKE]) == 1
+    assert call(q=None) == 1
+    assert call(out=None) == 1
+    assert call(cap=4096) == 3
+    assert call(ws_bytes=need - 1) == 4
+    assert call(q=ctypes.c_void_p(0x1008)) == 1
+    assert call(cache=ctypes.c_void_p(0x1008)) == 1
+    bad = _d(h=64, d_h=256)
+    assert lib.tpa_decode_step(ctypes.byref(bad), FAKE, 8192, 16, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               0.0, FAKE, 0, FAKE, need, None) == 2
