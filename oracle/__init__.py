@@ -53,6 +53,8 @@ def _load():
         lib.tpa_oracle_attention.argtypes = [ctypes.c_int] * 4 + [ctypes.c_int64] + [D] * 5 + [
             ctypes.c_int64, D, D, I64, ctypes.c_double, ctypes.c_double, D, ctypes.c_int]
         lib.tpa_oracle_attention.restype = ctypes.c_int
+        lib.tpa_oracle_query_from_factors.argtypes = [ctypes.c_int] * 3 + [ctypes.c_int64, D, D, D]
+        lib.tpa_oracle_query_from_factors.restype = None
         lib.tpa_oracle_factor_elems_per_token.argtypes = [ctypes.c_int] * 4
         lib.tpa_oracle_factor_elems_per_token.restype = ctypes.c_int64
         lib.tpa_oracle_dense_elems_per_token.argtypes = [ctypes.c_int] * 2
@@ -109,6 +111,17 @@ def attention(A_K, B_K, A_V, B_V, kv_pos, q, q_pos, q_nvis, base: float, scale: 
         q_nvis.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), float(base), float(scale), _dp(out), int(nt))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
+    return out
+
+
+def query_from_factors(A_Q, B_Q) -> np.ndarray:
+    """Query rows from query factors: q[n][i][c] = (1/R_Q) sum_r A_Q[n][r][i] B_Q[n][r][c] -> [n][h][d]."""
+    A_Q, B_Q = _f64(A_Q), _f64(B_Q)
+    n, RQ, h = A_Q.shape
+    d = B_Q.shape[2]
+    assert B_Q.shape == (n, RQ, d)
+    out = np.zeros((n, h, d), dtype=np.float64)
+    _load().tpa_oracle_query_from_factors(h, d, RQ, n, _dp(A_Q), _dp(B_Q), _dp(out))
     return out
 
 

@@ -135,6 +135,21 @@ int tpa_oracle_attention(int h, int d, int RK, int RV, int64_t n_kv, const doubl
 
 /* Per-token element counts the pages compare (tensor product decomposition paragraph):
  * a TPA cache holds (R_K + R_V)(h + d_h) elements per token, a dense MHA cache 2 h d_h. */
+/* Query rows from query factors (full TPA: the tensor product decomposition applied to Q, same page,
+ * Key design: tensor product decomposition):  q[n][i][c] = (1/R_Q) sum_r A_Q[n][r][i] B_Q[n][r][c],
+ * A_Q [n][R_Q][h], B_Q [n][R_Q][d] (unrotated), out [n][h][d].  The result is the query of step 3 above,
+ * rotated there at its position like any other query row. */
+void tpa_oracle_query_from_factors(int h, int d, int RQ, int64_t n, const double *AQ, const double *BQ,
+                                   double *out) {
+    for (int64_t t = 0; t < n; ++t)
+        for (int i = 0; i < h; ++i)
+            for (int c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (int r = 0; r < RQ; ++r) acc += AQ[(t * RQ + r) * h + i] * BQ[(t * RQ + r) * d + c];
+                out[(t * h + i) * d + c] = acc / RQ;
+            }
+}
+
 int64_t tpa_oracle_factor_elems_per_token(int h, int d, int RK, int RV) {
     return (int64_t)(RK + RV) * (int64_t)(h + d);
 }

@@ -52,3 +52,9 @@ def attention(A_K, B_K, A_V, B_V, kv_pos, q, q_pos, q_nvis, base, scale=None):
             heads.append([math.fsum(p[s] * vals[s][c] for s in range(nv)) / L for c in range(d)])
         out.append(heads)
     return out
+
+
+def query_from_factors(A_Q, B_Q):
+    """q[i][c] = (1/R_Q) sum_r A_Q[r][i] B_Q[r][c] for one query token, as fsum loops."""
+    RQ, h, d = len(A_Q), len(A_Q[0]), len(B_Q[0])
+    return [[math.fsum(A_Q[r][i] * B_Q[r][c] for r in range(RQ)) / RQ for c in range(d)] for i in range(h)]

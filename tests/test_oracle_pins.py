@@ -239,3 +239,66 @@ def test_brute_force_on_tiny_fp32_workload():
     want = brute_force.attention(A_K.tolist(), B_K.tolist(), A_V.tolist(), B_V.tolist(), list(range(64)),
                                  q.tolist(), [64], [64], w.rope_base)
     np.testing.assert_allclose(got, np.array(want)[0], rtol=0, atol=1e-12)
+
+
+# --- factored query (full TPA: Q = (1/R_Q) A_Q^T B_Q, same tensor product decomposition) --------------
+
+def test_query_factors_with_permutation_head_factor_select_rows():
+    """R_Q = h and A_Q = R_Q * P (P a permutation with no fixed points): q[i] is exactly row P(i) of B_Q,
+    so a transposed head factor, a dropped 1/R_Q or a wrong index fails."""
+    h, d = 5, 6
+    perm = [2, 3, 4, 0, 1]
+    rng = np.random.default_rng(3)
+    B_Q = rng.standard_normal((1, h, d))
+    A_Q = np.zeros((1, h, h))
+    for i in range(h):
+        A_Q[0, perm[i], i] = h
+    q = oracle.query_from_factors(A_Q, B_Q)[0]
+    for i in range(h):  # (h * x) / h is x to within one rounding
+        np.testing.assert_allclose(q[i], B_Q[0, perm[i]], rtol=2.3e-16, atol=0)
+
+
+@pytest.mark.parametrize("h,d,RQ", [(1, 2, 1), (4, 16, 3), (3, 8, 6)])
+def test_query_factors_match_brute_force(h, d, RQ):
+    rng = np.random.default_rng(h * 10 + RQ)
+    A_Q, B_Q = rng.standard_normal((2, RQ, h)), rng.standard_normal((2, RQ, d))
+    got = oracle.query_from_factors(A_Q, B_Q)
+    for t in range(2):
+        want = brute_force.query_from_factors(A_Q[t].tolist(), B_Q[t].tolist())
+        np.testing.assert_allclose(got[t], np.array(want), rtol=0, atol=1e-14)
+
+
+def test_query_factor_rank_permutation_and_rescaling_invariance():
+    rng = np.random.default_rng(8)
+    A_Q, B_Q = rng.standard_normal((1, 4, 6)), rng.standard_normal((1, 4, 10))
+    q = oracle.query_from_factors(A_Q, B_Q)
+    perm = [3, 1, 0, 2]
+    np.testing.assert_allclose(oracle.query_from_factors(A_Q[:, perm], B_Q[:, perm]), q, rtol=0, atol=1e-14)
+    c = np.array([2.0, -0.5, 4.0, 0.25])[None, :, None]
+    np.testing.assert_allclose(oracle.query_from_factors(A_Q * c, B_Q / c), q, rtol=0, atol=1e-13)
+
+
+def test_rope_of_query_factors_commutes_with_their_combination():
+    """Rotating the B_Q rows at a position and then combining equals combining and then rotating (RoPE is
+    linear), which is why the feature factor alone can be rotated (RoPE compatibility, Theorem 3.1)."""
+    rng = np.random.default_rng(9)
+    A_Q, B_Q = rng.standard_normal((1, 3, 4)), rng.standard_normal((1, 3, 16))
+    for pos in (0, 7, 4096, 131071):
+        a = oracle.rope_rows(oracle.query_from_factors(A_Q, B_Q)[0], pos, 1e4)
+        b = oracle.query_from_factors(A_Q, oracle.rope_rows(B_Q[0], pos, 1e4)[None])[0]
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_factored_query_decode_matches_brute_force():
+    """Full pipeline on a tiny case: query built from factors, then decode, against the brute force's own
+    query combination and attention."""
+    h, d, RK, RV, RQ, n = 4, 8, 2, 2, 3, 9
+    A_K, B_K, A_V, B_V, _ = _rand(77, n, h, d, RK, RV)
+    rng = np.random.default_rng(77)
+    A_Q, B_Q = rng.standard_normal((1, RQ, h)), rng.standard_normal((1, RQ, d))
+    q = oracle.query_from_factors(A_Q, B_Q)
+    got = oracle.decode(A_K, B_K, A_V, B_V, q[0], 1e4)
+    qb = brute_force.query_from_factors(A_Q[0].tolist(), B_Q[0].tolist())
+    want = brute_force.attention(A_K.tolist(), B_K.tolist(), A_V.tolist(), B_V.tolist(), list(range(n)), [qb],
+                                 [n], [n], 1e4)
+    np.testing.assert_allclose(got, np.array(want)[0], rtol=0, atol=1e-12)
