@@ -133,6 +133,10 @@ class DecodeBench:
         self.out = torch.empty(self.batch, w.h, w.d_h, dtype=torch.float32, device="cuda")
         self.bytes = decode_bytes(w, self.lens)
         self.step_bytes = step_bytes(w, self.lens)
+        # a rank-6 factored query (full TPA), its B_Q rows rotated at the query position
+        self.R_Q = 6
+        self.A_Q = mk((self.batch, self.R_Q, w.h), 1.0)
+        self.B_Q_rot = self.cache.rotate_queries(mk((self.batch, self.R_Q, w.d_h), 1 / np.sqrt(w.d_h)), self.pos)
 
     def step(self, i: int, out=None):
         """One fused decode step on cache replica i % n_rep (tpa_decode_step)."""
@@ -140,6 +144,11 @@ class DecodeBench:
         self.tpa.tpa_decode_step(self.dims, self.cache.buf, self.cache.capacity, self.rep_start[r], self.seq_len,
                                  self.max_len, self.new_AK, self.new_BK, self.new_AV, self.new_BV, self.q,
                                  self.out if out is None else out, self.ws)
+
+    def decode_fq(self, r: int, out=None):
+        """tpa_decode_fq over replica r: the same cache with a rank-R_Q factored query (built on chip)."""
+        self.tpa.tpa_decode_fq(self.dims, self.cache.buf, self.cache.capacity, self.rep_start[r], self.seq_len,
+                               self.max_len, self.A_Q, self.B_Q_rot, self.out if out is None else out, self.ws)
 
     def step_two_call(self, i: int):
         """The same step as two calls: append the new token + rotate the query, then decode the cached tokens."""
@@ -216,12 +225,16 @@ class DecodeBench:
         reps = max(1, -(-steps // self.n_rep))
         two = self._capture(self.step_two_call, self.n_rep)
         dec = self._capture(self.decode, self.n_rep)
+        fq = self._capture(self.decode_fq, self.n_rep)
         two.replay()
         dec.replay()
+        fq.replay()
         ms_two = self._time(two, self.n_rep, reps)
         ms_dec = self._time(dec, self.n_rep, reps)
+        ms_fq = self._time(fq, self.n_rep, reps)
         res.update(two_call_ms=ms_two, decode_ms=ms_dec, decode_tokens_per_s=toks / (ms_dec / 1e3),
-                   decode_GBps=self.bytes / (ms_dec / 1e3) / 1e9)
+                   decode_GBps=self.bytes / (ms_dec / 1e3) / 1e9, fq_ms=ms_fq,
+                   fq_GBps=self.bytes / (ms_fq / 1e3) / 1e9)
         return res
 
 
@@ -326,11 +339,14 @@ def main():
     extras = {}
     if not args.step_only:
         log(f"[{main_b.w.name}] two-call step {res['two_call_ms'] * 1e3:.2f} us, decode alone "
-            f"{res['decode_ms'] * 1e3:.2f} us, {res['decode_GBps']:.0f} GB/s")
+            f"{res['decode_ms'] * 1e3:.2f} us, {res['decode_GBps']:.0f} GB/s, factored query (R_Q 6) "
+            f"{res['fq_ms'] * 1e3:.2f} us")
         extras[main_b.w.name] = dict(two_call_step_us=round(res["two_call_ms"] * 1e3, 2),
                                      decode_us=round(res["decode_ms"] * 1e3, 2),
                                      decode_GBps=round(res["decode_GBps"], 1),
-                                     decode_hbm_frac=round(res["decode_GBps"] / HBM_PEAK_GBS, 4))
+                                     decode_hbm_frac=round(res["decode_GBps"] / HBM_PEAK_GBS, 4),
+                                     factored_query_rq6_decode_us=round(res["fq_ms"] * 1e3, 2),
+                                     factored_query_rq6_GBps=round(res["fq_GBps"], 1))
     if not args.no_extras and not args.step_only:
         for name in ("c3", "c4", "c5"):
             b = DecodeBench(name, min_bytes=4 * MALL_BYTES)
@@ -342,7 +358,7 @@ def main():
                                     GBps=round(r["decode_GBps"], 1),
                                     hbm_frac=round(r["decode_GBps"] / HBM_PEAK_GBS, 4))
             log(f"[{b.w.name}] decode {r['decode_ms'] * 1e3:.2f} us, {r['decode_GBps']:.0f} GB/s, fused step "
-                f"{r['ms_per_step'] * 1e3:.2f} us")
+                f"{r['ms_per_step'] * 1e3:.2f} us, factored query {r['fq_ms'] * 1e3:.2f} us")
             del b
             torch.cuda.empty_cache()
         p = prefill_bench(max(5, args.steps // 10), 3)

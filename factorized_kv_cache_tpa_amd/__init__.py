@@ -48,6 +48,10 @@ _EXPORTS = {
                          ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_int32,
                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p], ctypes.c_int32),
+    "tpa_decode_fq": ([ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                       ctypes.c_float, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                       ctypes.c_void_p], ctypes.c_int32),
     "tpa_prefill_chunk": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
                            ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int32),
@@ -211,6 +215,21 @@ def tpa_decode_step(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_s
         float(scale), _ptr(out, torch.float32, "out"), int(split_tokens), _ptr(workspace, name="workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "tpa_decode_step")
+
+
+def tpa_decode_fq(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_start: torch.Tensor,
+                  seq_len: torch.Tensor, max_len: int, A_Q: torch.Tensor, B_Q_rot: torch.Tensor, out: torch.Tensor,
+                  workspace: torch.Tensor, scale: float = 0.0, split_tokens: int = 0, stream=None) -> None:
+    """Factored-query decode: q~[b][i] = (1/R_Q) sum_r A_Q[b][r][i] B_Q_rot[b][r], built on chip, then
+    out[b] = attention over the seq_len[b] cached tokens.  A_Q [batch][R_Q][h], B_Q_rot [batch][R_Q][d_h]."""
+    dt = dims.torch_dtype
+    st = load().tpa_decode_fq(
+        _ref(dims), int(A_Q.shape[1]), _ptr(cache, name="cache"), int(capacity_tokens), seq_start.numel(),
+        _ptr(seq_start, torch.int64, "seq_start"), _ptr(seq_len, torch.int32, "seq_len"), int(max_len),
+        _ptr(A_Q, dt, "A_Q"), _ptr(B_Q_rot, dt, "B_Q_rot"), float(scale), _ptr(out, torch.float32, "out"),
+        int(split_tokens), _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "tpa_decode_fq")
 
 
 def tpa_prefill_chunk(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_start: torch.Tensor,

@@ -83,7 +83,7 @@ float resolve_scale(float scale, int d_h) { return scale > 0.f ? scale : float(1
 int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
                    const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *q, float scale,
                    float *out, int32_t split_tokens, void *workspace, int64_t workspace_bytes, void *stream,
-                   const tpa::StepInputs *step) {
+                   const tpa::StepInputs *step, int32_t r_q = 0, const void *a_q = nullptr) {
     int32_t st = check_dims(dims);
     if (st != TPA_OK) return st;
     if (batch < 0 || batch > 65535 || max_len < 0 || split_tokens < 0 || capacity_tokens < 0)
@@ -123,6 +123,8 @@ int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
         p.st = *step;
         p.rope = tpa::make_rope_table(dims->d_h, dims->rope_base);
     }
+    p.r_q = r_q;
+    p.a_q = a_q;
     const hipError_t e = tpa::launch_decode(L, p, as_stream(stream));
     return e == hipSuccess ? TPA_OK : TPA_ERR_HIP;
 }
@@ -232,6 +234,18 @@ int32_t tpa_decode_step(const tpa_dims *dims, void *cache, int64_t capacity_toke
     step.capacity = capacity_tokens;
     return run_decode(dims, cache, capacity_tokens, batch, seq_start, seq_len, max_len, q, scale, out, split_tokens,
                       workspace, workspace_bytes, stream, &step);
+}
+
+int32_t tpa_decode_fq(const tpa_dims *dims, int32_t R_Q, const void *cache, int64_t capacity_tokens, int32_t batch,
+                      const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *A_Q,
+                      const void *B_Q_rot, float scale, float *out, int32_t split_tokens, void *workspace,
+                      int64_t workspace_bytes, void *stream) {
+    const int32_t st = check_dims(dims);
+    if (st != TPA_OK) return st;
+    if (R_Q < 1 || R_Q > 16) return TPA_ERR_ARG;
+    if (batch > 0 && !A_Q) return TPA_ERR_ARG;
+    return run_decode(dims, cache, capacity_tokens, batch, seq_start, seq_len, max_len, B_Q_rot, scale, out,
+                      split_tokens, workspace, workspace_bytes, stream, nullptr, R_Q, A_Q);
 }
 
 int32_t tpa_prefill_chunk(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,

@@ -206,6 +206,10 @@ struct DecodeParams {
     int step;
     StepInputs st;
     RopeTable rope;
+    // Factored query (tpa_decode_fq) when r_q > 0: q holds B~_Q [batch][r_q][d_h] (rotated), a_q holds
+    // A_Q [batch][r_q][h].
+    int r_q;
+    const void *a_q;
 };
 
 struct PrefillParams {

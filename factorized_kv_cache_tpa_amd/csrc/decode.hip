@@ -152,9 +152,17 @@ __device__ __forceinline__ float wave_sum_across_groups(float x) {
     return x;
 }
 
-// kStep: a fused step (tpa_decode_step), a separate instantiation so the plain decode carries none of it.
-template <typename T, int HP, int DP, int RH, bool kStep>
+// Query modes, each its own instantiation so the plain decode carries none of the others:
+//   kQRot  -- q arrives rotated (tpa_decode);
+//   kStep  -- a fused step: q arrives unrotated, split 0 carries the new token (tpa_decode_step);
+//   kQFact -- q arrives as factors A_Q, B~_Q (B~_Q rotated), q~ = (1/R_Q) A_Q^T B~_Q (tpa_decode_fq).
+constexpr int kQRot = 0, kStepMode = 1, kQFact = 2;
+constexpr int kMaxRQ = 16;  // query rank limit of the factored mode
+
+template <typename T, int HP, int DP, int RH, int kMode>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
+    constexpr bool kStep = kMode == kStepMode;
+    constexpr bool kFact = kMode == kQFact;
     using M = Mfma<T>;
     using Frag = typename M::Frag;
     using GateRaw = typename M::GateRaw;
@@ -174,6 +182,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     __shared__ float sm_l[kWaves + 1][HP];
     __shared__ __attribute__((aligned(16))) float sm_o[kWaves][HP][DP + 4];
     constexpr int SH = kStep ? HP : 1, SD = kStep ? DP : 2;
+    // factored query: A_Q, B~_Q staged as fp32, then q~ built once per work-group (element type)
+    constexpr int QR = kFact ? kMaxRQ : 1, QH = kFact ? HP : 4, QD = kFact ? DP : 4;
+    __shared__ __attribute__((aligned(16))) float sm_aq[QR][QH];
+    __shared__ __attribute__((aligned(16))) float sm_bq[QR][QD];
+    __shared__ __attribute__((aligned(16))) T sm_q[QH][QD + 8];
     __shared__ F sm_cs[SD];             // fused step: cos/sin of the query's position
     __shared__ float sm_na[2][RH][SH];  // fused step, split 0: the new token's A_K, A_V
     __shared__ float sm_nb[2][RH][SD];  // ... and its B~_K (rotated, rounded as stored), B_V
@@ -266,10 +279,30 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     // fused step: this thread's RoPE frequency (pair j = tid), read now for the same reason
     const double theta_j = kStep && tid < DP / 2 ? p.rope.theta[tid] : 0.0;
 
+    // Factored query: this thread's share of A_Q (row-major [R_Q][h]) and B~_Q ([R_Q][d_h]), loaded
+    // before the stream for the same reason; elements past the real sizes are zeros.
+    constexpr int QA_PER = kFact ? (kMaxRQ * HP + kThreads - 1) / kThreads : 1;
+    constexpr int QB_PER = kFact ? (kMaxRQ * DP + kThreads - 1) / kThreads : 1;
+    float qa_raw[QA_PER], qb_raw[QB_PER];
+    if constexpr (kFact) {
+        const T *AQ = reinterpret_cast<const T *>(p.a_q) + int64_t(b) * p.r_q * p.h;
+        const T *BQ = reinterpret_cast<const T *>(p.q) + int64_t(b) * p.r_q * p.d_h;
+#pragma unroll
+        for (int k = 0; k < QA_PER; ++k) {
+            const int idx = tid + k * kThreads, r = idx / HP, i = idx % HP;
+            qa_raw[k] = r < p.r_q && i < p.h ? Elem<T>::to_f32(AQ[r * p.h + i]) : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < QB_PER; ++k) {
+            const int idx = tid + k * kThreads, r = idx / DP, d = idx % DP;
+            qb_raw[k] = r < p.r_q && d < p.d_h ? Elem<T>::to_f32(BQ[r * p.d_h + d]) : 0.f;
+        }
+    }
+
     // query operand (B of the score contraction; loaded first: memory returns in order, so the first
     // block can start as soon as its own loads land): lane holds q~[16 nb + c][4E kb + E g + e]
     Frag qf[KBS][NB];
-    {
+    if constexpr (!kFact) {
         const T *qb = reinterpret_cast<const T *>(p.q) + int64_t(b) * p.h * p.d_h;
 #pragma unroll
         for (int kb = 0; kb < KBS; ++kb)
@@ -289,7 +322,55 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                        // the second after its own set-up: a wave cannot pass its loads' issue until most of
                        // them have landed, so work placed behind both stages would wait for the stream)
         if (blk < full_end) load(s0, blk);
-        if (!kStep && blk + kWaves < full_end) load(s1, blk + kWaves);
+        if (kMode == kQRot && blk + kWaves < full_end) load(s1, blk + kWaves);
+    }
+    if constexpr (kFact) {
+        // Factored query, while the first blocks stream in: q~[i][d] = (1/R_Q) sum_r A_Q[r][i] B~_Q[r][d]
+        // (TPA notes page, tensor product decomposition applied to Q; B~_Q was rotated at the query's
+        // position, which commutes with the combination since RoPE is linear), computed once per
+        // work-group in 4 x 4 register tiles from LDS, rounded once to the element type, and read back as
+        // this lane's fragments.
+#pragma unroll
+        for (int k = 0; k < QA_PER; ++k) {
+            const int idx = tid + k * kThreads;
+            if (idx < kMaxRQ * HP) sm_aq[idx / HP][idx % HP] = qa_raw[k];
+        }
+#pragma unroll
+        for (int k = 0; k < QB_PER; ++k) {
+            const int idx = tid + k * kThreads;
+            if (idx < kMaxRQ * DP) sm_bq[idx / DP][idx % DP] = qb_raw[k];
+        }
+        __syncthreads();
+        const float inv_rq = 1.f / float(p.r_q);
+        for (int t = tid; t < (HP / 4) * (DP / 4); t += kThreads) {
+            const int h0 = 4 * (t / (DP / 4)), d0 = 4 * (t % (DP / 4));
+            float a4[4][4] = {};
+            for (int r = 0; r < p.r_q; ++r) {
+                const float4 av = *reinterpret_cast<const float4 *>(&sm_aq[r][h0]);
+                const float4 bv = *reinterpret_cast<const float4 *>(&sm_bq[r][d0]);
+                const float ar[4] = {av.x, av.y, av.z, av.w}, br[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) a4[i][j] = fmaf(ar[i], br[j], a4[i][j]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float x = a4[i][j] * inv_rq;
+                    if constexpr (sizeof(T) == 2)
+                        sm_q[h0 + i][d0 + j] = uint16_t(pack_bf16x2(x, 0.f) & 0xffffu);
+                    else
+                        sm_q[h0 + i][d0 + j] = x;
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kb = 0; kb < KBS; ++kb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) qf[kb][nb] = M::load(&sm_q[16 * nb + c][4 * E * kb + E * g]);
+        if (kTwoStages && blk + kWaves < full_end) load(s1, blk + kWaves);
     }
     if constexpr (kStep) {
         // Fused step, while the first blocks stream in: q arrives unrotated and sits at position len (the
@@ -684,12 +765,13 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
 
 template <typename T, int HP, int DP, int RH>
 hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
+    const dim3 grid(p.n_split, p.batch);
     if (p.step)
-        hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, true>), dim3(p.n_split, p.batch), dim3(kThreads), 0,
-                           s, p);
+        hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, kStepMode>), grid, dim3(kThreads), 0, s, p);
+    else if (p.r_q > 0)
+        hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, kQFact>), grid, dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, false>), dim3(p.n_split, p.batch), dim3(kThreads), 0,
-                           s, p);
+        hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, kQRot>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

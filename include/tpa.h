@@ -174,6 +174,22 @@ int32_t tpa_decode_step(const tpa_dims *dims, void *cache, int64_t capacity_toke
                         const void *B_K, const void *A_V, const void *B_V, const void *q, float scale, float *out,
                         int32_t split_tokens, void *workspace, int64_t workspace_bytes, void *stream);
 
+/* Factored-query decode (full TPA: the query is factorized like K and V; TPA notes page, tensor product
+ * decomposition, and its ablation's Q+K+V-factorized variant).  Per sequence b and head i the query row is
+ *     q~_b,i = (1/R_Q) sum_r A_Q[b][r][i] B~_Q[b][r][:]
+ * built on chip (fp32 sums, one rounding to dtype, never in device memory), then the same attention as
+ * tpa_decode over the seq_len[b] cached tokens.  B~_Q is the query feature factor already rotated to the
+ * query's position (tpa_cache_append with q_rows = R_Q): RoPE is linear, so rotating the factor rows is
+ * rotating the query (RoPE compatibility).
+ *   R_Q [host]                 query rank, 1..16 (TPA_ERR_ARG otherwise)
+ *   A_Q [batch][R_Q][h]        query head factor
+ *   B_Q_rot [batch][R_Q][d_h]  rotated query feature factor (16-byte aligned)
+ * Other arguments, the workspace (tpa_decode_workspace_bytes) and the error behaviour are tpa_decode's. */
+int32_t tpa_decode_fq(const tpa_dims *dims, int32_t R_Q, const void *cache, int64_t capacity_tokens, int32_t batch,
+                      const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *A_Q,
+                      const void *B_Q_rot, float scale, float *out, int32_t split_tokens, void *workspace,
+                      int64_t workspace_bytes, void *stream);
+
 /* Causal chunked prefill: chunk_len query rows per sequence attend to the
  * sequence's cached context and to the chunk's own tokens up to and including
  * their own (the chunk's factors must already be in the cache, appended at

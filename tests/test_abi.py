@@ -256,3 +256,21 @@ def test_decode_step_argument_checks(lib):
     bad = _d(h=64, d_h=256)
     assert lib.tpa_decode_step(ctypes.byref(bad), FAKE, 8192, 16, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, FAKE,
                                0.0, FAKE, 0, FAKE, need, None) == 2
+
+
+def test_decode_fq_argument_checks(lib):
+    d = _d()
+    ref = ctypes.byref(d)
+    need = lib.tpa_decode_workspace_bytes(ref, 16, 4096, 0)
+
+    def call(R_Q=6, a_q=FAKE, b_q=FAKE, cap=8192, ws_bytes=need):
+        return lib.tpa_decode_fq(ref, R_Q, FAKE, cap, 16, FAKE, FAKE, 4096, a_q, b_q, 0.0, FAKE, 0, FAKE, ws_bytes,
+                                 None)
+    for bad_rank in (0, 17, -1):
+        assert call(R_Q=bad_rank) == 1
+    assert call(a_q=None) == 1
+    assert call(b_q=None) == 1
+    assert call(b_q=ctypes.c_void_p(0x1008)) == 1  # B_Q_rot must be 16-byte aligned
+    assert call(cap=1024) == 3
+    assert call(ws_bytes=need - 1) == 4
+    assert lib.tpa_decode_fq(ref, 6, None, 0, 0, None, None, 0, None, None, 0.0, None, 0, None, 0, None) == 0
