@@ -258,29 +258,46 @@ def prefill_bench(steps: int, warmup: int):
     ctx_len = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
     out = torch.empty(B, chunk, w.h, w.d_h, dtype=torch.float32, device="cuda")
 
+    # the same chunk with rank-6 factored query rows (full TPA), B_Q rows rotated at ctx + j
+    R_Q = 6
+    rng = np.random.default_rng(w.seed + 6)
+    mk = lambda shape, sig: to_device(ti.to_storage(rng.standard_normal(shape, dtype=np.float32) * sig, w.dtype),
+                                      dims)
+    A_Q = mk((B, chunk, R_Q, w.h), 1.0)
+    B_Q_rot = cache.rotate_queries(mk((B * chunk, R_Q, w.d_h), 1 / np.sqrt(w.d_h)), q_pos).reshape(B, chunk, R_Q,
+                                                                                                   w.d_h)
+
     def call():
         tpa.tpa_prefill_chunk(dims, cache.buf, cache.capacity, cache.seq_start, ctx_len, ctx, chunk, q_rot, out)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
-        for _ in range(steps):
-            call()
-    g.replay()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+    def call_fq():
+        tpa.tpa_prefill_chunk_fq(dims, cache.buf, cache.capacity, cache.seq_start, ctx_len, ctx, chunk, A_Q, B_Q_rot,
+                                 out)
+
+    def timed(fn) -> float:
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+            for _ in range(steps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    ms = timed(call)
+    ms_fq = timed(call_fq)
     pairs = B * sum(ctx + j + 1 for j in range(chunk))
     flops = 4.0 * w.d_h * w.h * pairs
     tf = flops / (ms / 1e3) / 1e12
     return dict(workload=f"prefill_b{B}_ctx{ctx}_chunk{chunk}_h{w.h}_d{w.d_h}_r{w.R_K}_causal", ms=ms,
-                gflop=flops / 1e9, tflops=tf, mfma_frac=tf / MFMA_BF16_PEAK_TFLOPS)
+                gflop=flops / 1e9, tflops=tf, mfma_frac=tf / MFMA_BF16_PEAK_TFLOPS, factored_query_rq6_ms=ms_fq)
 
 
 def cpu_baseline(name: str, budget_s: float = 12.0):

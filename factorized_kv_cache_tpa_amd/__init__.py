@@ -52,6 +52,9 @@ _EXPORTS = {
                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                        ctypes.c_float, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
                        ctypes.c_void_p], ctypes.c_int32),
+    "tpa_prefill_chunk_fq": ([ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                              ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int32),
     "tpa_prefill_chunk": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
                            ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int32),
@@ -242,3 +245,17 @@ def tpa_prefill_chunk(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq
         int(chunk_len), _ptr(q_rot, dims.torch_dtype, "q_rot"), float(scale), _ptr(out, torch.float32, "out"),
         _stream(stream))
     _check(st, "tpa_prefill_chunk")
+
+
+def tpa_prefill_chunk_fq(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_start: torch.Tensor,
+                         ctx_len: torch.Tensor, max_ctx: int, chunk_len: int, A_Q: torch.Tensor, B_Q_rot: torch.Tensor,
+                         out: torch.Tensor, scale: float = 0.0, stream=None) -> None:
+    """Causal chunk with factored query rows: q~[b][j][i] = (1/R_Q) sum_r A_Q[b][j][r][i] B_Q_rot[b][j][r],
+    built on chip.  A_Q [batch][chunk][R_Q][h], B_Q_rot [batch][chunk][R_Q][d_h]."""
+    dt = dims.torch_dtype
+    st = load().tpa_prefill_chunk_fq(
+        _ref(dims), int(A_Q.shape[2]), _ptr(cache, name="cache"), int(capacity_tokens), seq_start.numel(),
+        _ptr(seq_start, torch.int64, "seq_start"), _ptr(ctx_len, torch.int32, "ctx_len"), int(max_ctx),
+        int(chunk_len), _ptr(A_Q, dt, "A_Q"), _ptr(B_Q_rot, dt, "B_Q_rot"), float(scale),
+        _ptr(out, torch.float32, "out"), _stream(stream))
+    _check(st, "tpa_prefill_chunk_fq")

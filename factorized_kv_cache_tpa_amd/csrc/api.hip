@@ -129,6 +129,42 @@ int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
     return e == hipSuccess ? TPA_OK : TPA_ERR_HIP;
 }
 
+// tpa_prefill_chunk and tpa_prefill_chunk_fq: host checks, then the prefill kernel.  r_q > 0: q holds the
+// rotated query feature factors and a_q the query head factors.
+int32_t run_prefill(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
+                    const int64_t *seq_start, const int32_t *ctx_len, int32_t max_ctx, int32_t chunk_len, const void *q,
+                    float scale, float *out, void *stream, int32_t r_q, const void *a_q) {
+    int32_t st = check_dims(dims);
+    if (st != TPA_OK) return st;
+    if (batch < 0 || batch > 65535 || max_ctx < 0 || chunk_len < 0 || capacity_tokens < 0) return TPA_ERR_ARG;
+    if (batch == 0 || chunk_len == 0) return TPA_OK;
+    if (!cache || !seq_start || !ctx_len || !q || !out) return TPA_ERR_ARG;
+    if (!aligned16(cache) || !aligned16(q) || !aligned16(out)) return TPA_ERR_ARG;
+    if (!isfinite(scale)) return TPA_ERR_ARG;
+    if (int64_t(max_ctx) + chunk_len > capacity_tokens) return TPA_ERR_CAPACITY;
+    const Layout L = layout_of(dims);
+    if (!tpa::prefill_supported(L)) return TPA_ERR_UNSUPPORTED;
+    tpa::PrefillParams p{};
+    p.cache = cache;
+    p.seq_start = seq_start;
+    p.ctx_len = ctx_len;
+    p.q = q;
+    p.out = out;
+    p.h = dims->h;
+    p.d_h = dims->d_h;
+    p.RK = dims->R_K;
+    p.RV = dims->R_V;
+    p.batch = batch;
+    p.chunk = chunk_len;
+    p.max_ctx = max_ctx;
+    p.score_mul = float(double(resolve_scale(scale, dims->d_h)) * M_LOG2E / dims->R_K);
+    p.out_mul = float(1.0 / dims->R_V);
+    p.r_q = r_q;
+    p.a_q = a_q;
+    const hipError_t e = tpa::launch_prefill(L, p, as_stream(stream));
+    return e == hipSuccess ? TPA_OK : TPA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -251,33 +287,20 @@ int32_t tpa_decode_fq(const tpa_dims *dims, int32_t R_Q, const void *cache, int6
 int32_t tpa_prefill_chunk(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
                           const int64_t *seq_start, const int32_t *ctx_len, int32_t max_ctx, int32_t chunk_len,
                           const void *q_rot, float scale, float *out, void *stream) {
-    int32_t st = check_dims(dims);
+    return run_prefill(dims, cache, capacity_tokens, batch, seq_start, ctx_len, max_ctx, chunk_len, q_rot, scale,
+                       out, stream, 0, nullptr);
+}
+
+int32_t tpa_prefill_chunk_fq(const tpa_dims *dims, int32_t R_Q, const void *cache, int64_t capacity_tokens,
+                             int32_t batch, const int64_t *seq_start, const int32_t *ctx_len, int32_t max_ctx,
+                             int32_t chunk_len, const void *A_Q, const void *B_Q_rot, float scale, float *out,
+                             void *stream) {
+    const int32_t st = check_dims(dims);
     if (st != TPA_OK) return st;
-    if (batch < 0 || batch > 65535 || max_ctx < 0 || chunk_len < 0 || capacity_tokens < 0) return TPA_ERR_ARG;
-    if (batch == 0 || chunk_len == 0) return TPA_OK;
-    if (!cache || !seq_start || !ctx_len || !q_rot || !out) return TPA_ERR_ARG;
-    if (!aligned16(cache) || !aligned16(q_rot) || !aligned16(out)) return TPA_ERR_ARG;
-    if (!isfinite(scale)) return TPA_ERR_ARG;
-    if (int64_t(max_ctx) + chunk_len > capacity_tokens) return TPA_ERR_CAPACITY;
-    const Layout L = layout_of(dims);
-    if (!tpa::prefill_supported(L)) return TPA_ERR_UNSUPPORTED;
-    tpa::PrefillParams p;
-    p.cache = cache;
-    p.seq_start = seq_start;
-    p.ctx_len = ctx_len;
-    p.q = q_rot;
-    p.out = out;
-    p.h = dims->h;
-    p.d_h = dims->d_h;
-    p.RK = dims->R_K;
-    p.RV = dims->R_V;
-    p.batch = batch;
-    p.chunk = chunk_len;
-    p.max_ctx = max_ctx;
-    p.score_mul = float(double(resolve_scale(scale, dims->d_h)) * M_LOG2E / dims->R_K);
-    p.out_mul = float(1.0 / dims->R_V);
-    const hipError_t e = tpa::launch_prefill(L, p, as_stream(stream));
-    return e == hipSuccess ? TPA_OK : TPA_ERR_HIP;
+    if (R_Q < 1 || R_Q > 16) return TPA_ERR_ARG;
+    if (batch > 0 && chunk_len > 0 && !A_Q) return TPA_ERR_ARG;
+    return run_prefill(dims, cache, capacity_tokens, batch, seq_start, ctx_len, max_ctx, chunk_len, B_Q_rot, scale,
+                       out, stream, R_Q, A_Q);
 }
 
 }  // extern "C"

@@ -222,6 +222,10 @@ struct PrefillParams {
     int batch, chunk, max_ctx;
     float score_mul;  // scale * log2(e) / R_K
     float out_mul;    // 1 / R_V
+    // Factored query (tpa_prefill_chunk_fq) when r_q > 0: q holds B~_Q [batch][chunk][r_q][d_h] (rotated),
+    // a_q holds A_Q [batch][chunk][r_q][h].
+    int r_q;
+    const void *a_q;
 };
 
 // Host: theta_j = base^(-2j/d_h) in fp64 (zeros past d_h/2).

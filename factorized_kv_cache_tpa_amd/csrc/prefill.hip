@@ -49,7 +49,8 @@ __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_c
 // LDS position of tile key k inside the value contraction's key order
 __device__ __forceinline__ int vpos(int k) { return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3); }
 
-template <int HP, int DP, int RH>
+// kFQ: the query rows arrive as factors (tpa_prefill_chunk_fq), a separate instantiation.
+template <int HP, int DP, int RH, bool kFQ>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams p) {
     constexpr int KS = DP / 16;  // score K steps
     constexpr int MB = DP / 32;  // value M blocks
@@ -270,7 +271,44 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
 
     // Q operand (B of S^T): lane supplies Q~[jq][16 ks + 8 hi + e]
     bf16x8 qf[KS];
-    {
+    if constexpr (kFQ) {
+        // factored query: Q~[jq][d] = (1/R_Q) sum_r A_Q[jq][r][head] B~_Q[jq][r][d] (TPA notes page, tensor
+        // product decomposition applied to Q; B~_Q rotated at the row's position), fp32 sums, one rounding
+        float x[KS][8] = {};
+        if (jq < p.chunk) {
+            const int64_t row = int64_t(b) * p.chunk + jq;
+            const uint16_t *aq = reinterpret_cast<const uint16_t *>(p.a_q) + row * p.r_q * p.h + head;
+            const uint16_t *bq = reinterpret_cast<const uint16_t *>(p.q) + row * p.r_q * p.d_h;
+            for (int r = 0; r < p.r_q; ++r) {
+                const float a = bf16_to_f32(aq[r * p.h]);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int d0 = 16 * ks + 8 * hi;
+                    if ((p.d_h & 7) == 0) {
+                        if (d0 < p.d_h) {
+                            const uint4 v = *reinterpret_cast<const uint4 *>(bq + r * p.d_h + d0);
+                            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                x[ks][e] = fmaf(a, __uint_as_float((e & 1) ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16)),
+                                                x[ks][e]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (d0 + e < p.d_h) x[ks][e] = fmaf(a, bf16_to_f32(bq[r * p.d_h + d0 + e]), x[ks][e]);
+                    }
+                }
+            }
+        }
+        const float inv_rq = 1.f / float(p.r_q);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[ks][e] *= inv_rq;
+            qf[ks] = pack8(x[ks]);
+        }
+    } else {
         const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) + (int64_t(b) * p.chunk + jq) * p.h * p.d_h +
                                int64_t(head) * p.d_h;
 #pragma unroll
@@ -429,7 +467,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
 template <int HP, int DP, int RH>
 hipError_t launch_one(const PrefillParams &p, hipStream_t s) {
     const dim3 grid(unsigned(((p.chunk + kQT - 1) / kQT) * p.h * p.batch));
-    hipLaunchKernelGGL((prefill_kernel<HP, DP, RH>), grid, dim3(kPrefillThreads), 0, s, p);
+    if (p.r_q > 0)
+        hipLaunchKernelGGL((prefill_kernel<HP, DP, RH, true>), grid, dim3(kPrefillThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((prefill_kernel<HP, DP, RH, false>), grid, dim3(kPrefillThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -206,6 +206,18 @@ int32_t tpa_prefill_chunk(const tpa_dims *dims, const void *cache, int64_t capac
                           const int64_t *seq_start, const int32_t *ctx_len, int32_t max_ctx, int32_t chunk_len,
                           const void *q_rot, float scale, float *out, void *stream);
 
+/* Causal chunked prefill with factored query rows (full TPA; the factored form of tpa_decode_fq): row j
+ * of sequence b has q~_b,j,i = (1/R_Q) sum_r A_Q[b][j][r][i] B~_Q[b][j][r][:], built on chip, then the
+ * attention of tpa_prefill_chunk.
+ *   R_Q [host]                            query rank, 1..16
+ *   A_Q [batch][chunk_len][R_Q][h]        query head factors
+ *   B_Q_rot [batch][chunk_len][R_Q][d_h]  query feature factors rotated at ctx_len[b] + j (16-byte aligned)
+ * Other arguments and the error behaviour are tpa_prefill_chunk's. */
+int32_t tpa_prefill_chunk_fq(const tpa_dims *dims, int32_t R_Q, const void *cache, int64_t capacity_tokens,
+                             int32_t batch, const int64_t *seq_start, const int32_t *ctx_len, int32_t max_ctx,
+                             int32_t chunk_len, const void *A_Q, const void *B_Q_rot, float scale, float *out,
+                             void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -274,3 +274,21 @@ def test_decode_fq_argument_checks(lib):
     assert call(cap=1024) == 3
     assert call(ws_bytes=need - 1) == 4
     assert lib.tpa_decode_fq(ref, 6, None, 0, 0, None, None, 0, None, None, 0.0, None, 0, None, 0, None) == 0
+
+
+def test_prefill_fq_argument_checks(lib):
+    d = _d(R_K=4, R_V=4)
+    ref = ctypes.byref(d)
+
+    def call(R_Q=6, a_q=FAKE, b_q=FAKE, cap=8192, out=FAKE):
+        return lib.tpa_prefill_chunk_fq(ref, R_Q, FAKE, cap, 1, FAKE, FAKE, 1024, 64, a_q, b_q, 0.0, out, None)
+    for bad_rank in (0, 17):
+        assert call(R_Q=bad_rank) == 1
+    assert call(a_q=None) == 1
+    assert call(b_q=None) == 1
+    assert call(b_q=ctypes.c_void_p(0x1008)) == 1
+    assert call(out=ctypes.c_void_p(0x1008)) == 1
+    assert call(cap=1000) == 3
+    f32 = _d(h=4, d_h=16, dtype="f32")
+    assert lib.tpa_prefill_chunk_fq(ctypes.byref(f32), 2, FAKE, 8192, 1, FAKE, FAKE, 64, 8, FAKE, FAKE, 0.0, FAKE,
+                                    None) == 2  # prefill is bf16 only

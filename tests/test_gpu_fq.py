@@ -1,4 +1,5 @@
-"""GPU parity of the factored-query decode, tpa_decode_fq, against the fp64 oracle.
+"""GPU parity of the factored-query decode (tpa_decode_fq) and prefill (tpa_prefill_chunk_fq) against the
+fp64 oracle.
 
 The query arrives as factors (A_Q [R_Q][h], B_Q [R_Q][d_h]); the library rotates the B_Q rows at the
 query's position (tpa_cache_append with q_rows = R_Q) and builds q~ = (1/R_Q) A_Q^T B~_Q on chip.  The
@@ -114,3 +115,34 @@ def test_fq_full_size_decode_b16_h32_d128_r1_n4096_rq6():
     got = st.run()
     for b in range(st.batch):
         assert_close(got[b], st.oracle(b), w.dtype, f"seq {b}")
+
+
+@pytest.mark.parametrize("h,d_h,R_K,R_V,R_Q,ctx,chunk", [(32, 128, 4, 4, 6, 100, 64), (16, 64, 2, 2, 3, [37, 0], 300),
+                                                          (32, 128, 1, 1, 1, 0, 33), (20, 48, 1, 3, 16, 65, 40)])
+def test_prefill_fq_matches_oracle(h, d_h, R_K, R_V, R_Q, ctx, chunk):
+    """Causal chunk with factored query rows (row j at position ctx + j sees tokens 0 .. ctx + j)."""
+    w = case_workload(h, d_h, R_K, R_V, ti.BF16)
+    ctxs = ctx if isinstance(ctx, list) else [ctx]
+    say(f"case: prefill fq h={h} d_h={d_h} R_K={R_K} R_V={R_V} R_Q={R_Q} ctx={ctxs} chunk={chunk}")
+    dims = dims_of(w)
+    seqs = random_sequences(w, [c + chunk for c in ctxs], seed=h + R_Q)
+    cache = FactorCache(dims, [c + chunk for c in ctxs])
+    for b, s in enumerate(seqs):
+        cache.append_host(b, s.A_K, s.B_K, s.A_V, s.B_V)
+    rng = np.random.default_rng(R_Q * 31 + chunk)
+    B = len(ctxs)
+    A_Q = ti.to_storage(rng.standard_normal((B, chunk, R_Q, h), dtype=np.float32), ti.BF16)
+    B_Q = ti.to_storage(rng.standard_normal((B, chunk, R_Q, d_h), dtype=np.float32) * (4.0 / np.sqrt(d_h)), ti.BF16)
+    pos = torch.tensor(np.concatenate([c + np.arange(chunk) for c in ctxs]), dtype=torch.int32, device="cuda")
+    B_Q_rot = cache.rotate_queries(to_device(B_Q, dims).reshape(B * chunk, R_Q, d_h), pos).reshape(B, chunk, R_Q, d_h)
+    out = torch.full((B, chunk, h, d_h), float("nan"), dtype=torch.float32, device="cuda")
+    tpa.tpa_prefill_chunk_fq(dims, cache.buf, cache.capacity, cache.seq_start,
+                             torch.tensor(ctxs, dtype=torch.int32, device="cuda"), max(ctxs), chunk,
+                             to_device(A_Q, dims), B_Q_rot, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b, s in enumerate(seqs):
+        q = oracle.query_from_factors(f64(A_Q[b], ti.BF16), f64(B_Q[b], ti.BF16))
+        ref = oracle.prefill(f64(s.A_K, ti.BF16), f64(s.B_K, ti.BF16), f64(s.A_V, ti.BF16), f64(s.B_V, ti.BF16), q,
+                             ctxs[b], w.rope_base)
+        assert_close(got[b], ref, ti.BF16, f"seq {b}")
