@@ -189,7 +189,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     __shared__ __attribute__((aligned(16))) T sm_q[QH][QD + 8];
     __shared__ F sm_cs[SD];             // fused step: cos/sin of the query's position
     __shared__ float sm_na[2][RH][SH];  // fused step, split 0: the new token's A_K, A_V
-    __shared__ float sm_nb[2][RH][SD];  // ... and its B~_K (rotated, rounded as stored), B_V
+    __shared__ __attribute__((aligned(16))) float sm_nb[2][RH][SD];  // ... its B_K, B_V (unrotated)
+    __shared__ float sm_wt[SH];         // ... and the weight of its value row per head (in-group merge)
     static_assert(RH * HP <= kThreads && RH * DP / 2 <= kThreads && DP / 2 <= kThreads,
                   "one new-token item and one RoPE pair per thread");
 
@@ -208,6 +209,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     // A fused step's split 0 carries the step's new token (even over an empty sequence): it writes the
     // token's record and folds the token's own score and value into its partial.
     const bool new_tok = kStep && split == 0 && !misaligned;
+    // ... and the sequence's last split with tokens (split 0 for an empty sequence) writes its record, so
+    // the two extra jobs land on different work-groups
+    const int last_split = nblk > 0 ? min(p.n_split - 1, (nblk - 1) / p.split_blocks) : 0;
+    const bool rec_tok = kStep && split == last_split && !misaligned;
     if (misaligned || (blk_begin >= nblk && !new_tok)) {
         // A split with no tokens (past the sequence's end, or the sequence is empty or misaligned) marks
         // its partial empty (max -inf, sum 0), so the merge kernel can read every split without first
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     const int tid = threadIdx.x;
     const int na_r = tid / HP, na_i = tid % HP, nb_r = tid / (DP / 2), nb_d = 2 * (tid % (DP / 2));
     T nak = T(0), nav = T(0), nbk0 = T(0), nbk1 = T(0), nbv0 = T(0), nbv1 = T(0);
-    if (kStep && new_tok) {
+    if (kStep && (new_tok || rec_tok)) {
         const T *AK = reinterpret_cast<const T *>(p.st.A_K) + int64_t(b) * p.RK * p.h;
         const T *AV = reinterpret_cast<const T *>(p.st.A_V) + int64_t(b) * p.RV * p.h;
         const T *BK = reinterpret_cast<const T *>(p.st.B_K) + int64_t(b) * p.RK * p.d_h;
@@ -373,19 +378,73 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         if (kTwoStages && blk + kWaves < full_end) load(s1, blk + kWaves);
     }
     if constexpr (kStep) {
-        // Fused step, while the first blocks stream in: q arrives unrotated and sits at position len (the
-        // number of cached tokens); rotate it in registers.  The table covers every padded pair (theta is
-        // zero past d_h / 2: an identity rotation of zeros).  Split 0 also writes the new token's record at
-        // slot len: no work-group of this kernel reads that slot's rows (a partly filled last block masks
-        // every row at or past len), and the next call sees it.
+        // Fused step, while the first blocks stream in.  q arrives unrotated and sits at position len (the
+        // number of cached tokens).  Split 0 stages the new token's factors in LDS and, after the one
+        // barrier the angle table needs anyway, takes the token's score per head from the still unrotated
+        // query fragments and the unrotated B_K: query and token share a position, so RoPE drops out of that
+        // score (RoPE compatibility, Theorem 3.1 with t = s).  Then every wave rotates its query fragments
+        // (the table covers every padded pair; theta is zero past d_h / 2: an identity rotation of zeros),
+        // and the sequence's last split writes the token's record at slot len: no work-group of this kernel
+        // reads that slot's rows (a partly filled last block masks every row at or past len), and the next
+        // call sees it.
+        if (new_tok) {
+            if (na_r < RH) {
+                sm_na[0][na_r][na_i] = Elem<T>::to_f32(nak);
+                sm_na[1][na_r][na_i] = Elem<T>::to_f32(nav);
+            }
+            if (nb_r < RH) {
+                sm_nb[0][nb_r][nb_d] = Elem<T>::to_f32(nbk0);
+                sm_nb[0][nb_r][nb_d + 1] = Elem<T>::to_f32(nbk1);
+                sm_nb[1][nb_r][nb_d] = Elem<T>::to_f32(nbv0);
+                sm_nb[1][nb_r][nb_d + 1] = Elem<T>::to_f32(nbv1);
+            }
+        }
         if (tid < DP / 2) rope_cos_sin<T>(sm_cs + 2 * tid, double(len), theta_j);
         __syncthreads();
+        if (new_tok) {
+            // the token's score per head: a lane sums its d-values, the four lane groups of a head are
+            // summed across (the same contraction as the cached tokens'); head block nb is taken by wave
+            // nb % kWaves, so the waves share the work
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                if (nb % kWaves != w) continue;  // wave-uniform; static register indexing
+                float dot[RH];
+#pragma unroll
+                for (int r = 0; r < RH; ++r) {
+                    float x = 0.f;
+#pragma unroll
+                    for (int kb = 0; kb < KBS; ++kb) {
+                        float bk[E];
+                        if constexpr (E == 8) {
+                            const float4 lo = *reinterpret_cast<const float4 *>(&sm_nb[0][r][4 * E * kb + E * g]);
+                            const float4 hi = *reinterpret_cast<const float4 *>(&sm_nb[0][r][4 * E * kb + E * g + 4]);
+                            bk[0] = lo.x; bk[1] = lo.y; bk[2] = lo.z; bk[3] = lo.w;
+                            bk[4] = hi.x; bk[5] = hi.y; bk[6] = hi.z; bk[7] = hi.w;
+                        } else {
+                            bk[0] = sm_nb[0][r][4 * E * kb + E * g];
+                        }
+#pragma unroll
+                        for (int e = 0; e < E; ++e) x = fmaf(M::value(qf[kb][nb], e), bk[e], x);
+                    }
+                    dot[r] = wave_sum_across_groups(x);
+                }
+                if (g == 0) {
+                    const int head = 16 * nb + c;
+                    float z = 0.f;
+#pragma unroll
+                    for (int r = 0; r < RH; ++r) z = fmaf(sm_na[0][r][head], dot[r], z);
+                    sm_m[kWaves][head] = head < p.h ? z * p.score_mul : -INFINITY;
+                    sm_l[kWaves][head] = head < p.h ? 1.f : 0.f;
+                }
+            }
+        }
 #pragma unroll
         for (int kb = 0; kb < KBS; ++kb)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) qf[kb][nb] = M::rotate_q(qf[kb][nb], 4 * E * kb + E * g, sm_cs);
-        if (new_tok) {
-            // the record, rotated and rounded exactly as tpa_cache_append stores it
+        const int64_t slot = start + len;
+        if (rec_tok && slot < p.st.capacity) {
+            // the record, B_K rotated and rounded exactly as tpa_cache_append stores it
             T k0 = nbk0, k1 = nbk1;
             if (nb_r < p.RK && nb_d < p.d_h) {
                 F y0, y1;
@@ -399,60 +458,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                     k1 = T(y1);
                 }
             }
-            const int64_t slot = start + len;
-            if (slot < p.st.capacity) {
-                T *rec = reinterpret_cast<T *>(p.st.cache) + (slot / TOK) * BLK;
-                const int row0 = int(slot % TOK) * RH;
-                const Layout Lay = make_layout(p.h, p.d_h, p.RK, p.RV, Elem<T>::dtype);
-                if (na_r < RH) {
-                    rec[Lay.gate(row0 + na_r, na_i)] = nak;
-                    rec[OFF_AV + Lay.gate(row0 + na_r, na_i)] = nav;
-                }
-                if (nb_r < RH) {
-                    rec[OFF_BK + Lay.bk(row0 + nb_r, nb_d)] = k0;
-                    rec[OFF_BK + Lay.bk(row0 + nb_r, nb_d + 1)] = k1;
-                    rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d)] = nbv0;
-                    rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d + 1)] = nbv1;
-                }
-            }
-            // the token's factors in LDS for its score and value row
+            T *rec = reinterpret_cast<T *>(p.st.cache) + (slot / TOK) * BLK;
+            const int row0 = int(slot % TOK) * RH;
+            const Layout Lay = make_layout(p.h, p.d_h, p.RK, p.RV, Elem<T>::dtype);
             if (na_r < RH) {
-                sm_na[0][na_r][na_i] = Elem<T>::to_f32(nak);
-                sm_na[1][na_r][na_i] = Elem<T>::to_f32(nav);
+                rec[Lay.gate(row0 + na_r, na_i)] = nak;
+                rec[OFF_AV + Lay.gate(row0 + na_r, na_i)] = nav;
             }
             if (nb_r < RH) {
-                sm_nb[0][nb_r][nb_d] = Elem<T>::to_f32(k0);
-                sm_nb[0][nb_r][nb_d + 1] = Elem<T>::to_f32(k1);
-                sm_nb[1][nb_r][nb_d] = Elem<T>::to_f32(nbv0);
-                sm_nb[1][nb_r][nb_d + 1] = Elem<T>::to_f32(nbv1);
-            }
-            __syncthreads();
-            // its score per head, from the rotated query fragments: a lane sums its d-values, the four
-            // lane groups of a head are summed across (the same contraction as the cached tokens')
-            if (w == 0) {
-                float dot[NB][RH];
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int r = 0; r < RH; ++r) {
-                        float x = 0.f;
-#pragma unroll
-                        for (int kb = 0; kb < KBS; ++kb)
-#pragma unroll
-                            for (int e = 0; e < E; ++e)
-                                x = fmaf(M::value(qf[kb][nb], e), sm_nb[0][r][4 * E * kb + E * g + e], x);
-                        dot[nb][r] = wave_sum_across_groups(x);
-                    }
-                if (g == 0)
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        const int head = 16 * nb + c;
-                        float z = 0.f;
-#pragma unroll
-                        for (int r = 0; r < RH; ++r) z = fmaf(sm_na[0][r][head], dot[nb][r], z);
-                        sm_m[kWaves][head] = head < p.h ? z * p.score_mul : -INFINITY;
-                        sm_l[kWaves][head] = head < p.h ? 1.f : 0.f;
-                    }
+                rec[OFF_BK + Lay.bk(row0 + nb_r, nb_d)] = k0;
+                rec[OFF_BK + Lay.bk(row0 + nb_r, nb_d + 1)] = k1;
+                rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d)] = nbv0;
+                rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d + 1)] = nbv1;
             }
         }
         if (kTwoStages && blk + kWaves < full_end) load(s1, blk + kWaves);
@@ -623,6 +640,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 #pragma unroll
         for (int ww = 1; ww <= kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][head]);
         wscale[nb] = run_m[nb] == -INFINITY ? 0.f : exp2f(run_m[nb] - mm);
+        if constexpr (kStep)
+            if (new_tok && w == 0 && g == 0)  // the new token's weight, once per head
+                sm_wt[head] = sm_m[kWaves][head] == -INFINITY ? 0.f : exp2f(sm_m[kWaves][head] - mm);
     }
     // every wave writes its rescaled accumulators to its own LDS slice; after one barrier all threads
     // sum the slices column by column straight into the split's partial
@@ -649,10 +669,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             o.w += x.w;
         }
         if constexpr (kStep) {
-            if (new_tok && sm_m[kWaves][hh] != -INFINITY) {  // the new token's value row, at its own weight
-                float mm = sm_m[0][hh];
-                for (int ww = 1; ww <= kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][hh]);
-                const float wt = exp2f(sm_m[kWaves][hh] - mm);
+            if (new_tok) {  // the new token's value row, at its own weight
+                const float wt = sm_wt[hh];
                 float v[4] = {0.f, 0.f, 0.f, 0.f};
                 for (int r = 0; r < RH; ++r)
 #pragma unroll
