@@ -14,8 +14,9 @@
 //     O^T += V_i^T P^T  (M = d_h, N = queries, K = keys)
 // A work-group owns 256 query rows of one head (8 waves x 32), so every
 // (key, head) pair is rebuilt at most twice per chunk of 512 rows.  The LDS
-// tiles are double-buffered: the factor loads of tile t+1 are issued between
-// the matrix-core instructions of tile t, then the waves rebuild tile t+1.  The key order inside the value contraction is
+// tiles are double-buffered: the factor loads of a later tile are issued between
+// the matrix-core instructions of tile t, and the waves rebuild tile t+1 (half of
+// them at the end of their iteration, half at its start: see prefill_kernel).  The key order inside the value contraction is
 // permuted (bits 2 and 3 of the key index swapped within each group of 16)
 // so that the score accumulator a lane holds is exactly its slice of P^T and
 // its slice of V^T is one 16-byte LDS read.
@@ -50,8 +51,19 @@ __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_c
 __device__ __forceinline__ int vpos(int k) { return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3); }
 
 // kFQ: the query rows arrive as factors (tpa_prefill_chunk_fq), a separate instantiation.
-template <int HP, int DP, int RH, bool kFQ>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams p) {
+// The double-buffered K~ and V^T tiles (row strides padded by 8 elements against bank conflicts).
+template <int DP>
+struct PrefillLds {
+    uint16_t k[2][kKT * (DP + 8)];
+    uint16_t v[2][DP * (kKT + 8)];
+};
+
+// One work-group's loop.  late: the second wave of each SIMD (waves 4..7), which rebuilds at the top of
+// its iteration instead of the end; see prefill_kernel.
+template <int HP, int DP, int RH, bool kFQ, bool late>
+__device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<DP> &lds) {
+    auto &sK = lds.k;
+    auto &sV = lds.v;
     constexpr int KS = DP / 16;  // score K steps
     constexpr int MB = DP / 32;  // value M blocks
     constexpr int NB = HP / 16;
@@ -62,8 +74,6 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     constexpr int SVS = kKT + 8;  // LDS row stride of V^T
     constexpr int BLK = 2 * kRows * (HP + DP);
     constexpr int OFF_AV = kRows * HP, OFF_BK = 2 * kRows * HP, OFF_BV = 2 * kRows * HP + kRows * DP;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKT * SKS];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][DP * SVS];
 
     // Work-groups are dispatched round-robin over the 8 XCDs (linear id mod 8), each with its own L2.
     // When the batch is a multiple of 8, the linear id is mapped so that all work-groups of a sequence
@@ -355,10 +365,16 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     fetch_k(raw, 0);
     fetch_v(raw, 0);
     rebuild_tile(raw, 0, 0);
+    if (late) {  // a late wave runs one tile further ahead with its loads
+        fetch_k(raw, min(1, n_kt - 1));
+        fetch_v(raw, min(1, n_kt - 1));
+    }
     __syncthreads();
     for (int kt = 0; kt < n_kt; ++kt) {
         const int buf = kt & 1;
-        const int kn = min(kt + 1, n_kt - 1);  // tile whose loads are issued now
+        if (late && kt + 1 < n_kt) rebuild_tile(raw, kt + 1, buf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);  // the next loads stay below the rebuild that frees their registers
+        const int kn = min(kt + 1 + int(late), n_kt - 1);  // tile whose loads are issued now
         const int key0 = kt * kKT;
         {
             const uint16_t *cK = sK[buf];
@@ -439,7 +455,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
                 __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // global loads
             }
         }
-        if (kt + 1 < n_kt) rebuild_tile(raw, kt + 1, buf ^ 1);
+        if (!late && kt + 1 < n_kt) rebuild_tile(raw, kt + 1, buf ^ 1);
         __syncthreads();
     }
 
@@ -462,6 +478,21 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
                 }
             }
     }
+}
+
+// Waves w and w + 4 share a SIMD.  Both run, per 64-key tile, two matrix-core phases (S, PV) and two
+// vector phases (softmax, rebuild of the next tile); the second wave of each SIMD takes its rebuild at
+// the top of the iteration, so the pair alternates (matrix cores | vector ALU) instead of contending for
+// the same unit in step.  One barrier per tile still orders it: every wave's share of tile t+1 is written
+// between the barriers that bracket iteration t, into the buffer nobody reads during iteration t.  Each
+// half is its own instantiation so the register allocator sees one loop shape at a time.
+template <int HP, int DP, int RH, bool kFQ>
+__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams p) {
+    __shared__ __attribute__((aligned(16))) PrefillLds<DP> lds;
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= kPrefillWaves / 2)
+        prefill_body<HP, DP, RH, kFQ, true>(p, lds);
+    else
+        prefill_body<HP, DP, RH, kFQ, false>(p, lds);
 }
 
 template <int HP, int DP, int RH>
