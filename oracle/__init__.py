@@ -60,6 +60,9 @@ def _load():
         lib.tpa_oracle_dense_elems_per_token.argtypes = [ctypes.c_int] * 2
         lib.tpa_oracle_dense_elems_per_token.restype = ctypes.c_int64
         lib.tpa_oracle_max_threads.restype = ctypes.c_int
+        U8 = ctypes.POINTER(ctypes.c_uint8)
+        lib.tpa_oracle_e4m3_decode_n.argtypes = [ctypes.c_int64, U8, D]
+        lib.tpa_oracle_e4m3_encode_n.argtypes = [ctypes.c_int64, D, U8]
         _lib = lib
     return _lib
 
@@ -143,6 +146,22 @@ def prefill(A_K, B_K, A_V, B_V, q, ctx: int, base: float, scale: Optional[float]
     j = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
     return attention(A_K, B_K, A_V, B_V, np.arange(np.shape(A_K)[0]), q[j], ctx + j, ctx + j + 1, base,
                      scale, threads)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """OCP E4M3 codes (uint8) -> their values in fp64 (NaN for S.1111.111)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    _load().tpa_oracle_e4m3_decode_n(c.size, c.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), _dp(out))
+    return out
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """fp64 values -> nearest OCP E4M3 codes (ties to even, saturating at +-448)."""
+    v = _f64(x)
+    out = np.empty(v.shape, dtype=np.uint8)
+    _load().tpa_oracle_e4m3_encode_n(v.size, _dp(v), out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    return out
 
 
 def factor_elems_per_token(h: int, d: int, RK: int, RV: int) -> int:

@@ -150,6 +150,48 @@ void tpa_oracle_query_from_factors(int h, int d, int RQ, int64_t n, const double
             }
 }
 
+/* ---- 8-bit factor storage (the pages' next step: TPA combined with low-bit storage, which they call
+ * unexplored; parity unpinned as a method, the codec itself is pinned).  Reading: every factor element is
+ * stored as an OCP 8-bit floating-point E4M3 code of (value / scale), one fixed scale per factor tensor;
+ * the stored value is code * scale.  E4M3 per the OCP 8-bit floating point specification: 1 sign bit,
+ * 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 is subnormal, m * 2^-9; exponent field
+ * e > 0 is 2^(e-7) * (1 + m/8); there are no infinities and only S.1111.111 is NaN, so the largest finite
+ * magnitude is 448 (S.1111.110).  The oracle's steps then run on the decoded values exactly as on any
+ * other factors. */
+double tpa_oracle_e4m3_decode(uint8_t code) {
+    const int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* Nearest code by brute force over the 127 non-negative finite codes, ties to the code with the even
+ * mantissa (round to nearest even); magnitudes above 448 saturate to 448; the sign is kept (so -0.0 and
+ * negative values below half the smallest subnormal give 0x80); NaN gives 0x7F. */
+uint8_t tpa_oracle_e4m3_encode(double x) {
+    if (isnan(x)) return 0x7F;
+    const int neg = signbit(x) != 0;
+    const double a = fabs(x);
+    int best = 0;
+    double best_err = INFINITY;
+    for (int c = 0; c <= 126; ++c) {
+        const double err = fabs(a - tpa_oracle_e4m3_decode((uint8_t)c));
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(best | (neg ? 0x80 : 0));
+}
+
+void tpa_oracle_e4m3_decode_n(int64_t n, const uint8_t *codes, double *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = tpa_oracle_e4m3_decode(codes[i]);
+}
+
+void tpa_oracle_e4m3_encode_n(int64_t n, const double *x, uint8_t *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = tpa_oracle_e4m3_encode(x[i]);
+}
+
 int64_t tpa_oracle_factor_elems_per_token(int h, int d, int RK, int RV) {
     return (int64_t)(RK + RV) * (int64_t)(h + d);
 }

@@ -302,3 +302,56 @@ def test_factored_query_decode_matches_brute_force():
     want = brute_force.attention(A_K.tolist(), B_K.tolist(), A_V.tolist(), B_V.tolist(), list(range(n)), [qb],
                                  [n], [n], 1e4)
     np.testing.assert_allclose(got, np.array(want)[0], rtol=0, atol=1e-12)
+
+
+# ---- OCP E4M3 codec used for 8-bit factor storage (OCP 8-bit floating point specification, E4M3)
+
+def test_e4m3_known_codes():
+    """Values fixed by the format: bias 7, 3 mantissa bits, subnormals m * 2^-9, largest finite 448,
+    S.1111.111 is NaN, sign bit 7."""
+    v = oracle.e4m3_decode(np.array([0x00, 0x01, 0x07, 0x08, 0x30, 0x38, 0x3C, 0x40, 0x77, 0x7E, 0x7F,
+                                     0x80, 0x81, 0xB8, 0xFE, 0xFF], dtype=np.uint8))
+    want = [0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 0.5, 1.0, 1.5, 2.0, 240.0, 448.0, np.nan,
+            -0.0, -(2.0 ** -9), -1.0, -448.0, np.nan]
+    np.testing.assert_array_equal(v, want)
+    assert math.copysign(1.0, v[11]) == -1.0  # 0x80 is negative zero
+
+
+def test_e4m3_finite_codes_are_monotone_and_round_trip():
+    codes = np.arange(256, dtype=np.uint8)
+    v = oracle.e4m3_decode(codes)
+    pos = v[:127]
+    assert np.all(np.diff(pos) > 0)  # 0x00 .. 0x7E strictly increasing
+    np.testing.assert_array_equal(v[128:255], -pos)  # sign bit mirrors
+    finite = np.isfinite(v)
+    assert finite.sum() == 254
+    np.testing.assert_array_equal(oracle.e4m3_encode(v[finite]), codes[finite])
+
+
+def test_e4m3_ties_go_to_even_and_range_ends():
+    v = oracle.e4m3_decode(np.arange(127, dtype=np.uint8))
+    mids = (v[:-1] + v[1:]) / 2  # exact in fp64
+    got = oracle.e4m3_encode(mids)
+    lower = np.arange(126)
+    np.testing.assert_array_equal(got, np.where(lower % 2 == 0, lower, lower + 1))
+    np.testing.assert_array_equal(oracle.e4m3_encode(np.nextafter(mids, np.inf)), lower + 1)
+    np.testing.assert_array_equal(oracle.e4m3_encode(np.nextafter(mids, -np.inf)), lower)
+    # saturation past 448 (no infinities in E4M3), signed underflow, NaN
+    np.testing.assert_array_equal(oracle.e4m3_encode([449.0, 464.0, 1e30, -1e30, np.inf, -np.inf]),
+                                  [0x7E, 0x7E, 0x7E, 0xFE, 0x7E, 0xFE])
+    np.testing.assert_array_equal(oracle.e4m3_encode([2.0 ** -11, -(2.0 ** -11), 2.0 ** -10, 1.5 * 2.0 ** -10]),
+                                  [0x00, 0x80, 0x00, 0x01])
+    assert oracle.e4m3_encode([np.nan])[0] == 0x7F
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    """torch's float8_e4m3fn cast (an independent implementation of the same format, round to nearest
+    even) agrees on every in-range value."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(200000) * np.exp(rng.uniform(-9.0, 6.0, 200000))
+    x = x[np.abs(x) <= 448.0]
+    want = torch.tensor(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.e4m3_encode(x), want)
+    codes = np.arange(256, dtype=np.uint8)
+    tv = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.e4m3_decode(codes), tv)
