@@ -22,6 +22,8 @@ __all__ = [
 
 TPA_F32 = 0
 TPA_BF16 = 1
+TPA_CACHE_NATIVE = 0
+TPA_CACHE_E4M3 = 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtpa.so")
 _lib = None
@@ -68,20 +70,38 @@ class TPAError(RuntimeError):
 
 
 class Dims(ctypes.Structure):
-    """tpa_dims: h, d_h, R_K, R_V, dtype (TPA_F32 / TPA_BF16), rope_base."""
+    """tpa_dims: h, d_h, R_K, R_V, dtype (TPA_F32 / TPA_BF16), cache_format (TPA_CACHE_NATIVE /
+    TPA_CACHE_E4M3), rope_base, cache_scale[4] (E4M3 scales of A_K, B_K, A_V, B_V; 0 means 1)."""
     _fields_ = [("h", ctypes.c_int32), ("d_h", ctypes.c_int32), ("R_K", ctypes.c_int32), ("R_V", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32), ("rope_base", ctypes.c_double)]
+                ("dtype", ctypes.c_int32), ("cache_format", ctypes.c_int32), ("rope_base", ctypes.c_double),
+                ("cache_scale", ctypes.c_float * 4)]
 
-    def __init__(self, h: int, d_h: int, R_K: int, R_V: int, dtype="bf16", rope_base: float = 1e4):
+    def __init__(self, h: int, d_h: int, R_K: int, R_V: int, dtype="bf16", rope_base: float = 1e4,
+                 cache_format: int = 0, cache_scale=(0.0, 0.0, 0.0, 0.0)):
         if isinstance(dtype, str):
             dtype = {"bf16": TPA_BF16, "f32": TPA_F32}[dtype]
         elif isinstance(dtype, torch.dtype):
             dtype = {torch.bfloat16: TPA_BF16, torch.float32: TPA_F32}[dtype]
-        super().__init__(int(h), int(d_h), int(R_K), int(R_V), int(dtype), 0, float(rope_base))
+        if isinstance(cache_format, str):
+            cache_format = {"native": TPA_CACHE_NATIVE, "e4m3": TPA_CACHE_E4M3}[cache_format]
+        super().__init__(int(h), int(d_h), int(R_K), int(R_V), int(dtype), int(cache_format), float(rope_base),
+                         (ctypes.c_float * 4)(*[float(x) for x in cache_scale]))
 
     @property
     def torch_dtype(self) -> torch.dtype:
+        """Element type of factors and queries at the boundary."""
         return torch.bfloat16 if self.dtype == TPA_BF16 else torch.float32
+
+    @property
+    def cache_torch_dtype(self) -> torch.dtype:
+        """Element type tpa_cache_read returns: uint8 codes for an E4M3 cache."""
+        return torch.uint8 if self.cache_format == TPA_CACHE_E4M3 else self.torch_dtype
+
+    def scale(self, k: int) -> float:
+        """Stored-value scale of factor k (0 A_K, 1 B_K, 2 A_V, 3 B_V)."""
+        if self.cache_format != TPA_CACHE_E4M3 or self.cache_scale[k] == 0.0:
+            return 1.0
+        return float(self.cache_scale[k])
 
 
 def library_path() -> str:
@@ -185,7 +205,8 @@ def tpa_cache_append(dims: Dims, cache: torch.Tensor, capacity_tokens: int, slot
 
 def tpa_cache_read(dims: Dims, cache: torch.Tensor, capacity_tokens: int, slot: torch.Tensor,
                    A_K: torch.Tensor, B_K: torch.Tensor, A_V: torch.Tensor, B_V: torch.Tensor, stream=None) -> None:
-    dt = dims.torch_dtype
+    """Stored factors of the given slots; uint8 E4M3 codes for an E4M3 cache."""
+    dt = dims.cache_torch_dtype
     st = load().tpa_cache_read(_ref(dims), _ptr(cache, name="cache"), int(capacity_tokens), slot.numel(),
                                _ptr(slot, torch.int64, "slot"), _ptr(A_K, dt, "A_K"), _ptr(B_K, dt, "B_K"),
                                _ptr(A_V, dt, "A_V"), _ptr(B_V, dt, "B_V"), _stream(stream))

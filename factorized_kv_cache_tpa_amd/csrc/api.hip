@@ -24,12 +24,25 @@ bool dims_valid(const tpa_dims *d) {
     if (d->d_h < 2 || d->d_h > 256 || (d->d_h & 1)) return false;
     if (d->R_K < 1 || d->R_K > 4 || d->R_V < 1 || d->R_V > 4) return false;
     if (d->dtype != TPA_F32 && d->dtype != TPA_BF16) return false;
-    if (d->reserved != 0) return false;
+    if (d->cache_format != TPA_CACHE_NATIVE && d->cache_format != TPA_CACHE_E4M3) return false;
+    if (d->cache_format == TPA_CACHE_E4M3) {
+        if (d->dtype != TPA_BF16) return false;
+        for (int k = 0; k < 4; ++k)
+            if (!(d->cache_scale[k] >= 0.f) || !isfinite(d->cache_scale[k])) return false;
+    }
     if (!(d->rope_base > 0.0) || !isfinite(d->rope_base)) return false;
     return true;
 }
 
-Layout layout_of(const tpa_dims *d) { return tpa::make_layout(d->h, d->d_h, d->R_K, d->R_V, d->dtype); }
+Layout layout_of(const tpa_dims *d) {
+    return tpa::make_layout(d->h, d->d_h, d->R_K, d->R_V, d->dtype, d->cache_format);
+}
+
+// Scale of factor k (0 A_K, 1 B_K, 2 A_V, 3 B_V): the stored value is code * scale for an E4M3 cache.
+double factor_scale(const tpa_dims *d, int k) {
+    if (d->cache_format != TPA_CACHE_E4M3 || d->cache_scale[k] == 0.f) return 1.0;
+    return double(d->cache_scale[k]);
+}
 
 int32_t check_dims(const tpa_dims *d) {
     if (!dims_valid(d)) return TPA_ERR_ARG;
@@ -95,6 +108,7 @@ int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
     // a step also writes slot seq_start + seq_len, so its last possible slot must exist too
     if (int64_t(max_len) + (step ? 1 : 0) > capacity_tokens) return TPA_ERR_CAPACITY;
     const Layout L = layout_of(dims);
+    if (step && L.f8) return TPA_ERR_UNSUPPORTED;
     const DecodePlan P = plan_decode(L, batch, max_len, split_tokens);
     if (!workspace || workspace_bytes < P.bytes) return TPA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TPA_ERR_WORKSPACE;
@@ -116,8 +130,9 @@ int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
     p.max_len = max_len;
     p.split_blocks = P.split_blocks;
     p.n_split = P.n_split;
-    p.score_mul = float(double(resolve_scale(scale, dims->d_h)) * M_LOG2E / dims->R_K);
-    p.out_mul = float(1.0 / dims->R_V);
+    p.score_mul = float(double(resolve_scale(scale, dims->d_h)) * M_LOG2E * factor_scale(dims, 0) *
+                        factor_scale(dims, 1) / dims->R_K);
+    p.out_mul = float(factor_scale(dims, 2) * factor_scale(dims, 3) / dims->R_V);
     if (step) {
         p.step = 1;
         p.st = *step;
@@ -157,8 +172,9 @@ int32_t run_prefill(const tpa_dims *dims, const void *cache, int64_t capacity_to
     p.batch = batch;
     p.chunk = chunk_len;
     p.max_ctx = max_ctx;
-    p.score_mul = float(double(resolve_scale(scale, dims->d_h)) * M_LOG2E / dims->R_K);
-    p.out_mul = float(1.0 / dims->R_V);
+    p.score_mul = float(double(resolve_scale(scale, dims->d_h)) * M_LOG2E * factor_scale(dims, 0) *
+                        factor_scale(dims, 1) / dims->R_K);
+    p.out_mul = float(factor_scale(dims, 2) * factor_scale(dims, 3) / dims->R_V);
     p.r_q = r_q;
     p.a_q = a_q;
     const hipError_t e = tpa::launch_prefill(L, p, as_stream(stream));
@@ -223,9 +239,11 @@ int32_t tpa_cache_append(const tpa_dims *dims, void *cache, int64_t capacity_tok
     if (n_kv + (n_q > 0 ? n_q * tpa::append_q_groups(q_rows, dims->d_h) : 0) > int64_t(0x7fffffff))
         return TPA_ERR_ARG;
     if (n_kv == 0 && n_q == 0) return TPA_OK;
+    float inv_scale[4];
+    for (int k = 0; k < 4; ++k) inv_scale[k] = float(1.0 / factor_scale(dims, k));
     const hipError_t e = tpa::launch_append(layout_of(dims), dims->h, dims->d_h, dims->R_K, dims->R_V,
                                             dims->rope_base, cache, capacity_tokens, n_kv, slot, kv_pos, A_K, B_K,
-                                            A_V, B_V, n_q, q_rows, q_pos, q_in, q_out, as_stream(stream));
+                                            A_V, B_V, n_q, q_rows, q_pos, q_in, q_out, inv_scale, as_stream(stream));
     return e == hipSuccess ? TPA_OK : TPA_ERR_HIP;
 }
 

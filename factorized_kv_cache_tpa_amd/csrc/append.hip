@@ -82,14 +82,20 @@ int64_t append_q_groups(int q_rows, int d_h) {
 
 namespace {
 
+// Inverse scales of A_K, B_K, A_V, B_V for an E4M3 cache (code = E4M3(value * inv)).
+struct InvScale {
+    float v[4];
+};
+
 // Grid: one work-group per cache token (n < n_kv), then append_q_groups(q_rows, d_h) work-groups per
 // query token, each rotating kAppendThreads * kQPairs consecutive pairs of that token's rows.
-template <typename T>
+// kF8: bf16 inputs, E4M3 cache (cache_raw holds bytes); otherwise the cache holds T.
+template <typename T, bool kF8>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(
-    Layout L, int h, int d_h, int RK, int RV, RopeTable rt, T *__restrict__ cache, int64_t capacity, int64_t n_kv,
-    const int64_t *__restrict__ slot, const int32_t *__restrict__ kv_pos, const T *__restrict__ A_K,
+    Layout L, int h, int d_h, int RK, int RV, RopeTable rt, void *__restrict__ cache_raw, int64_t capacity,
+    int64_t n_kv, const int64_t *__restrict__ slot, const int32_t *__restrict__ kv_pos, const T *__restrict__ A_K,
     const T *__restrict__ B_K, const T *__restrict__ A_V, const T *__restrict__ B_V, int64_t n_q, int q_rows,
-    int q_groups, const int32_t *__restrict__ q_pos, const T *q_in, T *q_out) {
+    int q_groups, const int32_t *__restrict__ q_pos, const T *q_in, T *q_out, InvScale inv) {
     using P = Pair<T>;
     using V = typename P::V;
     using F = typename RopeMath<T>::F;
@@ -120,8 +126,37 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
         rope_table<T>(cs, d_h, pos, theta);
         if (s < 0 || s >= capacity) return;  // uniform over the work-group, after the barrier
         const int TOK = L.tok_per_block();
-        T *blk = cache + (s / TOK) * L.block_elems();
         const int row0 = int(s % TOK) * L.RH;
+        if constexpr (kF8) {
+            // E4M3 record: every element is the code of its fp32 value times the inverse scale; B_K's pair
+            // is rotated in fp32 first (one rounding, straight to the code).  Padded rows and heads: code 0.
+            uint8_t *blk = reinterpret_cast<uint8_t *>(cache_raw) + (s / TOK) * L.block_elems();
+#pragma unroll
+            for (int k = 0; k < kKvGates; ++k) {
+                const int idx = tid + k * kAppendThreads, r = idx / L.HP, i = idx % L.HP;
+                if (idx < L.RH * L.HP) {
+                    const int off = L.gate(row0 + r, i);
+                    blk[L.off_ak() + off] = e4m3_one(Elem<T>::to_f32(ga[k]) * inv.v[0]);
+                    blk[L.off_av() + off] = e4m3_one(Elem<T>::to_f32(gv[k]) * inv.v[2]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kKvPairs; ++k) {
+                const int idx = tid + k * kAppendThreads, r = idx / HD, j = idx % HD, d = 2 * j;
+                if (idx < L.RH * HD) {
+                    float y0 = 0.f, y1 = 0.f;
+                    if (r < RK && d < d_h) rope_rotate(P::lo(kx[k]), P::hi(kx[k]), cs[2 * j], cs[2 * j + 1], y0, y1);
+                    // d even: d and d + 1 are adjacent bytes of one lane's 8-code run
+                    *reinterpret_cast<uint16_t *>(blk + L.off_bk() + L.bk(row0 + r, d)) =
+                        uint16_t(e4m3_pair(y0 * inv.v[1], y1 * inv.v[1]));
+                    const uint32_t vc = e4m3_pair(P::lo(vx[k]) * inv.v[3], P::hi(vx[k]) * inv.v[3]);
+                    blk[L.off_bv() + L.bv(row0 + r, d)] = uint8_t(vc & 0xffu);
+                    blk[L.off_bv() + L.bv(row0 + r, d + 1)] = uint8_t(vc >> 8);
+                }
+            }
+            return;
+        }
+        T *blk = reinterpret_cast<T *>(cache_raw) + (s / TOK) * L.block_elems();
 #pragma unroll
         for (int k = 0; k < kKvGates; ++k) {
             const int idx = tid + k * kAppendThreads, r = idx / L.HP, i = idx % L.HP;
@@ -213,7 +248,8 @@ RopeTable make_rope_table(int d_h, double base) {
 hipError_t launch_append(const Layout &L, int h, int d_h, int RK, int RV, double base, void *cache,
                          int64_t capacity, int64_t n_kv, const int64_t *slot, const int32_t *kv_pos,
                          const void *A_K, const void *B_K, const void *A_V, const void *B_V, int64_t n_q,
-                         int q_rows, const int32_t *q_pos, const void *q_in, void *q_out, hipStream_t s) {
+                         int q_rows, const int32_t *q_pos, const void *q_in, void *q_out, const float *inv_scale,
+                         hipStream_t s) {
     if (L.RH * L.DP / 2 > kKvPairs * kAppendThreads || L.RH * L.HP > kKvGates * kAppendThreads ||
         d_h / 2 > kAppendThreads)
         return hipErrorInvalidValue;  // outside the validated dimension range
@@ -222,16 +258,26 @@ hipError_t launch_append(const Layout &L, int h, int d_h, int RK, int RV, double
     if (grid == 0) return hipSuccess;
     if (grid > int64_t(0x7fffffff)) return hipErrorInvalidConfiguration;
     const RopeTable rt = make_rope_table(d_h, base);
-    if (L.es == 2) {
+    InvScale inv;
+    for (int k = 0; k < 4; ++k) inv.v[k] = inv_scale ? inv_scale[k] : 1.f;
+    if (L.f8) {
         using T = uint16_t;
-        hipLaunchKernelGGL(append_kernel<T>, dim3(unsigned(grid)), dim3(kAppendThreads), 0, s, L, h, d_h, RK, RV,
-                           rt, (T *)cache, capacity, n_kv, slot, kv_pos, (const T *)A_K, (const T *)B_K,
-                           (const T *)A_V, (const T *)B_V, n_q, q_rows, int(q_groups), q_pos, (const T *)q_in, (T *)q_out);
+        hipLaunchKernelGGL((append_kernel<T, true>), dim3(unsigned(grid)), dim3(kAppendThreads), 0, s, L, h, d_h, RK,
+                           RV, rt, cache, capacity, n_kv, slot, kv_pos, (const T *)A_K, (const T *)B_K,
+                           (const T *)A_V, (const T *)B_V, n_q, q_rows, int(q_groups), q_pos, (const T *)q_in,
+                           (T *)q_out, inv);
+    } else if (L.es == 2) {
+        using T = uint16_t;
+        hipLaunchKernelGGL((append_kernel<T, false>), dim3(unsigned(grid)), dim3(kAppendThreads), 0, s, L, h, d_h,
+                           RK, RV, rt, cache, capacity, n_kv, slot, kv_pos, (const T *)A_K, (const T *)B_K,
+                           (const T *)A_V, (const T *)B_V, n_q, q_rows, int(q_groups), q_pos, (const T *)q_in,
+                           (T *)q_out, inv);
     } else {
         using T = float;
-        hipLaunchKernelGGL(append_kernel<T>, dim3(unsigned(grid)), dim3(kAppendThreads), 0, s, L, h, d_h, RK, RV,
-                           rt, (T *)cache, capacity, n_kv, slot, kv_pos, (const T *)A_K, (const T *)B_K,
-                           (const T *)A_V, (const T *)B_V, n_q, q_rows, int(q_groups), q_pos, (const T *)q_in, (T *)q_out);
+        hipLaunchKernelGGL((append_kernel<T, false>), dim3(unsigned(grid)), dim3(kAppendThreads), 0, s, L, h, d_h,
+                           RK, RV, rt, cache, capacity, n_kv, slot, kv_pos, (const T *)A_K, (const T *)B_K,
+                           (const T *)A_V, (const T *)B_V, n_q, q_rows, int(q_groups), q_pos, (const T *)q_in,
+                           (T *)q_out, inv);
     }
     return hipGetLastError();
 }
@@ -240,7 +286,11 @@ hipError_t launch_read(const Layout &L, int h, int d_h, int RK, int RV, const vo
                        int64_t n, const int64_t *slot, void *A_K, void *B_K, void *A_V, void *B_V,
                        hipStream_t s) {
     if (n == 0) return hipSuccess;
-    if (L.es == 2) {
+    if (L.f8) {
+        using T = uint8_t;
+        hipLaunchKernelGGL(read_kernel<T>, dim3(unsigned(n)), dim3(kAppendThreads), 0, s, L, h, d_h, RK, RV,
+                           (const T *)cache, capacity, slot, (T *)A_K, (T *)B_K, (T *)A_V, (T *)B_V);
+    } else if (L.es == 2) {
         using T = uint16_t;
         hipLaunchKernelGGL(read_kernel<T>, dim3(unsigned(n)), dim3(kAppendThreads), 0, s, L, h, d_h, RK, RV,
                            (const T *)cache, capacity, slot, (T *)A_K, (T *)B_K, (T *)A_V, (T *)B_V);

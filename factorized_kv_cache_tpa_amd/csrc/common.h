@@ -25,6 +25,16 @@
 // so the score accumulator a lane holds (rows 4(lane/16)+v of both score
 // row blocks, one head) is exactly the k-slice it must supply to the value
 // contraction: no data moves between lanes between the two contractions.
+//
+// 8-bit factor storage (OCP E4M3 codes; bf16 queries and matrix-core
+// operands): the same per-lane pieces, one byte per element, with two pieces
+// paired per lane so that a lane still loads 16 (gates: 8) contiguous bytes:
+//   gates : [NB][lane 64][mblk 2][4]      (both row blocks of a head block)
+//   B~_K  : [KBS][lane 64][mblk 2][8]     (both row blocks of a k-block)
+//   B_V   : [MBV/2][lane 64][2][8]        (value M blocks 2j and 2j+1)
+// The kernels turn the codes into bf16 fragments and fp32 gates in registers;
+// a stored value is code * scale with one scale per factor tensor, folded into
+// the score and output multipliers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -55,6 +65,7 @@ __device__ __forceinline__ u32x2 stream_load8(const void *p) {
 struct Layout {
     int HP, DP, RH, E;  // padded heads, padded head dim, padded rank, k-values per lane
     int es;             // element size in bytes
+    int f8;             // 1: E4M3 codes in the paired 8-bit layout (bf16 queries)
 
     __host__ __device__ int tok_per_block() const { return kRows / RH; }
     __host__ __device__ int NB() const { return HP / 16; }
@@ -70,15 +81,18 @@ struct Layout {
     // element offsets inside a block region
     __host__ __device__ int gate(int row, int head) const {
         int mb = row >> 4, nb = head >> 4, lane = 16 * ((row & 15) >> 2) + (head & 15), v = row & 3;
+        if (f8) return ((nb * kWave + lane) * 2 + mb) * 4 + v;
         return ((mb * NB() + nb) * kWave + lane) * 4 + v;
     }
     __host__ __device__ int bk(int row, int d) const {
         int mb = row >> 4, kb = d / (4 * E), lane = 16 * ((d % (4 * E)) / E) + (row & 15), e = d % E;
+        if (f8) return ((kb * kWave + lane) * 2 + mb) * E + e;
         return ((mb * KBS() + kb) * kWave + lane) * E + e;
     }
     __host__ __device__ int bv(int row, int d) const {
         int t = 4 * (row >> 4) + (row & 3), g = (row & 15) >> 2;
         int q = t / E, e = t % E, mv = d >> 4, lane = 16 * g + (d & 15);
+        if (f8) return (((mv >> 1) * kWave + lane) * 2 + (mv & 1)) * E + e;  // E = 8: q = 0
         return ((mv * KBV() + q) * kWave + lane) * E + e;
     }
 };
@@ -91,10 +105,12 @@ __host__ __device__ inline int padded_rank(int RK, int RV) {
     return r <= 1 ? 1 : (r <= 2 ? 2 : 4);
 }
 
-__host__ __device__ inline Layout make_layout(int h, int d_h, int RK, int RV, int dtype) {
+// fmt 1: E4M3 storage (dtype must be bf16, checked by the caller)
+__host__ __device__ inline Layout make_layout(int h, int d_h, int RK, int RV, int dtype, int fmt = 0) {
     Layout L;
     L.E = dtype == 1 ? 8 : 1;
-    L.es = dtype == 1 ? 2 : 4;
+    L.es = fmt == 1 ? 1 : (dtype == 1 ? 2 : 4);
+    L.f8 = fmt == 1 ? 1 : 0;
     L.HP = round_up(h, 16);
     L.DP = round_up(d_h, dtype == 1 ? 32 : 16);
     L.RH = padded_rank(RK, RV);
@@ -118,6 +134,35 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);  // quiet NaN
     u += 0x7fffu + ((u >> 16) & 1u);
     return uint16_t(u >> 16);
+}
+
+// ---- OCP E4M3 codes (8-bit factor storage).  The gfx950 conversions decode exactly; the encoder rounds
+// to nearest even but turns magnitudes past 464 into NaN, so values are first clamped to the largest
+// finite magnitude, 448 (saturation; NaN stays NaN).
+__device__ __forceinline__ float e4m3_clamp(float x) { return fabsf(x) > 448.f ? copysignf(448.f, x) : x; }
+// two values -> two codes in the low 16 bits (first value in the low byte)
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
+    return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false)) & 0xffffu;
+}
+__device__ __forceinline__ uint8_t e4m3_one(float a) { return uint8_t(e4m3_pair(a, 0.f) & 0xffu); }
+// four codes (bytes of w, low first) -> four fp32
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float *g) {
+    const floatx2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(w), false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(w), true);
+    g[0] = lo.x;
+    g[1] = lo.y;
+    g[2] = hi.x;
+    g[3] = hi.y;
+}
+// four codes -> two packed bf16 pairs (exact: every E4M3 value is a bf16 value)
+__device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t w) {
+    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+// eight codes -> eight bf16 (an MFMA fragment's 16 bytes)
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+    const uint2 a = e4m3x4_to_bf16x4(w0), b = e4m3x4_to_bf16x4(w1);
+    return make_uint4(a.x, a.y, b.x, b.y);
 }
 
 template <typename T>
@@ -238,7 +283,8 @@ int64_t append_q_groups(int q_rows, int d_h);
 hipError_t launch_append(const Layout &L, int h, int d_h, int RK, int RV, double base, void *cache,
                          int64_t capacity, int64_t n_kv, const int64_t *slot, const int32_t *kv_pos,
                          const void *A_K, const void *B_K, const void *A_V, const void *B_V, int64_t n_q,
-                         int q_rows, const int32_t *q_pos, const void *q_in, void *q_out, hipStream_t s);
+                         int q_rows, const int32_t *q_pos, const void *q_in, void *q_out, const float *inv_scale,
+                         hipStream_t s);
 hipError_t launch_read(const Layout &L, int h, int d_h, int RK, int RV, const void *cache, int64_t capacity,
                        int64_t n, const int64_t *slot, void *A_K, void *B_K, void *A_V, void *B_V,
                        hipStream_t s);

@@ -159,8 +159,10 @@ __device__ __forceinline__ float wave_sum_across_groups(float x) {
 constexpr int kQRot = 0, kStepMode = 1, kQFact = 2;
 constexpr int kMaxRQ = 16;  // query rank limit of the factored mode
 
-template <typename T, int HP, int DP, int RH, int kMode>
+// kF8: the cache holds E4M3 codes in the paired 8-bit layout (T = uint16_t: bf16 queries and operands).
+template <typename T, int HP, int DP, int RH, int kMode, bool kF8>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
+    static_assert(!kF8 || (sizeof(T) == 2 && (DP / 16) % 2 == 0), "E4M3 storage: bf16 operands, paired value blocks");
     constexpr bool kStep = kMode == kStepMode;
     constexpr bool kFact = kMode == kQFact;
     using M = Mfma<T>;
@@ -224,35 +226,83 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     }
     const int blk_end = min(nblk, blk_begin + p.split_blocks);
     const int full_end = min(blk_end, len / TOK);  // blocks [blk_begin, full_end) hold TOK valid tokens
-    const T *seq = reinterpret_cast<const T *>(p.cache) + (start / TOK) * BLK;
+    constexpr int CES = kF8 ? 1 : int(sizeof(T));  // bytes per stored element
+    const char *seq = reinterpret_cast<const char *>(p.cache) + (start / TOK) * BLK * CES;
 
     // One block's operands, loaded straight from the cache in MFMA lane order: a scalar block base
     // plus one per-lane offset, so every load is one instruction with an immediate region offset.
-    struct Stage {
+    struct StageNative {
         GateRaw ak[2][NB], av[2][NB];
         Frag bk[2][KBS], bv[MBV][KBV];
     };
-    const uint32_t off_op = uint32_t(lane * E * sizeof(T));  // operand lane offset, bytes
-    const uint32_t off_gt = uint32_t(lane * 4 * sizeof(T));  // gate lane offset, bytes
+    // E4M3: a lane's 16 bytes hold its codes for both row blocks of a k-block (B~_K) or for value blocks
+    // 2j and 2j+1 (B_V); its 8 gate bytes hold both row blocks of a head block.  Decoded at use.
+    struct StageF8 {
+        u32x2 ak[NB], av[NB];
+        u32x4 bk[KBS], bv[MBV / 2];
+    };
+    using Stage = std::conditional_t<kF8, StageF8, StageNative>;
+    const uint32_t off_op = uint32_t(lane * E * sizeof(T));  // operand lane offset, bytes (native)
+    const uint32_t off_gt = uint32_t(lane * 4 * sizeof(T));  // gate lane offset, bytes (native)
     auto load = [&](Stage &st, int blk) {
-        const char *bp = reinterpret_cast<const char *>(seq + int64_t(blk) * BLK);
-        const T *op = reinterpret_cast<const T *>(bp + off_op);
-        const T *gt = reinterpret_cast<const T *>(bp + off_gt);
+        const char *bp = seq + int64_t(blk) * BLK * CES;
+        if constexpr (kF8) {
+            const char *op = bp + lane * 16;
+            const char *gt = bp + lane * 8;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int kb = 0; kb < KBS; ++kb) st.bk[mb][kb] = M::stream(op + OFF_BK + (mb * KBS + kb) * kWave * E);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+            for (int kb = 0; kb < KBS; ++kb) st.bk[kb] = stream_load16(op + OFF_BK + kb * kWave * 16);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                st.ak[mb][nb] = M::load_gates(gt + (mb * NB + nb) * kWave * 4);
-                st.av[mb][nb] = M::load_gates(gt + OFF_AV + (mb * NB + nb) * kWave * 4);
+                st.ak[nb] = stream_load8(gt + nb * kWave * 8);
+                st.av[nb] = stream_load8(gt + OFF_AV + nb * kWave * 8);
             }
 #pragma unroll
-        for (int mv = 0; mv < MBV; ++mv)
+            for (int j = 0; j < MBV / 2; ++j) st.bv[j] = stream_load16(op + OFF_BV + j * kWave * 16);
+        } else {
+            const T *op = reinterpret_cast<const T *>(bp + off_op);
+            const T *gt = reinterpret_cast<const T *>(bp + off_gt);
 #pragma unroll
-            for (int q = 0; q < KBV; ++q) st.bv[mv][q] = M::stream(op + OFF_BV + (mv * KBV + q) * kWave * E);
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int kb = 0; kb < KBS; ++kb) st.bk[mb][kb] = M::stream(op + OFF_BK + (mb * KBS + kb) * kWave * E);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    st.ak[mb][nb] = M::load_gates(gt + (mb * NB + nb) * kWave * 4);
+                    st.av[mb][nb] = M::load_gates(gt + OFF_AV + (mb * NB + nb) * kWave * 4);
+                }
+#pragma unroll
+            for (int mv = 0; mv < MBV; ++mv)
+#pragma unroll
+                for (int q = 0; q < KBV; ++q) st.bv[mv][q] = M::stream(op + OFF_BV + (mv * KBV + q) * kWave * E);
+        }
+    };
+    // The operands of a loaded stage: B~_K fragment (row block mb, k-block kb), the 4 gates of row block
+    // mb and head block nb, and the B_V fragment of value block mv (k-block q).
+    auto frag_bk = [&](const Stage &st, int mb, int kb) -> Frag {
+        if constexpr (kF8) {
+            const u32x4 r = st.bk[kb];
+            return __builtin_bit_cast(Frag, mb ? e4m3x8_to_bf16x8(r.z, r.w) : e4m3x8_to_bf16x8(r.x, r.y));
+        } else {
+            return st.bk[mb][kb];
+        }
+    };
+    auto gates = [&](const Stage &st, bool value, int mb, int nb, float *gv) {
+        if constexpr (kF8) {
+            const u32x2 r = value ? st.av[nb] : st.ak[nb];
+            e4m3x4_to_f32(mb ? r.y : r.x, gv);
+        } else {
+            M::unpack_gates(value ? st.av[mb][nb] : st.ak[mb][nb], gv);
+        }
+    };
+    auto frag_bv = [&](const Stage &st, int mv, int q) -> Frag {
+        if constexpr (kF8) {
+            const u32x4 r = st.bv[mv >> 1];
+            return __builtin_bit_cast(Frag, (mv & 1) ? e4m3x8_to_bf16x8(r.z, r.w) : e4m3x8_to_bf16x8(r.x, r.y));
+        } else {
+            return st.bv[mv][q];
+        }
     };
 
     // Fused step, split 0: this thread's item of the new token (one head-factor pair (A_K, A_V) of row
@@ -505,7 +555,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             for (int nb = 0; nb < NB; ++nb) {
                 floatx4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < KBS; ++kb) a = M::mma(st.bk[mb][kb], qf[kb][nb], a);
+                for (int kb = 0; kb < KBS; ++kb) a = M::mma(frag_bk(st, mb, kb), qf[kb][nb], a);
                 u[mb][nb] = a;
             }
 
@@ -516,8 +566,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             float ak[2][4], av[2][4];
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
-                M::unpack_gates(st.ak[mb][nb], ak[mb]);
-                M::unpack_gates(st.av[mb][nb], av[mb]);
+                gates(st, false, mb, nb, ak[mb]);
+                gates(st, true, mb, nb, av[mb]);
             }
             float z[2][TPL];
             float mx = -INFINITY;
@@ -560,24 +610,22 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                 }
         }
 
-        if (kTail) {  // rows beyond the sequence: their stored B_V may be anything, zero them
+        // ---- 5. value contraction (in a tail block, rows beyond the sequence have arbitrary stored B_V:
+        // their slots are zeroed in the operand)
 #pragma unroll
-            for (int q = 0; q < KBV; ++q) {
-                unsigned bits = 0;
+        for (int q = 0; q < KBV; ++q) {
+            unsigned bits = 0;
+            if (kTail) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const int t = E * q + e;
                     const int row = 16 * (t / 4) + 4 * g + (t % 4);
                     if (row / RH >= valid) bits |= 1u << e;
                 }
-#pragma unroll
-                for (int mv = 0; mv < MBV; ++mv) st.bv[mv][q] = M::mask(st.bv[mv][q], bits);
             }
-        }
-
-        // ---- 5. value contraction
+            Frag bvf[MBV];
 #pragma unroll
-        for (int q = 0; q < KBV; ++q)
+            for (int mv = 0; mv < MBV; ++mv) bvf[mv] = kTail ? M::mask(frag_bv(st, mv, q), bits) : frag_bv(st, mv, q);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 float x[E];
@@ -588,8 +636,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                 }
                 const Frag wf = M::pack(x);
 #pragma unroll
-                for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] = M::mma(st.bv[mv][q], wf, acc[mv][nb]);
+                for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] = M::mma(bvf[mv], wf, acc[mv][nb]);
             }
+        }
     };
     using Full = std::integral_constant<bool, false>;
     using Tail = std::integral_constant<bool, true>;
@@ -782,23 +831,34 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
 }
 
 template <typename T, int HP, int DP, int RH>
-hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
+hipError_t launch_split(const DecodeParams &p, bool f8, hipStream_t s) {
     const dim3 grid(p.n_split, p.batch);
+    if constexpr (sizeof(T) == 2) {
+        if (f8) {  // no fused step over an E4M3 cache (rejected by the caller)
+            if (p.step) return hipErrorInvalidValue;
+            if (p.r_q > 0)
+                hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, kQFact, true>), grid, dim3(kThreads), 0, s, p);
+            else
+                hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, kQRot, true>), grid, dim3(kThreads), 0, s, p);
+            return hipGetLastError();
+        }
+    }
+    if (f8) return hipErrorInvalidValue;
     if (p.step)
-        hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, kStepMode>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, kStepMode, false>), grid, dim3(kThreads), 0, s, p);
     else if (p.r_q > 0)
-        hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, kQFact>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, kQFact, false>), grid, dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, kQRot>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, kQRot, false>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
 template <typename T, int HP, int DP>
-hipError_t launch_split_rank(int RH, const DecodeParams &p, hipStream_t s) {
+hipError_t launch_split_rank(int RH, const DecodeParams &p, bool f8, hipStream_t s) {
     switch (RH) {
-        case 1: return launch_split<T, HP, DP, 1>(p, s);
-        case 2: return launch_split<T, HP, DP, 2>(p, s);
-        case 4: return launch_split<T, HP, DP, 4>(p, s);
+        case 1: return launch_split<T, HP, DP, 1>(p, f8, s);
+        case 2: return launch_split<T, HP, DP, 2>(p, f8, s);
+        case 4: return launch_split<T, HP, DP, 4>(p, f8, s);
     }
     return hipErrorInvalidValue;
 }
@@ -812,9 +872,11 @@ hipError_t launch_split_rank(int RH, const DecodeParams &p, hipStream_t s) {
 
 }  // namespace
 
+// An E4M3 cache runs the bf16 shapes (its operands are bf16 after decoding).
 bool decode_supported(const Layout &L) {
+    const int es = L.f8 ? 2 : L.es;
 #define X(T, ES, HP_, DP_) \
-    if (L.es == ES && L.HP == HP_ && L.DP == DP_) return true;
+    if (es == ES && L.HP == HP_ && L.DP == DP_) return true;
     TPA_DECODE_SHAPES(X)
 #undef X
     return false;
@@ -823,10 +885,11 @@ bool decode_supported(const Layout &L) {
 hipError_t launch_decode(const Layout &L, const DecodeParams &p, hipStream_t s) {
     hipError_t e = hipErrorInvalidValue;
     bool found = false;
+    const int es = L.f8 ? 2 : L.es;
 #define X(T, ES, HP_, DP_)                                         \
-    if (!found && L.es == ES && L.HP == HP_ && L.DP == DP_) {       \
+    if (!found && es == ES && L.HP == HP_ && L.DP == DP_) {         \
         found = true;                                              \
-        e = launch_split_rank<T, HP_, DP_>(L.RH, p, s);            \
+        e = launch_split_rank<T, HP_, DP_>(L.RH, p, L.f8 != 0, s); \
     }
     TPA_DECODE_SHAPES(X)
 #undef X

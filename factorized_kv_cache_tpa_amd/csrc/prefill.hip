@@ -60,7 +60,7 @@ struct PrefillLds {
 
 // One work-group's loop.  late: the second wave of each SIMD (waves 4..7), which rebuilds at the top of
 // its iteration instead of the end; see prefill_kernel.
-template <int HP, int DP, int RH, bool kFQ, bool late>
+template <int HP, int DP, int RH, bool kFQ, bool late, bool kF8>
 __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<DP> &lds) {
     auto &sK = lds.k;
     auto &sV = lds.v;
@@ -109,7 +109,8 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
         }
         return;
     }
-    const uint16_t *seq = reinterpret_cast<const uint16_t *>(p.cache) + (start / TOK) * int64_t(BLK);
+    constexpr uint32_t CES = kF8 ? 1u : 2u;  // bytes per stored element (E4M3 codes, or bf16)
+    const char *seq = reinterpret_cast<const char *>(p.cache) + (start / TOK) * int64_t(BLK) * CES;
     const int j_last = min(p.chunk, j0 + kQT) - 1;
     const int n_keys = ctx + j_last + 1;  // keys any row of this work-group sees (all appended)
     const int n_kt = (n_keys + kKT - 1) / kKT;
@@ -132,38 +133,77 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
     const int kk = tid / C8, c8 = tid % C8;    // key of item 0, its feature chunk
     const int krow0 = (kk % TOK) * RH;         // the key's first factor row in its block
     const int kv0 = krow0 & 3;                 // its first gate inside a 4-gate chunk
-    // byte offsets from the tile's first block (unsigned 32-bit: scalar base + vector offset addressing)
-    const uint32_t k_off_blk = uint32_t((kk / TOK) * BLK) * 2u;  // block of item 0 inside the tile
+    // byte offsets from the tile's first block (unsigned 32-bit: scalar base + vector offset addressing).
+    // An E4M3 cache stores the same pieces at one byte per element, paired per lane (gates: both row
+    // blocks; B~_K: both row blocks of a k-block; B_V: value blocks 2j, 2j+1).
+    const uint32_t k_off_blk = uint32_t((kk / TOK) * BLK) * CES;  // block of item 0 inside the tile
+    const int k_mb = krow0 >> 4, k_gl = 16 * ((krow0 & 15) >> 2) + gate_lane;
     const uint32_t k_off_gate =
-        k_off_blk + uint32_t((((krow0 >> 4) * NB + gate_nb) * kWave + 16 * ((krow0 & 15) >> 2) + gate_lane) * 4) * 2u;
+        k_off_blk + (kF8 ? uint32_t(((gate_nb * kWave + k_gl) * 2 + k_mb) * 4)
+                         : uint32_t(((k_mb * NB + gate_nb) * kWave + k_gl) * 4) * 2u);
     uint32_t k_off_b[RH];
 #pragma unroll
     for (int r = 0; r < RH; ++r) {
         const int row = krow0 + r, d0 = 8 * c8;
-        k_off_b[r] = k_off_blk +
-                     uint32_t(OFF_BK + (((row >> 4) * KBS + (d0 >> 5)) * kWave + 16 * ((d0 & 31) >> 3) + (row & 15)) * 8) * 2u;
+        const int kb = d0 >> 5, bl = 16 * ((d0 & 31) >> 3) + (row & 15);
+        k_off_b[r] = k_off_blk + (kF8 ? uint32_t(OFF_BK + ((kb * kWave + bl) * 2 + (row >> 4)) * 8)
+                                      : uint32_t(OFF_BK + (((row >> 4) * KBS + kb) * kWave + bl) * 8) * 2u);
     }
     const int vrow = tid / kWave, vcl = tid % kWave, vg4 = vcl >> 4;
     const int vbi = vrow % BPT, vmv0 = (vrow / BPT) * V_ITEMS;  // block inside the tile, first feature group
+    // E4M3: with an even item count (vmv0 even) a thread loads its value chunks two at a time (one
+    // 16-byte pair piece); a single item loads its own 8 bytes of the pair piece.
+    constexpr bool VPAIR = V_ITEMS % 2 == 0;
     // feature of item u: 16 (vmv0 + u) + vcl % 16; chunk of item u: (vmv0 + u) * 64 + vcl
-    const uint32_t v_off = uint32_t(vbi * BLK + OFF_BV + (vmv0 * kWave + vcl) * 8) * 2u;
-    const uint32_t v_off_gate = uint32_t(vbi * BLK + OFF_AV + (gate_nb * kWave + 16 * vg4 + gate_lane) * 4) * 2u;
+    const uint32_t v_off = kF8 ? uint32_t(vbi * BLK + OFF_BV + (((vmv0 >> 1) * kWave + vcl) * 2 + (VPAIR ? 0 : (vmv0 & 1))) * 8)
+                               : uint32_t(vbi * BLK + OFF_BV + (vmv0 * kWave + vcl) * 8) * 2u;
+    const int v_gl = 16 * vg4 + gate_lane;
+    const uint32_t v_off_gate = kF8 ? uint32_t(vbi * BLK + OFF_AV + (gate_nb * kWave + v_gl) * 8)
+                                    : uint32_t(vbi * BLK + OFF_AV + (gate_nb * kWave + v_gl) * 4) * 2u;
 
     // raw factor data of one tile, in registers between its loads and its rebuild
-    struct Raw {
+    struct RawNative {
         uint2 kg[K_ITEMS];
         uint4 kb_raw[K_ITEMS][RH];
         uint4 vx[V_ITEMS];
         uint2 vg[2];
+    };
+    struct RawF8 {  // E4M3 codes: 4 gates per word, 8 features per uint2, two value chunks per uint4
+        uint32_t kg[K_ITEMS];
+        uint2 kb_raw[K_ITEMS][RH];
+        uint4 vx[VPAIR ? V_ITEMS / 2 : 1];
+        uint2 vx1;  // single-item case
+        uint2 vg;
+    };
+    using Raw = std::conditional_t<kF8, RawF8, RawNative>;
+    // the rebuild's inputs as bf16 (E4M3 codes decode exactly to bf16)
+    auto in_kg = [&](const Raw &raw, int u) -> uint2 {
+        if constexpr (kF8) return e4m3x4_to_bf16x4(raw.kg[u]);
+        else return raw.kg[u];
+    };
+    auto in_kb = [&](const Raw &raw, int u, int r) -> uint4 {
+        if constexpr (kF8) return e4m3x8_to_bf16x8(raw.kb_raw[u][r].x, raw.kb_raw[u][r].y);
+        else return raw.kb_raw[u][r];
+    };
+    auto in_vx = [&](const Raw &raw, int u) -> uint4 {
+        if constexpr (kF8) {
+            if constexpr (!VPAIR) return e4m3x8_to_bf16x8(raw.vx1.x, raw.vx1.y);
+            const uint4 w = raw.vx[u >> 1];
+            return (u & 1) ? e4m3x8_to_bf16x8(w.z, w.w) : e4m3x8_to_bf16x8(w.x, w.y);
+        } else {
+            return raw.vx[u];
+        }
+    };
+    auto in_vg = [&](const Raw &raw, int m) -> uint2 {
+        if constexpr (kF8) return e4m3x4_to_bf16x4(m ? raw.vg.y : raw.vg.x);
+        else return raw.vg[m];
     };
     // Loads of one tile, in two halves (the K~ inputs, the V inputs) so that each half can be issued
     // between the matrix-core instructions of one phase.  Only the last tile may reach past n_keys:
     // there a block past the last live one is replaced by that block (its keys are zeroed in the
     // rebuild), so no address leaves the sequence's slots.  No branches: the selects keep each half in
     // the basic block it is placed in.
-    auto tile_base = [&](int kt) {
-        return reinterpret_cast<const char *>(seq + int64_t((kt * kKT) / TOK) * BLK);  // tile's first block
-    };
+    auto tile_base = [&](int kt) { return seq + int64_t((kt * kKT) / TOK) * BLK * CES; };  // tile's first block
     auto tile_last_blk = [&](int kt) {  // last block with live keys, tile-relative (large if the tile is whole)
         const int key0 = kt * kKT;
         return key0 + kKT <= n_keys ? 1 << 20 : (n_keys - 1) / TOK - key0 / TOK;
@@ -174,21 +214,39 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
 #pragma unroll
         for (int u = 0; u < K_ITEMS; ++u) {
             // item u's block lies u * (K_STEP / TOK) blocks past item 0's
-            const uint32_t delta = uint32_t(min(kk / TOK + u * (K_STEP / TOK), last_blk) * BLK) * 2u - k_off_blk;
-            raw.kg[u] = *reinterpret_cast<const uint2 *>(tb + (k_off_gate + delta));
+            const uint32_t delta = uint32_t(min(kk / TOK + u * (K_STEP / TOK), last_blk) * BLK) * CES - k_off_blk;
+            if constexpr (kF8) {
+                raw.kg[u] = *reinterpret_cast<const uint32_t *>(tb + (k_off_gate + delta));
 #pragma unroll
-            for (int r = 0; r < RH; ++r) raw.kb_raw[u][r] = *reinterpret_cast<const uint4 *>(tb + (k_off_b[r] + delta));
+                for (int r = 0; r < RH; ++r) raw.kb_raw[u][r] = *reinterpret_cast<const uint2 *>(tb + (k_off_b[r] + delta));
+            } else {
+                raw.kg[u] = *reinterpret_cast<const uint2 *>(tb + (k_off_gate + delta));
+#pragma unroll
+                for (int r = 0; r < RH; ++r) raw.kb_raw[u][r] = *reinterpret_cast<const uint4 *>(tb + (k_off_b[r] + delta));
+            }
         }
     };
     auto fetch_v = [&](Raw &raw, int kt) {
         const char *tb = tile_base(kt);
-        const uint32_t delta = uint32_t((min(vbi, tile_last_blk(kt)) - vbi) * BLK) * 2u;
+        const uint32_t delta = uint32_t((min(vbi, tile_last_blk(kt)) - vbi) * BLK) * CES;
+        if constexpr (kF8) {
+            if constexpr (VPAIR) {
 #pragma unroll
-        for (int u = 0; u < V_ITEMS; ++u)
-            raw.vx[u] = *reinterpret_cast<const uint4 *>(tb + (v_off + uint32_t(u * kWave * 8 * 2) + delta));
+                for (int u2 = 0; u2 < V_ITEMS / 2; ++u2)
+                    raw.vx[u2] = *reinterpret_cast<const uint4 *>(tb + (v_off + uint32_t(u2 * kWave * 16) + delta));
+            } else {
+                static_assert(V_ITEMS == 1, "odd item counts are single items");
+                raw.vx1 = *reinterpret_cast<const uint2 *>(tb + (v_off + delta));
+            }
+            raw.vg = *reinterpret_cast<const uint2 *>(tb + (v_off_gate + delta));
+        } else {
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-            raw.vg[m] = *reinterpret_cast<const uint2 *>(tb + (v_off_gate + uint32_t(m * NB * kWave * 4 * 2) + delta));
+            for (int u = 0; u < V_ITEMS; ++u)
+                raw.vx[u] = *reinterpret_cast<const uint4 *>(tb + (v_off + uint32_t(u * kWave * 8 * 2) + delta));
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                raw.vg[m] = *reinterpret_cast<const uint2 *>(tb + (v_off_gate + uint32_t(m * NB * kWave * 4 * 2) + delta));
+        }
     };
     // Partial: true only for a tile that reaches past n_keys (its dead keys are written as zeros).
     auto rebuild = [&](Raw &raw, int kt, int buf, auto partial_tag) {
@@ -196,21 +254,21 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
         const int key0 = kt * kKT;
         uint16_t *dK = sK[buf];
         uint16_t *dV = sV[buf];
-        auto &kg = raw.kg;
-        auto &kb_raw = raw.kb_raw;
-        auto &vx = raw.vx;
-        auto &vg = raw.vg;
         // -- K~ rows: K~[key][d] = sum_r A_K[key][r] B~_K[key][r][d]
 #pragma unroll
         for (int u = 0; u < K_ITEMS; ++u) {
             const int k = kk + u * K_STEP;
-            const uint32_t gw[2] = {kg[u].x, kg[u].y};
+            const uint2 kgu = in_kg(raw, u);
+            const uint32_t gw[2] = {kgu.x, kgu.y};
+            uint4 kbr[RH];
+#pragma unroll
+            for (int r = 0; r < RH; ++r) kbr[r] = in_kb(raw, u, r);
             float kv[8];
 #pragma unroll
             for (int w2 = 0; w2 < 4; ++w2) {  // feature pairs (2 w2, 2 w2 + 1)
                 if (RH == 1) {
                     const uint32_t a = (kv0 & 1) ? (gw[kv0 >> 1] >> 16) : (gw[kv0 >> 1] & 0xffffu);
-                    const uint32_t bw = (&kb_raw[u][0].x)[w2];
+                    const uint32_t bw = (&kbr[0].x)[w2];
                     kv[2 * w2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(bw & 0xffffu), 0.f, false);
                     kv[2 * w2 + 1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(bw >> 16), 0.f, false);
                 } else {
@@ -218,7 +276,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
 #pragma unroll
                     for (int rp = 0; rp < RH / 2; ++rp) {  // rank pairs (2 rp, 2 rp + 1)
                         const uint32_t a = gw[(kv0 >> 1) + rp];
-                        const uint32_t b0 = (&kb_raw[u][2 * rp].x)[w2], b1 = (&kb_raw[u][2 * rp + 1].x)[w2];
+                        const uint32_t b0 = (&kbr[2 * rp].x)[w2], b1 = (&kbr[2 * rp + 1].x)[w2];
                         const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x05040100u);  // (b0[d], b1[d])
                         const uint32_t hi2 = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // (b0[d+1], b1[d+1])
                         kv[2 * w2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(lo), kv[2 * w2], false);
@@ -238,12 +296,14 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
 #pragma unroll
         for (int u = 0; u < V_ITEMS; ++u) {
             const int vd = 16 * (vmv0 + u) + (vcl & 15);  // the feature this chunk holds
-            const uint32_t xw[4] = {vx[u].x, vx[u].y, vx[u].z, vx[u].w};
+            const uint4 vxu = in_vx(raw, u);
+            const uint32_t xw[4] = {vxu.x, vxu.y, vxu.z, vxu.w};
             float v_one[2];  // RH == 4: the one token of each half, packed together below
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 // rows 16 m + 4 vg4 + 0..3 of the block: TPH whole tokens
-                const uint32_t gw[2] = {vg[m].x, vg[m].y};
+                const uint2 vgm = in_vg(raw, m);
+                const uint32_t gw[2] = {vgm.x, vgm.y};
                 float vt[TPH];
 #pragma unroll
                 for (int tl = 0; tl < TPH; ++tl) {
@@ -486,31 +546,31 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
 // the same unit in step.  One barrier per tile still orders it: every wave's share of tile t+1 is written
 // between the barriers that bracket iteration t, into the buffer nobody reads during iteration t.  Each
 // half is its own instantiation so the register allocator sees one loop shape at a time.
-template <int HP, int DP, int RH, bool kFQ>
+template <int HP, int DP, int RH, bool kFQ, bool kF8>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams p) {
     __shared__ __attribute__((aligned(16))) PrefillLds<DP> lds;
     if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= kPrefillWaves / 2)
-        prefill_body<HP, DP, RH, kFQ, true>(p, lds);
+        prefill_body<HP, DP, RH, kFQ, true, kF8>(p, lds);
     else
-        prefill_body<HP, DP, RH, kFQ, false>(p, lds);
+        prefill_body<HP, DP, RH, kFQ, false, kF8>(p, lds);
 }
 
-template <int HP, int DP, int RH>
+template <int HP, int DP, int RH, bool kF8>
 hipError_t launch_one(const PrefillParams &p, hipStream_t s) {
     const dim3 grid(unsigned(((p.chunk + kQT - 1) / kQT) * p.h * p.batch));
     if (p.r_q > 0)
-        hipLaunchKernelGGL((prefill_kernel<HP, DP, RH, true>), grid, dim3(kPrefillThreads), 0, s, p);
+        hipLaunchKernelGGL((prefill_kernel<HP, DP, RH, true, kF8>), grid, dim3(kPrefillThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((prefill_kernel<HP, DP, RH, false>), grid, dim3(kPrefillThreads), 0, s, p);
+        hipLaunchKernelGGL((prefill_kernel<HP, DP, RH, false, kF8>), grid, dim3(kPrefillThreads), 0, s, p);
     return hipGetLastError();
 }
 
-template <int HP, int DP>
+template <int HP, int DP, bool kF8>
 hipError_t launch_rank(int RH, const PrefillParams &p, hipStream_t s) {
     switch (RH) {
-        case 1: return launch_one<HP, DP, 1>(p, s);
-        case 2: return launch_one<HP, DP, 2>(p, s);
-        case 4: return launch_one<HP, DP, 4>(p, s);
+        case 1: return launch_one<HP, DP, 1, kF8>(p, s);
+        case 2: return launch_one<HP, DP, 2, kF8>(p, s);
+        case 4: return launch_one<HP, DP, 4, kF8>(p, s);
     }
     return hipErrorInvalidValue;
 }
@@ -519,8 +579,9 @@ hipError_t launch_rank(int RH, const PrefillParams &p, hipStream_t s) {
 
 }  // namespace
 
+// bf16 operands: a bf16 cache, or an E4M3 cache (decoded to bf16 in the rebuild)
 bool prefill_supported(const Layout &L) {
-    if (L.es != 2) return false;
+    if (L.es != 2 && !L.f8) return false;
 #define X(HP_, DP_) \
     if (L.HP == HP_ && L.DP == DP_) return true;
     TPA_PREFILL_SHAPES(X)
@@ -529,8 +590,9 @@ bool prefill_supported(const Layout &L) {
 }
 
 hipError_t launch_prefill(const Layout &L, const PrefillParams &p, hipStream_t s) {
-#define X(HP_, DP_) \
-    if (L.es == 2 && L.HP == HP_ && L.DP == DP_) return launch_rank<HP_, DP_>(L.RH, p, s);
+#define X(HP_, DP_)                                                                   \
+    if (L.f8 && L.HP == HP_ && L.DP == DP_) return launch_rank<HP_, DP_, true>(L.RH, p, s); \
+    if (L.es == 2 && L.HP == HP_ && L.DP == DP_) return launch_rank<HP_, DP_, false>(L.RH, p, s);
     TPA_PREFILL_SHAPES(X)
 #undef X
     return hipErrorInvalidValue;

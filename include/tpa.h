@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define TPA_ABI_VERSION 1
+#define TPA_ABI_VERSION 2
 
 typedef enum tpa_status {
     TPA_OK = 0,
@@ -63,21 +63,39 @@ typedef enum tpa_status {
 
 typedef enum tpa_dtype { TPA_F32 = 0, TPA_BF16 = 1 } tpa_dtype;
 
+/* How the cache stores factor elements.
+ *   TPA_CACHE_NATIVE  in dims->dtype (fp32 or bf16).
+ *   TPA_CACHE_E4M3    one byte per element: the OCP 8-bit floating-point E4M3
+ *                     code of value / scale (1 sign, 4 exponent bits with bias 7,
+ *                     3 mantissa bits; largest finite magnitude 448, no
+ *                     infinities), rounded to nearest even and saturating at 448;
+ *                     the stored value is code * scale, with one scale per factor
+ *                     tensor (dims->cache_scale).  Requires dtype TPA_BF16 (inputs
+ *                     and queries stay bf16).  This is the low-bit factor storage
+ *                     the TPA notes page lists as unexplored (Limitations): it
+ *                     halves the bytes per cached token again, with the rounding
+ *                     error of a 3-bit mantissa on every factor element. */
+typedef enum tpa_cache_format { TPA_CACHE_NATIVE = 0, TPA_CACHE_E4M3 = 1 } tpa_cache_format;
+
 /* Problem statement of one attention layer (TPA notes page, tensor product
  * decomposition and RoPE compatibility):
- *   h          number of heads, 1..64
- *   d_h        head dimension, even, 2..256
- *   R_K, R_V   factor ranks of K and V, 1..4
- *   dtype      element type of factors, queries and the cache
- *   rope_base  RoPE base (theta_j = rope_base^(-2j/d_h)), > 0 */
+ *   h             number of heads, 1..64
+ *   d_h           head dimension, even, 2..256
+ *   R_K, R_V      factor ranks of K and V, 1..4
+ *   dtype         element type of factors and queries (and of the cache, when native)
+ *   cache_format  a tpa_cache_format
+ *   rope_base     RoPE base (theta_j = rope_base^(-2j/d_h)), > 0
+ *   cache_scale   TPA_CACHE_E4M3 only: scales of A_K, B_K, A_V, B_V (finite, >= 0;
+ *                 0 means 1).  Ignored for a native cache. */
 typedef struct tpa_dims {
     int32_t h;
     int32_t d_h;
     int32_t R_K;
     int32_t R_V;
     int32_t dtype;
-    int32_t reserved; /* must be 0 */
+    int32_t cache_format;
     double rope_base;
+    float cache_scale[4];
 } tpa_dims;
 
 int32_t tpa_abi_version(void);
@@ -114,15 +132,20 @@ int64_t tpa_cache_bytes(const tpa_dims *dims, int64_t capacity_tokens);
  *   q_in, q_out    [n_q][q_rows][d_h]; q_out = RoPE(q_in); q_out may equal q_in
  *   B_K, B_V, q_in and q_out must be aligned to two elements (rotary pairs are
  *   moved as one word) and the cache to 16 bytes; TPA_ERR_ARG otherwise.
- * Angles are computed in fp64, rotations in fp64, rounded once to dtype. */
+ * Angles are formed and reduced mod 2 pi in fp64; cos, sin and the rotation are
+ * fp32 for bf16 (fp64 for fp32), rounded once to dtype.  With TPA_CACHE_E4M3
+ * every factor element is stored as the code of value / scale (B_K: its fp32
+ * rotation divided by the scale); queries stay dtype. */
 int32_t tpa_cache_append(const tpa_dims *dims, void *cache, int64_t capacity_tokens, int64_t n_kv,
                          const int64_t *slot, const int32_t *kv_pos, int64_t slot_hi, const void *A_K,
                          const void *B_K, const void *A_V, const void *B_V, int64_t n_q, int32_t q_rows,
                          const int32_t *q_pos, const void *q_in, void *q_out, void *stream);
 
 /* Read n tokens back out of the cache in natural layout (B_K as stored, i.e.
- * rotated).  Same array shapes as tpa_cache_append; slots out of range read as
- * zeros.  For tests and cache export. */
+ * rotated).  Same array shapes as tpa_cache_append, in the stored element type:
+ * dims->dtype for a native cache, one uint8 E4M3 code per element for
+ * TPA_CACHE_E4M3 (value = code * scale); slots out of range read as zeros.
+ * For tests and cache export. */
 int32_t tpa_cache_read(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int64_t n,
                        const int64_t *slot, void *A_K, void *B_K, void *A_V, void *B_V, void *stream);
 
@@ -159,9 +182,10 @@ int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
  * tpa_cache_append writes it), rotate the query at position N, and attend over the N cached tokens and
  * the new one (the one-query decode of the TPA notes page, FlashTPA; RoPE compatibility, Theorem 3.1):
  *     out[b][i] = sum_{s <= N} softmax_s(scale * q~_b,i . K~_s[i,:]) V_s[i,:]
- * Two kernel launches (split, merge) and no separate append: the split kernel rotates the query in
- * registers, the merge kernel folds in the new token's own score and value (query and token share a
- * position, so RoPE cancels in that score) and writes its record.
+ * Two kernel launches (split, merge) and no separate append: every split work-group rotates the query in
+ * registers, the sequence's first split folds in the new token's own score and value (query and token share
+ * a position, so RoPE cancels in that score) and its last split writes the token's record.  A native cache
+ * only: with TPA_CACHE_E4M3 the call returns TPA_ERR_UNSUPPORTED (append, then tpa_decode).
  *   A_K [batch][R_K][h], B_K [batch][R_K][d_h], A_V [batch][R_V][h], B_V [batch][R_V][d_h]
  *                     the new token's factors, unrotated
  *   q [batch][h][d_h]  the step's query, unrotated (16-byte aligned)

@@ -30,8 +30,8 @@ def say(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def dims_of(w: ti.Workload) -> tpa.Dims:
-    return tpa.Dims(w.h, w.d_h, w.R_K, w.R_V, w.dtype, w.rope_base)
+def dims_of(w: ti.Workload, cache_format: int = 0, cache_scale=(0.0, 0.0, 0.0, 0.0)) -> tpa.Dims:
+    return tpa.Dims(w.h, w.d_h, w.R_K, w.R_V, w.dtype, w.rope_base, cache_format, cache_scale)
 
 
 def errors(gpu: np.ndarray, ref: np.ndarray):
@@ -61,9 +61,10 @@ class DecodeSetup:
     """Cache + rotated queries for a batch of decode sequences."""
 
     def __init__(self, w: ti.Workload, seqs: Sequence[ti.Sequence], lens: Optional[Sequence[int]] = None,
-                 extra_capacity: int = 0, q_positions: Optional[Sequence[int]] = None):
+                 extra_capacity: int = 0, q_positions: Optional[Sequence[int]] = None,
+                 dims: Optional[tpa.Dims] = None):
         self.w = w
-        self.dims = dims_of(w)
+        self.dims = dims_of(w) if dims is None else dims
         self.seqs = list(seqs)
         self.lens = [s.n_tokens for s in self.seqs] if lens is None else list(lens)
         self.cache = FactorCache(self.dims, [n + extra_capacity for n in self.lens])
@@ -92,20 +93,24 @@ class DecodeSetup:
         torch.cuda.synchronize()
         return out.cpu().numpy()
 
+    def factors(self, b: int, n: int):
+        """The cached factor values the oracle attends over (fp64)."""
+        return stored_factors(self.seqs[b], n, self.w, self.dims)
+
     def oracle(self, b: int, scale: Optional[float] = None) -> np.ndarray:
         s, dt = self.seqs[b], self.w.dtype
         n = self.lens[b]
-        return oracle.attention(f64(s.A_K[:n], dt), f64(s.B_K[:n], dt), f64(s.A_V[:n], dt), f64(s.B_V[:n], dt),
-                                np.arange(n), f64(s.q[:1], dt), [self.q_positions[b]], [n], self.w.rope_base,
-                                scale)[0]
+        return oracle.attention(*self.factors(b, n), np.arange(n), f64(s.q[:1], dt), [self.q_positions[b]], [n],
+                                self.w.rope_base, scale)[0]
 
 
 class PrefillSetup:
     """Cache holding ctx + chunk tokens per sequence, rotated chunk query rows."""
 
-    def __init__(self, w: ti.Workload, seqs: Sequence[ti.Sequence], ctx: Sequence[int]):
+    def __init__(self, w: ti.Workload, seqs: Sequence[ti.Sequence], ctx: Sequence[int],
+                 dims: Optional[tpa.Dims] = None):
         self.w = w
-        self.dims = dims_of(w)
+        self.dims = dims_of(w) if dims is None else dims
         self.seqs = list(seqs)
         self.ctx = list(ctx)
         self.chunk = self.seqs[0].q.shape[0]
@@ -132,8 +137,28 @@ class PrefillSetup:
 
     def oracle(self, b: int, rows=None) -> np.ndarray:
         s, dt = self.seqs[b], self.w.dtype
-        return oracle.prefill(f64(s.A_K, dt), f64(s.B_K, dt), f64(s.A_V, dt), f64(s.B_V, dt), f64(s.q, dt),
-                              self.ctx[b], self.w.rope_base, rows=rows)
+        return oracle.prefill(*stored_factors(s, s.n_tokens, self.w, self.dims), f64(s.q, dt), self.ctx[b],
+                              self.w.rope_base, rows=rows)
+
+
+def e4m3_values(x: np.ndarray, scale: float) -> np.ndarray:
+    """Stored values of an E4M3 cache: code = E4M3(x / scale), value = code * scale (the oracle's codec)."""
+    return oracle.e4m3_decode(oracle.e4m3_encode(np.asarray(x, dtype=np.float64) / scale)) * scale
+
+
+def stored_factors(s: ti.Sequence, n: int, w: ti.Workload, dims: tpa.Dims):
+    """The first n tokens' factors as the cache holds them, in fp64, computed on the oracle side only.
+    Native cache: the inputs.  E4M3 cache: every factor through the oracle's codec; B_K is stored rotated
+    (RoPE on B only), so its stored value is rotated back to the token's position 0 frame, and the
+    oracle, which rotates whole key rows itself, sees exactly the stored key."""
+    dt = w.dtype
+    A_K, B_K, A_V, B_V = (f64(x[:n], dt) for x in (s.A_K, s.B_K, s.A_V, s.B_V))
+    if dims.cache_format != tpa.TPA_CACHE_E4M3:
+        return A_K, B_K, A_V, B_V
+    A_K, A_V, B_V = e4m3_values(A_K, dims.scale(0)), e4m3_values(A_V, dims.scale(2)), e4m3_values(B_V, dims.scale(3))
+    B_K = np.stack([oracle.rope_rows(e4m3_values(oracle.rope_rows(B_K[t], t, w.rope_base), dims.scale(1)), -t,
+                                     w.rope_base) for t in range(n)]) if n else B_K
+    return A_K, B_K, A_V, B_V
 
 
 def case_workload(h, d_h, R_K, R_V, dtype=ti.BF16, base=1e4, seed=7) -> ti.Workload:

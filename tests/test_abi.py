@@ -47,7 +47,7 @@ def test_binding_covers_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert tpa.tpa_abi_version() == 1
+    assert tpa.tpa_abi_version() == 2
     for code, word in [(0, "TPA_OK"), (1, "ARG"), (2, "UNSUPPORTED"), (3, "CAPACITY"), (4, "WORKSPACE"),
                        (5, "HIP")]:
         assert word in tpa.tpa_status_string(code)
@@ -116,10 +116,51 @@ def test_bad_dims_rejected(lib, kw):
     assert st == 1
 
 
-def test_reserved_field_must_be_zero(lib):
+def test_cache_format_field_is_checked(lib):
     d = _d()
-    d.reserved = 1
+    d.cache_format = 2
     assert lib.tpa_supported(ctypes.byref(d)) == 0
+    assert lib.tpa_block_tokens(ctypes.byref(d)) <= 0
+
+
+def test_dims_struct_matches_header_layout():
+    """int32 x 6, double, float x 4: the binding's struct has the header's size and offsets."""
+    assert ctypes.sizeof(tpa.Dims) == 48
+    assert tpa.Dims.rope_base.offset == 24 and tpa.Dims.cache_scale.offset == 32
+
+
+@pytest.mark.parametrize("h,d,R,per_token_bytes", [(32, 128, 1, 320), (16, 64, 2, 320), (32, 128, 4, 1280)])
+def test_e4m3_cache_is_one_byte_per_element(h, d, R, per_token_bytes):
+    """8-bit factor storage: (R_K + R_V)(h + d_h) bytes per token, half the bf16 cache."""
+    dims = _d(h=h, d_h=d, R_K=R, R_V=R, cache_format="e4m3")
+    assert per_token_bytes == (R + R) * (h + d)
+    tok = tpa.tpa_block_tokens(dims)
+    assert tok == 32 // R
+    assert tpa.tpa_cache_bytes(dims, 10 * tok) == 10 * tok * per_token_bytes
+    assert tpa.tpa_supported(dims)
+
+
+@pytest.mark.parametrize("kw", [dict(dtype="f32"), dict(cache_scale=(1.0, -1.0, 1.0, 1.0)),
+                                dict(cache_scale=(float("nan"), 1.0, 1.0, 1.0)),
+                                dict(cache_scale=(1.0, 1.0, float("inf"), 1.0))])
+def test_e4m3_cache_needs_bf16_and_valid_scales(lib, kw):
+    d = _d(cache_format="e4m3", **kw)
+    assert lib.tpa_supported(ctypes.byref(d)) == 0
+    assert lib.tpa_cache_bytes(ctypes.byref(d), 64) == -1
+
+
+def test_e4m3_scales_ignored_by_native_cache(lib):
+    d = _d(cache_scale=(-1.0, 0.0, 0.0, 0.0))
+    assert lib.tpa_supported(ctypes.byref(d)) == 1
+
+
+def test_decode_step_over_e4m3_cache_is_unsupported(lib):
+    d = _d(cache_format="e4m3")
+    ref = ctypes.byref(d)
+    need = lib.tpa_decode_workspace_bytes(ref, 16, 4096, 0)
+    st = lib.tpa_decode_step(ref, FAKE, 8192, 16, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, FAKE, 0, FAKE,
+                             need, None)
+    assert st == 2
 
 
 def test_null_dims_rejected(lib):

@@ -1,0 +1,199 @@
+"""GPU parity of the 8-bit factor cache (TPA_CACHE_E4M3) against the fp64 oracle.
+
+The cache stores every factor element as the OCP E4M3 code of value / scale (the low-bit factor
+storage the TPA notes page lists as unexplored).  The oracle side computes the stored values with its own
+codec (pinned on the CPU against the format's definition and torch's e4m3fn cast), never from the
+library's cache: A_K, A_V, B_V are quantized directly; B_K is quantized after its rotation at the token's
+position and rotated back, so the oracle's full-key RoPE reproduces the stored key.  Parity then holds to
+the usual bf16 bounds, since the kernels compute on the decoded values (exact in bf16).
+"""
+import numpy as np
+import pytest
+import torch
+
+import factorized_kv_cache_tpa_amd as tpa
+import oracle
+import tpa_inputs as ti
+from factorized_kv_cache_tpa_amd.cache import FactorCache, to_device
+from tests.gpu_cases import (DecodeSetup, PrefillSetup, assert_close, case_workload, dims_of, e4m3_values, f64,
+                             random_sequences, say, stored_factors)
+
+pytestmark = pytest.mark.gpu
+
+E4M3 = tpa.TPA_CACHE_E4M3
+SHAPES = [(32, 128, 1, 1), (32, 128, 2, 2), (32, 128, 4, 4), (16, 64, 2, 2), (16, 64, 1, 1), (32, 64, 1, 3),
+          (20, 48, 2, 2)]
+
+
+def _read_codes(dims, cache, n):
+    slots = torch.arange(n, dtype=torch.int64, device="cuda") + cache.starts[0]
+    outs = [torch.zeros((n, r, k), dtype=torch.uint8, device="cuda") for r, k in
+            ((dims.R_K, dims.h), (dims.R_K, dims.d_h), (dims.R_V, dims.h), (dims.R_V, dims.d_h))]
+    tpa.tpa_cache_read(dims, cache.buf, cache.capacity, slots, *outs)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in outs]
+
+
+def _assert_codes(got, x, scale, exact, what):
+    """got: the library's codes; x: the exact fp64 values.  The oracle's code of x / scale must be matched,
+    except (when not `exact`) where x / scale lies so close to a rounding midpoint that the library's fp32
+    arithmetic (rotation, scaling) may land on the other side: then both codes must be equally near."""
+    v = np.asarray(x, dtype=np.float64) / scale
+    want = oracle.e4m3_encode(v)
+    diff = got != want
+    if exact:
+        assert not diff.any(), f"{what}: {int(diff.sum())} codes differ"
+        return
+    if diff.any():
+        d_got = np.abs(oracle.e4m3_decode(got[diff]) - v[diff])
+        d_want = np.abs(oracle.e4m3_decode(want[diff]) - v[diff])
+        assert np.all(np.abs(d_got - d_want) <= 4e-6 * np.abs(v[diff]) + 1e-30), f"{what}: a code off a near tie"
+        assert diff.mean() < 1e-3, f"{what}: {diff.mean():.2e} of the codes differ"
+    say(f"  {what}: {int(diff.sum())} near-tie codes of {diff.size}")
+
+
+@pytest.mark.parametrize("h,d_h,R_K,R_V", SHAPES)
+@pytest.mark.parametrize("scales", [(0.0, 0.0, 0.0, 0.0), (0.5, 2.0, 0.25, 4.0), (0.3, 1.7, 0.05, 3.0)])
+def test_append_codes_match_oracle_codec(h, d_h, R_K, R_V, scales):
+    w = case_workload(h, d_h, R_K, R_V)
+    dims = dims_of(w, E4M3, scales)
+    n = 70
+    say(f"case: e4m3 append h={h} d_h={d_h} R_K={R_K} R_V={R_V} scales={scales}")
+    s = random_sequences(w, [n], seed=h + d_h + R_K)[0]
+    cache = FactorCache(dims, [n])
+    cache.append_host(0, s.A_K, s.B_K, s.A_V, s.B_V)
+    ak, bk, av, bv = _read_codes(dims, cache, n)
+    dt = w.dtype
+    pow2 = all(x == 0.0 or float(np.log2(x)).is_integer() for x in scales)
+    _assert_codes(ak, f64(s.A_K, dt), dims.scale(0), pow2, "A_K")
+    _assert_codes(av, f64(s.A_V, dt), dims.scale(2), pow2, "A_V")
+    _assert_codes(bv, f64(s.B_V, dt), dims.scale(3), pow2, "B_V")
+    rot = np.stack([oracle.rope_rows(f64(s.B_K[t], dt), t, w.rope_base) for t in range(n)])
+    _assert_codes(bk, rot, dims.scale(1), False, "B_K (rotated)")
+
+
+def test_append_saturates_at_the_largest_finite_code():
+    """Inputs far beyond 448 * scale store +-448 (0x7E / 0xFE), never NaN."""
+    w = case_workload(16, 64, 1, 1)
+    dims = dims_of(w, E4M3)
+    s = random_sequences(w, [40], seed=3)[0]
+    big = lambda a: ti.to_storage(ti.to_f64(a, w.dtype).astype(np.float32) * 3000.0, w.dtype)
+    cache = FactorCache(dims, [40])
+    cache.append_host(0, big(s.A_K), big(s.B_K), big(s.A_V), big(s.B_V))
+    codes = _read_codes(dims, cache, 40)
+    for c, x in zip(codes, (s.A_K, s.B_K, s.A_V, s.B_V)):
+        assert not np.any((c & 0x7F) == 0x7F), "NaN code"
+    sat = np.abs(ti.to_f64(big(s.A_K), w.dtype)) > 464.0
+    assert sat.any()
+    np.testing.assert_array_equal(codes[0][sat], np.where(ti.to_f64(big(s.A_K), w.dtype)[sat] > 0, 0x7E, 0xFE))
+
+
+@pytest.mark.parametrize("h,d_h,R_K,R_V", SHAPES)
+@pytest.mark.parametrize("q_scale", [1.0, 8.0])
+def test_decode_matches_oracle(h, d_h, R_K, R_V, q_scale):
+    w = case_workload(h, d_h, R_K, R_V)
+    lens = [1, 31, 32, 33, 300, 1000]
+    say(f"case: e4m3 decode h={h} d_h={d_h} R_K={R_K} R_V={R_V} q_scale={q_scale}")
+    s = DecodeSetup(w, random_sequences(w, lens, q_scale=q_scale, seed=h * 7 + d_h), dims=dims_of(w, E4M3))
+    ref = np.stack([s.oracle(b) for b in range(s.batch)])
+    for split in (0, 64):
+        assert_close(s.run(split_tokens=split), ref, w.dtype, f"split_tokens={split}")
+
+
+@pytest.mark.parametrize("scales", [(0.5, 2.0, 0.25, 4.0), (0.3, 1.7, 0.05, 3.0)])
+def test_decode_with_scales(scales):
+    """Scales fold into the score and output multipliers: same parity bound."""
+    w = case_workload(32, 128, 2, 2)
+    say(f"case: e4m3 decode scales={scales}")
+    s = DecodeSetup(w, random_sequences(w, [5, 200, 777], q_scale=6.0, seed=21), dims=dims_of(w, E4M3, scales))
+    ref = np.stack([s.oracle(b) for b in range(s.batch)])
+    assert_close(s.run(), ref, w.dtype, "scaled")
+
+
+def test_decode_saturated_cache():
+    """A cache whose factors saturate at 448 still decodes what it stores."""
+    w = case_workload(16, 64, 1, 1)
+    seqs = random_sequences(w, [64, 130], seed=8)
+    for sq in seqs:
+        for name in ("A_K", "A_V"):
+            setattr(sq, name, ti.to_storage(ti.to_f64(getattr(sq, name), w.dtype).astype(np.float32) * 600.0, w.dtype))
+    s = DecodeSetup(w, seqs, dims=dims_of(w, E4M3, (0.0, 0.0, 0.0, 0.0)))
+    ref = np.stack([s.oracle(b, scale=1e-3) for b in range(s.batch)])
+    assert_close(s.run(scale=1e-3), ref, w.dtype, "saturated A factors")
+
+
+def test_full_size_decode_b16_h32_d128_r1_n4096():
+    """The 16 x 4096-token, h=32, d_h=128, R=1 workload over an E4M3 cache, every sequence checked."""
+    w = ti.get("c2")
+    say(f"case: e4m3 full size {w.name}")
+    s = DecodeSetup(w, ti.decode_batch(w), lens=list(ti.decode_lengths(w)), dims=dims_of(w, E4M3))
+    got = s.run()
+    for b in range(s.batch):
+        assert_close(got[b], s.oracle(b), w.dtype, f"seq {b}")
+
+
+def test_decode_fq_matches_oracle():
+    """Factored query (R_Q = 6) over an E4M3 cache."""
+    w = case_workload(32, 128, 2, 2)
+    dims = dims_of(w, E4M3)
+    lens = [3, 64, 700, 2100]
+    say("case: e4m3 decode fq R_Q=6")
+    s = DecodeSetup(w, random_sequences(w, lens, seed=31), dims=dims)
+    rng = np.random.default_rng(6)
+    B = len(lens)
+    A_Q = ti.to_storage(rng.standard_normal((B, 6, w.h), dtype=np.float32), w.dtype)
+    B_Q = ti.to_storage(rng.standard_normal((B, 6, w.d_h), dtype=np.float32) * (4.0 / np.sqrt(w.d_h)), w.dtype)
+    pos = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    B_Q_rot = s.cache.rotate_queries(to_device(B_Q, dims), pos)
+    ws = torch.zeros(tpa.tpa_decode_workspace_bytes(dims, B, max(lens)), dtype=torch.uint8, device="cuda")
+    out = torch.full((B, w.h, w.d_h), float("nan"), dtype=torch.float32, device="cuda")
+    tpa.tpa_decode_fq(dims, s.cache.buf, s.cache.capacity, s.cache.seq_start, s.seq_len, max(lens),
+                      to_device(A_Q, dims), B_Q_rot, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        q = oracle.query_from_factors(f64(A_Q[b:b + 1], w.dtype), f64(B_Q[b:b + 1], w.dtype))[0]
+        ref = oracle.decode(*stored_factors(s.seqs[b], lens[b], w, dims), q, w.rope_base)
+        assert_close(got[b], ref, w.dtype, f"seq {b}")
+
+
+@pytest.mark.parametrize("h,d_h,R_K,R_V,ctx,chunk", [(32, 128, 4, 4, [100], 64), (16, 64, 1, 1, [37, 0], 300),
+                                                     (32, 128, 1, 1, [0, 70], 33), (20, 48, 1, 3, [65], 40),
+                                                     (16, 64, 2, 2, [200, 5], 130)])
+def test_prefill_matches_oracle(h, d_h, R_K, R_V, ctx, chunk):
+    w = case_workload(h, d_h, R_K, R_V)
+    say(f"case: e4m3 prefill h={h} d_h={d_h} R_K={R_K} R_V={R_V} ctx={ctx} chunk={chunk}")
+    seqs = random_sequences(w, [c + chunk for c in ctx], n_q=chunk, q_scale=3.0, seed=h + chunk)
+    s = PrefillSetup(w, seqs, ctx, dims=dims_of(w, E4M3))
+    got = s.run()
+    ref = np.stack([s.oracle(b) for b in range(len(seqs))])
+    assert_close(got, ref, w.dtype, "all rows")
+
+
+def test_prefill_fq_matches_oracle():
+    w = case_workload(32, 128, 4, 4)
+    dims = dims_of(w, E4M3)
+    ctx, chunk, R_Q = [100, 0], 96, 6
+    say("case: e4m3 prefill fq")
+    seqs = random_sequences(w, [c + chunk for c in ctx], seed=12)
+    cache = FactorCache(dims, [c + chunk for c in ctx])
+    for b, sq in enumerate(seqs):
+        cache.append_host(b, sq.A_K, sq.B_K, sq.A_V, sq.B_V)
+    rng = np.random.default_rng(R_Q)
+    B = len(ctx)
+    A_Q = ti.to_storage(rng.standard_normal((B, chunk, R_Q, w.h), dtype=np.float32), w.dtype)
+    B_Q = ti.to_storage(rng.standard_normal((B, chunk, R_Q, w.d_h), dtype=np.float32) * (4.0 / np.sqrt(w.d_h)),
+                        w.dtype)
+    pos = torch.tensor(np.concatenate([c + np.arange(chunk) for c in ctx]), dtype=torch.int32, device="cuda")
+    B_Q_rot = cache.rotate_queries(to_device(B_Q, dims).reshape(B * chunk, R_Q, w.d_h), pos).reshape(
+        B, chunk, R_Q, w.d_h)
+    out = torch.full((B, chunk, w.h, w.d_h), float("nan"), dtype=torch.float32, device="cuda")
+    tpa.tpa_prefill_chunk_fq(dims, cache.buf, cache.capacity, cache.seq_start,
+                             torch.tensor(ctx, dtype=torch.int32, device="cuda"), max(ctx), chunk,
+                             to_device(A_Q, dims), B_Q_rot, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b, sq in enumerate(seqs):
+        q = oracle.query_from_factors(f64(A_Q[b], w.dtype), f64(B_Q[b], w.dtype))
+        ref = oracle.prefill(*stored_factors(sq, sq.n_tokens, w, dims), q, ctx[b], w.rope_base)
+        assert_close(got[b], ref, w.dtype, f"seq {b}")
