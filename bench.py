@@ -67,10 +67,11 @@ def decode_traffic():
     return int(round(d["step_call_traffic_bytes"]))
 
 
-def decode_bytes(w, lens) -> int:
-    """Algorithmic bytes of one decode: the factor stream plus the query read and the fp32 output write."""
+def decode_bytes(w, lens, cache_es=None) -> int:
+    """Algorithmic bytes of one decode: the factor stream plus the query read and the fp32 output write.
+    cache_es: bytes per stored factor element (1 for an E4M3 cache; default the element type's)."""
     es = 2 if w.dtype == "bf16" else 4
-    per_tok = (w.R_K + w.R_V) * (w.h + w.d_h) * es
+    per_tok = (w.R_K + w.R_V) * (w.h + w.d_h) * (es if cache_es is None else cache_es)
     return int(np.sum(lens)) * per_tok + len(lens) * w.h * w.d_h * (es + 4)
 
 
@@ -85,7 +86,7 @@ def step_bytes(w, lens) -> int:
 class DecodeBench:
     """Cache replicas + per-step buffers for one decode workload."""
 
-    def __init__(self, name: str, min_bytes: int):
+    def __init__(self, name: str, min_bytes: int, cache_format: int = 0):
         import torch
         import factorized_kv_cache_tpa_amd as tpa
         import tpa_inputs as ti
@@ -93,7 +94,8 @@ class DecodeBench:
 
         self.torch, self.tpa = torch, tpa
         w = self.w = ti.get(name)
-        self.dims = tpa.Dims(w.h, w.d_h, w.R_K, w.R_V, w.dtype, w.rope_base)
+        self.dims = tpa.Dims(w.h, w.d_h, w.R_K, w.R_V, w.dtype, w.rope_base, cache_format)
+        self.e4m3 = cache_format == tpa.TPA_CACHE_E4M3
         t0 = time.time()
         seqs = ti.decode_batch(w)
         self.lens = ti.decode_lengths(w)
@@ -131,7 +133,7 @@ class DecodeBench:
         ws = tpa.tpa_decode_workspace_bytes(self.dims, self.batch, self.max_len)
         self.ws = torch.zeros(ws, dtype=torch.uint8, device="cuda")
         self.out = torch.empty(self.batch, w.h, w.d_h, dtype=torch.float32, device="cuda")
-        self.bytes = decode_bytes(w, self.lens)
+        self.bytes = decode_bytes(w, self.lens, 1 if self.e4m3 else None)
         self.step_bytes = step_bytes(w, self.lens)
         # a rank-6 factored query (full TPA), its B_Q rows rotated at the query position
         self.R_Q = 6
@@ -181,6 +183,25 @@ class DecodeBench:
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) / (reps * n_calls)
+
+    def run_decode_only(self, steps: int, warmup: int):
+        """tpa_decode and tpa_decode_fq alone (an E4M3 cache has no fused step), graphs over the replicas."""
+        torch = self.torch
+        self.cache.rotate_queries(self.q, self.pos, q_out=self.q_rot)
+        for i in range(warmup):
+            self.decode(i % self.n_rep)
+        torch.cuda.synchronize()
+        self.cap_stream = torch.cuda.Stream()
+        reps = max(1, -(-steps // self.n_rep))
+        dec = self._capture(self.decode, self.n_rep)
+        fq = self._capture(self.decode_fq, self.n_rep)
+        dec.replay()
+        fq.replay()
+        ms_dec = self._time(dec, self.n_rep, reps)
+        ms_fq = self._time(fq, self.n_rep, reps)
+        toks = float(np.sum(self.lens))
+        return dict(decode_ms=ms_dec, decode_tokens_per_s=toks / (ms_dec / 1e3),
+                    decode_GBps=self.bytes / (ms_dec / 1e3) / 1e9, fq_ms=ms_fq)
 
     def run(self, steps: int, warmup: int, step_only: bool = False):
         """Time exactly `steps` fused steps.  The calls are recorded once into HIP graphs (a pass over all cache
@@ -238,15 +259,16 @@ class DecodeBench:
         return res
 
 
-def prefill_bench(steps: int, warmup: int):
-    """Causal chunk: 8 sequences x (2048 cached + 512 chunk rows), h=32, d_h=128, R=4, bf16."""
+def prefill_bench(steps: int, warmup: int, cache_format: int = 0):
+    """Causal chunk: 8 sequences x (2048 cached + 512 chunk rows), h=32, d_h=128, R=4, bf16 (cache_format 1:
+    the same over an E4M3 factor cache)."""
     import torch
     import factorized_kv_cache_tpa_amd as tpa
     import tpa_inputs as ti
     from factorized_kv_cache_tpa_amd.cache import FactorCache, to_device
 
     w = ti.get("c5")
-    dims = tpa.Dims(w.h, w.d_h, w.R_K, w.R_V, w.dtype, w.rope_base)
+    dims = tpa.Dims(w.h, w.d_h, w.R_K, w.R_V, w.dtype, w.rope_base, cache_format)
     seqs = ti.prefill_batch(w)
     B, ctx, chunk = w.prefill_batch, w.prefill_ctx, w.prefill_chunk
     cache = FactorCache(dims, [ctx + chunk] * B)
@@ -382,6 +404,22 @@ def main():
         pname = p.pop("workload")
         extras[pname] = {k: round(v, 4) for k, v in p.items()}
         log(f"[prefill] {p['ms'] * 1e3:.1f} us, {p['tflops']:.1f} TFLOP/s, {100 * p['mfma_frac']:.1f}% MFMA")
+        # the same workloads over an 8-bit (E4M3) factor cache: half the bytes per cached token
+        for name in (MAIN, "c3", "c4", "c5"):
+            b = DecodeBench(name, min_bytes=4 * MALL_BYTES, cache_format=tpa.TPA_CACHE_E4M3)
+            r = b.run_decode_only(max(10, args.steps // 4), max(3, args.warmup // 4))
+            extras[b.w.name]["e4m3_cache"] = dict(
+                decode_us=round(r["decode_ms"] * 1e3, 2), cached_tokens_per_s=round(r["decode_tokens_per_s"], 1),
+                GBps=round(r["decode_GBps"], 1), hbm_frac=round(r["decode_GBps"] / HBM_PEAK_GBS, 4),
+                factored_query_rq6_decode_us=round(r["fq_ms"] * 1e3, 2))
+            log(f"[{b.w.name}] E4M3 cache: decode {r['decode_ms'] * 1e3:.2f} us, {r['decode_GBps']:.0f} GB/s")
+            del b
+            torch.cuda.empty_cache()
+        p8 = prefill_bench(max(5, args.steps // 10), 3, cache_format=tpa.TPA_CACHE_E4M3)
+        extras[pname]["e4m3_cache"] = dict(ms=round(p8["ms"], 4), tflops=round(p8["tflops"], 1),
+                                           mfma_frac=round(p8["mfma_frac"], 4),
+                                           factored_query_rq6_ms=round(p8["factored_query_rq6_ms"], 4))
+        log(f"[prefill] E4M3 cache: {p8['ms'] * 1e3:.1f} us, {p8['tflops']:.1f} TFLOP/s")
 
     achieved = res["step_GBps"]
     line = {

@@ -371,13 +371,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     // Two register stages (the next block's loads in flight while one is consumed) wherever they
     // fit in the register file; wide fp32 operands use one stage.
     constexpr bool kTwoStages = sizeof(T) == 2 || HP * DP <= 1024;
-    Stage s0, s1;
+    // An E4M3 stage is half the bytes (and registers) of a bf16 one, so that path keeps four blocks per
+    // wave in flight (s0..s3) to hold as many bytes in flight as the bf16 path does with two.
+    constexpr int kStages = kF8 ? 4 : (kTwoStages ? 2 : 1);
+    Stage s0, s1, s2, s3;
     int blk = blk_begin + w;
     if (kTwoStages) {  // start streaming the first two blocks before anything else (a fused step issues
                        // the second after its own set-up: a wave cannot pass its loads' issue until most of
                        // them have landed, so work placed behind both stages would wait for the stream)
         if (blk < full_end) load(s0, blk);
         if (kMode == kQRot && blk + kWaves < full_end) load(s1, blk + kWaves);
+        if (kStages == 4 && kMode == kQRot && blk + 2 * kWaves < full_end) load(s2, blk + 2 * kWaves);
+        if (kStages == 4 && kMode == kQRot && blk + 3 * kWaves < full_end) load(s3, blk + 3 * kWaves);
     }
     if constexpr (kFact) {
         // Factored query, while the first blocks stream in: q~[i][d] = (1/R_Q) sum_r A_Q[r][i] B~_Q[r][d]
@@ -426,6 +431,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) qf[kb][nb] = M::load(&sm_q[16 * nb + c][4 * E * kb + E * g]);
         if (kTwoStages && blk + kWaves < full_end) load(s1, blk + kWaves);
+        if (kStages == 4 && blk + 2 * kWaves < full_end) load(s2, blk + 2 * kWaves);
+        if (kStages == 4 && blk + 3 * kWaves < full_end) load(s3, blk + 3 * kWaves);
     }
     if constexpr (kStep) {
         // Fused step, while the first blocks stream in.  q arrives unrotated and sits at position len (the
@@ -643,7 +650,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     using Full = std::integral_constant<bool, false>;
     using Tail = std::integral_constant<bool, true>;
 
-    if (kTwoStages) {
+    if constexpr (kStages == 4) {
+        // four-stage software pipeline: stage k holds block blk + k * kWaves; each processed stage is
+        // refilled with the block four strides ahead
+        while (blk < full_end) {
+            process(s0, Full{}, TOK);
+            blk += kWaves;
+            if (blk + 3 * kWaves < full_end) load(s0, blk + 3 * kWaves);
+            if (blk >= full_end) break;
+            process(s1, Full{}, TOK);
+            blk += kWaves;
+            if (blk + 3 * kWaves < full_end) load(s1, blk + 3 * kWaves);
+            if (blk >= full_end) break;
+            process(s2, Full{}, TOK);
+            blk += kWaves;
+            if (blk + 3 * kWaves < full_end) load(s2, blk + 3 * kWaves);
+            if (blk >= full_end) break;
+            process(s3, Full{}, TOK);
+            blk += kWaves;
+            if (blk + 3 * kWaves < full_end) load(s3, blk + 3 * kWaves);
+        }
+    } else if (kTwoStages) {
         // software pipeline over the full blocks: while one stage is being consumed, the next block's
         // loads are in flight
         while (blk < full_end) {
