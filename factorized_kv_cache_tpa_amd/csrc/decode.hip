@@ -371,18 +371,24 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     // Two register stages (the next block's loads in flight while one is consumed) wherever they
     // fit in the register file; wide fp32 operands use one stage.
     constexpr bool kTwoStages = sizeof(T) == 2 || HP * DP <= 1024;
-    // An E4M3 stage is half the bytes (and registers) of a bf16 one, so that path keeps four blocks per
-    // wave in flight (s0..s3) to hold as many bytes in flight as the bf16 path does with two.
-    constexpr int kStages = kF8 ? 4 : (kTwoStages ? 2 : 1);
-    Stage s0, s1, s2, s3;
+    Stage s0, s1;
     int blk = blk_begin + w;
+    // The two stages are loaded unconditionally, clamped to the split's last block (which every wave
+    // may read): a wave with a single block reads one block twice, but the loads then sit in fixed
+    // program order, so the compiler can wait for each stage exactly instead of draining every load in
+    // flight at the top of the pipelined loop below.
+    // (Outside a fused step every work-group that gets here has a block; a fused step's split 0 of an
+    // empty sequence has none and loads nothing, a branch that leaves that mode's waits conservative.)
+    const int last_blk = blk_end - 1;
+    const bool any_blk = !kStep || blk_end > blk_begin;
+    auto load_clamped = [&](Stage &st, int b) {
+        if (any_blk) load(st, b < last_blk ? b : last_blk);
+    };
     if (kTwoStages) {  // start streaming the first two blocks before anything else (a fused step issues
                        // the second after its own set-up: a wave cannot pass its loads' issue until most of
                        // them have landed, so work placed behind both stages would wait for the stream)
-        if (blk < full_end) load(s0, blk);
-        if (kMode == kQRot && blk + kWaves < full_end) load(s1, blk + kWaves);
-        if (kStages == 4 && kMode == kQRot && blk + 2 * kWaves < full_end) load(s2, blk + 2 * kWaves);
-        if (kStages == 4 && kMode == kQRot && blk + 3 * kWaves < full_end) load(s3, blk + 3 * kWaves);
+        load_clamped(s0, blk);
+        if (kMode == kQRot) load_clamped(s1, blk + kWaves);
     }
     if constexpr (kFact) {
         // Factored query, while the first blocks stream in: q~[i][d] = (1/R_Q) sum_r A_Q[r][i] B~_Q[r][d]
@@ -430,9 +436,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         for (int kb = 0; kb < KBS; ++kb)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) qf[kb][nb] = M::load(&sm_q[16 * nb + c][4 * E * kb + E * g]);
-        if (kTwoStages && blk + kWaves < full_end) load(s1, blk + kWaves);
-        if (kStages == 4 && blk + 2 * kWaves < full_end) load(s2, blk + 2 * kWaves);
-        if (kStages == 4 && blk + 3 * kWaves < full_end) load(s3, blk + 3 * kWaves);
+        if (kTwoStages) load_clamped(s1, blk + kWaves);
     }
     if constexpr (kStep) {
         // Fused step, while the first blocks stream in.  q arrives unrotated and sits at position len (the
@@ -529,7 +533,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                 rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d + 1)] = nbv1;
             }
         }
-        if (kTwoStages && blk + kWaves < full_end) load(s1, blk + kWaves);
+        if (kTwoStages) load_clamped(s1, blk + kWaves);
     }
 
 
@@ -650,27 +654,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     using Full = std::integral_constant<bool, false>;
     using Tail = std::integral_constant<bool, true>;
 
-    if constexpr (kStages == 4) {
-        // four-stage software pipeline: stage k holds block blk + k * kWaves; each processed stage is
-        // refilled with the block four strides ahead
-        while (blk < full_end) {
+    // Steady state: stage k holds block blk + k * kWaves and both refills are real blocks, so the loop
+    // issues the same loads in the same order every iteration and each stage waits for exactly its own
+    // loads (with a conditional refill the compiler cannot count the loads issued after a stage and
+    // drains everything in flight at the top of every iteration).  The wave's last blocks then run
+    // through the loop after it, whose refills are conditional.
+    if (kTwoStages) {
+        while (blk + 3 * kWaves < full_end) {
             process(s0, Full{}, TOK);
-            blk += kWaves;
-            if (blk + 3 * kWaves < full_end) load(s0, blk + 3 * kWaves);
-            if (blk >= full_end) break;
+            load(s0, blk + 2 * kWaves);
             process(s1, Full{}, TOK);
-            blk += kWaves;
-            if (blk + 3 * kWaves < full_end) load(s1, blk + 3 * kWaves);
-            if (blk >= full_end) break;
-            process(s2, Full{}, TOK);
-            blk += kWaves;
-            if (blk + 3 * kWaves < full_end) load(s2, blk + 3 * kWaves);
-            if (blk >= full_end) break;
-            process(s3, Full{}, TOK);
-            blk += kWaves;
-            if (blk + 3 * kWaves < full_end) load(s3, blk + 3 * kWaves);
+            load(s1, blk + 3 * kWaves);
+            blk += 2 * kWaves;
         }
-    } else if (kTwoStages) {
+    }
+    if (kTwoStages) {
         // software pipeline over the full blocks: while one stage is being consumed, the next block's
         // loads are in flight
         while (blk < full_end) {
