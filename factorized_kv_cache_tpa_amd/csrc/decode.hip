@@ -657,8 +657,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     // Steady state: stage k holds block blk + k * kWaves and both refills are real blocks, so the loop
     // issues the same loads in the same order every iteration and each stage waits for exactly its own
     // loads (with a conditional refill the compiler cannot count the loads issued after a stage and
-    // drains everything in flight at the top of every iteration).  The wave's last blocks then run
-    // through the loop after it, whose refills are conditional.
+    // drains everything in flight at the top of every iteration).
     if (kTwoStages) {
         while (blk + 3 * kWaves < full_end) {
             process(s0, Full{}, TOK);
@@ -669,16 +668,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         }
     }
     if (kTwoStages) {
-        // software pipeline over the full blocks: while one stage is being consumed, the next block's
-        // loads are in flight
-        while (blk < full_end) {
+        // The last (at most three) full blocks of the wave, in straight-line code so that the first one
+        // still waits only for its own stage: blk in s0, blk + kWaves in s1, blk + 2 kWaves refilled
+        // into s0.
+        if (blk < full_end) {
             process(s0, Full{}, TOK);
+            if (blk + 2 * kWaves < full_end) load(s0, blk + 2 * kWaves);
             blk += kWaves;
-            if (blk + kWaves < full_end) load(s0, blk + kWaves);
-            if (blk >= full_end) break;
-            process(s1, Full{}, TOK);
-            blk += kWaves;
-            if (blk + kWaves < full_end) load(s1, blk + kWaves);
+            if (blk < full_end) {
+                process(s1, Full{}, TOK);
+                blk += kWaves;
+                if (blk < full_end) {
+                    process(s0, Full{}, TOK);
+                    blk += kWaves;
+                }
+            }
         }
     } else {
         for (; blk < full_end; blk += kWaves) {
