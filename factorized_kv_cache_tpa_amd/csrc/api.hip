@@ -108,7 +108,6 @@ int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
     // a step also writes slot seq_start + seq_len, so its last possible slot must exist too
     if (int64_t(max_len) + (step ? 1 : 0) > capacity_tokens) return TPA_ERR_CAPACITY;
     const Layout L = layout_of(dims);
-    if (step && L.f8) return TPA_ERR_UNSUPPORTED;
     const DecodePlan P = plan_decode(L, batch, max_len, split_tokens);
     if (!workspace || workspace_bytes < P.bytes) return TPA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TPA_ERR_WORKSPACE;
@@ -136,6 +135,7 @@ int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
     if (step) {
         p.step = 1;
         p.st = *step;
+        for (int k = 0; k < 4; ++k) p.st.inv_scale[k] = float(1.0 / factor_scale(dims, k));
         p.rope = tpa::make_rope_table(dims->d_h, dims->rope_base);
     }
     p.r_q = r_q;

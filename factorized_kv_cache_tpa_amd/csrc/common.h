@@ -231,6 +231,7 @@ struct StepInputs {
     const void *A_K, *B_K, *A_V, *B_V;
     void *cache;       // the cache, written at slot seq_start[b] + seq_len[b]
     int64_t capacity;  // slots in the cache
+    float inv_scale[4];  // E4M3 cache: code = E4M3(value * inv_scale) for A_K, B_K, A_V, B_V
 };
 
 // Parameters of one decode call, shared by the split and merge kernels.

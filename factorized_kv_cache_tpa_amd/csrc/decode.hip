@@ -448,21 +448,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         // and the sequence's last split writes the token's record at slot len: no work-group of this kernel
         // reads that slot's rows (a partly filled last block masks every row at or past len), and the next
         // call sees it.
-        if (new_tok) {
-            if (na_r < RH) {
-                sm_na[0][na_r][na_i] = Elem<T>::to_f32(nak);
-                sm_na[1][na_r][na_i] = Elem<T>::to_f32(nav);
-            }
-            if (nb_r < RH) {
-                sm_nb[0][nb_r][nb_d] = Elem<T>::to_f32(nbk0);
-                sm_nb[0][nb_r][nb_d + 1] = Elem<T>::to_f32(nbk1);
-                sm_nb[1][nb_r][nb_d] = Elem<T>::to_f32(nbv0);
-                sm_nb[1][nb_r][nb_d + 1] = Elem<T>::to_f32(nbv1);
-            }
-        }
-        if (tid < DP / 2) rope_cos_sin<T>(sm_cs + 2 * tid, double(len), theta_j);
-        __syncthreads();
-        if (new_tok) {
+        // Over an E4M3 cache the token enters as its stored values, exactly as tpa_cache_append and then a
+        // decode would see it: every factor is rounded to its code and decoded back, B_K after its rotation,
+        // which no longer cancels in the score; so split 0 stages the rotated, decoded B~_K after the
+        // table and takes the score from the rotated query fragments behind a second barrier.
+        auto token_score = [&]() {
             // the token's score per head: a lane sums its d-values, the four lane groups of a head are
             // summed across (the same contraction as the cached tokens'); head block nb is taken by wave
             // nb % kWaves, so the waves share the work
@@ -498,39 +488,103 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                     sm_l[kWaves][head] = head < p.h ? 1.f : 0.f;
                 }
             }
+        };
+        // E4M3 codes of the token's items (A_K, A_V of this thread's head-factor item; B_V of its pair)
+        uint32_t ak8 = 0, av8 = 0, bv8 = 0;
+        if constexpr (kF8) {
+            ak8 = e4m3_one(Elem<T>::to_f32(nak) * p.st.inv_scale[0]);
+            av8 = e4m3_one(Elem<T>::to_f32(nav) * p.st.inv_scale[2]);
+            bv8 = e4m3_pair(Elem<T>::to_f32(nbv0) * p.st.inv_scale[3], Elem<T>::to_f32(nbv1) * p.st.inv_scale[3]);
         }
+        if (new_tok) {
+            if (na_r < RH) {
+                if constexpr (kF8) {
+                    sm_na[0][na_r][na_i] = __builtin_amdgcn_cvt_f32_fp8(int(ak8), 0);
+                    sm_na[1][na_r][na_i] = __builtin_amdgcn_cvt_f32_fp8(int(av8), 0);
+                } else {
+                    sm_na[0][na_r][na_i] = Elem<T>::to_f32(nak);
+                    sm_na[1][na_r][na_i] = Elem<T>::to_f32(nav);
+                }
+            }
+            if (nb_r < RH) {
+                if constexpr (kF8) {
+                    const floatx2 v = __builtin_amdgcn_cvt_pk_f32_fp8(int(bv8), false);
+                    sm_nb[1][nb_r][nb_d] = v.x;
+                    sm_nb[1][nb_r][nb_d + 1] = v.y;
+                } else {
+                    sm_nb[0][nb_r][nb_d] = Elem<T>::to_f32(nbk0);
+                    sm_nb[0][nb_r][nb_d + 1] = Elem<T>::to_f32(nbk1);
+                    sm_nb[1][nb_r][nb_d] = Elem<T>::to_f32(nbv0);
+                    sm_nb[1][nb_r][nb_d + 1] = Elem<T>::to_f32(nbv1);
+                }
+            }
+        }
+        if (tid < DP / 2) rope_cos_sin<T>(sm_cs + 2 * tid, double(len), theta_j);
+        __syncthreads();
+        if constexpr (!kF8)
+            if (new_tok) token_score();
 #pragma unroll
         for (int kb = 0; kb < KBS; ++kb)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) qf[kb][nb] = M::rotate_q(qf[kb][nb], 4 * E * kb + E * g, sm_cs);
         const int64_t slot = start + len;
-        if (rec_tok && slot < p.st.capacity) {
-            // the record, B_K rotated and rounded exactly as tpa_cache_append stores it
-            T k0 = nbk0, k1 = nbk1;
-            if (nb_r < p.RK && nb_d < p.d_h) {
-                F y0, y1;
-                rope_rotate(F(Elem<T>::to_f32(nbk0)), F(Elem<T>::to_f32(nbk1)), sm_cs[nb_d], sm_cs[nb_d + 1], y0, y1);
-                if constexpr (sizeof(T) == 2) {
-                    const uint32_t pk = pack_bf16x2(y0, y1);
-                    k0 = T(pk & 0xffffu);
-                    k1 = T(pk >> 16);
-                } else {
-                    k0 = T(y0);
-                    k1 = T(y1);
+        // the token's B~_K pair, rotated as tpa_cache_append rotates it
+        F y0 = F(0), y1 = F(0);
+        if ((kF8 ? (new_tok || rec_tok) : rec_tok) && nb_r < p.RK && nb_d < p.d_h)
+            rope_rotate(F(Elem<T>::to_f32(nbk0)), F(Elem<T>::to_f32(nbk1)), sm_cs[nb_d], sm_cs[nb_d + 1], y0, y1);
+        uint32_t bk8 = 0;
+        if constexpr (kF8) {
+            bk8 = e4m3_pair(float(y0) * p.st.inv_scale[1], float(y1) * p.st.inv_scale[1]);
+            if (new_tok) {
+                if (nb_r < RH) {
+                    const floatx2 v = __builtin_amdgcn_cvt_pk_f32_fp8(int(bk8), false);
+                    sm_nb[0][nb_r][nb_d] = v.x;
+                    sm_nb[0][nb_r][nb_d + 1] = v.y;
                 }
+                __syncthreads();  // split 0 only (uniform over the work-group)
+                token_score();
             }
-            T *rec = reinterpret_cast<T *>(p.st.cache) + (slot / TOK) * BLK;
+        }
+        if (rec_tok && slot < p.st.capacity) {
             const int row0 = int(slot % TOK) * RH;
-            const Layout Lay = make_layout(p.h, p.d_h, p.RK, p.RV, Elem<T>::dtype);
-            if (na_r < RH) {
-                rec[Lay.gate(row0 + na_r, na_i)] = nak;
-                rec[OFF_AV + Lay.gate(row0 + na_r, na_i)] = nav;
-            }
-            if (nb_r < RH) {
-                rec[OFF_BK + Lay.bk(row0 + nb_r, nb_d)] = k0;
-                rec[OFF_BK + Lay.bk(row0 + nb_r, nb_d + 1)] = k1;
-                rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d)] = nbv0;
-                rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d + 1)] = nbv1;
+            if constexpr (kF8) {
+                // the E4M3 record: the same codes tpa_cache_append writes, in the paired 8-bit layout
+                uint8_t *rec = reinterpret_cast<uint8_t *>(p.st.cache) + (slot / TOK) * BLK;
+                const Layout Lay = make_layout(p.h, p.d_h, p.RK, p.RV, Elem<T>::dtype, 1);
+                if (na_r < RH) {
+                    rec[Lay.gate(row0 + na_r, na_i)] = uint8_t(ak8);
+                    rec[OFF_AV + Lay.gate(row0 + na_r, na_i)] = uint8_t(av8);
+                }
+                if (nb_r < RH) {
+                    *reinterpret_cast<uint16_t *>(rec + OFF_BK + Lay.bk(row0 + nb_r, nb_d)) = uint16_t(bk8);
+                    rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d)] = uint8_t(bv8 & 0xffu);
+                    rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d + 1)] = uint8_t(bv8 >> 8);
+                }
+            } else {
+                // the record, B_K rotated and rounded exactly as tpa_cache_append stores it
+                T k0 = nbk0, k1 = nbk1;
+                if (nb_r < p.RK && nb_d < p.d_h) {
+                    if constexpr (sizeof(T) == 2) {
+                        const uint32_t pk = pack_bf16x2(y0, y1);
+                        k0 = T(pk & 0xffffu);
+                        k1 = T(pk >> 16);
+                    } else {
+                        k0 = T(y0);
+                        k1 = T(y1);
+                    }
+                }
+                T *rec = reinterpret_cast<T *>(p.st.cache) + (slot / TOK) * BLK;
+                const Layout Lay = make_layout(p.h, p.d_h, p.RK, p.RV, Elem<T>::dtype);
+                if (na_r < RH) {
+                    rec[Lay.gate(row0 + na_r, na_i)] = nak;
+                    rec[OFF_AV + Lay.gate(row0 + na_r, na_i)] = nav;
+                }
+                if (nb_r < RH) {
+                    rec[OFF_BK + Lay.bk(row0 + nb_r, nb_d)] = k0;
+                    rec[OFF_BK + Lay.bk(row0 + nb_r, nb_d + 1)] = k1;
+                    rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d)] = nbv0;
+                    rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d + 1)] = nbv1;
+                }
             }
         }
         if (kTwoStages) load_clamped(s1, blk + kWaves);
@@ -863,9 +917,10 @@ template <typename T, int HP, int DP, int RH>
 hipError_t launch_split(const DecodeParams &p, bool f8, hipStream_t s) {
     const dim3 grid(p.n_split, p.batch);
     if constexpr (sizeof(T) == 2) {
-        if (f8) {  // no fused step over an E4M3 cache (rejected by the caller)
-            if (p.step) return hipErrorInvalidValue;
-            if (p.r_q > 0)
+        if (f8) {
+            if (p.step)
+                hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, kStepMode, true>), grid, dim3(kThreads), 0, s, p);
+            else if (p.r_q > 0)
                 hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, kQFact, true>), grid, dim3(kThreads), 0, s, p);
             else
                 hipLaunchKernelGGL((decode_split_kernel<T, HP, DP, RH, kQRot, true>), grid, dim3(kThreads), 0, s, p);

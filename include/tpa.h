@@ -184,8 +184,9 @@ int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
  *     out[b][i] = sum_{s <= N} softmax_s(scale * q~_b,i . K~_s[i,:]) V_s[i,:]
  * Two kernel launches (split, merge) and no separate append: every split work-group rotates the query in
  * registers, the sequence's first split folds in the new token's own score and value (query and token share
- * a position, so RoPE cancels in that score) and its last split writes the token's record.  A native cache
- * only: with TPA_CACHE_E4M3 the call returns TPA_ERR_UNSUPPORTED (append, then tpa_decode).
+ * a position, so RoPE cancels in that score) and its last split writes the token's record.  Over a
+ * TPA_CACHE_E4M3 cache the token enters as its stored values (codes decoded back, B_K rotated before its
+ * rounding), exactly as tpa_cache_append followed by tpa_decode would see it.
  *   A_K [batch][R_K][h], B_K [batch][R_K][d_h], A_V [batch][R_V][h], B_V [batch][R_V][d_h]
  *                     the new token's factors, unrotated
  *   q [batch][h][d_h]  the step's query, unrotated (16-byte aligned)

@@ -154,13 +154,15 @@ def test_e4m3_scales_ignored_by_native_cache(lib):
     assert lib.tpa_supported(ctypes.byref(d)) == 1
 
 
-def test_decode_step_over_e4m3_cache_is_unsupported(lib):
+def test_decode_step_over_e4m3_cache_checks_its_workspace(lib):
+    """The fused step runs over an E4M3 cache too; its host checks (here: a workspace one byte short) still
+    reject before any launch."""
     d = _d(cache_format="e4m3")
     ref = ctypes.byref(d)
     need = lib.tpa_decode_workspace_bytes(ref, 16, 4096, 0)
     st = lib.tpa_decode_step(ref, FAKE, 8192, 16, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, FAKE, 0, FAKE,
-                             need, None)
-    assert st == 2
+                             need - 1, None)
+    assert st == 4
 
 
 def test_null_dims_rejected(lib):

@@ -197,3 +197,62 @@ def test_prefill_fq_matches_oracle():
         q = oracle.query_from_factors(f64(A_Q[b], w.dtype), f64(B_Q[b], w.dtype))
         ref = oracle.prefill(*stored_factors(sq, sq.n_tokens, w, dims), q, ctx[b], w.rope_base)
         assert_close(got[b], ref, w.dtype, f"seq {b}")
+
+
+# ---- the fused step over an E4M3 cache
+
+from tests.test_gpu_step import StepSetup, check_record_is_what_append_writes  # noqa: E402
+
+STEP_SHAPES = [(32, 128, 1, 1), (16, 64, 2, 2), (32, 128, 4, 4), (20, 48, 1, 3)]
+
+
+@pytest.mark.parametrize("h,d_h,R_K,R_V", STEP_SHAPES)
+@pytest.mark.parametrize("q_scale", [1.0, 6.0])
+def test_step_matches_oracle(h, d_h, R_K, R_V, q_scale):
+    """The step's token enters as its stored values: the oracle attends over the N + 1 tokens' stored
+    values (its own codec), the query at position N."""
+    w = case_workload(h, d_h, R_K, R_V)
+    lens = [0, 1, 31, 32, 33, 300, 1000]
+    say(f"case: e4m3 step h={h} d_h={d_h} R_K={R_K} R_V={R_V} q_scale={q_scale}")
+    st = StepSetup(w, lens, q_scale=q_scale, seed=h + d_h + R_K, dims=dims_of(w, E4M3))
+    got = st.run().cpu().numpy()
+    for b in range(st.batch):
+        assert_close(got[b], st.oracle(b), w.dtype, f"seq {b} (N={lens[b]})")
+
+
+@pytest.mark.parametrize("h,d_h,R_K,R_V", STEP_SHAPES)
+@pytest.mark.parametrize("scales", [(0.0, 0.0, 0.0, 0.0), (0.3, 1.7, 0.05, 3.0)])
+def test_step_record_is_what_append_writes(h, d_h, R_K, R_V, scales):
+    """The step's record is byte-identical to tpa_cache_append's codes for the same token."""
+    w = case_workload(h, d_h, R_K, R_V)
+    lens = [5, 40, 131]
+    check_record_is_what_append_writes(StepSetup(w, lens, seed=11, dims=dims_of(w, E4M3, scales)), lens)
+
+
+def test_decode_after_step_sees_the_written_token():
+    w = case_workload(32, 128, 1, 1)
+    lens = [7, 64, 129]
+    dims = dims_of(w, E4M3)
+    st = StepSetup(w, lens, seed=5, dims=dims)
+    st.run()
+    q_rot = st.cache.rotate_queries(st.q, st.seq_len)
+    ws = torch.zeros(tpa.tpa_decode_workspace_bytes(dims, st.batch, st.max_len + 1), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty(st.batch, w.h, w.d_h, dtype=torch.float32, device="cuda")
+    tpa.tpa_decode(dims, st.cache.buf, st.cache.capacity, st.cache.seq_start, st.seq_len + 1, st.max_len + 1,
+                   q_rot, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(st.batch):
+        assert_close(got[b], st.oracle(b), w.dtype, f"seq {b}")
+
+
+def test_step_full_size_decode_b16_h32_d128_r1_n4096():
+    w = ti.get("c2")
+    say(f"case: e4m3 step full size {w.name}")
+    lens = list(ti.decode_lengths(w))
+    seqs = [ti.draw_sequence(np.random.SeedSequence([w.seed, 77, b]), lens[b] + 1, 1, w) for b in range(w.batch)]
+    st = StepSetup(w, lens, seqs=seqs, dims=dims_of(w, E4M3))
+    got = st.run().cpu().numpy()
+    for b in range(st.batch):
+        assert_close(got[b], st.oracle(b), w.dtype, f"seq {b}")

@@ -13,7 +13,7 @@ import factorized_kv_cache_tpa_amd as tpa
 import oracle
 import tpa_inputs as ti
 from factorized_kv_cache_tpa_amd.cache import FactorCache, to_device
-from tests.gpu_cases import assert_close, case_workload, dims_of, f64, random_sequences, say
+from tests.gpu_cases import assert_close, case_workload, dims_of, f64, random_sequences, say, stored_factors
 
 pytestmark = pytest.mark.gpu
 
@@ -21,8 +21,8 @@ pytestmark = pytest.mark.gpu
 class StepSetup:
     """N cached tokens per sequence (N = lens[b]) and the step's token N + query, all seeded."""
 
-    def __init__(self, w: ti.Workload, lens, q_scale: float = 1.0, seed: int = 0, seqs=None):
-        self.w, self.dims, self.lens = w, dims_of(w), list(lens)
+    def __init__(self, w: ti.Workload, lens, q_scale: float = 1.0, seed: int = 0, seqs=None, dims=None):
+        self.w, self.dims, self.lens = w, dims_of(w) if dims is None else dims, list(lens)
         self.seqs = seqs if seqs is not None else random_sequences(w, [n + 1 for n in lens], q_scale=q_scale,
                                                                    seed=seed)
         self.cache = FactorCache(self.dims, [n + 1 for n in self.lens])
@@ -50,8 +50,8 @@ class StepSetup:
 
     def oracle(self, b: int) -> np.ndarray:
         s, n, dt = self.seqs[b], self.lens[b], self.w.dtype
-        return oracle.prefill(f64(s.A_K[:n + 1], dt), f64(s.B_K[:n + 1], dt), f64(s.A_V[:n + 1], dt),
-                              f64(s.B_V[:n + 1], dt), f64(s.q[:1], dt), n, self.w.rope_base)[0]
+        return oracle.prefill(*stored_factors(s, n + 1, self.w, self.dims), f64(s.q[:1], dt), n,
+                              self.w.rope_base)[0]
 
 
 SHAPES = [(32, 128, 1, 1, ti.BF16, 1e4), (16, 64, 2, 2, ti.BF16, 1e4), (32, 128, 4, 4, ti.BF16, 5e5),
@@ -81,11 +81,7 @@ def test_step_with_no_cached_tokens_returns_the_new_value_row():
         assert_close(got[b], v, ti.BF16, f"seq {b}")
 
 
-@pytest.mark.parametrize("h,d_h,R_K,R_V,dtype,base", SHAPES)
-def test_step_record_is_what_append_writes(h, d_h, R_K, R_V, dtype, base):
-    w = case_workload(h, d_h, R_K, R_V, dtype, base)
-    lens = [5, 40, 131]
-    st = StepSetup(w, lens, seed=11)
+def check_record_is_what_append_writes(st: StepSetup, lens):
     st.run()
     # the same tokens through tpa_cache_append into a fresh cache of the same geometry
     ref = FactorCache(st.dims, [n + 1 for n in lens])
@@ -94,12 +90,20 @@ def test_step_record_is_what_append_writes(h, d_h, R_K, R_V, dtype, base):
     tpa.tpa_cache_append(st.dims, ref.buf, ref.capacity, slots, pos, st.A_K, st.B_K, st.A_V, st.B_V)
     reads = []
     for cache in (st.cache, ref):
-        outs = [torch.zeros_like(x) for x in (st.A_K, st.B_K, st.A_V, st.B_V)]
+        outs = [torch.zeros(x.shape, dtype=st.dims.cache_torch_dtype, device="cuda")
+                for x in (st.A_K, st.B_K, st.A_V, st.B_V)]
         tpa.tpa_cache_read(st.dims, cache.buf, cache.capacity, slots, *outs)
         reads.append(outs)
     torch.cuda.synchronize()
     for name, a, b in zip(("A_K", "B_K", "A_V", "B_V"), *reads):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
+
+
+@pytest.mark.parametrize("h,d_h,R_K,R_V,dtype,base", SHAPES)
+def test_step_record_is_what_append_writes(h, d_h, R_K, R_V, dtype, base):
+    w = case_workload(h, d_h, R_K, R_V, dtype, base)
+    lens = [5, 40, 131]
+    check_record_is_what_append_writes(StepSetup(w, lens, seed=11), lens)
 
 
 def test_decode_after_step_sees_the_written_token():
