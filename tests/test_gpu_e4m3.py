@@ -256,3 +256,93 @@ def test_step_full_size_decode_b16_h32_d128_r1_n4096():
     got = st.run().cpu().numpy()
     for b in range(st.batch):
         assert_close(got[b], st.oracle(b), w.dtype, f"seq {b}")
+
+
+# ---- edge cases over an E4M3 cache
+
+def test_empty_misaligned_and_tail_garbage():
+    """Empty sequence -> zeros; misaligned start -> NaN; unwritten slots (0xFF = NaN codes) past seq_len and
+    the written tokens past a shortened seq_len never leak into the output."""
+    w = case_workload(32, 128, 4, 4)
+    dims = dims_of(w, E4M3)
+    seqs = random_sequences(w, [0, 13, 29, 40], seed=13)
+    s = DecodeSetup(w, seqs, dims=dims)
+    out = s.run()
+    assert np.all(out[0] == 0.0)
+    assert_close(out[1:], np.stack([s.oracle(b) for b in (1, 2, 3)]), w.dtype, "full lengths")
+    short = torch.tensor([0, 5, 21, 40], dtype=torch.int32, device="cuda")
+    out = s.run(seq_len=short)
+    for b, n in ((1, 5), (2, 21)):
+        sq = seqs[b]
+        ref = oracle.attention(*stored_factors(sq, n, w, dims), np.arange(n), f64(sq.q, w.dtype), [len(sq.A_K)],
+                               [n], w.rope_base)[0]
+        assert_close(out[b], ref, w.dtype, f"seq {b} first {n} tokens")
+    bad = s.cache.seq_start.clone()
+    bad[3] += 1
+    out = s.run(seq_start=bad)
+    assert np.all(np.isnan(out[3]))
+    assert_close(out[1], s.oracle(1), w.dtype, "aligned row")
+
+
+def test_split_sizes_and_determinism():
+    w = case_workload(16, 64, 2, 2)
+    s = DecodeSetup(w, random_sequences(w, [3000, 1234, 17], q_scale=8.0, seed=5), dims=dims_of(w, E4M3))
+    ref = np.stack([s.oracle(b) for b in range(s.batch)])
+    for split in (0, 16, 128, 4096):
+        assert_close(s.run(split_tokens=split), ref, w.dtype, f"split {split}")
+    assert np.array_equal(s.run(), s.run()), "two identical calls differ"
+
+
+def test_prefill_rows_equal_gpu_decodes():
+    """Prefill row j over an E4M3 cache equals the decode of the same query over ctx + j + 1 tokens."""
+    w = case_workload(32, 128, 2, 2)
+    dims = dims_of(w, E4M3)
+    ctx, chunk = [90], 70
+    seqs = random_sequences(w, [ctx[0] + chunk], n_q=chunk, q_scale=3.0, seed=44)
+    p = PrefillSetup(w, seqs, ctx, dims=dims)
+    got = p.run()[0]
+    ws = torch.zeros(tpa.tpa_decode_workspace_bytes(dims, 1, ctx[0] + chunk), dtype=torch.uint8, device="cuda")
+    for j in (0, 1, 33, chunk - 1):
+        out = torch.empty(1, w.h, w.d_h, dtype=torch.float32, device="cuda")
+        q_row = p.q_rot[:, j].contiguous()
+        tpa.tpa_decode(dims, p.cache.buf, p.cache.capacity, p.cache.seq_start,
+                       torch.tensor([ctx[0] + j + 1], dtype=torch.int32, device="cuda"), ctx[0] + chunk, q_row, out, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(got[j], out.cpu().numpy()[0], rtol=0, atol=2e-3, err_msg=f"row {j}")
+
+
+def test_step_graph_replays_match_eager():
+    """The E4M3 fused step captured once and replayed with eager work between: every replay equals the eager
+    output bit for bit (the step rewrites the same record)."""
+    w = case_workload(32, 128, 1, 1)
+    st = StepSetup(w, [100, 2048, 4000], seed=13, dims=dims_of(w, E4M3))
+    ws = st.workspace()
+    eager = st.run(ws=ws).clone()
+    out = torch.empty_like(eager)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        st.run(out=out, ws=ws)
+    for i in range(4):
+        out.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        del junk
+
+
+def test_step_misaligned_start_gives_nan_and_writes_nothing():
+    w = case_workload(32, 128, 1, 1)
+    st = StepSetup(w, [40, 40], seed=9, dims=dims_of(w, E4M3))
+    before = st.cache.buf.clone()
+    bad = st.cache.seq_start.clone()
+    bad[1] += 1  # not a block boundary
+    got = st.run(seq_start=bad).cpu().numpy()
+    assert np.all(np.isnan(got[1]))
+    assert_close(got[0], st.oracle(0), w.dtype, "seq 0")
+    changed = (st.cache.buf != before).nonzero().flatten()
+    blk = tpa.tpa_cache_bytes(st.dims, tpa.tpa_block_tokens(st.dims))
+    assert changed.numel() > 0
+    assert int(changed.min()) >= (40 // 32) * blk and int(changed.max()) < (40 // 32 + 1) * blk
