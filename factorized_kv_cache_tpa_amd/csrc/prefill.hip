@@ -555,8 +555,441 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         prefill_body<HP, DP, RH, kFQ, false, kF8>(p, lds);
 }
 
+// ===================================================================================================
+// Wide form (bf16 cache, d_h = 128, chunks of more than 256 rows): a work-group owns 512 query rows of
+// one head, so each (key, head) pair is rebuilt once per 512 rows and the factor bytes a work-group
+// loads per query row halve.  8 waves x 64 rows: each wave holds two 32-row blocks, w and 15 - w of the
+// tile, so every wave has the same causal extent; 32-key tiles.  The factor pieces a wave rebuilds from
+// are fetched straight into a wave-private LDS staging area (global_load_lds), so they hold no
+// registers in flight, and each wave only reads back pieces it fetched itself, so the staging needs no
+// barrier, only the wave's own vmcnt wait.  The ping-pong of the two waves of a SIMD is kept.
+constexpr int kW2Rows = 64;                        // query rows per wave
+constexpr int kQT2 = kW2Rows * kPrefillWaves;      // query rows per work-group
+constexpr int kKT2 = 32;                           // keys per tile
+
+template <int DP, int RH>
+struct Prefill2Lds {
+    static constexpr int TOK = kRows / RH;
+    static constexpr int BPT = kKT2 / TOK;                   // cache blocks per tile
+    static constexpr int MVG = kPrefillWaves / BPT;          // waves sharing one block's value chunks
+    static constexpr int V_ITEMS = (DP / 16) / MVG;          // value chunks per lane
+    static constexpr int PIECES = RH + V_ITEMS;              // 16-byte pieces per lane
+    static constexpr int GATE_OFF = PIECES * 1024;           // then 3 gate slots (12 bytes used of 16 per lane)
+    static constexpr int RAW_BYTES = GATE_OFF + 3 * 1024;
+    uint16_t k[2][kKT2 * (DP + 8)];
+    uint16_t v[2][DP * (kKT2 + 8)];
+    char raw[kPrefillWaves][RAW_BYTES];
+};
+
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
+template <int HP, int DP, int RH, bool kFQ, bool late>
+__device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Lds<DP, RH> &lds) {
+    using LD = Prefill2Lds<DP, RH>;
+    constexpr int KS = DP / 16;
+    constexpr int MB = DP / 32;
+    constexpr int NB = HP / 16;
+    constexpr int KBS = DP / 32;
+    constexpr int TOK = LD::TOK, BPT = LD::BPT, MVG = LD::MVG, V_ITEMS = LD::V_ITEMS;
+    constexpr int SKS = DP + 8;
+    constexpr int SVS = kKT2 + 8;
+    constexpr int BLK = 2 * kRows * (HP + DP);
+    constexpr int OFF_AV = kRows * HP, OFF_BK = 2 * kRows * HP, OFF_BV = 2 * kRows * HP + kRows * DP;
+    constexpr int C8 = DP / 8;
+    static_assert(kKT2 * C8 == kPrefillThreads, "one K~ item per thread");
+    static_assert(MVG * BPT == kPrefillWaves && V_ITEMS * MVG == DP / 16, "V items must tile the group");
+
+    const int n_qt = (p.chunk + kQT2 - 1) / kQT2;
+    const int L = blockIdx.x;
+    int b, head, qt;
+    if (p.batch % kXcds == 0) {
+        const int per_seq = p.h * n_qt;
+        b = L % kXcds + kXcds * (L / (kXcds * per_seq));
+        const int r = (L / kXcds) % per_seq;
+        head = r / n_qt;
+        qt = r % n_qt;
+    } else {
+        qt = L % n_qt;
+        head = (L / n_qt) % p.h;
+        b = L / (n_qt * p.h);
+    }
+    const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hi = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j0 = qt * kQT2;
+    const int jw[2] = {j0 + 32 * w, j0 + 32 * (2 * kPrefillWaves - 1 - w)};  // the wave's two row blocks
+    const int jq[2] = {jw[0] + col, jw[1] + col};
+    int ctx = p.ctx_len[b];
+    const int64_t start = p.seq_start[b];
+    ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
+    float *out = p.out + int64_t(b) * p.chunk * p.h * p.d_h;
+
+    if (start < 0 || start % TOK != 0) {
+        for (int idx = tid; idx < kQT2 * p.d_h; idx += kPrefillThreads) {
+            const int j = j0 + idx / p.d_h, d = idx % p.d_h;
+            if (j < p.chunk) out[(int64_t(j) * p.h + head) * p.d_h + d] = __builtin_nanf("");
+        }
+        return;
+    }
+    const char *seq = reinterpret_cast<const char *>(p.cache) + (start / TOK) * int64_t(BLK) * 2;
+    const int j_last = min(p.chunk, j0 + kQT2) - 1;
+    const int n_keys = ctx + j_last + 1;
+    const int n_kt = (n_keys + kKT2 - 1) / kKT2;
+    const int gate_lane = head & 15, gate_nb = head >> 4;
+
+    // ---- this lane's pieces.  K~: wave w owns one 16-row group of the tile's factor rows (16 / RH keys)
+    // over RH of the 4 32-feature column blocks, so each of its RH fetches is one whole, contiguous 1 KB
+    // piece of the cache block; lane (key kl, chunk) then reads the RH rank pieces of its key from the
+    // staging area.  V: V_ITEMS contiguous value chunks of one cache block.
+    constexpr int WPG = 4 / RH;                       // waves per 16-row group
+    const int gi = w / WPG;                           // the wave's 16-row group inside the tile
+    const int kbw0 = (w % WPG) * RH;                  // its first 32-feature column block
+    const int kl = lane / (4 * RH);                   // this lane's key inside the group
+    const int k_blk = gi / 2, k_mb = gi % 2;          // cache block (tile-relative) and row group in it
+    const uint32_t k_off_b = uint32_t(k_blk * BLK + OFF_BK + ((k_mb * KBS + kbw0) * kWave + lane) * 8) * 2u;
+    const int k_gl = 16 * ((kl * RH) >> 2) + gate_lane;
+    const uint32_t k_off_gate = uint32_t(k_blk * BLK + ((k_mb * NB + gate_nb) * kWave + k_gl) * 4) * 2u;
+    const int vrow = w, vcl = lane, vg4 = vcl >> 4;
+    const int vbi = vrow % BPT, vmv0 = (vrow / BPT) * V_ITEMS;
+    const uint32_t v_off = uint32_t(vbi * BLK + OFF_BV + (vmv0 * kWave + vcl) * 8) * 2u;
+    const int v_gl = 16 * vg4 + gate_lane;
+    const uint32_t v_off_gate = uint32_t(vbi * BLK + OFF_AV + (gate_nb * kWave + v_gl) * 4) * 2u;
+
+    char *rw = lds.raw[w];
+    auto tile_base = [&](int kt) { return seq + int64_t((kt * kKT2) / TOK) * BLK * 2; };
+    auto tile_last_blk = [&](int kt) {
+        const int key0 = kt * kKT2;
+        return key0 + kKT2 <= n_keys ? 1 << 20 : (n_keys - 1) / TOK - key0 / TOK;
+    };
+    // Fetch of one tile's pieces into the wave's staging area (the 8-byte gate pieces as 12-byte
+    // transfers, which land 16 bytes apart).  Blocks past the last live one are replaced by it.
+    auto fetch = [&](int kt) {
+        const char *tb = tile_base(kt);
+        const int last_blk = tile_last_blk(kt);
+        // the per-lane offsets are rebuilt here (opaque to the optimizer) rather than kept live per piece
+        uint32_t ko = k_off_b + uint32_t((min(k_blk, last_blk) - k_blk) * BLK) * 2u;
+        uint32_t kg = k_off_gate - k_off_b;
+        uint32_t vo = v_off + uint32_t((min(vbi, last_blk) - vbi) * BLK) * 2u;
+        uint32_t vg = v_off_gate - v_off;
+        asm volatile("" : "+v"(ko), "+v"(kg), "+v"(vo), "+v"(vg));
+#pragma unroll
+        for (int q = 0; q < RH; ++q)
+            __builtin_amdgcn_global_load_lds(tb + uint32_t(ko + q * kWave * 16), (lds_ptr)(rw + q * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(tb + uint32_t(ko + kg), (lds_ptr)(rw + LD::GATE_OFF), 12, 0, 0);
+#pragma unroll
+        for (int u = 0; u < V_ITEMS; ++u)
+            __builtin_amdgcn_global_load_lds(tb + uint32_t(vo + u * kWave * 16), (lds_ptr)(rw + (RH + u) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            __builtin_amdgcn_global_load_lds(tb + uint32_t(vo + vg + m * NB * kWave * 8),
+                                             (lds_ptr)(rw + LD::GATE_OFF + (1 + m) * 1024), 12, 0, 0);
+    };
+    // The rebuild: bf16 pair products with fp32 accumulation, one bf16 rounding.
+    // Its per-lane addresses are derived from an opaque copy of the lane index, so they live only here.
+    auto rebuild = [&](int kt, int buf, auto partial_tag) {
+        constexpr bool kPartial = decltype(partial_tag)::value;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int key0 = kt * kKT2;
+        const char *rl = rw + 16 * ln;  // this lane's 16-byte slot of each staged piece
+        const int kl_ = ln / (4 * RH), cl_ = ln % (4 * RH);
+        const int kb_ = kbw0 + cl_ / 4, sub_ = cl_ % 4;
+        const int kk_ = (16 * gi) / RH + kl_;
+        const int kv0_ = (kl_ * RH) & 3;
+        {
+            const uint32_t *gp = reinterpret_cast<const uint32_t *>(rl + LD::GATE_OFF);
+            const uint32_t gw[2] = {gp[0], gp[1]};
+            // rank pieces of this lane's key: position 16 sub + kl RH + r of column block kb
+            const char *kp = rw + (kb_ - kbw0) * 1024 + 16 * (16 * sub_ + kl_ * RH);
+            uint4 kbr[RH];
+#pragma unroll
+            for (int r = 0; r < RH; ++r) kbr[r] = *reinterpret_cast<const uint4 *>(kp + 16 * r);
+            float kv[8];
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {  // feature pairs (2 w2, 2 w2 + 1)
+                if (RH == 1) {
+                    const uint32_t a = (kv0_ & 1) ? (gw[kv0_ >> 1] >> 16) : (gw[kv0_ >> 1] & 0xffffu);
+                    const uint32_t bw = (&kbr[0].x)[w2];
+                    kv[2 * w2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(bw & 0xffffu), 0.f, false);
+                    kv[2 * w2 + 1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(bw >> 16), 0.f, false);
+                } else {
+                    kv[2 * w2] = kv[2 * w2 + 1] = 0.f;
+#pragma unroll
+                    for (int rp = 0; rp < RH / 2; ++rp) {  // rank pairs (2 rp, 2 rp + 1)
+                        const uint32_t a = gw[(kv0_ >> 1) + rp];
+                        const uint32_t b0 = (&kbr[2 * rp].x)[w2], b1 = (&kbr[2 * rp + 1].x)[w2];
+                        const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x05040100u);
+                        const uint32_t hi2 = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+                        kv[2 * w2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(lo), kv[2 * w2], false);
+                        kv[2 * w2 + 1] =
+                            __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(hi2), kv[2 * w2 + 1], false);
+                    }
+                }
+            }
+            uint4 packed = make_uint4(pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3]), pack_bf16x2(kv[4], kv[5]),
+                                      pack_bf16x2(kv[6], kv[7]));
+            if (kPartial && key0 + kk_ >= n_keys) packed = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(&lds.k[buf][kk_ * SKS + 32 * kb_ + 8 * sub_]) = packed;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int vg4_ = ln >> 4;
+        const int kbase = vbi * TOK;
+        constexpr int TPH = 4 / RH;
+        uint32_t gv[2][2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const uint32_t *gp = reinterpret_cast<const uint32_t *>(rl + LD::GATE_OFF + (1 + m) * 1024);
+            gv[m][0] = gp[0];
+            gv[m][1] = gp[1];
+        }
+        uint16_t *dV = &lds.v[buf][(16 * vmv0 + (ln & 15)) * SVS];
+#pragma unroll
+        for (int u = 0; u < V_ITEMS; ++u) {
+            const uint4 vxu = *reinterpret_cast<const uint4 *>(rl + (RH + u) * 1024);
+            const uint32_t xw[4] = {vxu.x, vxu.y, vxu.z, vxu.w};
+            float v_one[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                float vt[TPH];
+#pragma unroll
+                for (int tl = 0; tl < TPH; ++tl) {
+                    float acc = 0.f;
+                    if (RH == 1) {
+                        const uint32_t a = (tl & 1) ? (gv[m][tl >> 1] >> 16) : (gv[m][tl >> 1] & 0xffffu);
+                        const uint32_t x = (tl & 1) ? (xw[2 * m + (tl >> 1)] >> 16) : (xw[2 * m + (tl >> 1)] & 0xffffu);
+                        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(x), 0.f, false);
+                    } else {
+#pragma unroll
+                        for (int rp = 0; rp < RH / 2; ++rp)
+                            acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(gv[m][(tl * RH) / 2 + rp]),
+                                                                  as_bf16x2(xw[2 * m + (tl * RH) / 2 + rp]), acc, false);
+                    }
+                    vt[tl] = acc;
+                    if (kPartial && key0 + kbase + (16 * m + 4 * vg4_) / RH + tl >= n_keys) vt[tl] = 0.f;
+                }
+                uint16_t *dst = dV + 16 * u * SVS + vpos(kbase + (16 * m + 4 * vg4_) / RH);
+                if constexpr (TPH == 4) {
+                    *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(vt[0], vt[1]), pack_bf16x2(vt[2], vt[3]));
+                } else if constexpr (TPH == 2) {
+                    *reinterpret_cast<uint32_t *>(dst) = pack_bf16x2(vt[0], vt[1]);
+                } else {
+                    v_one[m] = vt[0];
+                }
+            }
+            if constexpr (TPH == 1) {
+                const uint32_t pk = pack_bf16x2(v_one[0], v_one[1]);
+                dV[16 * u * SVS + vpos(kbase + vg4_)] = uint16_t(pk & 0xffffu);
+                dV[16 * u * SVS + vpos(kbase + 4 + vg4_)] = uint16_t(pk >> 16);
+            }
+        }
+    };
+    auto rebuild_tile = [&](int kt, int buf) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's staged pieces have landed
+        if (kt * kKT2 + kKT2 <= n_keys)
+            rebuild(kt, buf, std::false_type{});
+        else
+            rebuild(kt, buf, std::true_type{});
+    };
+
+    // Q operands of the two row blocks
+    bf16x8 qf[2][KS];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        if constexpr (kFQ) {
+            float x[KS][8] = {};
+            if (jq[nb] < p.chunk) {
+                const int64_t row = int64_t(b) * p.chunk + jq[nb];
+                const uint16_t *aq = reinterpret_cast<const uint16_t *>(p.a_q) + row * p.r_q * p.h + head;
+                const uint16_t *bq = reinterpret_cast<const uint16_t *>(p.q) + row * p.r_q * p.d_h;
+                for (int r = 0; r < p.r_q; ++r) {
+                    const float a = bf16_to_f32(aq[r * p.h]);
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const int d0 = 16 * ks + 8 * hi;
+                        const uint4 v = *reinterpret_cast<const uint4 *>(bq + r * p.d_h + d0);
+                        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            x[ks][e] = fmaf(a, __uint_as_float((e & 1) ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16)),
+                                            x[ks][e]);
+                    }
+                }
+            }
+            const float inv_rq = 1.f / float(p.r_q);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[ks][e] *= inv_rq;
+                qf[nb][ks] = pack8(x[ks]);
+            }
+        } else {
+            const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) +
+                                   (int64_t(b) * p.chunk + jq[nb]) * p.h * p.d_h + int64_t(head) * p.d_h;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int d0 = 16 * ks + 8 * hi;
+                qf[nb][ks] = jq[nb] < p.chunk ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qrow + d0))
+                                              : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+            }
+        }
+    }
+
+    floatx16 acc[2][MB];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[nb][mb][v] = 0.f;
+    const float sm = p.score_mul, lazy_raw = kLazyPrefill / sm;
+    float run_m[2] = {-INFINITY, -INFINITY}, neg_ms[2] = {INFINITY, INFINITY}, run_l[2] = {0.f, 0.f};
+    int wave_last[2], jq_vis[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        wave_last[nb] = min(p.chunk - 1, jw[nb] + 31);
+        jq_vis[nb] = jq[nb] < p.chunk ? ctx + jq[nb] : -1;
+    }
+    const bf16x2 ones2 = as_bf16x2(0x3F803F80u);
+
+    // The pieces of the tile a wave rebuilds next are fetched while it runs the matrix-core
+    // instructions of the current tile (interleaved with the first row block's score products).
+    fetch(0);
+    rebuild_tile(0, 0);
+    if (late) fetch(min(1, n_kt - 1));
+    __syncthreads();
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int buf = kt & 1;
+        if (late && kt + 1 < n_kt) rebuild_tile(kt + 1, buf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int kf = min(kt + 1 + int(late), n_kt - 1);  // tile whose pieces are fetched now
+        const int key0 = kt * kKT2;
+        {
+            const uint16_t *cK = lds.k[buf];
+            const uint16_t *cV = lds.v[buf];
+            // the two row blocks one after the other (one score tile live at a time): the later block
+            // first (it carries the fetches), then the earlier one, skipped once its rows see no key
+            // of the tile
+#pragma unroll
+            for (int nbi = 0; nbi < 2; ++nbi) {
+                const int nb = 1 - nbi;
+                __builtin_amdgcn_sched_barrier(0);
+                if (nb == 0 && key0 > ctx + wave_last[0]) continue;
+                floatx16 s;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) s[v] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&cK[col * SKS + 16 * ks + 8 * hi]);
+                    s = mma32(a, qf[nb][ks], s);
+                }
+                if (nb == 1) {
+                    fetch(kf);
+                    // operand reads two ahead of the matrix cores, the fetches between them
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+                    for (int i = 0; i < KS - 2; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);
+                } else {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+                    for (int i = 0; i < KS - 2; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                }
+                if (key0 + kKT2 - 1 > ctx + jw[nb] || wave_last[nb] < jw[nb] + 31) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int key = key0 + 8 * (v >> 2) + 4 * hi + (v & 3);
+                        s[v] = key <= jq_vis[nb] ? s[v] : -INFINITY;
+                    }
+                }
+                float mx = -INFINITY;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
+                if (__any(mx > run_m[nb] + lazy_raw)) {
+                    const float mn = fmaxf(run_m[nb], fmaxf(mx, __shfl_xor(mx, 32, kWave)));
+                    if (mn != -INFINITY) {
+                        const float alpha = __builtin_amdgcn_exp2f((run_m[nb] - mn) * sm);
+                        run_m[nb] = mn;
+                        neg_ms[nb] = -mn * sm;
+                        run_l[nb] *= alpha;
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] *= alpha;
+                    }
+                }
+#pragma unroll
+                for (int v = 0; v < 16; ++v) s[v] = __builtin_amdgcn_exp2f(fmaf(s[v], sm, neg_ms[nb]));
+#pragma unroll
+                for (int ks4 = 0; ks4 < 2; ++ks4) {
+                    const int o8 = 8 * ks4;
+                    const uint32_t pw[4] = {pack_bf16x2(s[o8], s[o8 + 1]), pack_bf16x2(s[o8 + 2], s[o8 + 3]),
+                                            pack_bf16x2(s[o8 + 4], s[o8 + 5]), pack_bf16x2(s[o8 + 6], s[o8 + 7])};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        run_l[nb] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw[i]), ones2, run_l[nb], false);
+                    const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&cV[(32 * mb + col) * SVS + 16 * ks4 + 8 * hi]);
+                        acc[nb][mb] = mma32(a, pf, acc[nb][mb]);
+                    }
+                }
+            }
+        }
+        if (!late && kt + 1 < n_kt) rebuild_tile(kt + 1, buf ^ 1);
+        __syncthreads();
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // the last (unused) fetches have landed
+
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const float l = run_l[nb] + __shfl_xor(run_l[nb], 32, kWave);
+        if (jq[nb] < p.chunk) {
+            const float inv = p.out_mul / l;
+            float *o = out + (int64_t(jq[nb]) * p.h + head) * p.d_h;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    const int d = 32 * mb + 8 * v4 + 4 * hi;
+                    *reinterpret_cast<float4 *>(o + d) =
+                        make_float4(acc[nb][mb][4 * v4] * inv, acc[nb][mb][4 * v4 + 1] * inv, acc[nb][mb][4 * v4 + 2] * inv,
+                                    acc[nb][mb][4 * v4 + 3] * inv);
+                }
+        }
+    }
+}
+
+template <int HP, int DP, int RH, bool kFQ>
+__global__ __launch_bounds__(kPrefillThreads) void prefill2_kernel(PrefillParams p) {
+    __shared__ __attribute__((aligned(16))) Prefill2Lds<DP, RH> lds;
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= kPrefillWaves / 2)
+        prefill2_body<HP, DP, RH, kFQ, true>(p, lds);
+    else
+        prefill2_body<HP, DP, RH, kFQ, false>(p, lds);
+}
+
+// The wide form pays off once a chunk fills more than one 256-row work-group.
+bool use_wide(const PrefillParams &p) { return p.d_h == 128 && p.chunk > kQT; }
+
 template <int HP, int DP, int RH, bool kF8>
 hipError_t launch_one(const PrefillParams &p, hipStream_t s) {
+    if constexpr (DP == 128 && !kF8) {
+        if (use_wide(p)) {
+            const dim3 grid2(unsigned(((p.chunk + kQT2 - 1) / kQT2) * p.h * p.batch));
+            if (p.r_q > 0)
+                hipLaunchKernelGGL((prefill2_kernel<HP, DP, RH, true>), grid2, dim3(kPrefillThreads), 0, s, p);
+            else
+                hipLaunchKernelGGL((prefill2_kernel<HP, DP, RH, false>), grid2, dim3(kPrefillThreads), 0, s, p);
+            return hipGetLastError();
+        }
+    }
     const dim3 grid(unsigned(((p.chunk + kQT - 1) / kQT) * p.h * p.batch));
     if (p.r_q > 0)
         hipLaunchKernelGGL((prefill_kernel<HP, DP, RH, true, kF8>), grid, dim3(kPrefillThreads), 0, s, p);

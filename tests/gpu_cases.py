@@ -127,10 +127,11 @@ class PrefillSetup:
                                                                       self.w.d_h)
         self.ctx_len = torch.tensor(self.ctx, dtype=torch.int32, device="cuda")
 
-    def run(self, scale: float = 0.0) -> np.ndarray:
+    def run(self, scale: float = 0.0, seq_start=None) -> np.ndarray:
         out = torch.full((len(self.seqs), self.chunk, self.w.h, self.w.d_h), float("nan"), dtype=torch.float32,
                          device="cuda")
-        tpa.tpa_prefill_chunk(self.dims, self.cache.buf, self.cache.capacity, self.cache.seq_start, self.ctx_len,
+        starts = self.cache.seq_start if seq_start is None else seq_start
+        tpa.tpa_prefill_chunk(self.dims, self.cache.buf, self.cache.capacity, starts, self.ctx_len,
                               max(self.ctx), self.chunk, self.q_rot, out, scale=scale)
         torch.cuda.synchronize()
         return out.cpu().numpy()

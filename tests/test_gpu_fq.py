@@ -118,6 +118,7 @@ def test_fq_full_size_decode_b16_h32_d128_r1_n4096_rq6():
 
 
 @pytest.mark.parametrize("h,d_h,R_K,R_V,R_Q,ctx,chunk", [(32, 128, 4, 4, 6, 100, 64), (16, 64, 2, 2, 3, [37, 0], 300),
+                                                          (32, 128, 4, 4, 6, [5, 130], 400),
                                                           (32, 128, 1, 1, 1, 0, 33), (20, 48, 1, 3, 16, 65, 40)])
 def test_prefill_fq_matches_oracle(h, d_h, R_K, R_V, R_Q, ctx, chunk):
     """Causal chunk with factored query rows (row j at position ctx + j sees tokens 0 .. ctx + j)."""

@@ -45,3 +45,42 @@ def test_full_size_prefill_sampled_rows():
     rows = np.array([0, 1, 31, 32, 127, 128, 255, 256, 383, 384, 510, 511])
     for b in (0, 3, 7):
         assert_close(out[b][rows], s.oracle(b, rows=rows), w.dtype, f"seq {b} rows")
+
+
+# Chunks of more than 256 rows at d_h = 128 run the wide form (512 query rows per work-group, factor
+# pieces staged through LDS); these cases cover it with ragged chunk ends, a second row tile, short and
+# empty contexts and every rank.
+# (q_scale sets how peaked the softmax is: at R = 1 the rebuilt keys are largest, and a very peaked
+# softmax over bf16 operands amplifies their rounding in the output, so the sharp case uses R = 4.)
+@pytest.mark.parametrize("h,R,q_scale", [(32, 4, 2.0), (32, 2, 2.0), (32, 1, 2.0), (20, 4, 2.0), (32, 4, 10.0)])
+@pytest.mark.parametrize("ctx,chunk", [([0, 45], 300), ([257], 700), ([64, 1000, 3], 257)])
+def test_wide_chunks(h, R, q_scale, ctx, chunk):
+    w = case_workload(h, 128, R, R)
+    say(f"case: wide prefill h={h} R={R} q_scale={q_scale} ctx={ctx} chunk={chunk}")
+    seqs = random_sequences(w, [c + chunk for c in ctx], n_q=chunk, q_scale=q_scale, seed=h * R + chunk)
+    s = PrefillSetup(w, seqs, ctx)
+    out = s.run()
+    ref = np.stack([s.oracle(b) for b in range(len(seqs))])
+    assert_close(out, ref, w.dtype, "all rows")
+
+
+@pytest.mark.parametrize("chunk", [100, 400])
+def test_misaligned_start_gives_nan(chunk):
+    """A sequence whose first slot is not a block boundary reports NaN rows; the others are unaffected."""
+    w = case_workload(32, 128, 2, 2)
+    say(f"case: misaligned prefill chunk={chunk}")
+    ctx = [40, 70]
+    seqs = random_sequences(w, [c + chunk for c in ctx], n_q=chunk, seed=chunk)
+    s = PrefillSetup(w, seqs, ctx)
+    bad = s.cache.seq_start.clone()
+    bad[1] += 1
+    out = s.run(seq_start=bad)
+    assert np.all(np.isnan(out[1]))
+    assert_close(out[0], s.oracle(0), w.dtype, "aligned sequence")
+
+
+def test_wide_prefill_is_deterministic():
+    w = case_workload(32, 128, 4, 4)
+    seqs = random_sequences(w, [600, 333 + 300], n_q=300, seed=3)
+    s = PrefillSetup(w, seqs, [300, 333])
+    assert np.array_equal(s.run(), s.run())
