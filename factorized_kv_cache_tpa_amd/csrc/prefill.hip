@@ -13,7 +13,9 @@
 //     online softmax per query (a lane owns one query column)
 //     O^T += V_i^T P^T  (M = d_h, N = queries, K = keys)
 // A work-group owns 256 query rows of one head (8 waves x 32), so every
-// (key, head) pair is rebuilt at most twice per chunk of 512 rows.  The LDS
+// (key, head) pair is rebuilt at most twice per chunk of 512 rows; chunks of
+// more than 256 rows at d_h = 128 take the wide form further down (512 rows
+// per work-group, factor pieces staged in LDS by direct loads).  The LDS
 // tiles are double-buffered: the factor loads of a later tile are issued between
 // the matrix-core instructions of tile t, and the waves rebuild tile t+1 (half of
 // them at the end of their iteration, half at its start: see prefill_kernel).  The key order inside the value contraction is
