@@ -1010,7 +1010,8 @@ hipError_t launch_rank(int RH, const PrefillParams &p, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-#define TPA_PREFILL_SHAPES(X) X(16, 64) X(16, 128) X(32, 64) X(32, 128) X(64, 64) X(64, 128)
+// (the padded (heads, head dim) pairs the cache layer supports with bf16 operands)
+#define TPA_PREFILL_SHAPES(X) X(16, 64) X(16, 128) X(32, 64) X(32, 128) X(64, 64)
 
 }  // namespace
 

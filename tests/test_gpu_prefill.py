@@ -52,7 +52,8 @@ def test_full_size_prefill_sampled_rows():
 # empty contexts and every rank.
 # (q_scale sets how peaked the softmax is: at R = 1 the rebuilt keys are largest, and a very peaked
 # softmax over bf16 operands amplifies their rounding in the output, so the sharp case uses R = 4.)
-@pytest.mark.parametrize("h,R,q_scale", [(32, 4, 2.0), (32, 2, 2.0), (32, 1, 2.0), (20, 4, 2.0), (32, 4, 10.0)])
+@pytest.mark.parametrize("h,R,q_scale", [(32, 4, 2.0), (32, 2, 2.0), (32, 1, 2.0), (20, 4, 2.0), (16, 4, 2.0),
+                                         (32, 4, 10.0)])
 @pytest.mark.parametrize("ctx,chunk", [([0, 45], 300), ([257], 700), ([64, 1000, 3], 257)])
 def test_wide_chunks(h, R, q_scale, ctx, chunk):
     w = case_workload(h, 128, R, R)
