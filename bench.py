@@ -359,6 +359,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--step-only", action="store_true",
                     help="time only the fused step of the main workload (for profiled runs)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the causal prefill workload and print its own JSON line (for profiled runs)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 64 MiB device copy three times (scale reference for the HBM byte "
                          "counters of a profiled run)")
@@ -372,6 +374,11 @@ def main():
     import factorized_kv_cache_tpa_amd as tpa
     tpa.load()  # fails loudly when the HIP library is missing
     torch.cuda.set_device(0)
+
+    if args.prefill_only:
+        p = prefill_bench(max(5, args.steps // 10), 3)
+        print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in p.items()}), flush=True)
+        return
 
     main_b = DecodeBench(MAIN, min_bytes=4 * MALL_BYTES)
     res = main_b.run(args.steps, args.warmup, step_only=args.step_only)
