@@ -85,3 +85,16 @@ def test_wide_prefill_is_deterministic():
     seqs = random_sequences(w, [600, 333 + 300], n_q=300, seed=3)
     s = PrefillSetup(w, seqs, [300, 333])
     assert np.array_equal(s.run(), s.run())
+
+
+@pytest.mark.parametrize("R_K,R_V", [(1, 3), (4, 2)])
+def test_wide_unequal_ranks(R_K, R_V):
+    """Unequal key and value ranks: the layout pads both to the larger rank with zero factor rows."""
+    w = case_workload(32, 128, R_K, R_V)
+    say(f"case: wide prefill R_K={R_K} R_V={R_V}")
+    ctx, chunk = [33, 280], 290
+    seqs = random_sequences(w, [c + chunk for c in ctx], n_q=chunk, q_scale=2.0, seed=R_K * 10 + R_V)
+    s = PrefillSetup(w, seqs, ctx)
+    out = s.run()
+    ref = np.stack([s.oracle(b) for b in range(len(seqs))])
+    assert_close(out, ref, w.dtype, "all rows")
