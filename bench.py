@@ -46,7 +46,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_bytes_decode_b16_h32_d128_r1_
 def decode_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("decode.hip", "common.h"):
+    for f in ("decode.hip", "common.h", "api.hip"):  # the kernels and the split planner
         with open(os.path.join(ROOT, "factorized_kv_cache_tpa_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

