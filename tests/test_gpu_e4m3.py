@@ -170,10 +170,25 @@ def test_prefill_matches_oracle(h, d_h, R_K, R_V, ctx, chunk):
     assert_close(got, ref, w.dtype, "all rows")
 
 
-def test_prefill_fq_matches_oracle():
+# long chunks (more than 256 rows) over an E4M3 cache: several row tiles, ragged ends, unequal ranks
+@pytest.mark.parametrize("h,R_K,R_V,ctx,chunk", [(32, 4, 4, [0, 45], 300), (32, 2, 2, [257], 700),
+                                                 (32, 1, 1, [64, 3], 290), (16, 4, 4, [10], 400),
+                                                 (32, 1, 3, [33], 280)])
+def test_long_chunk_prefill_matches_oracle(h, R_K, R_V, ctx, chunk):
+    w = case_workload(h, 128, R_K, R_V)
+    say(f"case: e4m3 long-chunk prefill h={h} R_K={R_K} R_V={R_V} ctx={ctx} chunk={chunk}")
+    seqs = random_sequences(w, [c + chunk for c in ctx], n_q=chunk, q_scale=2.0, seed=h + chunk + R_V)
+    s = PrefillSetup(w, seqs, ctx, dims=dims_of(w, E4M3))
+    got = s.run()
+    ref = np.stack([s.oracle(b) for b in range(len(seqs))])
+    assert_close(got, ref, w.dtype, "all rows")
+
+
+@pytest.mark.parametrize("chunk", [96, 300])
+def test_prefill_fq_matches_oracle(chunk):
     w = case_workload(32, 128, 4, 4)
     dims = dims_of(w, E4M3)
-    ctx, chunk, R_Q = [100, 0], 96, 6
+    ctx, R_Q = [100, 0], 6
     say("case: e4m3 prefill fq")
     seqs = random_sequences(w, [c + chunk for c in ctx], seed=12)
     cache = FactorCache(dims, [c + chunk for c in ctx])
