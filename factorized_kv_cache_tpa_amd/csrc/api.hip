@@ -162,6 +162,8 @@ int32_t run_prefill(const tpa_dims *dims, const void *cache, int64_t capacity_to
     if (int64_t(max_ctx) + chunk_len > capacity_tokens) return TPA_ERR_CAPACITY;
     const Layout L = layout_of(dims);
     if (!tpa::prefill_supported(L)) return TPA_ERR_UNSUPPORTED;
+    const int64_t groups = (int64_t(chunk_len) + tpa::kPrefillRows - 1) / tpa::kPrefillRows * dims->h * batch;
+    if (groups * tpa::kPrefillThreads > tpa::kMaxGridItems) return TPA_ERR_ARG;
     tpa::PrefillParams p{};
     p.cache = cache;
     p.seq_start = seq_start;
@@ -238,8 +240,9 @@ int32_t tpa_cache_append(const tpa_dims *dims, void *cache, int64_t capacity_tok
         if (!pair_aligned(q_in) || !pair_aligned(q_out)) return TPA_ERR_ARG;
         if (int64_t(q_rows) * dims->d_h > int64_t(1) << 24) return TPA_ERR_ARG;
     }
-    // one work-group per cache token and append_q_groups per query token
-    if (n_kv + (n_q > 0 ? n_q * tpa::append_q_groups(q_rows, dims->d_h) : 0) > int64_t(0x7fffffff))
+    // one work-group per cache token and append_q_groups per query token, in one 1-D launch
+    if ((n_kv + (n_q > 0 ? n_q * tpa::append_q_groups(q_rows, dims->d_h) : 0)) * tpa::kAppendThreads >
+        tpa::kMaxGridItems)
         return TPA_ERR_ARG;
     if (n_kv == 0 && n_q == 0) return TPA_OK;
     float inv_scale[4];
@@ -254,7 +257,7 @@ int32_t tpa_cache_read(const tpa_dims *dims, const void *cache, int64_t capacity
                        const int64_t *slot, void *A_K, void *B_K, void *A_V, void *B_V, void *stream) {
     int32_t st = check_dims(dims);
     if (st != TPA_OK) return st;
-    if (capacity_tokens < 0 || n < 0 || n > int64_t(0x7fffffff)) return TPA_ERR_ARG;
+    if (capacity_tokens < 0 || n < 0 || n * tpa::kAppendThreads > tpa::kMaxGridItems) return TPA_ERR_ARG;
     if (n == 0) return TPA_OK;
     if (!cache || !slot || !A_K || !B_K || !A_V || !B_V) return TPA_ERR_ARG;
     const hipError_t e = tpa::launch_read(layout_of(dims), dims->h, dims->d_h, dims->R_K, dims->R_V, cache,

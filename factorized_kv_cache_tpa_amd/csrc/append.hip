@@ -18,8 +18,6 @@
 namespace tpa {
 namespace {
 
-constexpr int kAppendThreads = 128;
-
 // cos and sin of pos * theta_j for the d_h/2 pairs of one position, shared by the work-group.
 // theta is this thread's theta_j (j = threadIdx.x < d_h/2; d_h/2 <= kAppendThreads), loaded up front.
 template <typename T>

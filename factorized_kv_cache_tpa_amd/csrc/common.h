@@ -44,6 +44,11 @@ namespace tpa {
 
 constexpr int kRows = 32;  // factor rows per cache block
 constexpr int kWave = 64;
+constexpr int kAppendThreads = 128;   // work-items per append / read work-group
+constexpr int kPrefillThreads = 512;  // work-items per prefill work-group
+constexpr int kPrefillRows = 256;     // query rows per prefill work-group (the wide form takes twice as many)
+// A one-dimensional launch counts its work-items (work-groups x work-items per group) in 32 bits.
+constexpr int64_t kMaxGridItems = 0xFFFFFFFFll;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));

@@ -30,8 +30,9 @@ namespace tpa {
 namespace {
 
 constexpr int kPrefillWaves = 8;
-constexpr int kPrefillThreads = kPrefillWaves * kWave;
+static_assert(kPrefillThreads == kPrefillWaves * kWave, "one prefill work-group is 8 waves");
 constexpr int kQT = 32 * kPrefillWaves;  // query rows per work-group
+static_assert(kQT == kPrefillRows, "the launch planner sizes grids by these rows");
 constexpr int kKT = 64;                  // keys per tile
 constexpr float kLazyPrefill = 8.0f;     // headroom of the lazy reference max, log2 units
 constexpr int kXcds = 8;                 // MI355X: 8 XCDs, 32 CUs and one L2 each

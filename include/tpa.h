@@ -54,7 +54,9 @@ extern "C" {
 
 typedef enum tpa_status {
     TPA_OK = 0,
-    TPA_ERR_ARG = 1,         /* null pointer, bad dimension or count, misaligned size */
+    TPA_ERR_ARG = 1,         /* null pointer, bad dimension or count, misaligned size, or a call whose
+                                launch would count more than 2^32 - 1 work-items (append and read: 128
+                                per cache token; prefill: 512 per 256 query rows of one head) */
     TPA_ERR_UNSUPPORTED = 2, /* valid shape with no compiled kernel (see tpa_supported) */
     TPA_ERR_CAPACITY = 3,    /* a slot at or beyond the cache capacity */
     TPA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than tpa_decode_workspace_bytes */

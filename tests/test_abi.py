@@ -201,6 +201,19 @@ def test_append_argument_checks(lib):
                                 None) == 0
 
 
+def test_calls_beyond_one_launch_rejected(lib):
+    """A one-dimensional launch counts work-items in 32 bits: a call that would need more is refused on the
+    host instead of launching a wrapped grid."""
+    d = _d(R_K=4, R_V=4)
+    ref = ctypes.byref(d)
+    n = 1 << 25  # 2^25 tokens x 128 work-items = 2^32
+    assert lib.tpa_cache_append(ref, FAKE, n, n, FAKE, FAKE, n, FAKE, FAKE, FAKE, FAKE, 0, 0, None, None, None,
+                                None) == 1
+    assert lib.tpa_cache_read(ref, FAKE, n, n, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    # 65535 sequences x 2^17 rows x 32 heads: 2^9 row groups per head, 2^9 x 32 x 65535 groups x 512 > 2^32
+    assert lib.tpa_prefill_chunk(ref, FAKE, 1 << 18, 65535, FAKE, FAKE, 0, 1 << 17, FAKE, 0.0, FAKE, None) == 1
+
+
 def test_decode_argument_checks(lib):
     d = _d()
     ref = ctypes.byref(d)
