@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "TPAError", "Dims", "load", "library_path", "tpa_abi_version", "tpa_status_string", "tpa_supported",
     "tpa_block_tokens", "tpa_cache_bytes", "tpa_cache_append", "tpa_cache_read", "tpa_decode_workspace_bytes",
-    "tpa_decode", "tpa_prefill_chunk", "TPA_F32", "TPA_BF16",
+    "tpa_decode", "tpa_decode_step", "tpa_decode_fq", "tpa_prefill_chunk", "tpa_prefill_chunk_fq", "TPA_F32",
+    "TPA_BF16", "TPA_CACHE_NATIVE", "TPA_CACHE_E4M3",
 ]
 
 TPA_F32 = 0
@@ -139,6 +140,27 @@ def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype] = None, name: s
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _numel(t: Optional[torch.Tensor], n: int, name: str) -> None:
+    """The C ABI takes bare pointers, so the binding checks element counts against the documented shapes
+    before any launch: a short output would otherwise be written past its end."""
+    if t is not None and t.numel() != n:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+
+
+def _cache_fits(dims: Dims, cache: torch.Tensor, capacity_tokens: int) -> None:
+    need = tpa_cache_bytes(dims, capacity_tokens)
+    if cache is not None and need > 0 and cache.numel() * cache.element_size() < need:
+        raise ValueError(f"cache has {cache.numel() * cache.element_size()} bytes, a capacity of "
+                         f"{capacity_tokens} tokens needs {need}")
+
+
+def _factor_counts(dims: Dims, n: int, A_K, B_K, A_V, B_V) -> None:
+    _numel(A_K, n * dims.R_K * dims.h, "A_K")
+    _numel(B_K, n * dims.R_K * dims.d_h, "B_K")
+    _numel(A_V, n * dims.R_V * dims.h, "A_V")
+    _numel(B_V, n * dims.R_V * dims.d_h, "B_V")
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -193,6 +215,12 @@ def tpa_cache_append(dims: Dims, cache: torch.Tensor, capacity_tokens: int, slot
             raise ValueError("q_in is required with q_pos")
         q_out = q_in if q_out is None else q_out
         q_rows = q_in.numel() // (n_q * dims.d_h)
+        _numel(q_in, max(q_rows, 1) * n_q * dims.d_h, "q_in")
+        _numel(q_out, q_in.numel(), "q_out")
+    _numel(kv_pos, n_kv, "kv_pos")
+    _factor_counts(dims, n_kv, A_K, B_K, A_V, B_V)
+    if n_kv:
+        _cache_fits(dims, cache, capacity_tokens)
     lib = load()
     st = lib.tpa_cache_append(
         _ref(dims), _ptr(cache, name="cache"), int(capacity_tokens), n_kv, _ptr(slot, torch.int64, "slot"),
@@ -207,6 +235,8 @@ def tpa_cache_read(dims: Dims, cache: torch.Tensor, capacity_tokens: int, slot: 
                    A_K: torch.Tensor, B_K: torch.Tensor, A_V: torch.Tensor, B_V: torch.Tensor, stream=None) -> None:
     """Stored factors of the given slots; uint8 E4M3 codes for an E4M3 cache."""
     dt = dims.cache_torch_dtype
+    _factor_counts(dims, slot.numel(), A_K, B_K, A_V, B_V)
+    _cache_fits(dims, cache, capacity_tokens)
     st = load().tpa_cache_read(_ref(dims), _ptr(cache, name="cache"), int(capacity_tokens), slot.numel(),
                                _ptr(slot, torch.int64, "slot"), _ptr(A_K, dt, "A_K"), _ptr(B_K, dt, "B_K"),
                                _ptr(A_V, dt, "A_V"), _ptr(B_V, dt, "B_V"), _stream(stream))
@@ -217,6 +247,11 @@ def tpa_decode(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_start:
                seq_len: torch.Tensor, max_len: int, q_rot: torch.Tensor, out: torch.Tensor,
                workspace: torch.Tensor, scale: float = 0.0, split_tokens: int = 0, stream=None) -> None:
     """out[b][h][d_h] (fp32) = attention of q_rot[b] over the seq_len[b] cached tokens of sequence b."""
+    batch = seq_start.numel()
+    _numel(seq_len, batch, "seq_len")
+    _numel(q_rot, batch * dims.h * dims.d_h, "q_rot")
+    _numel(out, batch * dims.h * dims.d_h, "out")
+    _cache_fits(dims, cache, capacity_tokens)
     st = load().tpa_decode(
         _ref(dims), _ptr(cache, name="cache"), int(capacity_tokens), seq_start.numel(),
         _ptr(seq_start, torch.int64, "seq_start"), _ptr(seq_len, torch.int32, "seq_len"), int(max_len),
@@ -232,6 +267,12 @@ def tpa_decode_step(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_s
     """One fused decode step: append each sequence's new token at slot seq_start[b] + seq_len[b] (B_K rotated
     there), rotate q[b] at position seq_len[b], and write out[b] = attention over the seq_len[b] + 1 tokens."""
     dt = dims.torch_dtype
+    batch = seq_start.numel()
+    _numel(seq_len, batch, "seq_len")
+    _factor_counts(dims, batch, A_K, B_K, A_V, B_V)
+    _numel(q, batch * dims.h * dims.d_h, "q")
+    _numel(out, batch * dims.h * dims.d_h, "out")
+    _cache_fits(dims, cache, capacity_tokens)
     st = load().tpa_decode_step(
         _ref(dims), _ptr(cache, name="cache"), int(capacity_tokens), seq_start.numel(),
         _ptr(seq_start, torch.int64, "seq_start"), _ptr(seq_len, torch.int32, "seq_len"), int(max_len),
@@ -247,6 +288,13 @@ def tpa_decode_fq(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_sta
     """Factored-query decode: q~[b][i] = (1/R_Q) sum_r A_Q[b][r][i] B_Q_rot[b][r], built on chip, then
     out[b] = attention over the seq_len[b] cached tokens.  A_Q [batch][R_Q][h], B_Q_rot [batch][R_Q][d_h]."""
     dt = dims.torch_dtype
+    batch = seq_start.numel()
+    if A_Q.dim() != 3 or A_Q.shape[0] != batch or A_Q.shape[2] != dims.h:
+        raise ValueError(f"A_Q must be [batch][R_Q][h] = [{batch}][R_Q][{dims.h}], got {list(A_Q.shape)}")
+    _numel(seq_len, batch, "seq_len")
+    _numel(B_Q_rot, batch * A_Q.shape[1] * dims.d_h, "B_Q_rot")
+    _numel(out, batch * dims.h * dims.d_h, "out")
+    _cache_fits(dims, cache, capacity_tokens)
     st = load().tpa_decode_fq(
         _ref(dims), int(A_Q.shape[1]), _ptr(cache, name="cache"), int(capacity_tokens), seq_start.numel(),
         _ptr(seq_start, torch.int64, "seq_start"), _ptr(seq_len, torch.int32, "seq_len"), int(max_len),
@@ -260,6 +308,11 @@ def tpa_prefill_chunk(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq
                       ctx_len: torch.Tensor, max_ctx: int, chunk_len: int, q_rot: torch.Tensor, out: torch.Tensor,
                       scale: float = 0.0, stream=None) -> None:
     """out[b][j][h][d_h] (fp32): causal attention of chunk row j over slots 0 .. ctx_len[b] + j."""
+    batch = seq_start.numel()
+    _numel(ctx_len, batch, "ctx_len")
+    _numel(q_rot, batch * chunk_len * dims.h * dims.d_h, "q_rot")
+    _numel(out, batch * chunk_len * dims.h * dims.d_h, "out")
+    _cache_fits(dims, cache, capacity_tokens)
     st = load().tpa_prefill_chunk(
         _ref(dims), _ptr(cache, name="cache"), int(capacity_tokens), seq_start.numel(),
         _ptr(seq_start, torch.int64, "seq_start"), _ptr(ctx_len, torch.int32, "ctx_len"), int(max_ctx),
@@ -274,6 +327,14 @@ def tpa_prefill_chunk_fq(dims: Dims, cache: torch.Tensor, capacity_tokens: int, 
     """Causal chunk with factored query rows: q~[b][j][i] = (1/R_Q) sum_r A_Q[b][j][r][i] B_Q_rot[b][j][r],
     built on chip.  A_Q [batch][chunk][R_Q][h], B_Q_rot [batch][chunk][R_Q][d_h]."""
     dt = dims.torch_dtype
+    batch = seq_start.numel()
+    if A_Q.dim() != 4 or A_Q.shape[0] != batch or A_Q.shape[1] != chunk_len or A_Q.shape[3] != dims.h:
+        raise ValueError(f"A_Q must be [batch][chunk][R_Q][h] = [{batch}][{chunk_len}][R_Q][{dims.h}], "
+                         f"got {list(A_Q.shape)}")
+    _numel(ctx_len, batch, "ctx_len")
+    _numel(B_Q_rot, batch * chunk_len * A_Q.shape[2] * dims.d_h, "B_Q_rot")
+    _numel(out, batch * chunk_len * dims.h * dims.d_h, "out")
+    _cache_fits(dims, cache, capacity_tokens)
     st = load().tpa_prefill_chunk_fq(
         _ref(dims), int(A_Q.shape[2]), _ptr(cache, name="cache"), int(capacity_tokens), seq_start.numel(),
         _ptr(seq_start, torch.int64, "seq_start"), _ptr(ctx_len, torch.int32, "ctx_len"), int(max_ctx),

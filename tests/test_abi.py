@@ -348,3 +348,55 @@ def test_prefill_fq_argument_checks(lib):
     f32 = _d(h=4, d_h=16, dtype="f32")
     assert lib.tpa_prefill_chunk_fq(ctypes.byref(f32), 2, FAKE, 8192, 1, FAKE, FAKE, 64, 8, FAKE, FAKE, 0.0, FAKE,
                                     None) == 2  # prefill is bf16 only
+
+
+def test_binding_checks_shapes_before_any_launch():
+    """The binding compares element counts with the documented shapes (the C ABI sees bare pointers) and
+    raises before touching the device; host tensors are enough to exercise it."""
+    import torch
+
+    d = tpa.Dims(32, 128, 2, 2, "bf16")
+    cap = 64
+    cache = torch.empty(tpa.tpa_cache_bytes(d, cap), dtype=torch.uint8)
+    start = torch.zeros(2, dtype=torch.int64)
+    lens = torch.full((2,), 10, dtype=torch.int32)
+    q = torch.empty(2, 32, 128, dtype=torch.bfloat16)
+    out = torch.empty(2, 32, 128, dtype=torch.float32)
+    ws = torch.empty(1 << 20, dtype=torch.uint8)
+    f = lambda n, R, w: torch.empty(n, R, w, dtype=torch.bfloat16)  # noqa: E731
+    with pytest.raises(ValueError, match="out has"):
+        tpa.tpa_decode(d, cache, cap, start, lens, 10, q, out[:, :, :64], ws)
+    with pytest.raises(ValueError, match="q_rot has"):
+        tpa.tpa_decode(d, cache, cap, start, lens, 10, q[:1], out, ws)
+    with pytest.raises(ValueError, match="seq_len has"):
+        tpa.tpa_decode(d, cache, cap, start, lens[:1], 10, q, out, ws)
+    with pytest.raises(ValueError, match="cache has"):
+        tpa.tpa_decode(d, cache[:1000], cap, start, lens, 10, q, out, ws)
+    with pytest.raises(ValueError, match="B_V has"):
+        tpa.tpa_decode_step(d, cache, cap, start, lens, 10, f(2, 2, 32), f(2, 2, 128), f(2, 2, 32), f(2, 1, 128),
+                            q, out, ws)
+    with pytest.raises(ValueError, match="A_Q must be"):
+        tpa.tpa_decode_fq(d, cache, cap, start, lens, 10, f(2, 3, 16), f(2, 3, 128), out, ws)
+    with pytest.raises(ValueError, match="B_Q_rot has"):
+        tpa.tpa_decode_fq(d, cache, cap, start, lens, 10, f(2, 3, 32), f(2, 2, 128), out, ws)
+    chunk = 5
+    qp = torch.empty(2, chunk, 32, 128, dtype=torch.bfloat16)
+    outp = torch.empty(2, chunk, 32, 128, dtype=torch.float32)
+    with pytest.raises(ValueError, match="out has"):
+        tpa.tpa_prefill_chunk(d, cache, cap, start, lens, 10, chunk, qp, outp[:, :4])
+    with pytest.raises(ValueError, match="q_rot has"):
+        tpa.tpa_prefill_chunk(d, cache, cap, start, lens, 10, chunk + 1, qp, outp)
+    with pytest.raises(ValueError, match="A_Q must be"):
+        tpa.tpa_prefill_chunk_fq(d, cache, cap, start, lens, 10, chunk,
+                                 torch.empty(2, chunk, 3, 32, 1, dtype=torch.bfloat16), qp, outp)
+    slot = torch.zeros(3, dtype=torch.int64)
+    pos = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="A_K has"):
+        tpa.tpa_cache_append(d, cache, cap, slot, pos, f(2, 2, 32), f(3, 2, 128), f(3, 2, 32), f(3, 2, 128))
+    with pytest.raises(ValueError, match="kv_pos has"):
+        tpa.tpa_cache_append(d, cache, cap, slot, pos[:2], f(3, 2, 32), f(3, 2, 128), f(3, 2, 32), f(3, 2, 128))
+    with pytest.raises(ValueError, match="q_in has"):
+        tpa.tpa_cache_append(d, cache, cap, slot[:0], pos[:0], f(0, 2, 32), f(0, 2, 128), f(0, 2, 32),
+                             f(0, 2, 128), q_pos=pos, q_in=torch.empty(3, 2, 100, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="B_K has"):
+        tpa.tpa_cache_read(d, cache, cap, slot, f(3, 2, 32), f(3, 1, 128), f(3, 2, 32), f(3, 2, 128))
