@@ -26,7 +26,11 @@ def test_tiny_fp32_workload():
 @pytest.mark.parametrize("h,d_h,R_K,R_V,dtype", [
     (32, 128, 1, 1, ti.BF16), (32, 128, 2, 2, ti.BF16), (32, 128, 4, 4, ti.BF16), (16, 64, 2, 2, ti.BF16),
     (16, 64, 1, 1, ti.BF16), (32, 64, 1, 3, ti.BF16), (4, 16, 1, 1, ti.F32), (16, 32, 2, 2, ti.F32),
-    (32, 128, 3, 1, ti.F32), (20, 48, 2, 2, ti.BF16), (6, 30, 1, 2, ti.F32)])
+    (32, 128, 3, 1, ti.F32), (20, 48, 2, 2, ti.BF16), (6, 30, 1, 2, ti.F32),
+    # the remaining compiled (padded heads, padded head dim) pairs: 64 heads, head dim 32, and the
+    # fp32 pairs not covered above
+    (64, 64, 1, 1, ti.BF16), (56, 32, 2, 2, ti.BF16), (16, 128, 2, 2, ti.BF16), (8, 64, 1, 1, ti.F32),
+    (24, 32, 2, 1, ti.F32), (12, 128, 1, 1, ti.F32), (30, 64, 2, 2, ti.F32)])
 @pytest.mark.parametrize("q_scale", [1.0, 12.0])
 def test_small_shapes_ragged(h, d_h, R_K, R_V, dtype, q_scale):
     """Several blocks per split and a ragged tail; q_scale 12 sharpens the softmax."""

@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 E4M3 = tpa.TPA_CACHE_E4M3
 SHAPES = [(32, 128, 1, 1), (32, 128, 2, 2), (32, 128, 4, 4), (16, 64, 2, 2), (16, 64, 1, 1), (32, 64, 1, 3),
-          (20, 48, 2, 2)]
+          (20, 48, 2, 2), (64, 64, 1, 1), (56, 32, 2, 2), (16, 128, 2, 2)]
 
 
 def _read_codes(dims, cache, n):
@@ -159,7 +159,8 @@ def test_decode_fq_matches_oracle():
 
 @pytest.mark.parametrize("h,d_h,R_K,R_V,ctx,chunk", [(32, 128, 4, 4, [100], 64), (16, 64, 1, 1, [37, 0], 300),
                                                      (32, 128, 1, 1, [0, 70], 33), (20, 48, 1, 3, [65], 40),
-                                                     (16, 64, 2, 2, [200, 5], 130)])
+                                                     (16, 64, 2, 2, [200, 5], 130), (64, 64, 1, 1, [40], 90),
+                                                     (16, 128, 2, 2, [70, 0], 100)])
 def test_prefill_matches_oracle(h, d_h, R_K, R_V, ctx, chunk):
     w = case_workload(h, d_h, R_K, R_V)
     say(f"case: e4m3 prefill h={h} d_h={d_h} R_K={R_K} R_V={R_V} ctx={ctx} chunk={chunk}")

@@ -8,7 +8,8 @@ from tests.gpu_cases import (DecodeSetup, PrefillSetup, assert_close, case_workl
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("h,d_h,R", [(32, 128, 4), (32, 128, 1), (16, 64, 2), (20, 48, 3)])
+@pytest.mark.parametrize("h,d_h,R", [(32, 128, 4), (32, 128, 1), (16, 64, 2), (20, 48, 3), (16, 128, 2), (64, 64, 1),
+                                     (56, 64, 4)])
 @pytest.mark.parametrize("ctx,chunk", [([0, 45, 300], 70), ([64, 2], 160), ([257], 129)])
 @pytest.mark.parametrize("q_scale", [1.0, 10.0])
 def test_small_chunks(h, d_h, R, ctx, chunk, q_scale):
