@@ -219,7 +219,7 @@ def test_prefill_fq_matches_oracle(chunk):
 
 from tests.test_gpu_step import StepSetup, check_record_is_what_append_writes  # noqa: E402
 
-STEP_SHAPES = [(32, 128, 1, 1), (16, 64, 2, 2), (32, 128, 4, 4), (20, 48, 1, 3)]
+STEP_SHAPES = [(32, 128, 1, 1), (16, 64, 2, 2), (32, 128, 4, 4), (20, 48, 1, 3), (64, 64, 1, 1), (16, 128, 2, 2)]
 
 
 @pytest.mark.parametrize("h,d_h,R_K,R_V", STEP_SHAPES)

@@ -57,7 +57,8 @@ class FQSetup:
 
 CASES = [(32, 128, 1, 1, ti.BF16, 1e4, 1), (32, 128, 1, 1, ti.BF16, 1e4, 6), (32, 128, 2, 2, ti.BF16, 5e5, 16),
          (16, 64, 2, 2, ti.BF16, 1e4, 3), (20, 48, 1, 3, ti.BF16, 1e4, 2), (4, 16, 1, 1, ti.F32, 1e4, 2),
-         (32, 128, 3, 2, ti.F32, 5e5, 16)]
+         (32, 128, 3, 2, ti.F32, 5e5, 16), (64, 64, 2, 2, ti.BF16, 1e4, 4), (56, 32, 2, 2, ti.BF16, 1e4, 5),
+         (16, 128, 2, 2, ti.F32, 1e4, 3)]
 
 
 @pytest.mark.parametrize("h,d_h,R_K,R_V,dtype,base,R_Q", CASES)
@@ -119,7 +120,8 @@ def test_fq_full_size_decode_b16_h32_d128_r1_n4096_rq6():
 
 @pytest.mark.parametrize("h,d_h,R_K,R_V,R_Q,ctx,chunk", [(32, 128, 4, 4, 6, 100, 64), (16, 64, 2, 2, 3, [37, 0], 300),
                                                           (32, 128, 4, 4, 6, [5, 130], 400),
-                                                          (32, 128, 1, 1, 1, 0, 33), (20, 48, 1, 3, 16, 65, 40)])
+                                                          (32, 128, 1, 1, 1, 0, 33), (20, 48, 1, 3, 16, 65, 40),
+                                                          (64, 64, 1, 1, 4, [20, 3], 80), (16, 128, 2, 2, 5, 40, 300)])
 def test_prefill_fq_matches_oracle(h, d_h, R_K, R_V, R_Q, ctx, chunk):
     """Causal chunk with factored query rows (row j at position ctx + j sees tokens 0 .. ctx + j)."""
     w = case_workload(h, d_h, R_K, R_V, ti.BF16)

@@ -55,7 +55,9 @@ class StepSetup:
 
 
 SHAPES = [(32, 128, 1, 1, ti.BF16, 1e4), (16, 64, 2, 2, ti.BF16, 1e4), (32, 128, 4, 4, ti.BF16, 5e5),
-          (20, 48, 1, 3, ti.BF16, 1e4), (4, 16, 1, 1, ti.F32, 1e4), (32, 128, 3, 2, ti.F32, 5e5)]
+          (20, 48, 1, 3, ti.BF16, 1e4), (4, 16, 1, 1, ti.F32, 1e4), (32, 128, 3, 2, ti.F32, 5e5),
+          (64, 64, 1, 1, ti.BF16, 1e4), (56, 32, 2, 2, ti.BF16, 1e4), (16, 128, 2, 2, ti.BF16, 5e5),
+          (30, 64, 2, 1, ti.F32, 1e4)]
 
 
 @pytest.mark.parametrize("h,d_h,R_K,R_V,dtype,base", SHAPES)
