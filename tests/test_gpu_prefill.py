@@ -99,3 +99,36 @@ def test_wide_unequal_ranks(R_K, R_V):
     out = s.run()
     ref = np.stack([s.oracle(b) for b in range(len(seqs))])
     assert_close(out, ref, w.dtype, "all rows")
+
+
+@pytest.mark.parametrize("chunk", [120, 300])
+def test_graph_replay_matches_eager(chunk):
+    """Query RoPE (tpa_cache_append) + tpa_prefill_chunk recorded in a HIP graph (both prefill forms):
+    every replay, with eager work in between, equals the eager result bit for bit."""
+    import torch
+
+    import factorized_kv_cache_tpa_amd as tpa
+    from factorized_kv_cache_tpa_amd.cache import to_device
+    w = case_workload(32, 128, 2, 2)
+    say(f"case: prefill graph replay chunk={chunk}")
+    ctx = [64, 200]
+    seqs = random_sequences(w, [c + chunk for c in ctx], n_q=chunk, q_scale=2.0, seed=chunk + 5)
+    s = PrefillSetup(w, seqs, ctx)
+    eager = s.run()
+    q = to_device(np.stack([x.q for x in seqs]), s.dims).reshape(len(seqs) * chunk, w.h, w.d_h)
+    q_pos = torch.tensor(np.concatenate([c + np.arange(chunk) for c in ctx]), dtype=torch.int32, device="cuda")
+    q_rot = torch.empty_like(q)
+    out = torch.empty(len(seqs), chunk, w.h, w.d_h, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        s.cache.rotate_queries(q, q_pos, q_out=q_rot)
+        tpa.tpa_prefill_chunk(s.dims, s.cache.buf, s.cache.capacity, s.cache.seq_start, s.ctx_len, max(ctx), chunk,
+                              q_rot.view(len(seqs), chunk, w.h, w.d_h), out)
+    for k in range(3):
+        out.fill_(float("nan"))
+        q_rot.zero_()
+        _ = (torch.randn(1000, device="cuda") * 2).sum().item()  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager), f"replay {k}"
