@@ -244,8 +244,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     using Stage = std::conditional_t<kF8, StageF8, StageNative>;
     const uint32_t off_op = uint32_t(lane * E * sizeof(T));  // operand lane offset, bytes (native)
     const uint32_t off_gt = uint32_t(lane * 4 * sizeof(T));  // gate lane offset, bytes (native)
-    auto load = [&](Stage &st, int blk) {
-        const char *bp = seq + int64_t(blk) * BLK * CES;
+    auto load = [&](Stage &st, int blk, bool real = true) {
+        const char *bp = real ? seq + int64_t(blk) * BLK * CES : reinterpret_cast<const char *>(p.cache);
         if constexpr (kF8) {
             const char *op = bp + lane * 16;
             const char *gt = bp + lane * 8;
@@ -377,13 +377,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     // may read): a wave with a single block reads one block twice, but the loads then sit in fixed
     // program order, so the compiler can wait for each stage exactly instead of draining every load in
     // flight at the top of the pipelined loop below.
-    // (Outside a fused step every work-group that gets here has a block; a fused step's split 0 of an
-    // empty sequence has none and loads nothing, a branch that leaves that mode's waits conservative.)
+    // (Outside a fused step every work-group that gets here has a block.  A fused step's split 0 of an
+    // empty sequence has none: its stages read the cache's first block instead and never use it, so that
+    // no load sits behind a branch, which would leave every wait of the mode conservative.)
     const int last_blk = blk_end - 1;
     const bool any_blk = !kStep || blk_end > blk_begin;
-    auto load_clamped = [&](Stage &st, int b) {
-        if (any_blk) load(st, b < last_blk ? b : last_blk);
-    };
+    auto load_clamped = [&](Stage &st, int b) { load(st, b < last_blk ? b : last_blk, any_blk); };
     if (kTwoStages) {  // start streaming the first two blocks before anything else (a fused step issues
                        // the second after its own set-up: a wave cannot pass its loads' issue until most of
                        // them have landed, so work placed behind both stages would wait for the stream)
