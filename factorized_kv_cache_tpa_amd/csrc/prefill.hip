@@ -439,6 +439,9 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
         __builtin_amdgcn_sched_barrier(0);  // the next loads stay below the rebuild that frees their registers
         const int kn = min(kt + 1 + int(late), n_kt - 1);  // tile whose loads are issued now
         const int key0 = kt * kKT;
+        // the matrix-core phase runs at a higher wave priority than the rebuild, so when both waves of a
+        // SIMD can issue, the one feeding the matrix cores goes first
+        __builtin_amdgcn_s_setprio(3);
         {
             const uint16_t *cK = sK[buf];
             const uint16_t *cV = sV[buf];
@@ -518,6 +521,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
                 __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // global loads
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         if (!late && kt + 1 < n_kt) rebuild_tile(raw, kt + 1, buf ^ 1);
         __syncthreads();
     }
@@ -865,6 +869,9 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
         __builtin_amdgcn_sched_barrier(0);
         const int kf = min(kt + 1 + int(late), n_kt - 1);  // tile whose pieces are fetched now
         const int key0 = kt * kKT2;
+        // the matrix-core phase runs at a higher wave priority than the rebuild, so when both waves of a
+        // SIMD can issue, the one feeding the matrix cores goes first
+        __builtin_amdgcn_s_setprio(3);
         {
             const uint16_t *cK = lds.k[buf];
             const uint16_t *cV = lds.v[buf];
@@ -945,6 +952,7 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         if (!late && kt + 1 < n_kt) rebuild_tile(kt + 1, buf ^ 1);
         __syncthreads();
     }
