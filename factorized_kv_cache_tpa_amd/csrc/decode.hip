@@ -825,19 +825,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 
 }
 
-// Second pass: merge the per-split partials.  One work-group per (head, sequence);
+// Second pass: merge the per-split partials.  One work-group of kThr threads per (head, sequence);
 // thread t owns output columns 4 (t % C4) .. +3 and the splits j = t / C4 (mod JL),
-// where C4 = DP / 4 and JL = 256 / C4.  Each thread folds its splits with the
+// where C4 = DP / 4 and JL = kThr / C4.  Each thread folds its splits with the
 // same rescaling rule, loads issued eight at a time, and the JL lanes of a column
 // group are folded once more through LDS.  (A fused step's new token is already part
-// of split 0's partial.)
-constexpr int kMergeThreads = 256;
+// of split 0's partial.)  The launch takes 128 threads when every lane then has one round of
+// loads (a short call: the smaller work-group finishes sooner), else 256.
 constexpr int kMergeUnroll = 8;
 
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p, int HP, int DP, int TOK) {
-    __shared__ float sm[kMergeThreads][6];
+template <int kThr>
+__global__ __launch_bounds__(kThr) void decode_merge_kernel(DecodeParams p, int HP, int DP, int TOK) {
+    __shared__ float sm[kThr][6];
     const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int C4 = DP / 4, JL = kMergeThreads / C4;
+    const int C4 = DP / 4, JL = kThr / C4;
     const int c4 = tid % C4, jl = tid / C4;
     // Every split wrote a partial (an empty one has max -inf), so the loads below do not wait on the
     // sequence's length; only its start is read, for the misaligned case.
@@ -977,8 +978,12 @@ hipError_t launch_decode(const Layout &L, const DecodeParams &p, hipStream_t s) 
     TPA_DECODE_SHAPES(X)
 #undef X
     if (!found || e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(L.HP, p.batch), dim3(kMergeThreads), 0, s, p, L.HP, L.DP,
-                       L.tok_per_block());
+    if (p.n_split <= (128 / (L.DP / 4)) * kMergeUnroll)
+        hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(L.HP, p.batch), dim3(128), 0, s, p, L.HP, L.DP,
+                           L.tok_per_block());
+    else
+        hipLaunchKernelGGL(decode_merge_kernel<256>, dim3(L.HP, p.batch), dim3(256), 0, s, p, L.HP, L.DP,
+                           L.tok_per_block());
     return hipGetLastError();
 }
 
