@@ -136,10 +136,10 @@ class DecodeBench:
         self.out = torch.empty(self.batch, w.h, w.d_h, dtype=torch.float32, device="cuda")
         self.bytes = decode_bytes(w, self.lens, 1 if self.e4m3 else None)
         self.step_bytes = step_bytes(w, self.lens, 1 if self.e4m3 else None)
-        # a rank-6 factored query (full TPA), its B_Q rows rotated at the query position
+        # a rank-6 factored query (full TPA), unrotated: the kernel builds and rotates it at the query position
         self.R_Q = 6
         self.A_Q = mk((self.batch, self.R_Q, w.h), 1.0)
-        self.B_Q_rot = self.cache.rotate_queries(mk((self.batch, self.R_Q, w.d_h), 1 / np.sqrt(w.d_h)), self.pos)
+        self.B_Q = mk((self.batch, self.R_Q, w.d_h), 1 / np.sqrt(w.d_h))
 
     def step(self, i: int, out=None):
         """One fused decode step on cache replica i % n_rep (tpa_decode_step)."""
@@ -151,7 +151,7 @@ class DecodeBench:
     def decode_fq(self, r: int, out=None):
         """tpa_decode_fq over replica r: the same cache with a rank-R_Q factored query (built on chip)."""
         self.tpa.tpa_decode_fq(self.dims, self.cache.buf, self.cache.capacity, self.rep_start[r], self.seq_len,
-                               self.max_len, self.A_Q, self.B_Q_rot, self.out if out is None else out, self.ws)
+                               self.max_len, self.A_Q, self.B_Q, self.out if out is None else out, self.ws)
 
     def step_two_call(self, i: int):
         """The same step as two calls: append the new token + rotate the query, then decode the cached tokens."""
@@ -281,21 +281,19 @@ def prefill_bench(steps: int, warmup: int, cache_format: int = 0):
     ctx_len = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
     out = torch.empty(B, chunk, w.h, w.d_h, dtype=torch.float32, device="cuda")
 
-    # the same chunk with rank-6 factored query rows (full TPA), B_Q rows rotated at ctx + j
+    # the same chunk with rank-6 factored query rows (full TPA), unrotated (row j is rotated at ctx + j on chip)
     R_Q = 6
     rng = np.random.default_rng(w.seed + 6)
     mk = lambda shape, sig: to_device(ti.to_storage(rng.standard_normal(shape, dtype=np.float32) * sig, w.dtype),
                                       dims)
     A_Q = mk((B, chunk, R_Q, w.h), 1.0)
-    B_Q_rot = cache.rotate_queries(mk((B * chunk, R_Q, w.d_h), 1 / np.sqrt(w.d_h)), q_pos).reshape(B, chunk, R_Q,
-                                                                                                   w.d_h)
+    B_Q = mk((B, chunk, R_Q, w.d_h), 1 / np.sqrt(w.d_h))
 
     def call():
         tpa.tpa_prefill_chunk(dims, cache.buf, cache.capacity, cache.seq_start, ctx_len, ctx, chunk, q_rot, out)
 
     def call_fq():
-        tpa.tpa_prefill_chunk_fq(dims, cache.buf, cache.capacity, cache.seq_start, ctx_len, ctx, chunk, A_Q, B_Q_rot,
-                                 out)
+        tpa.tpa_prefill_chunk_fq(dims, cache.buf, cache.capacity, cache.seq_start, ctx_len, ctx, chunk, A_Q, B_Q, out)
 
     def timed(fn) -> float:
         for _ in range(warmup):

@@ -283,22 +283,23 @@ def tpa_decode_step(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_s
 
 
 def tpa_decode_fq(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_start: torch.Tensor,
-                  seq_len: torch.Tensor, max_len: int, A_Q: torch.Tensor, B_Q_rot: torch.Tensor, out: torch.Tensor,
+                  seq_len: torch.Tensor, max_len: int, A_Q: torch.Tensor, B_Q: torch.Tensor, out: torch.Tensor,
                   workspace: torch.Tensor, scale: float = 0.0, split_tokens: int = 0, stream=None) -> None:
-    """Factored-query decode: q~[b][i] = (1/R_Q) sum_r A_Q[b][r][i] B_Q_rot[b][r], built on chip, then
-    out[b] = attention over the seq_len[b] cached tokens.  A_Q [batch][R_Q][h], B_Q_rot [batch][R_Q][d_h]."""
+    """Factored-query decode: q~[b][i] = RoPE at seq_len[b] of (1/R_Q) sum_r A_Q[b][r][i] B_Q[b][r], built on
+    chip, then out[b] = attention over the seq_len[b] cached tokens.  A_Q [batch][R_Q][h], B_Q [batch][R_Q][d_h]
+    (unrotated)."""
     dt = dims.torch_dtype
     batch = seq_start.numel()
     if A_Q.dim() != 3 or A_Q.shape[0] != batch or A_Q.shape[2] != dims.h:
         raise ValueError(f"A_Q must be [batch][R_Q][h] = [{batch}][R_Q][{dims.h}], got {list(A_Q.shape)}")
     _numel(seq_len, batch, "seq_len")
-    _numel(B_Q_rot, batch * A_Q.shape[1] * dims.d_h, "B_Q_rot")
+    _numel(B_Q, batch * A_Q.shape[1] * dims.d_h, "B_Q")
     _numel(out, batch * dims.h * dims.d_h, "out")
     _cache_fits(dims, cache, capacity_tokens)
     st = load().tpa_decode_fq(
         _ref(dims), int(A_Q.shape[1]), _ptr(cache, name="cache"), int(capacity_tokens), seq_start.numel(),
         _ptr(seq_start, torch.int64, "seq_start"), _ptr(seq_len, torch.int32, "seq_len"), int(max_len),
-        _ptr(A_Q, dt, "A_Q"), _ptr(B_Q_rot, dt, "B_Q_rot"), float(scale), _ptr(out, torch.float32, "out"),
+        _ptr(A_Q, dt, "A_Q"), _ptr(B_Q, dt, "B_Q"), float(scale), _ptr(out, torch.float32, "out"),
         int(split_tokens), _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "tpa_decode_fq")
@@ -322,22 +323,23 @@ def tpa_prefill_chunk(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq
 
 
 def tpa_prefill_chunk_fq(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_start: torch.Tensor,
-                         ctx_len: torch.Tensor, max_ctx: int, chunk_len: int, A_Q: torch.Tensor, B_Q_rot: torch.Tensor,
+                         ctx_len: torch.Tensor, max_ctx: int, chunk_len: int, A_Q: torch.Tensor, B_Q: torch.Tensor,
                          out: torch.Tensor, scale: float = 0.0, stream=None) -> None:
-    """Causal chunk with factored query rows: q~[b][j][i] = (1/R_Q) sum_r A_Q[b][j][r][i] B_Q_rot[b][j][r],
-    built on chip.  A_Q [batch][chunk][R_Q][h], B_Q_rot [batch][chunk][R_Q][d_h]."""
+    """Causal chunk with factored query rows: q~[b][j][i] = RoPE at ctx_len[b] + j of
+    (1/R_Q) sum_r A_Q[b][j][r][i] B_Q[b][j][r], built on chip.  A_Q [batch][chunk][R_Q][h],
+    B_Q [batch][chunk][R_Q][d_h] (unrotated)."""
     dt = dims.torch_dtype
     batch = seq_start.numel()
     if A_Q.dim() != 4 or A_Q.shape[0] != batch or A_Q.shape[1] != chunk_len or A_Q.shape[3] != dims.h:
         raise ValueError(f"A_Q must be [batch][chunk][R_Q][h] = [{batch}][{chunk_len}][R_Q][{dims.h}], "
                          f"got {list(A_Q.shape)}")
     _numel(ctx_len, batch, "ctx_len")
-    _numel(B_Q_rot, batch * chunk_len * A_Q.shape[2] * dims.d_h, "B_Q_rot")
+    _numel(B_Q, batch * chunk_len * A_Q.shape[2] * dims.d_h, "B_Q")
     _numel(out, batch * chunk_len * dims.h * dims.d_h, "out")
     _cache_fits(dims, cache, capacity_tokens)
     st = load().tpa_prefill_chunk_fq(
         _ref(dims), int(A_Q.shape[2]), _ptr(cache, name="cache"), int(capacity_tokens), seq_start.numel(),
         _ptr(seq_start, torch.int64, "seq_start"), _ptr(ctx_len, torch.int32, "ctx_len"), int(max_ctx),
-        int(chunk_len), _ptr(A_Q, dt, "A_Q"), _ptr(B_Q_rot, dt, "B_Q_rot"), float(scale),
+        int(chunk_len), _ptr(A_Q, dt, "A_Q"), _ptr(B_Q, dt, "B_Q"), float(scale),
         _ptr(out, torch.float32, "out"), _stream(stream))
     _check(st, "tpa_prefill_chunk_fq")

@@ -3,7 +3,11 @@
 Sequences get consecutive slots starting at a block boundary (the library's
 layout groups ``tpa_block_tokens()`` slots per block), so slot
 ``seq_start[b] + j`` holds token j of sequence b, at position j.  All data
-movement into the cache goes through ``tpa_cache_append``.
+movement into the cache goes through ``tpa_cache_append``.  Each sequence owns
+the capacity it was given and no more: an append past it raises instead of
+writing into the next sequence's slots.  A fused decode step
+(``tpa_decode_step``) writes the token at slot ``seq_start[b] + seq_len[b]``,
+so it needs one free slot per sequence.
 """
 from __future__ import annotations
 
@@ -33,10 +37,13 @@ class FactorCache:
         starts: List[int] = []
         pos = 0
         for cap in capacities:
+            if int(cap) < 0:
+                raise ValueError("negative sequence capacity")
             starts.append(pos)
             pos += (int(cap) + self.block - 1) // self.block * self.block
         self.capacity = max(pos, self.block)
         self.starts = starts
+        self.capacities = [int(c) for c in capacities]
         nbytes = tpa_cache_bytes(dims, self.capacity)
         self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
         if fill_byte is not None:
@@ -52,6 +59,9 @@ class FactorCache:
     def append(self, b: int, A_K: torch.Tensor, B_K: torch.Tensor, A_V: torch.Tensor, B_V: torch.Tensor,
                first_pos: int = 0, stream=None) -> None:
         n = A_K.shape[0]
+        if first_pos < 0 or first_pos + n > self.capacities[b]:
+            raise ValueError(f"sequence {b}: tokens {first_pos}..{first_pos + n - 1} do not fit its capacity of "
+                             f"{self.capacities[b]} tokens")
         pos = torch.arange(first_pos, first_pos + n, dtype=torch.int32, device=self.device)
         slot = pos.to(torch.int64) + self.starts[b]
         tpa_cache_append(self.dims, self.buf, self.capacity, slot, pos, A_K, B_K, A_V, B_V,

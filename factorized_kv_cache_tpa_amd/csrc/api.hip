@@ -122,6 +122,7 @@ int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
     p.seq_len = seq_len;
     p.q = q;
     p.out = out;
+    p.capacity = capacity_tokens;
     p.ws_o = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + P.off_o);
     p.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + P.off_ml);
     p.h = dims->h;
@@ -139,8 +140,9 @@ int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
         p.step = 1;
         p.st = *step;
         for (int k = 0; k < 4; ++k) p.st.inv_scale[k] = float(1.0 / factor_scale(dims, k));
-        p.rope = tpa::make_rope_table(dims->d_h, dims->rope_base);
     }
+    // the fused step rotates its query, the factored query its built query row, at position seq_len[b]
+    if (step || r_q > 0) p.rope = tpa::make_rope_table(dims->d_h, dims->rope_base);
     p.r_q = r_q;
     p.a_q = a_q;
     const hipError_t e = tpa::launch_decode(L, p, as_stream(stream));
@@ -148,7 +150,7 @@ int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
 }
 
 // tpa_prefill_chunk and tpa_prefill_chunk_fq: host checks, then the prefill kernel.  r_q > 0: q holds the
-// rotated query feature factors and a_q the query head factors.
+// unrotated query feature factors and a_q the query head factors.
 int32_t run_prefill(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
                     const int64_t *seq_start, const int32_t *ctx_len, int32_t max_ctx, int32_t chunk_len, const void *q,
                     float scale, float *out, void *stream, int32_t r_q, const void *a_q) {
@@ -170,6 +172,7 @@ int32_t run_prefill(const tpa_dims *dims, const void *cache, int64_t capacity_to
     p.ctx_len = ctx_len;
     p.q = q;
     p.out = out;
+    p.capacity = capacity_tokens;
     p.h = dims->h;
     p.d_h = dims->d_h;
     p.RK = dims->R_K;
@@ -182,6 +185,7 @@ int32_t run_prefill(const tpa_dims *dims, const void *cache, int64_t capacity_to
     p.out_mul = float(factor_scale(dims, 2) * factor_scale(dims, 3) / dims->R_V);
     p.r_q = r_q;
     p.a_q = a_q;
+    if (r_q > 0) p.rope = tpa::make_rope_table(dims->d_h, dims->rope_base);
     const hipError_t e = tpa::launch_prefill(L, p, as_stream(stream));
     return e == hipSuccess ? TPA_OK : TPA_ERR_HIP;
 }
@@ -298,13 +302,13 @@ int32_t tpa_decode_step(const tpa_dims *dims, void *cache, int64_t capacity_toke
 
 int32_t tpa_decode_fq(const tpa_dims *dims, int32_t R_Q, const void *cache, int64_t capacity_tokens, int32_t batch,
                       const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *A_Q,
-                      const void *B_Q_rot, float scale, float *out, int32_t split_tokens, void *workspace,
+                      const void *B_Q, float scale, float *out, int32_t split_tokens, void *workspace,
                       int64_t workspace_bytes, void *stream) {
     const int32_t st = check_dims(dims);
     if (st != TPA_OK) return st;
     if (R_Q < 1 || R_Q > 16) return TPA_ERR_ARG;
     if (batch > 0 && !A_Q) return TPA_ERR_ARG;
-    return run_decode(dims, cache, capacity_tokens, batch, seq_start, seq_len, max_len, B_Q_rot, scale, out,
+    return run_decode(dims, cache, capacity_tokens, batch, seq_start, seq_len, max_len, B_Q, scale, out,
                       split_tokens, workspace, workspace_bytes, stream, nullptr, R_Q, A_Q);
 }
 
@@ -317,13 +321,13 @@ int32_t tpa_prefill_chunk(const tpa_dims *dims, const void *cache, int64_t capac
 
 int32_t tpa_prefill_chunk_fq(const tpa_dims *dims, int32_t R_Q, const void *cache, int64_t capacity_tokens,
                              int32_t batch, const int64_t *seq_start, const int32_t *ctx_len, int32_t max_ctx,
-                             int32_t chunk_len, const void *A_Q, const void *B_Q_rot, float scale, float *out,
+                             int32_t chunk_len, const void *A_Q, const void *B_Q, float scale, float *out,
                              void *stream) {
     const int32_t st = check_dims(dims);
     if (st != TPA_OK) return st;
     if (R_Q < 1 || R_Q > 16) return TPA_ERR_ARG;
     if (batch > 0 && chunk_len > 0 && !A_Q) return TPA_ERR_ARG;
-    return run_prefill(dims, cache, capacity_tokens, batch, seq_start, ctx_len, max_ctx, chunk_len, B_Q_rot, scale,
+    return run_prefill(dims, cache, capacity_tokens, batch, seq_start, ctx_len, max_ctx, chunk_len, B_Q, scale,
                        out, stream, R_Q, A_Q);
 }
 

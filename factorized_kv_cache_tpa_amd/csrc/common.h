@@ -248,6 +248,7 @@ struct DecodeParams {
     float *out;     // [batch][h][d_h]
     float *ws_o;    // [batch][n_split][HP][DP]
     float *ws_ml;   // [batch][n_split][HP][2]
+    int64_t capacity;  // cache slots: a sequence reaching past them (or misaligned) gets NaN output
     int h, d_h, RK, RV;
     int batch, max_len, split_blocks, n_split;
     float score_mul;  // scale * log2(e) / R_K
@@ -257,8 +258,8 @@ struct DecodeParams {
     int step;
     StepInputs st;
     RopeTable rope;
-    // Factored query (tpa_decode_fq) when r_q > 0: q holds B~_Q [batch][r_q][d_h] (rotated), a_q holds
-    // A_Q [batch][r_q][h].
+    // Factored query (tpa_decode_fq) when r_q > 0: q holds B_Q [batch][r_q][d_h] (unrotated; the built
+    // query is rotated at position seq_len[b] with the rope table), a_q holds A_Q [batch][r_q][h].
     int r_q;
     const void *a_q;
 };
@@ -269,15 +270,25 @@ struct PrefillParams {
     const int32_t *ctx_len;
     const void *q;  // [batch][chunk][h][d_h]
     float *out;     // [batch][chunk][h][d_h]
+    int64_t capacity;  // cache slots: a sequence reaching past them (or misaligned) gets NaN output
     int h, d_h, RK, RV;
     int batch, chunk, max_ctx;
     float score_mul;  // scale * log2(e) / R_K
     float out_mul;    // 1 / R_V
-    // Factored query (tpa_prefill_chunk_fq) when r_q > 0: q holds B~_Q [batch][chunk][r_q][d_h] (rotated),
-    // a_q holds A_Q [batch][chunk][r_q][h].
+    // Factored query (tpa_prefill_chunk_fq) when r_q > 0: q holds B_Q [batch][chunk][r_q][d_h] (unrotated;
+    // row j's built query is rotated at position ctx_len[b] + j with the rope table), a_q holds
+    // A_Q [batch][chunk][r_q][h].
     int r_q;
     const void *a_q;
+    RopeTable rope;
 };
+
+// A sequence the kernels refuse to read: its first slot is negative or not at a block boundary, or its
+// slots [start, start + n_slots) reach past the cache's capacity.  Such a sequence gets NaN output and no
+// slot of it is read or written (the host can only check sizes; starts and lengths live in device memory).
+__host__ __device__ inline bool seq_rejected(int64_t start, int64_t n_slots, int tok_per_block, int64_t capacity) {
+    return start < 0 || start % tok_per_block != 0 || start > capacity - n_slots;
+}
 
 // Host: theta_j = base^(-2j/d_h) in fp64 (zeros past d_h/2).
 RopeTable make_rope_table(int d_h, double base);

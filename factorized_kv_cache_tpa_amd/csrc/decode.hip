@@ -155,7 +155,8 @@ __device__ __forceinline__ float wave_sum_across_groups(float x) {
 // Query modes, each its own instantiation so the plain decode carries none of the others:
 //   kQRot  -- q arrives rotated (tpa_decode);
 //   kStep  -- a fused step: q arrives unrotated, split 0 carries the new token (tpa_decode_step);
-//   kQFact -- q arrives as factors A_Q, B~_Q (B~_Q rotated), q~ = (1/R_Q) A_Q^T B~_Q (tpa_decode_fq).
+//   kQFact -- q arrives as factors A_Q, B_Q (unrotated), q~ = RoPE((1/R_Q) A_Q^T B_Q) at position len
+//             (tpa_decode_fq).
 constexpr int kQRot = 0, kStepMode = 1, kQFact = 2;
 constexpr int kMaxRQ = 16;  // query rank limit of the factored mode
 
@@ -183,13 +184,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     __shared__ float sm_m[kWaves + 1][HP];
     __shared__ float sm_l[kWaves + 1][HP];
     __shared__ __attribute__((aligned(16))) float sm_o[kWaves][HP][DP + 4];
-    constexpr int SH = kStep ? HP : 1, SD = kStep ? DP : 2;
+    constexpr int SH = kStep ? HP : 1, SD = (kStep || kFact) ? DP : 2;
     // factored query: A_Q, B~_Q staged as fp32, then q~ built once per work-group (element type)
     constexpr int QR = kFact ? kMaxRQ : 1, QH = kFact ? HP : 4, QD = kFact ? DP : 4;
     __shared__ __attribute__((aligned(16))) float sm_aq[QR][QH];
     __shared__ __attribute__((aligned(16))) float sm_bq[QR][QD];
     __shared__ __attribute__((aligned(16))) T sm_q[QH][QD + 8];
-    __shared__ F sm_cs[SD];             // fused step: cos/sin of the query's position
+    __shared__ F sm_cs[SD];             // fused step, factored query: cos/sin of the query's position
     __shared__ float sm_na[2][RH][SH];  // fused step, split 0: the new token's A_K, A_V
     __shared__ __attribute__((aligned(16))) float sm_nb[2][RH][SD];  // ... its B_K, B_V (unrotated)
     __shared__ float sm_wt[SH];         // ... and the weight of its value row per head (in-group merge)
@@ -207,18 +208,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
     const int nblk = (len + TOK - 1) / TOK;
     const int blk_begin = split * p.split_blocks;
-    const bool misaligned = start < 0 || start % TOK != 0;
+    // A sequence that is misaligned, or whose slots (a fused step: and the new token's slot) reach past
+    // the capacity, is not read at all: NaN output.
+    const bool rejected = seq_rejected(start, int64_t(len) + (kStep ? 1 : 0), TOK, p.capacity);
     // A fused step's split 0 carries the step's new token (even over an empty sequence): it writes the
     // token's record and folds the token's own score and value into its partial.
-    const bool new_tok = kStep && split == 0 && !misaligned;
+    const bool new_tok = kStep && split == 0 && !rejected;
     // ... and the sequence's last split with tokens (split 0 for an empty sequence) writes its record, so
     // the two extra jobs land on different work-groups
     const int last_split = nblk > 0 ? min(p.n_split - 1, (nblk - 1) / p.split_blocks) : 0;
-    const bool rec_tok = kStep && split == last_split && !misaligned;
-    if (misaligned || (blk_begin >= nblk && !new_tok)) {
-        // A split with no tokens (past the sequence's end, or the sequence is empty or misaligned) marks
-        // its partial empty (max -inf, sum 0), so the merge kernel can read every split without first
-        // reading the sequence lengths; the merge writes zeros (empty) or NaN (misaligned).
+    const bool rec_tok = kStep && split == last_split && !rejected;
+    if (rejected || (blk_begin >= nblk && !new_tok)) {
+        // A split with no tokens (past the sequence's end, or the sequence is empty or rejected) marks
+        // its partial empty (max -inf, sum 0), so the merge kernel can read every split without waiting
+        // for anything else; the merge writes zeros (empty) or NaN (rejected).
         const int64_t part = int64_t(b) * p.n_split + split;
         for (int head = threadIdx.x; head < HP; head += kThreads)
             *reinterpret_cast<float2 *>(p.ws_ml + (part * HP + head) * 2) = make_float2(-INFINITY, 0.f);
@@ -331,11 +334,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         sm_m[kWaves][head] = -INFINITY;
         sm_l[kWaves][head] = 0.f;
     }
-    // fused step: this thread's RoPE frequency (pair j = tid), read now for the same reason
-    const double theta_j = kStep && tid < DP / 2 ? p.rope.theta[tid] : 0.0;
+    // fused step, factored query: this thread's RoPE frequency (pair j = tid), read now for the same reason
+    const double theta_j = (kStep || kFact) && tid < DP / 2 ? p.rope.theta[tid] : 0.0;
 
-    // Factored query: this thread's share of A_Q (row-major [R_Q][h]) and B~_Q ([R_Q][d_h]), loaded
-    // before the stream for the same reason; elements past the real sizes are zeros.
+    // Factored query: this thread's share of A_Q (row-major [R_Q][h]) and B_Q ([R_Q][d_h], unrotated),
+    // loaded before the stream for the same reason; elements past the real sizes are zeros.
     constexpr int QA_PER = kFact ? (kMaxRQ * HP + kThreads - 1) / kThreads : 1;
     constexpr int QB_PER = kFact ? (kMaxRQ * DP + kThreads - 1) / kThreads : 1;
     float qa_raw[QA_PER], qb_raw[QB_PER];
@@ -390,11 +393,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         if (kMode == kQRot) load_clamped(s1, blk + kWaves);
     }
     if constexpr (kFact) {
-        // Factored query, while the first blocks stream in: q~[i][d] = (1/R_Q) sum_r A_Q[r][i] B~_Q[r][d]
-        // (TPA notes page, tensor product decomposition applied to Q; B~_Q was rotated at the query's
-        // position, which commutes with the combination since RoPE is linear), computed once per
-        // work-group in 4 x 4 register tiles from LDS, rounded once to the element type, and read back as
-        // this lane's fragments.
+        // Factored query, while the first blocks stream in: q[i][d] = (1/R_Q) sum_r A_Q[r][i] B_Q[r][d]
+        // (TPA notes page, tensor product decomposition applied to Q), computed once per work-group in
+        // 4 x 4 register tiles from LDS, then rotated to the query's position len (RoPE is linear, so
+        // rotating the combined row equals combining rotated B_Q rows: RoPE compatibility), all in fp32
+        // (fp64 for fp32 queries), rounded once to the element type, and read back as this lane's
+        // fragments.
+        if (tid < DP / 2) rope_cos_sin<T>(sm_cs + 2 * tid, double(len), theta_j);
 #pragma unroll
         for (int k = 0; k < QA_PER; ++k) {
             const int idx = tid + k * kThreads;
@@ -419,16 +424,22 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 #pragma unroll
                     for (int j = 0; j < 4; ++j) a4[i][j] = fmaf(ar[i], br[j], a4[i][j]);
             }
+            // features d0 .. d0 + 3 are the rotary pairs d0 / 2 and d0 / 2 + 1
+            const F c0 = sm_cs[d0], s0 = sm_cs[d0 + 1], c1 = sm_cs[d0 + 2], s1 = sm_cs[d0 + 3];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
+                F y[4];
+                rope_rotate(F(a4[i][0]), F(a4[i][1]), c0, s0, y[0], y[1]);
+                rope_rotate(F(a4[i][2]), F(a4[i][3]), c1, s1, y[2], y[3]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float x = a4[i][j] * inv_rq;
+                    const float x = float(y[j] * F(inv_rq));
                     if constexpr (sizeof(T) == 2)
                         sm_q[h0 + i][d0 + j] = uint16_t(pack_bf16x2(x, 0.f) & 0xffffu);
                     else
                         sm_q[h0 + i][d0 + j] = x;
                 }
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -841,9 +852,11 @@ __global__ __launch_bounds__(kThr) void decode_merge_kernel(DecodeParams p, int 
     const int C4 = DP / 4, JL = kThr / C4;
     const int c4 = tid % C4, jl = tid / C4;
     // Every split wrote a partial (an empty one has max -inf), so the loads below do not wait on the
-    // sequence's length; only its start is read, for the misaligned case.
+    // sequence's start and length; those only decide the rejected case (the split kernel's predicate).
     const int64_t start = p.seq_start[b];
-    const bool misaligned = start < 0 || start % TOK != 0;
+    int len = p.seq_len[b];
+    len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
+    const bool rejected = seq_rejected(start, int64_t(len) + (p.step ? 1 : 0), TOK, p.capacity);
     const int n_valid = p.n_split;
 
     float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
@@ -900,7 +913,7 @@ __global__ __launch_bounds__(kThr) void decode_merge_kernel(DecodeParams p, int 
         M = Mn;
     }
     float o[4] = {o0, o1, o2, o3};
-    if (misaligned) {
+    if (rejected) {
         o[0] = o[1] = o[2] = o[3] = __builtin_nanf("");
     } else if (L == 0.f) {  // no tokens
         o[0] = o[1] = o[2] = o[3] = 0.f;

@@ -53,6 +53,66 @@ __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_c
 // LDS position of tile key k inside the value contraction's key order
 __device__ __forceinline__ int vpos(int k) { return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3); }
 
+// Factored query row (tpa_prefill_chunk_fq): the MFMA B-operand fragments of query row jq that a lane of
+// a 32x32x16 product supplies (features 16 ks + 8 hi + e, e < 8):
+//     q[d] = (1/R_Q) sum_r A_Q[jq][r][head] B_Q[jq][r][d]    (TPA notes page, tensor product decomposition
+//                                                             applied to Q)
+// summed in fp32, then rotated to the row's position pos with the append's arithmetic (fp64 angle
+// reduction, fp32 rotation; RoPE is linear, so rotating the combined row equals combining rotated B_Q
+// rows), and rounded once to bf16.  Rows past the chunk are zeros.
+template <int KS>
+__device__ __forceinline__ void factored_query_row(const PrefillParams &p, int b, int jq, int head, int hi, int pos,
+                                                   bf16x8 *qf) {
+    float x[KS][8] = {};
+    if (jq < p.chunk) {
+        const int64_t row = int64_t(b) * p.chunk + jq;
+        const uint16_t *aq = reinterpret_cast<const uint16_t *>(p.a_q) + row * p.r_q * p.h + head;
+        const uint16_t *bq = reinterpret_cast<const uint16_t *>(p.q) + row * p.r_q * p.d_h;
+        for (int r = 0; r < p.r_q; ++r) {
+            const float a = bf16_to_f32(aq[r * p.h]);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int d0 = 16 * ks + 8 * hi;
+                if ((p.d_h & 7) == 0) {
+                    if (d0 < p.d_h) {
+                        const uint4 v = *reinterpret_cast<const uint4 *>(bq + r * p.d_h + d0);
+                        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            x[ks][e] = fmaf(a, __uint_as_float((e & 1) ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16)),
+                                            x[ks][e]);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (d0 + e < p.d_h) x[ks][e] = fmaf(a, bf16_to_f32(bq[r * p.d_h + d0 + e]), x[ks][e]);
+                }
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const int d = 16 * ks + 8 * hi + e;  // even: the pair (d, d + 1)
+                if (d < p.d_h) {
+                    float cs[2];
+                    rope_cos_sin<uint16_t>(cs, double(pos), p.rope.theta[d >> 1]);
+                    float y0, y1;
+                    rope_rotate(x[ks][e], x[ks][e + 1], cs[0], cs[1], y0, y1);
+                    x[ks][e] = y0;
+                    x[ks][e + 1] = y1;
+                }
+            }
+    }
+    const float inv_rq = 1.f / float(p.r_q);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[ks][e] *= inv_rq;
+        qf[ks] = pack8(x[ks]);
+    }
+}
+
 // kFQ: the query rows arrive as factors (tpa_prefill_chunk_fq), a separate instantiation.
 // The double-buffered K~ and V^T tiles (row strides padded by 8 elements against bank conflicts).
 template <int DP>
@@ -105,7 +165,8 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
     ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
     float *out = p.out + int64_t(b) * p.chunk * p.h * p.d_h;
 
-    if (start < 0 || start % TOK != 0) {  // misaligned sequence: report NaN
+    // a misaligned sequence, or one whose context and chunk reach past the capacity: NaN, nothing read
+    if (seq_rejected(start, int64_t(ctx) + p.chunk, TOK, p.capacity)) {
         for (int idx = tid; idx < kQT * p.d_h; idx += kPrefillThreads) {
             const int j = j0 + idx / p.d_h, d = idx % p.d_h;
             if (j < p.chunk) out[(int64_t(j) * p.h + head) * p.d_h + d] = __builtin_nanf("");
@@ -345,42 +406,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
     // Q operand (B of S^T): lane supplies Q~[jq][16 ks + 8 hi + e]
     bf16x8 qf[KS];
     if constexpr (kFQ) {
-        // factored query: Q~[jq][d] = (1/R_Q) sum_r A_Q[jq][r][head] B~_Q[jq][r][d] (TPA notes page, tensor
-        // product decomposition applied to Q; B~_Q rotated at the row's position), fp32 sums, one rounding
-        float x[KS][8] = {};
-        if (jq < p.chunk) {
-            const int64_t row = int64_t(b) * p.chunk + jq;
-            const uint16_t *aq = reinterpret_cast<const uint16_t *>(p.a_q) + row * p.r_q * p.h + head;
-            const uint16_t *bq = reinterpret_cast<const uint16_t *>(p.q) + row * p.r_q * p.d_h;
-            for (int r = 0; r < p.r_q; ++r) {
-                const float a = bf16_to_f32(aq[r * p.h]);
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const int d0 = 16 * ks + 8 * hi;
-                    if ((p.d_h & 7) == 0) {
-                        if (d0 < p.d_h) {
-                            const uint4 v = *reinterpret_cast<const uint4 *>(bq + r * p.d_h + d0);
-                            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                x[ks][e] = fmaf(a, __uint_as_float((e & 1) ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16)),
-                                                x[ks][e]);
-                        }
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (d0 + e < p.d_h) x[ks][e] = fmaf(a, bf16_to_f32(bq[r * p.d_h + d0 + e]), x[ks][e]);
-                    }
-                }
-            }
-        }
-        const float inv_rq = 1.f / float(p.r_q);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[ks][e] *= inv_rq;
-            qf[ks] = pack8(x[ks]);
-        }
+        factored_query_row<KS>(p, b, jq, head, hi, ctx + jq, qf);
     } else {
         const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) + (int64_t(b) * p.chunk + jq) * p.h * p.d_h +
                                int64_t(head) * p.d_h;
@@ -630,7 +656,7 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
     ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
     float *out = p.out + int64_t(b) * p.chunk * p.h * p.d_h;
 
-    if (start < 0 || start % TOK != 0) {
+    if (seq_rejected(start, int64_t(ctx) + p.chunk, TOK, p.capacity)) {  // as in the 256-row form
         for (int idx = tid; idx < kQT2 * p.d_h; idx += kPrefillThreads) {
             const int j = j0 + idx / p.d_h, d = idx % p.d_h;
             if (j < p.chunk) out[(int64_t(j) * p.h + head) * p.d_h + d] = __builtin_nanf("");
@@ -802,32 +828,7 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
         if constexpr (kFQ) {
-            float x[KS][8] = {};
-            if (jq[nb] < p.chunk) {
-                const int64_t row = int64_t(b) * p.chunk + jq[nb];
-                const uint16_t *aq = reinterpret_cast<const uint16_t *>(p.a_q) + row * p.r_q * p.h + head;
-                const uint16_t *bq = reinterpret_cast<const uint16_t *>(p.q) + row * p.r_q * p.d_h;
-                for (int r = 0; r < p.r_q; ++r) {
-                    const float a = bf16_to_f32(aq[r * p.h]);
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        const int d0 = 16 * ks + 8 * hi;
-                        const uint4 v = *reinterpret_cast<const uint4 *>(bq + r * p.d_h + d0);
-                        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            x[ks][e] = fmaf(a, __uint_as_float((e & 1) ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16)),
-                                            x[ks][e]);
-                    }
-                }
-            }
-            const float inv_rq = 1.f / float(p.r_q);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[ks][e] *= inv_rq;
-                qf[nb][ks] = pack8(x[ks]);
-            }
+            factored_query_row<KS>(p, b, jq[nb], head, hi, ctx + jq[nb], qf[nb]);
         } else {
             const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) +
                                    (int64_t(b) * p.chunk + jq[nb]) * p.h * p.d_h + int64_t(head) * p.d_h;

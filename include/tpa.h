@@ -30,8 +30,11 @@
  *   - Every call returns a tpa_status.  All argument checks run on the host
  *     before any HIP call; a rejected call launches nothing.  TPA_ERR_HIP
  *     reports a failed launch (hipGetLastError).  Values held in device
- *     memory (slots, lengths) cannot be checked on the host; what the
- *     kernels do with bad ones is stated per entry point.
+ *     memory (slots, starts, lengths) cannot be checked on the host; the
+ *     kernels check them against capacity_tokens: an append skips a slot
+ *     outside the cache, and a decode or prefill sequence whose slots are
+ *     not all inside it (or whose start is not a block boundary) gets NaN
+ *     output while no slot outside the cache is read or written.
  *
  * Cache layout (opaque; written by tpa_cache_append, read back by
  * tpa_cache_read).  Tokens are grouped into blocks of tpa_block_tokens()
@@ -50,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TPA_ABI_VERSION 2
+#define TPA_ABI_VERSION 3
 
 typedef enum tpa_status {
     TPA_OK = 0,
@@ -160,9 +163,12 @@ int64_t tpa_decode_workspace_bytes(const tpa_dims *dims, int32_t batch, int32_t 
  *     out[b][i] = sum_s softmax_s(scale * q~_b,i . K~_s[i,:]) V_s[i,:]
  * over s = 0 .. seq_len[b]-1, with K~_s, V_s from the cached factors.
  *   seq_start[batch]  int64 first slot of each sequence; must be a multiple of
- *                     tpa_block_tokens() (a misaligned sequence gets NaN output)
+ *                     tpa_block_tokens()
  *   seq_len[batch]    int32 cached tokens of each sequence (0 gives a zero output;
  *                     values above max_len are clamped to max_len)
+ *                     A sequence with a misaligned start, or with
+ *                     seq_start + seq_len > capacity_tokens, gets NaN output and
+ *                     none of its slots is read (checked on the device).
  *   max_len           [host] >= every seq_len; sizes the launch
  *   q_rot [batch][h][d_h]  queries already rotated to their positions (tpa_cache_append)
  *   scale             softmax scale; <= 0 selects 1/sqrt(d_h)
@@ -173,7 +179,7 @@ int64_t tpa_decode_workspace_bytes(const tpa_dims *dims, int32_t batch, int32_t 
  *                     (running max, sum, unnormalized output) between the split kernel and the
  *                     merge kernel.  One workspace serves one call at a time: calls that overlap
  *                     on it race.
- * Slots of a sequence must lie inside the cache (seq_start + max_len <= capacity). */
+ * max_len <= capacity_tokens, else TPA_ERR_CAPACITY. */
 int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
                    const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *q_rot,
                    float scale, float *out, int32_t split_tokens, void *workspace, int64_t workspace_bytes,
@@ -195,7 +201,8 @@ int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
  *   seq_len[batch]     cached tokens before the step; not modified (the caller advances it)
  *   max_len [host]     >= every seq_len; max_len + 1 <= capacity_tokens (TPA_ERR_CAPACITY otherwise)
  * Other arguments, the workspace (tpa_decode_workspace_bytes(dims, batch, max_len, split_tokens)) and the
- * error behaviour are those of tpa_decode; a slot at or past the capacity is not written. */
+ * error behaviour are those of tpa_decode, except that the new token's slot must also be inside the cache
+ * (seq_start + seq_len + 1 <= capacity_tokens, else NaN output and nothing written). */
 int32_t tpa_decode_step(const tpa_dims *dims, void *cache, int64_t capacity_tokens, int32_t batch,
                         const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *A_K,
                         const void *B_K, const void *A_V, const void *B_V, const void *q, float scale, float *out,
@@ -203,46 +210,55 @@ int32_t tpa_decode_step(const tpa_dims *dims, void *cache, int64_t capacity_toke
 
 /* Factored-query decode (full TPA: the query is factorized like K and V; TPA notes page, tensor product
  * decomposition, and its ablation's Q+K+V-factorized variant).  Per sequence b and head i the query row is
- *     q~_b,i = (1/R_Q) sum_r A_Q[b][r][i] B~_Q[b][r][:]
- * built on chip (fp32 sums, one rounding to dtype, never in device memory), then the same attention as
- * tpa_decode over the seq_len[b] cached tokens.  B~_Q is the query feature factor already rotated to the
- * query's position (tpa_cache_append with q_rows = R_Q): RoPE is linear, so rotating the factor rows is
- * rotating the query (RoPE compatibility).
- *   R_Q [host]                 query rank, 1..16 (TPA_ERR_ARG otherwise)
- *   A_Q [batch][R_Q][h]        query head factor
- *   B_Q_rot [batch][R_Q][d_h]  rotated query feature factor (16-byte aligned)
+ *     q~_b,i = RoPE_N((1/R_Q) sum_r A_Q[b][r][i] B_Q[b][r][:]),   N = seq_len[b]
+ * built on chip and never in device memory: fp32 sums, the rotation at the query's position N with the
+ * append's arithmetic (RoPE is linear, so rotating the combined row is rotating the factor rows: RoPE
+ * compatibility), one rounding to dtype.  Then the same attention as tpa_decode over the N cached tokens.
+ *   R_Q [host]             query rank, 1..16 (TPA_ERR_ARG otherwise)
+ *   A_Q [batch][R_Q][h]    query head factor
+ *   B_Q [batch][R_Q][d_h]  query feature factor, unrotated (16-byte aligned)
  * Other arguments, the workspace (tpa_decode_workspace_bytes) and the error behaviour are tpa_decode's. */
 int32_t tpa_decode_fq(const tpa_dims *dims, int32_t R_Q, const void *cache, int64_t capacity_tokens, int32_t batch,
                       const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *A_Q,
-                      const void *B_Q_rot, float scale, float *out, int32_t split_tokens, void *workspace,
+                      const void *B_Q, float scale, float *out, int32_t split_tokens, void *workspace,
                       int64_t workspace_bytes, void *stream);
 
 /* Causal chunked prefill: chunk_len query rows per sequence attend to the
  * sequence's cached context and to the chunk's own tokens up to and including
  * their own (the chunk's factors must already be in the cache, appended at
  * slots seq_start[b] + ctx_len[b] + j).  Row j of sequence b sees slots
- * seq_start[b] + 0 .. seq_start[b] + ctx_len[b] + j.  K~ and V for one head
- * are rebuilt from the factors on chip, never in device memory.
+ * seq_start[b] + 0 .. seq_start[b] + ctx_len[b] + j:
+ *     out[b][j][i] = sum_{s <= ctx_len[b] + j} softmax_s(scale * q~_b,j,i . K~_s[i,:]) V_s[i,:]
+ * The pages state no prefill algorithm: they give the factor form of K and V
+ * (tensor product decomposition), RoPE on the B factors (RoPE compatibility)
+ * and the principle that attention is computed from the factors without
+ * materializing K and V (FlashTPA).  This entry point applies them to a chunk
+ * of query rows under the textbook causal mask: K~ and V for one head are
+ * rebuilt from the factors on chip, never in device memory.
  *   ctx_len[batch]   int32 cached tokens before the chunk (<= max_ctx)
- *   max_ctx          [host] >= every ctx_len
+ *   max_ctx          [host] >= every ctx_len; max_ctx + chunk_len <= capacity_tokens
+ *                    (TPA_ERR_CAPACITY otherwise)
  *   chunk_len        [host] rows per sequence
  *   q_rot [batch][chunk_len][h][d_h]  rotated query rows (row j at position ctx_len[b] + j)
  *   out   [batch][chunk_len][h][d_h]  fp32
+ * A sequence with a misaligned start, or with seq_start + ctx_len + chunk_len >
+ * capacity_tokens, gets NaN rows and none of its slots is read.
  * Currently bf16 only (TPA_ERR_UNSUPPORTED for fp32). */
 int32_t tpa_prefill_chunk(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
                           const int64_t *seq_start, const int32_t *ctx_len, int32_t max_ctx, int32_t chunk_len,
                           const void *q_rot, float scale, float *out, void *stream);
 
-/* Causal chunked prefill with factored query rows (full TPA; the factored form of tpa_decode_fq): row j
- * of sequence b has q~_b,j,i = (1/R_Q) sum_r A_Q[b][j][r][i] B~_Q[b][j][r][:], built on chip, then the
- * attention of tpa_prefill_chunk.
- *   R_Q [host]                            query rank, 1..16
- *   A_Q [batch][chunk_len][R_Q][h]        query head factors
- *   B_Q_rot [batch][chunk_len][R_Q][d_h]  query feature factors rotated at ctx_len[b] + j (16-byte aligned)
+/* Causal chunked prefill with factored query rows (full TPA, TPA notes page, tensor product decomposition
+ * applied to Q; the factored form of tpa_decode_fq): row j of sequence b has
+ *     q~_b,j,i = RoPE_{ctx_len[b]+j}((1/R_Q) sum_r A_Q[b][j][r][i] B_Q[b][j][r][:])
+ * built on chip (fp32 sums and rotation, one rounding to bf16), then the attention of tpa_prefill_chunk.
+ *   R_Q [host]                        query rank, 1..16
+ *   A_Q [batch][chunk_len][R_Q][h]    query head factors
+ *   B_Q [batch][chunk_len][R_Q][d_h]  query feature factors, unrotated (16-byte aligned)
  * Other arguments and the error behaviour are tpa_prefill_chunk's. */
 int32_t tpa_prefill_chunk_fq(const tpa_dims *dims, int32_t R_Q, const void *cache, int64_t capacity_tokens,
                              int32_t batch, const int64_t *seq_start, const int32_t *ctx_len, int32_t max_ctx,
-                             int32_t chunk_len, const void *A_Q, const void *B_Q_rot, float scale, float *out,
+                             int32_t chunk_len, const void *A_Q, const void *B_Q, float scale, float *out,
                              void *stream);
 
 #ifdef __cplusplus

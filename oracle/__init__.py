@@ -164,6 +164,23 @@ def e4m3_encode(x) -> np.ndarray:
     return out
 
 
+def round_to_bf16(x) -> np.ndarray:
+    """Nearest bf16 value of each fp64 value, ties to even (returned as fp64).  The storage format of a bf16
+    cache: 8 significant bits, the fp32 exponent range.  Computed as round-to-odd to fp32 (truncate, then set
+    the last bit when inexact), which keeps the two guard bits that the final round to nearest even needs,
+    so the result equals a direct rounding of x.  Finite inputs inside the fp32 range."""
+    v = _f64(x)
+    t = v.astype(np.float32)
+    # truncate toward zero: step back one fp32 unit where the fp32 rounding went past |x|
+    over = np.abs(t.astype(np.float64)) > np.abs(v)
+    t = np.where(over, np.nextafter(t, np.float32(0)), t)
+    bits = t.view(np.uint32).copy()
+    inexact = t.astype(np.float64) != v
+    bits |= inexact.astype(np.uint32)  # round to odd
+    rne = (bits + np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return rne.view(np.float32).astype(np.float64)
+
+
 def factor_elems_per_token(h: int, d: int, RK: int, RV: int) -> int:
     return int(_load().tpa_oracle_factor_elems_per_token(h, d, RK, RV))
 

@@ -1,14 +1,13 @@
 """Shared set-up for the GPU parity tests: build a factor cache through the C ABI
 from seeded inputs, run decode / prefill, and compare with the fp64 oracle.
 
-Tolerances (element-wise over the whole output tensor):
-  bf16 factors, fp32 accumulation: max-abs <= 1e-2 * M and rel-L2 <= 5e-3
-  fp32 inputs:                     max-abs <= 1e-5 * M and rel-L2 <= 1e-5
-with M = max(1, max|oracle|).  For the five measured workloads the outputs are
-below 0.1 in magnitude, so M = 1 and these are the plain absolute bounds.  Small
-stress cases (few tokens, rank 1, sharpened softmax) reach outputs of 3..10,
-where a bf16 value itself is only defined to +-0.03; there the absolute bound
-scales with the output magnitude, i.e. the same relative precision.
+Tolerances (element-wise over the whole output tensor), the stated ones:
+  bf16 factors, fp32 accumulation: max-abs <= 1e-2 and rel-L2 <= 5e-3
+  fp32 inputs:                     max-abs <= 1e-5 and rel-L2 <= 1e-5
+Every case meets the rel-L2 bound.  A few stress cases (rank-1 factors, whose
+outputs reach |5..10|, under a sharpened softmax or with few visible tokens)
+exceed the max-abs bound; each is marked, with its measured error and the
+cause, as an expected failure of that bound alone (``known_max_abs_excess``).
 """
 from __future__ import annotations
 
@@ -16,6 +15,7 @@ import sys
 from typing import List, Optional, Sequence
 
 import numpy as np
+import pytest
 import torch
 
 import factorized_kv_cache_tpa_amd as tpa
@@ -43,14 +43,51 @@ def errors(gpu: np.ndarray, ref: np.ndarray):
     return max_abs, rel
 
 
+class MaxAbsExceeded(AssertionError):
+    """The output meets the rel-L2 bound but not the max-abs bound."""
+
+
 def assert_close(gpu, ref, dtype: str, what: str = ""):
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
     max_abs, rel = errors(gpu, ref)
     tol_abs, tol_rel = TOL[dtype]
-    mag = max(1.0, float(np.abs(ref).max())) if np.size(ref) else 1.0
-    tol_abs *= mag
-    say(f"  {what}: max_abs={max_abs:.3e} (bound {tol_abs:.1e}) rel_l2={rel:.3e}")
-    assert max_abs <= tol_abs and rel <= tol_rel, f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}"
+    say(f"  {what}: max_abs={max_abs:.3e} (bound {tol_abs:.1e}) rel_l2={rel:.3e} (bound {tol_rel:.1e})")
+    assert rel <= tol_rel, f"{what}: rel_l2={rel:.3e} > {tol_rel:.1e} (max_abs={max_abs:.3e})"
+    if max_abs > tol_abs:
+        raise MaxAbsExceeded(f"{what}: max_abs={max_abs:.3e} > {tol_abs:.1e} (rel_l2={rel:.3e})")
+
+
+class Checks:
+    """Runs several assert_close checks and raises a max-abs excess only after all of them, so that every
+    rel-L2 check of a test runs even where one comparison exceeds the max-abs bound."""
+
+    def __init__(self):
+        self.excess = []
+
+    def close(self, gpu, ref, dtype: str, what: str = "") -> None:
+        try:
+            assert_close(gpu, ref, dtype, what)
+        except MaxAbsExceeded as e:
+            self.excess.append(str(e))
+
+    def done(self) -> None:
+        if self.excess:
+            raise MaxAbsExceeded("; ".join(self.excess))
+
+
+# Causes of the known max-abs excesses (the measured figures are in each test's table).
+STORAGE_CAUSE = ("sharpened softmax over rank-1 factors (outputs up to |5..7|): the bf16 storage of the rotated "
+                 "B_K and of the rotated query alone moves the exact output by more than 1e-2 "
+                 "(tests/test_storage_rounding.py shows it on the CPU, with no kernel involved)")
+REBUILD_CAUSE = ("prefill rebuilds rank-1 K~ and V rows (|V| up to ~10) and rounds them to bf16 for the matrix "
+                 "cores: 2^-9 of the output where few tokens carry the softmax")
+
+
+def known_max_abs_excess(request, measured: str, cause: str) -> None:
+    """Mark the running test as an expected failure of the max-abs bound alone: a rel-L2 miss, a non-finite
+    output or any other error still fails it, and so does a pass (strict), so the list stays current."""
+    request.applymarker(pytest.mark.xfail(raises=MaxAbsExceeded, strict=True,
+                                          reason=f"measured {measured}; cause: {cause}"))
 
 
 def f64(a, dtype):
@@ -81,12 +118,14 @@ class DecodeSetup:
         self.max_len = max(self.lens) if self.lens else 0
 
     def run(self, split_tokens: int = 0, scale: float = 0.0, seq_start: Optional[torch.Tensor] = None,
-            seq_len: Optional[torch.Tensor] = None, max_len: Optional[int] = None) -> np.ndarray:
+            seq_len: Optional[torch.Tensor] = None, max_len: Optional[int] = None,
+            capacity: Optional[int] = None) -> np.ndarray:
+        """capacity: the capacity the call declares (default the cache's own)."""
         max_len = self.max_len if max_len is None else max_len
         ws_bytes = tpa.tpa_decode_workspace_bytes(self.dims, self.batch, max_len, split_tokens)
         ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
         out = torch.full((self.batch, self.w.h, self.w.d_h), float("nan"), dtype=torch.float32, device="cuda")
-        tpa.tpa_decode(self.dims, self.cache.buf, self.cache.capacity,
+        tpa.tpa_decode(self.dims, self.cache.buf, self.cache.capacity if capacity is None else capacity,
                        self.cache.seq_start if seq_start is None else seq_start,
                        self.seq_len if seq_len is None else seq_len, max_len, self.q_rot, out, ws, scale=scale,
                        split_tokens=split_tokens)
@@ -108,7 +147,7 @@ class PrefillSetup:
     """Cache holding ctx + chunk tokens per sequence, rotated chunk query rows."""
 
     def __init__(self, w: ti.Workload, seqs: Sequence[ti.Sequence], ctx: Sequence[int],
-                 dims: Optional[tpa.Dims] = None):
+                 dims: Optional[tpa.Dims] = None, extra_capacity: int = 0):
         self.w = w
         self.dims = dims_of(w) if dims is None else dims
         self.seqs = list(seqs)
@@ -116,7 +155,7 @@ class PrefillSetup:
         self.chunk = self.seqs[0].q.shape[0]
         assert all(s.q.shape[0] == self.chunk for s in self.seqs)
         assert all(s.n_tokens == c + self.chunk for s, c in zip(self.seqs, self.ctx))
-        self.cache = FactorCache(self.dims, [s.n_tokens for s in self.seqs])
+        self.cache = FactorCache(self.dims, [s.n_tokens + extra_capacity for s in self.seqs])
         for b, s in enumerate(self.seqs):
             self.cache.append_host(b, s.A_K, s.B_K, s.A_V, s.B_V)
         q = np.stack([s.q for s in self.seqs])  # [batch][chunk][h][d]
@@ -127,11 +166,13 @@ class PrefillSetup:
                                                                       self.w.d_h)
         self.ctx_len = torch.tensor(self.ctx, dtype=torch.int32, device="cuda")
 
-    def run(self, scale: float = 0.0, seq_start=None) -> np.ndarray:
+    def run(self, scale: float = 0.0, seq_start=None, capacity: Optional[int] = None) -> np.ndarray:
+        """capacity: the capacity the call declares (default the cache's own)."""
         out = torch.full((len(self.seqs), self.chunk, self.w.h, self.w.d_h), float("nan"), dtype=torch.float32,
                          device="cuda")
         starts = self.cache.seq_start if seq_start is None else seq_start
-        tpa.tpa_prefill_chunk(self.dims, self.cache.buf, self.cache.capacity, starts, self.ctx_len,
+        cap = self.cache.capacity if capacity is None else capacity
+        tpa.tpa_prefill_chunk(self.dims, self.cache.buf, cap, starts, self.ctx_len,
                               max(self.ctx), self.chunk, self.q_rot, out, scale=scale)
         torch.cuda.synchronize()
         return out.cpu().numpy()

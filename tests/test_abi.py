@@ -47,7 +47,7 @@ def test_binding_covers_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert tpa.tpa_abi_version() == 2
+    assert tpa.tpa_abi_version() == 3
     for code, word in [(0, "TPA_OK"), (1, "ARG"), (2, "UNSUPPORTED"), (3, "CAPACITY"), (4, "WORKSPACE"),
                        (5, "HIP")]:
         assert word in tpa.tpa_status_string(code)
@@ -326,7 +326,7 @@ def test_decode_fq_argument_checks(lib):
         assert call(R_Q=bad_rank) == 1
     assert call(a_q=None) == 1
     assert call(b_q=None) == 1
-    assert call(b_q=ctypes.c_void_p(0x1008)) == 1  # B_Q_rot must be 16-byte aligned
+    assert call(b_q=ctypes.c_void_p(0x1008)) == 1  # B_Q must be 16-byte aligned
     assert call(cap=1024) == 3
     assert call(ws_bytes=need - 1) == 4
     assert lib.tpa_decode_fq(ref, 6, None, 0, 0, None, None, 0, None, None, 0.0, None, 0, None, 0, None) == 0
@@ -377,7 +377,7 @@ def test_binding_checks_shapes_before_any_launch():
                             q, out, ws)
     with pytest.raises(ValueError, match="A_Q must be"):
         tpa.tpa_decode_fq(d, cache, cap, start, lens, 10, f(2, 3, 16), f(2, 3, 128), out, ws)
-    with pytest.raises(ValueError, match="B_Q_rot has"):
+    with pytest.raises(ValueError, match="B_Q has"):
         tpa.tpa_decode_fq(d, cache, cap, start, lens, 10, f(2, 3, 32), f(2, 2, 128), out, ws)
     chunk = 5
     qp = torch.empty(2, chunk, 32, 128, dtype=torch.bfloat16)

@@ -5,7 +5,8 @@ import torch
 
 import oracle
 import tpa_inputs as ti
-from tests.gpu_cases import DecodeSetup, assert_close, case_workload, f64, random_sequences, say
+from tests.gpu_cases import (STORAGE_CAUSE, Checks, DecodeSetup, assert_close, case_workload, f64,
+                             known_max_abs_excess, random_sequences, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,14 +33,26 @@ def test_tiny_fp32_workload():
     (64, 64, 1, 1, ti.BF16), (56, 32, 2, 2, ti.BF16), (16, 128, 2, 2, ti.BF16), (8, 64, 1, 1, ti.F32),
     (24, 32, 2, 1, ti.F32), (12, 128, 1, 1, ti.F32), (30, 64, 2, 2, ti.F32)])
 @pytest.mark.parametrize("q_scale", [1.0, 12.0])
-def test_small_shapes_ragged(h, d_h, R_K, R_V, dtype, q_scale):
+def test_small_shapes_ragged(h, d_h, R_K, R_V, dtype, q_scale, request):
     """Several blocks per split and a ragged tail; q_scale 12 sharpens the softmax."""
     w = case_workload(h, d_h, R_K, R_V, dtype)
     lens = [1, 7, 33, 100, 257, 600]
+    known = SHARP_RANK1.get((h, d_h, R_K, R_V, dtype, q_scale))
+    if known:
+        known_max_abs_excess(request, known, STORAGE_CAUSE)
     say(f"case: decode h={h} d_h={d_h} R_K={R_K} R_V={R_V} {dtype} q_scale={q_scale}")
     s = DecodeSetup(w, random_sequences(w, lens, q_scale=q_scale, seed=h * 31 + d_h))
+    ref = np.stack([s.oracle(b) for b in range(s.batch)])
+    chk = Checks()
     for split in (0, 16, 64):
-        _check_all(s, s.run(split_tokens=split), f"split_tokens={split}")
+        chk.close(s.run(split_tokens=split), ref, w.dtype, f"split_tokens={split}")
+    chk.done()
+
+
+# Sharpened rank-1 cases whose max-abs error exceeds 1e-2 (measured on MI355X, split 0; rel-L2 within 5e-3).
+SHARP_RANK1 = {(32, 128, 1, 1, ti.BF16, 12.0): "max-abs 1.14e-2, rel-L2 1.8e-3 (outputs up to |5.8|)",
+               (16, 64, 1, 1, ti.BF16, 12.0): "max-abs 1.87e-2, rel-L2 2.4e-3 (outputs up to |7.1|)",
+               (64, 64, 1, 1, ti.BF16, 12.0): "max-abs 2.45e-2, rel-L2 2.6e-3 (outputs up to |5.6|)"}
 
 
 def test_split_size_invariance_and_determinism():
@@ -83,6 +96,27 @@ def test_misaligned_start_gives_nan():
     assert_close(out[0], s.oracle(0), w.dtype, "aligned row")
 
 
+def test_slots_past_capacity_give_nan():
+    """A sequence whose slots reach past the capacity the call declares gets NaN output; the others are
+    unaffected.  The cache buffer is allocated (NaN-filled) well past the declared capacity, so a read the
+    guard missed would stay inside the allocation and show up as a wrong output, not as a fault."""
+    w = case_workload(32, 128, 2, 2)
+    lens = [40, 100, 7]
+    say("case: decode with slots past the declared capacity")
+    s = DecodeSetup(w, random_sequences(w, lens, seed=14), extra_capacity=512)
+    start1 = s.cache.starts[1]
+    for declared in (start1 + lens[1] - 1, start1 + 1):  # one slot short; most of the sequence outside
+        if declared < s.max_len:
+            continue  # the host would refuse the call (max_len > capacity)
+        out = s.run(capacity=declared)
+        assert np.all(np.isnan(out[1])), f"declared capacity {declared}"
+        assert_close(out[0], s.oracle(0), w.dtype, f"sequence inside the capacity ({declared})")
+        if s.cache.starts[2] + lens[2] > declared:
+            assert np.all(np.isnan(out[2]))
+    out = s.run(capacity=start1 + lens[1])  # exactly enough
+    assert_close(out[:2], np.stack([s.oracle(0), s.oracle(1)]), w.dtype, "exactly at the capacity")
+
+
 def test_cache_tail_garbage_is_ignored():
     """The cache is pre-filled with NaN bit patterns; tokens past seq_len in a block must not leak in."""
     w = case_workload(32, 128, 4, 4)
@@ -118,17 +152,18 @@ def test_full_size_long_context():
     _check_all(s, s.run(), w.name)
 
 
-def test_full_size_ragged_decode_sampled():
-    """128 ragged sequences on the GPU in the benchmark's launch configuration; 8 checked by the oracle."""
+def test_full_size_ragged_decode_all_sequences():
+    """128 ragged sequences (lengths uniform in [1024, 32768]) in the benchmark's launch configuration; the
+    whole output is compared with the oracle (every sequence, every head)."""
+    import time
     w = ti.get("c5")
     say(f"case: full-size ragged decode {w.name}")
-    lens = ti.decode_lengths(w)
     s = DecodeSetup(w, ti.decode_batch(w))
     out = s.run()
-    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 1, 63, 64, 126, 127})
-    ref = np.stack([s.oracle(b) for b in pick])
-    assert_close(out[pick], ref, w.dtype, f"sampled sequences {pick}")
-    assert np.all(np.isfinite(out))
+    t0 = time.perf_counter()
+    ref = np.stack([s.oracle(b) for b in range(s.batch)])
+    say(f"  oracle over {int(np.sum(s.lens))} cached tokens: {time.perf_counter() - t0:.1f}s")
+    assert_close(out, ref, w.dtype, "all 128 sequences")
 
 
 def test_graph_replay_matches_eager():

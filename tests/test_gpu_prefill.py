@@ -3,16 +3,38 @@ import numpy as np
 import pytest
 
 import tpa_inputs as ti
-from tests.gpu_cases import (DecodeSetup, PrefillSetup, assert_close, case_workload, random_sequences, say)
+from tests.gpu_cases import (REBUILD_CAUSE, STORAGE_CAUSE, DecodeSetup, PrefillSetup, assert_close, case_workload,
+                             known_max_abs_excess, random_sequences, say)
 
 pytestmark = pytest.mark.gpu
+
+# Rank-1 prefill cases whose max-abs error exceeds 1e-2 (measured on MI355X; rel-L2 within 5e-3), keyed by
+# (h, d_h, R, ctx, chunk, q_scale).  Outputs of rows that see few tokens reach |V| ~ 10 at rank 1.
+RANK1_PREFILL = {
+    (32, 128, 1, (0, 45, 300), 70, 1.0): "max-abs 1.49e-2, rel-L2 2.0e-3",
+    (64, 64, 1, (0, 45, 300), 70, 1.0): "max-abs 1.51e-2, rel-L2 2.1e-3",
+    (32, 128, 1, (64, 2), 160, 1.0): "max-abs 1.04e-2, rel-L2 2.2e-3",
+    (32, 128, 1, (0, 45, 300), 70, 10.0): "max-abs 3.43e-2, rel-L2 3.6e-3",
+    (64, 64, 1, (0, 45, 300), 70, 10.0): "max-abs 5.97e-2, rel-L2 4.2e-3",
+    (32, 128, 1, (64, 2), 160, 10.0): "max-abs 3.50e-2, rel-L2 3.9e-3",
+    (64, 64, 1, (64, 2), 160, 10.0): "max-abs 8.09e-2, rel-L2 4.3e-3",
+    (32, 128, 1, (257,), 129, 10.0): "max-abs 3.42e-2, rel-L2 4.8e-3",
+    (64, 64, 1, (257,), 129, 10.0): "max-abs 5.40e-2, rel-L2 4.9e-3",
+    (32, 128, 1, (0, 45), 300, 2.0): "max-abs 1.01e-2, rel-L2 2.2e-3",
+    (32, 128, 1, (0, 45), 300, 6.0): "max-abs 2.12e-2, rel-L2 3.1e-3",
+    (32, 128, 1, (257,), 700, 6.0): "max-abs 4.41e-2, rel-L2 4.1e-3",
+    (32, 128, 1, (64, 1000, 3), 257, 6.0): "max-abs 2.58e-2, rel-L2 3.0e-3",
+}
 
 
 @pytest.mark.parametrize("h,d_h,R", [(32, 128, 4), (32, 128, 1), (16, 64, 2), (20, 48, 3), (16, 128, 2), (64, 64, 1),
                                      (56, 64, 4)])
 @pytest.mark.parametrize("ctx,chunk", [([0, 45, 300], 70), ([64, 2], 160), ([257], 129)])
 @pytest.mark.parametrize("q_scale", [1.0, 10.0])
-def test_small_chunks(h, d_h, R, ctx, chunk, q_scale):
+def test_small_chunks(h, d_h, R, ctx, chunk, q_scale, request):
+    known = RANK1_PREFILL.get((h, d_h, R, tuple(ctx), chunk, q_scale))
+    if known:
+        known_max_abs_excess(request, known, REBUILD_CAUSE if q_scale == 1.0 else REBUILD_CAUSE + "; and " + STORAGE_CAUSE)
     w = case_workload(h, d_h, R, R)
     say(f"case: prefill h={h} d_h={d_h} R={R} ctx={ctx} chunk={chunk} q_scale={q_scale}")
     seqs = random_sequences(w, [c + chunk for c in ctx], n_q=chunk, q_scale=q_scale, seed=h + chunk)
@@ -35,28 +57,31 @@ def test_prefill_rows_match_gpu_decode():
     assert_close(pre[rows], dec, w.dtype, "prefill rows vs decodes")
 
 
-def test_full_size_prefill_sampled_rows():
-    """8 sequences x (2048 cached + 512-row causal chunk), h=32, d_h=128, R=4; oracle on sampled rows."""
+def test_full_size_prefill_all_rows():
+    """8 sequences x (2048 cached + 512-row causal chunk), h=32, d_h=128, R=4: every row of every sequence
+    compared with the oracle."""
+    import time
     w = ti.get("c5")
     say(f"case: full-size prefill of {w.name}")
     seqs = ti.prefill_batch(w)
     s = PrefillSetup(w, seqs, [w.prefill_ctx] * w.prefill_batch)
     out = s.run()
-    assert np.all(np.isfinite(out))
-    rows = np.array([0, 1, 31, 32, 127, 128, 255, 256, 383, 384, 510, 511])
-    for b in (0, 3, 7):
-        assert_close(out[b][rows], s.oracle(b, rows=rows), w.dtype, f"seq {b} rows")
+    t0 = time.perf_counter()
+    ref = np.stack([s.oracle(b) for b in range(len(seqs))])
+    say(f"  oracle over {len(seqs)} x {w.prefill_chunk} rows: {time.perf_counter() - t0:.1f}s")
+    assert_close(out, ref, w.dtype, "all 8 x 512 rows")
 
 
 # Chunks of more than 256 rows at d_h = 128 run the wide form (512 query rows per work-group, factor
 # pieces staged through LDS); these cases cover it with ragged chunk ends, a second row tile, short and
 # empty contexts and every rank.
-# (q_scale sets how peaked the softmax is: at R = 1 the rebuilt keys are largest, and a very peaked
-# softmax over bf16 operands amplifies their rounding in the output, so the sharp case uses R = 4.)
 @pytest.mark.parametrize("h,R,q_scale", [(32, 4, 2.0), (32, 2, 2.0), (32, 1, 2.0), (20, 4, 2.0), (16, 4, 2.0),
-                                         (32, 4, 10.0)])
+                                         (32, 4, 10.0), (32, 1, 6.0)])
 @pytest.mark.parametrize("ctx,chunk", [([0, 45], 300), ([257], 700), ([64, 1000, 3], 257)])
-def test_wide_chunks(h, R, q_scale, ctx, chunk):
+def test_wide_chunks(h, R, q_scale, ctx, chunk, request):
+    known = RANK1_PREFILL.get((h, 128, R, tuple(ctx), chunk, q_scale))
+    if known:
+        known_max_abs_excess(request, known, REBUILD_CAUSE if q_scale <= 2.0 else REBUILD_CAUSE + "; and " + STORAGE_CAUSE)
     w = case_workload(h, 128, R, R)
     say(f"case: wide prefill h={h} R={R} q_scale={q_scale} ctx={ctx} chunk={chunk}")
     seqs = random_sequences(w, [c + chunk for c in ctx], n_q=chunk, q_scale=q_scale, seed=h * R + chunk)
@@ -79,6 +104,22 @@ def test_misaligned_start_gives_nan(chunk):
     out = s.run(seq_start=bad)
     assert np.all(np.isnan(out[1]))
     assert_close(out[0], s.oracle(0), w.dtype, "aligned sequence")
+
+
+@pytest.mark.parametrize("chunk", [100, 400])
+def test_chunk_past_capacity_gives_nan(chunk):
+    """A sequence whose context and chunk reach past the capacity the call declares reports NaN rows; the
+    other is unaffected.  The buffer is allocated past the declared capacity, so a missed guard would read
+    inside the allocation (NaN-filled beyond the appended tokens) and be seen, never fault."""
+    w = case_workload(32, 128, 2, 2)
+    say(f"case: prefill past the declared capacity chunk={chunk}")
+    ctx = [40, 70]
+    seqs = random_sequences(w, [c + chunk for c in ctx], n_q=chunk, seed=chunk + 1)
+    s = PrefillSetup(w, seqs, ctx, extra_capacity=256)
+    declared = s.cache.starts[1] + ctx[1] + chunk - 1
+    out = s.run(capacity=declared)
+    assert np.all(np.isnan(out[1]))
+    assert_close(out[0], s.oracle(0), w.dtype, "sequence inside the capacity")
 
 
 def test_wide_prefill_is_deterministic():

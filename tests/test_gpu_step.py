@@ -39,11 +39,12 @@ class StepSetup:
         n = tpa.tpa_decode_workspace_bytes(self.dims, self.batch, self.max_len, split_tokens)
         return torch.zeros(max(n, 256), dtype=torch.uint8, device="cuda")
 
-    def run(self, split_tokens: int = 0, seq_start=None, out=None, ws=None) -> torch.Tensor:
+    def run(self, split_tokens: int = 0, seq_start=None, out=None, ws=None, capacity=None) -> torch.Tensor:
+        """capacity: the capacity the call declares (default the cache's own)."""
         out = torch.full((self.batch, self.w.h, self.w.d_h), float("nan"), dtype=torch.float32,
                          device="cuda") if out is None else out
         ws = self.workspace(split_tokens) if ws is None else ws
-        tpa.tpa_decode_step(self.dims, self.cache.buf, self.cache.capacity,
+        tpa.tpa_decode_step(self.dims, self.cache.buf, self.cache.capacity if capacity is None else capacity,
                             self.cache.seq_start if seq_start is None else seq_start, self.seq_len, self.max_len,
                             self.A_K, self.B_K, self.A_V, self.B_V, self.q, out, ws, split_tokens=split_tokens)
         return out
@@ -160,6 +161,24 @@ def test_step_misaligned_start_gives_nan_and_writes_nothing():
     assert np.all(np.isnan(got[1]))
     assert_close(got[0], st.oracle(0), ti.BF16, "seq 0")
     # only sequence 0's slot 40 changed
+    changed = (st.cache.buf != before).nonzero().flatten()
+    blk = tpa.tpa_cache_bytes(st.dims, tpa.tpa_block_tokens(st.dims))
+    assert changed.numel() > 0
+    assert int(changed.min()) >= (40 // 32) * blk and int(changed.max()) < (40 // 32 + 1) * blk
+
+
+def test_step_new_slot_past_capacity_gives_nan_and_writes_nothing():
+    """The cached tokens fit the declared capacity but the new token's slot does not: NaN output for that
+    sequence and no write; the other sequence steps normally.  The buffer holds more than the declared
+    capacity, so a missed guard would write inside the allocation (and be seen), never fault."""
+    w = case_workload(32, 128, 1, 1, ti.BF16)
+    lens = [40, 70]
+    st = StepSetup(w, lens, seed=19)
+    declared = st.cache.starts[1] + lens[1]  # sequence 1's slot 70 is the first slot past it
+    before = st.cache.buf.clone()
+    got = st.run(capacity=declared).cpu().numpy()
+    assert np.all(np.isnan(got[1]))
+    assert_close(got[0], st.oracle(0), ti.BF16, "seq 0")
     changed = (st.cache.buf != before).nonzero().flatten()
     blk = tpa.tpa_cache_bytes(st.dims, tpa.tpa_block_tokens(st.dims))
     assert changed.numel() > 0
