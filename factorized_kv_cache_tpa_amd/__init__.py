@@ -17,8 +17,8 @@ import torch
 __all__ = [
     "TPAError", "Dims", "load", "library_path", "tpa_abi_version", "tpa_status_string", "tpa_supported",
     "tpa_block_tokens", "tpa_cache_bytes", "tpa_cache_append", "tpa_cache_read", "tpa_decode_workspace_bytes",
-    "tpa_decode", "tpa_decode_step", "tpa_decode_fq", "tpa_prefill_chunk", "tpa_prefill_chunk_fq", "TPA_F32",
-    "TPA_BF16", "TPA_CACHE_NATIVE", "TPA_CACHE_E4M3",
+    "tpa_decode", "tpa_decode_noalloc", "TPA_DECODE_NOALLOC_MAX_BYTES", "tpa_decode_step", "tpa_decode_fq",
+    "tpa_prefill_chunk", "tpa_prefill_chunk_fq", "TPA_F32", "TPA_BF16", "TPA_CACHE_NATIVE", "TPA_CACHE_E4M3",
 ]
 
 TPA_F32 = 0
@@ -47,6 +47,9 @@ _EXPORTS = {
     "tpa_decode": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                     ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p], ctypes.c_int32),
+    "tpa_decode_noalloc": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                            ctypes.c_int32, ctypes.c_void_p], ctypes.c_int32),
     "tpa_decode_step": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                          ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_int32,
@@ -258,6 +261,27 @@ def tpa_decode(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_start:
         _ptr(q_rot, dims.torch_dtype, "q_rot"), float(scale), _ptr(out, torch.float32, "out"), int(split_tokens),
         _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "tpa_decode")
+
+
+TPA_DECODE_NOALLOC_MAX_BYTES = 16 << 20  # the static partials array of tpa_decode_noalloc (tpa.h)
+
+
+def tpa_decode_noalloc(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_start: torch.Tensor,
+                       seq_len: torch.Tensor, max_len: int, q_rot: torch.Tensor, out: torch.Tensor, scale: float = 0.0,
+                       split_tokens: int = 0, stream=None) -> None:
+    """tpa_decode with its partials in the library's static device array: no workspace, no allocation.
+    Calls that overlap on one GPU race (they share the array)."""
+    batch = seq_start.numel()
+    _numel(seq_len, batch, "seq_len")
+    _numel(q_rot, batch * dims.h * dims.d_h, "q_rot")
+    _numel(out, batch * dims.h * dims.d_h, "out")
+    _cache_fits(dims, cache, capacity_tokens)
+    st = load().tpa_decode_noalloc(
+        _ref(dims), _ptr(cache, name="cache"), int(capacity_tokens), seq_start.numel(),
+        _ptr(seq_start, torch.int64, "seq_start"), _ptr(seq_len, torch.int32, "seq_len"), int(max_len),
+        _ptr(q_rot, dims.torch_dtype, "q_rot"), float(scale), _ptr(out, torch.float32, "out"), int(split_tokens),
+        _stream(stream))
+    _check(st, "tpa_decode_noalloc")
 
 
 def tpa_decode_step(dims: Dims, cache: torch.Tensor, capacity_tokens: int, seq_start: torch.Tensor,

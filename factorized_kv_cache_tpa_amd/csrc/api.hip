@@ -3,8 +3,17 @@
 // side effect and the checks work on a machine without a GPU.
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/tpa.h"
 #include "common.h"
+
+// tpa_decode_noalloc keeps the per-split partials (the workspace of tpa_decode) in this array instead of
+// a caller's buffer.  Each GPU the library runs on holds its own copy until the process ends; in host code
+// the name is only a stand-in, so its device address is looked up per device (scratch_address below) and
+// only that address is ever passed on.
+constexpr int64_t kScratchBytes = TPA_DECODE_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -94,12 +103,38 @@ inline bool aligned16(const void *ptr) { return reinterpret_cast<uintptr_t>(ptr)
 
 float resolve_scale(float scale, int d_h) { return scale > 0.f ? scale : float(1.0 / sqrt(double(d_h))); }
 
-// tpa_decode and tpa_decode_step: host checks, the split plan, then the split and merge kernels.
-// `step` is null for a plain decode over rotated queries.
+// Device address of this device's copy of `scratch`, looked up once per device with that device current
+// (the caller's current device, which must be the one its stream runs on).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int32_t scratch_address(void *stream, void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TPA_ERR_HIP;
+    if (stream) {
+        int sdev = -1;
+        if (hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &sdev) != hipSuccess) return TPA_ERR_HIP;
+        if (sdev != dev) return TPA_ERR_ARG;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TPA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return TPA_OK;
+}
+
+// tpa_decode, tpa_decode_step, tpa_decode_fq and tpa_decode_noalloc: host checks, the split plan, then the
+// split and merge kernels.  `step` is null for a plain decode over rotated queries.  use_scratch: the
+// partials go to the static scratch array (the workspace arguments are ignored).
 int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
                    const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *q, float scale,
                    float *out, int32_t split_tokens, void *workspace, int64_t workspace_bytes, void *stream,
-                   const tpa::StepInputs *step, int32_t r_q = 0, const void *a_q = nullptr) {
+                   const tpa::StepInputs *step, int32_t r_q = 0, const void *a_q = nullptr,
+                   bool use_scratch = false) {
     int32_t st = check_dims(dims);
     if (st != TPA_OK) return st;
     if (batch < 0 || batch > 65535 || max_len < 0 || split_tokens < 0 || capacity_tokens < 0)
@@ -112,6 +147,13 @@ int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
     if (int64_t(max_len) + (step ? 1 : 0) > capacity_tokens) return TPA_ERR_CAPACITY;
     const Layout L = layout_of(dims);
     const DecodePlan P = plan_decode(L, batch, max_len, split_tokens);
+    if (use_scratch) {
+        if (P.bytes > kScratchBytes) return TPA_ERR_WORKSPACE;
+        if (P.n_split > 65535) return TPA_ERR_ARG;
+        const int32_t sst = scratch_address(stream, &workspace);  // the only HIP calls before the launch
+        if (sst != TPA_OK) return sst;
+        workspace_bytes = kScratchBytes;
+    }
     if (!workspace || workspace_bytes < P.bytes) return TPA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TPA_ERR_WORKSPACE;
     if (P.n_split > 65535) return TPA_ERR_ARG;
@@ -280,6 +322,13 @@ int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
                    void *stream) {
     return run_decode(dims, cache, capacity_tokens, batch, seq_start, seq_len, max_len, q_rot, scale, out,
                       split_tokens, workspace, workspace_bytes, stream, nullptr);
+}
+
+int32_t tpa_decode_noalloc(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
+                           const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *q_rot,
+                           float scale, float *out, int32_t split_tokens, void *stream) {
+    return run_decode(dims, cache, capacity_tokens, batch, seq_start, seq_len, max_len, q_rot, scale, out,
+                      split_tokens, nullptr, 0, stream, nullptr, 0, nullptr, true);
 }
 
 int32_t tpa_decode_step(const tpa_dims *dims, void *cache, int64_t capacity_tokens, int32_t batch,

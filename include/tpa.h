@@ -22,9 +22,11 @@
  *   - Pointers are DEVICE pointers unless marked [host].  Element arrays hold
  *     `dims->dtype` elements (fp32 or bf16); outputs are fp32.
  *   - The caller owns every buffer (allocate with hipMalloc or a framework
- *     allocator).  The library allocates nothing, keeps no mutable global
- *     state, never synchronizes, and enqueues its kernels on `stream`
- *     (a hipStream_t; NULL = the null stream).  Completion is asynchronous.
+ *     allocator).  The library allocates nothing, never synchronizes, and
+ *     enqueues its kernels on `stream` (a hipStream_t; NULL = the null
+ *     stream).  Completion is asynchronous.  Its only mutable global state is
+ *     the per-device address of the static partials array of
+ *     tpa_decode_noalloc.
  *   - The cache, q_rot and prefill's out must be 16-byte aligned (wide vector
  *     loads and stores); hipMalloc and framework allocators give 256 bytes.
  *   - Every call returns a tpa_status.  All argument checks run on the host
@@ -184,6 +186,24 @@ int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
                    const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *q_rot,
                    float scale, float *out, int32_t split_tokens, void *workspace, int64_t workspace_bytes,
                    void *stream);
+
+/* tpa_decode for callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same split and merge kernels, with the per-split partials in a
+ * static device array of the library instead of a caller workspace.  The call allocates nothing and calls
+ * no allocating routine.
+ *   - The array holds TPA_DECODE_NOALLOC_MAX_BYTES; a call whose tpa_decode_workspace_bytes(dims, batch,
+ *     max_len, split_tokens) exceeds it is rejected with TPA_ERR_WORKSPACE before any launch.
+ *   - Each GPU holds its own copy, from the library's first use on that device until the process ends; its
+ *     address is looked up on the first call on a device.  The caller's current device must be the device
+ *     `stream` runs on (TPA_ERR_ARG otherwise; TPA_ERR_HIP if the lookup fails).
+ *   - Every call on one GPU shares that GPU's copy: calls that overlap on one GPU (other streams, other
+ *     threads) race and give wrong results.  Nothing in it needs clearing: each call writes every partial
+ *     it reads.
+ * Arguments, results and the other error behaviour are those of tpa_decode. */
+#define TPA_DECODE_NOALLOC_MAX_BYTES (16ll << 20)
+int32_t tpa_decode_noalloc(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
+                           const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *q_rot,
+                           float scale, float *out, int32_t split_tokens, void *stream);
 
 /* Fused single decode step (one new token per sequence): for each sequence b with N = seq_len[b] cached
  * tokens, write the new token's factors into slot seq_start[b] + N (B_K rotated at position N, exactly as

@@ -314,6 +314,29 @@ def test_decode_step_argument_checks(lib):
                                0.0, FAKE, 0, FAKE, need, None) == 2
 
 
+def test_decode_noalloc_argument_checks(lib):
+    """The host checks of tpa_decode, plus the limit of the static partials array: a plan larger than it is
+    refused with TPA_ERR_WORKSPACE before any HIP call."""
+    d = _d()
+    ref = ctypes.byref(d)
+
+    def call(batch=16, max_len=4096, split=0, cap=8192, cache=FAKE, q=FAKE, out=FAKE):
+        return lib.tpa_decode_noalloc(ref, cache, cap, batch, FAKE, FAKE, max_len, q, 0.0, out, split, None)
+    assert lib.tpa_decode_noalloc(ref, None, 0, 0, None, None, 0, None, 0.0, None, 0, None) == 0  # batch 0
+    assert call(cache=None) == 1
+    assert call(out=None) == 1
+    assert call(q=ctypes.c_void_p(0x1008)) == 1
+    assert call(cap=1024) == 3
+    # 4096 sequences of 4096 tokens in 32-token splits: 128 partials of 16 KiB each per sequence
+    big = lib.tpa_decode_workspace_bytes(ref, 4096, 4096, 32)
+    assert big > tpa.TPA_DECODE_NOALLOC_MAX_BYTES
+    assert call(batch=4096, split=32) == 4
+    small = lib.tpa_decode_workspace_bytes(ref, 16, 4096, 0)
+    assert small <= tpa.TPA_DECODE_NOALLOC_MAX_BYTES
+    m = re.search(r"#define TPA_DECODE_NOALLOC_MAX_BYTES \((\d+)ll << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == tpa.TPA_DECODE_NOALLOC_MAX_BYTES
+
+
 def test_decode_fq_argument_checks(lib):
     d = _d()
     ref = ctypes.byref(d)
