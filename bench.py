@@ -1,24 +1,37 @@
-"""Benchmark of decode over a TPA factor cache on one MI355X.
+"""Benchmark of the TPA factor-cache hot path on one MI355X.
 
-One step = one decode step of the whole hot path for a batch, in one call:
-  tpa_decode_step  (per sequence: the step's new token is appended -- B_K rotated
-                    and stored --, the query is rotated, and the query attends over
-                    the cached tokens and the new one; split + merge kernels)
-on the workload "decode_b16_h32_d128_r1_n4096": 16 sequences x 4096 cached
-tokens, h=32, d_h=128, R_K=R_V=1, bf16 factors, RoPE base 10000, synthetic
-seeded inputs.  The cache is replicated and the replicas are visited in turn so
-every step streams its factors from HBM rather than from the 256 MB
-last-level cache.  The same step as two calls (tpa_cache_append, then
-tpa_decode over the cached tokens) and tpa_decode alone are timed beside it.
+One step = one serving iteration of the largest workload,
+"ragged_decode_b128_h32_d128_r4_plus_prefill_b8_ctx2048_chunk512"
+(h=32, d_h=128, R_K=R_V=4, bf16 factors, RoPE base 10000, seeded synthetic inputs):
+  1. tpa_decode_step over 128 sequences whose cached lengths are uniform in [1024, 32768]: each
+     sequence's new token is appended (B_K rotated and stored), its query is rotated, and the
+     query attends over the cached tokens and the new one (split + merge kernels);
+  2. tpa_cache_append of a 512-token chunk for each of 8 more sequences holding 2048 cached
+     tokens, which also rotates the chunk's 512 query rows;
+  3. tpa_prefill_chunk: row j of each chunk attends causally over tokens 0 .. 2048 + j.
+Every input is resident in device memory before the timed region.  value = cached tokens the
+decode attends to (the sum of the 128 lengths) per second of whole-step time.
 
-Printed: one JSON line with the metric (cached tokens/s), the step's achieved
-HBM bandwidth against the 8 TB/s peak, the other measured workloads (decode
-shapes and the causal prefill chunk against the bf16 matrix-core peak), and the
-fp64 CPU oracle timed on the host as a reference baseline.
+The line carries:
+  roofline          the dominant kernel pair, tpa_decode_step's split + merge: algorithmic bytes
+                    (factor stream, query, output, the new token's factors and record) over the
+                    call's median duration, timed with HIP events on its own stream in a graph,
+                    against 8 TB/s; traffic = rocprofv3 FETCH_SIZE + WRITE_SIZE bytes per call
+                    (profiles/), or null when the kernels changed since the counters were taken;
+  roofline_prefill  the prefill kernel: causal-exact flops over its median duration against the
+                    2.5 PFLOP/s dense bf16 matrix-core peak, with the counters' busy fraction;
+  legs              each part of the step timed alone (median of 5 windows);
+  stream_probe_GBps a plain streaming read of 2 GiB with the decode's load width and hint;
+  extras            the other decode workloads (16 x 4096, 64 x 8192, 4 x 131072) and the same
+                    workloads over an 8-bit E4M3 factor cache;
+  cpu_baseline      the fp64 oracle on the host's cores over a bounded sample of the same
+                    workload (decode cached-tokens/s; prefill GFLOP/s), as a reported baseline.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -30,41 +43,39 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
 MALL_BYTES = 256 << 20
-MAIN = "c2"
+HEADLINE = "c5"
+REPEATS = 5
+CSRC = os.path.join(ROOT, "factorized_kv_cache_tpa_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_bytes_decode_b16_h32_d128_r1_n4096.json")
-
-
-def decode_source_hash() -> str:
-    import hashlib
+def source_hash(files) -> str:
     h = hashlib.sha256()
-    for f in ("decode.hip", "common.h", "api.hip"):  # the kernels and the split planner
-        with open(os.path.join(ROOT, "factorized_kv_cache_tpa_amd", "csrc", f), "rb") as fh:
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def decode_traffic():
-    """HBM bytes per tpa_decode_step call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by
-    a plain copy of known size); None when that summary is missing or the decode kernels changed since."""
+DECODE_SOURCES = ("decode.hip", "common.h", "api.hip")    # the decode kernels and the split planner
+PREFILL_SOURCES = ("prefill.hip", "common.h", "api.hip")
+
+
+def profile_record(name: str, sources):
+    """A committed counter summary (profiles/<name>.json) if its source hash matches the current kernels."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(os.path.join(PROFILES, name + ".json")) as fh:
             d = json.load(fh)
     except (OSError, ValueError):
         return None
-    if d.get("source_hash") != decode_source_hash():
-        return None
-    if "step_call_traffic_bytes" not in d:
-        return None
-    return int(round(d["step_call_traffic_bytes"]))
+    return d if d.get("source_hash") == source_hash(sources) else None
 
 
 def decode_bytes(w, lens, cache_es=None) -> int:
@@ -84,8 +95,49 @@ def step_bytes(w, lens, cache_es=None) -> int:
     return decode_bytes(w, lens, cache_es) + len(lens) * per_tok * (es + ces)
 
 
+class Timer:
+    """HIP graphs replayed on one capture stream, timed with events recorded on that stream."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.stream = torch.cuda.Stream()
+
+    def capture(self, fn, n: int):
+        torch = self.torch
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream):
+            for i in range(n):
+                fn(i)
+        torch.cuda.synchronize()
+        return g
+
+    def window_ms(self, graph, replays: int) -> float:
+        torch = self.torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.stream):
+            a.record(self.stream)
+            for _ in range(replays):
+                graph.replay()
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    def median_call_ms(self, fn, n_calls: int, min_calls: int = 20) -> float:
+        """Median over REPEATS windows of the milliseconds per call; a window replays a graph of n_calls
+        calls as often as needed to reach min_calls calls."""
+        g = self.capture(fn, n_calls)
+        self.window_ms(g, 1)  # warm replay
+        replays = max(1, -(-min_calls // n_calls))
+        ms = [self.window_ms(g, replays) / (replays * n_calls) for _ in range(REPEATS)]
+        return float(np.median(ms))
+
+
 class DecodeBench:
-    """Cache replicas + per-step buffers for one decode workload."""
+    """Cache replicas + per-step buffers for one decode workload (replicas keep every call streaming from HBM
+    rather than from the 256 MB last-level cache)."""
 
     def __init__(self, name: str, min_bytes: int, cache_format: int = 0):
         import torch
@@ -112,10 +164,12 @@ class DecodeBench:
             for r in range(self.n_rep):
                 self.cache.append(r * self.batch + b, *dev)
             del dev
+        self.q = to_device(np.stack([s.q[0] for s in seqs]), self.dims)
+        del seqs
         torch.cuda.synchronize()
         log(f"[{w.name}] {self.n_rep} cache replica(s), {self.cache.nbytes / 1e9:.2f} GB, built in "
             f"{time.time() - t0:.1f}s")
-        # the step's new token (factors at position N) and its query, as the producer would hand them over
+        # the step's new token (factors at position N), as the producer would hand it over
         rng = np.random.default_rng(w.seed)
         mk = lambda shape, sig: to_device(ti.to_storage(rng.standard_normal(shape, dtype=np.float32) * sig,
                                                         w.dtype), self.dims)
@@ -123,7 +177,6 @@ class DecodeBench:
         self.new_BK = mk((self.batch, w.R_K, w.d_h), 1 / np.sqrt(w.R_K))
         self.new_AV = mk((self.batch, w.R_V, w.h), 1 / np.sqrt(w.R_V))
         self.new_BV = mk((self.batch, w.R_V, w.d_h), 1 / np.sqrt(w.R_V))
-        self.q = to_device(np.stack([s.q[0] for s in seqs]), self.dims)
         self.q_rot = torch.empty_like(self.q)
         self.pos = torch.tensor(self.lens, dtype=torch.int32, device="cuda")
         starts = self.cache.seq_start.view(self.n_rep, self.batch)
@@ -136,10 +189,12 @@ class DecodeBench:
         self.out = torch.empty(self.batch, w.h, w.d_h, dtype=torch.float32, device="cuda")
         self.bytes = decode_bytes(w, self.lens, 1 if self.e4m3 else None)
         self.step_bytes = step_bytes(w, self.lens, 1 if self.e4m3 else None)
+        self.tokens = float(np.sum(self.lens))
         # a rank-6 factored query (full TPA), unrotated: the kernel builds and rotates it at the query position
         self.R_Q = 6
         self.A_Q = mk((self.batch, self.R_Q, w.h), 1.0)
         self.B_Q = mk((self.batch, self.R_Q, w.d_h), 1 / np.sqrt(w.d_h))
+        self.cache.rotate_queries(self.q, self.pos, q_out=self.q_rot)
 
     def step(self, i: int, out=None):
         """One fused decode step on cache replica i % n_rep (tpa_decode_step)."""
@@ -148,10 +203,16 @@ class DecodeBench:
                                  self.max_len, self.new_AK, self.new_BK, self.new_AV, self.new_BV, self.q,
                                  self.out if out is None else out, self.ws)
 
-    def decode_fq(self, r: int, out=None):
-        """tpa_decode_fq over replica r: the same cache with a rank-R_Q factored query (built on chip)."""
+    def decode(self, i: int, out=None):
+        r = i % self.n_rep
+        self.tpa.tpa_decode(self.dims, self.cache.buf, self.cache.capacity, self.rep_start[r], self.seq_len,
+                            self.max_len, self.q_rot, self.out if out is None else out, self.ws)
+
+    def decode_fq(self, i: int):
+        """tpa_decode_fq over replica i: the same cache with a rank-R_Q factored query (built on chip)."""
+        r = i % self.n_rep
         self.tpa.tpa_decode_fq(self.dims, self.cache.buf, self.cache.capacity, self.rep_start[r], self.seq_len,
-                               self.max_len, self.A_Q, self.B_Q, self.out if out is None else out, self.ws)
+                               self.max_len, self.A_Q, self.B_Q, self.out, self.ws)
 
     def step_two_call(self, i: int):
         """The same step as two calls: append the new token + rotate the query, then decode the cached tokens."""
@@ -161,309 +222,360 @@ class DecodeBench:
                              q_out=self.q_rot)
         self.decode(r)
 
-    def decode(self, r: int, out=None):
-        self.tpa.tpa_decode(self.dims, self.cache.buf, self.cache.capacity, self.rep_start[r], self.seq_len,
-                            self.max_len, self.q_rot, self.out if out is None else out, self.ws)
-
-    def _capture(self, fn, n: int):
-        torch = self.torch
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=self.cap_stream):
-            for i in range(n):
-                fn(i)
-        return g
-
-    def _time(self, graph, n_calls: int, reps: int) -> float:
-        """Milliseconds per call over `reps` back-to-back replays of a graph of `n_calls` calls."""
-        torch = self.torch
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(reps):
-            graph.replay()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / (reps * n_calls)
-
-    def run_decode_only(self, steps: int, warmup: int):
-        """tpa_decode and tpa_decode_fq alone (an E4M3 cache has no fused step), graphs over the replicas."""
-        torch = self.torch
-        self.cache.rotate_queries(self.q, self.pos, q_out=self.q_rot)
-        for i in range(warmup):
-            self.decode(i % self.n_rep)
-        torch.cuda.synchronize()
-        self.cap_stream = torch.cuda.Stream()
-        reps = max(1, -(-steps // self.n_rep))
-        dec = self._capture(self.decode, self.n_rep)
-        fq = self._capture(self.decode_fq, self.n_rep)
-        dec.replay()
-        fq.replay()
-        ms_dec = self._time(dec, self.n_rep, reps)
-        ms_fq = self._time(fq, self.n_rep, reps)
-        toks = float(np.sum(self.lens))
-        return dict(decode_ms=ms_dec, decode_tokens_per_s=toks / (ms_dec / 1e3),
-                    decode_GBps=self.bytes / (ms_dec / 1e3) / 1e9, fq_ms=ms_fq)
-
-    def run(self, steps: int, warmup: int, step_only: bool = False):
-        """Time exactly `steps` fused steps.  The calls are recorded once into HIP graphs (a pass over all cache
-        replicas per graph) so the GPU is never waiting on the Python launch path."""
-        torch = self.torch
-        for i in range(warmup):
-            self.step(i)
-        torch.cuda.synchronize()
-        self.cap_stream = torch.cuda.Stream()
-        full = self._capture(self.step, self.n_rep)
-        rem = steps % self.n_rep
-        part = self._capture(self.step, rem) if rem else None
-        full.replay()
-        torch.cuda.synchronize()
-
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        wall0 = time.perf_counter()
-        a.record()
-        for _ in range(steps // self.n_rep):
-            full.replay()
-        if part is not None:
-            part.replay()
-        b.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        ms_step = a.elapsed_time(b) / steps
-        # a replay must reproduce the eager result bit for bit (the step is deterministic and rewrites the
-        # same record)
-        got = self.out.clone()
-        ref = torch.empty_like(self.out)
-        self.step((steps - 1) % self.n_rep, out=ref)
-        torch.cuda.synchronize()
-        if not torch.equal(got, ref):
-            raise RuntimeError("graph replay of tpa_decode_step differs from the eager call")
-        toks = float(np.sum(self.lens))
-        res = dict(ms_per_step=ms_step, wall_s=wall, tokens_per_s=toks / (ms_step / 1e3), bytes=self.step_bytes,
-                   step_GBps=self.step_bytes / (ms_step / 1e3) / 1e9)
-        if step_only:
-            return res
-        # the two-call step and tpa_decode alone, each a pass over the replicas per graph, same stream
-        reps = max(1, -(-steps // self.n_rep))
-        two = self._capture(self.step_two_call, self.n_rep)
-        dec = self._capture(self.decode, self.n_rep)
-        fq = self._capture(self.decode_fq, self.n_rep)
-        two.replay()
-        dec.replay()
-        fq.replay()
-        ms_two = self._time(two, self.n_rep, reps)
-        ms_dec = self._time(dec, self.n_rep, reps)
-        ms_fq = self._time(fq, self.n_rep, reps)
-        res.update(two_call_ms=ms_two, decode_ms=ms_dec, decode_tokens_per_s=toks / (ms_dec / 1e3),
-                   decode_GBps=self.bytes / (ms_dec / 1e3) / 1e9, fq_ms=ms_fq,
-                   fq_GBps=self.bytes / (ms_fq / 1e3) / 1e9)
+    def legs(self, timer: Timer, fused: bool = True) -> dict:
+        """Median milliseconds per call of each decode form (graphs over the replicas)."""
+        n = self.n_rep
+        res = dict(decode_ms=timer.median_call_ms(self.decode, n), fq_ms=timer.median_call_ms(self.decode_fq, n))
+        if fused:
+            res["step_ms"] = timer.median_call_ms(self.step, n)
+            res["two_call_ms"] = timer.median_call_ms(self.step_two_call, n)
+        self.cache.rotate_queries(self.q, self.pos, q_out=self.q_rot)  # the two-call form rotated in place
         return res
 
 
-def prefill_bench(steps: int, warmup: int, cache_format: int = 0):
-    """Causal chunk: 8 sequences x (2048 cached + 512 chunk rows), h=32, d_h=128, R=4, bf16 (cache_format 1:
-    the same over an E4M3 factor cache)."""
+class PrefillBench:
+    """The ragged workload's prefill part: 8 sequences of 2048 cached tokens, each appending and attending a
+    512-token causal chunk.  cache_format 1: the same over an E4M3 factor cache."""
+
+    def __init__(self, cache_format: int = 0):
+        import torch
+        import factorized_kv_cache_tpa_amd as tpa
+        import tpa_inputs as ti
+        from factorized_kv_cache_tpa_amd.cache import FactorCache, to_device
+
+        self.torch, self.tpa = torch, tpa
+        w = self.w = ti.get(HEADLINE)
+        self.dims = tpa.Dims(w.h, w.d_h, w.R_K, w.R_V, w.dtype, w.rope_base, cache_format)
+        seqs = ti.prefill_batch(w)
+        B, ctx, chunk = self.B, self.ctx, self.chunk = w.prefill_batch, w.prefill_ctx, w.prefill_chunk
+        self.cache = FactorCache(self.dims, [ctx + chunk] * B)
+        for b, s in enumerate(seqs):  # the cached context; the chunk is appended by every step
+            self.cache.append_host(b, s.A_K[:ctx], s.B_K[:ctx], s.A_V[:ctx], s.B_V[:ctx])
+        cat = lambda x: to_device(np.concatenate([getattr(s, x)[ctx:] for s in seqs]), self.dims)
+        self.c_AK, self.c_BK, self.c_AV, self.c_BV = (cat(x) for x in ("A_K", "B_K", "A_V", "B_V"))
+        self.q = to_device(np.stack([s.q for s in seqs]), self.dims).reshape(B * chunk, w.h, w.d_h)
+        self.q_rot = torch.empty_like(self.q)
+        self.pos = torch.arange(ctx, ctx + chunk, dtype=torch.int32, device="cuda").repeat(B)
+        starts = torch.tensor(self.cache.starts, dtype=torch.int64, device="cuda")
+        self.slot = (starts.repeat_interleave(chunk) + self.pos.to(torch.int64)).contiguous()
+        self.ctx_len = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+        self.out = torch.empty(B, chunk, w.h, w.d_h, dtype=torch.float32, device="cuda")
+        pairs = B * sum(ctx + j + 1 for j in range(chunk))
+        self.flops = 4.0 * w.d_h * w.h * pairs
+        es = 2
+        self.append_bytes = B * chunk * ((w.R_K + w.R_V) * (w.h + w.d_h) * (es + (1 if cache_format else es)) +
+                                         2 * w.h * w.d_h * es)
+        # rank-6 factored query rows (full TPA), unrotated (row j is rotated at ctx + j on chip)
+        self.R_Q = 6
+        rng = np.random.default_rng(w.seed + 6)
+        mk = lambda shape, sig: to_device(ti.to_storage(rng.standard_normal(shape, dtype=np.float32) * sig,
+                                                        w.dtype), self.dims)
+        self.A_Q = mk((B, chunk, self.R_Q, w.h), 1.0)
+        self.B_Q = mk((B, chunk, self.R_Q, w.d_h), 1 / np.sqrt(w.d_h))
+        self.append(0)
+        torch.cuda.synchronize()
+
+    def append(self, i: int = 0):
+        """The chunk's factors into the cache (B_K rotated) and its query rows rotated."""
+        self.tpa.tpa_cache_append(self.dims, self.cache.buf, self.cache.capacity, self.slot, self.pos, self.c_AK,
+                                  self.c_BK, self.c_AV, self.c_BV, q_pos=self.pos, q_in=self.q, q_out=self.q_rot)
+
+    def prefill(self, i: int = 0, out=None):
+        w = self.w
+        self.tpa.tpa_prefill_chunk(self.dims, self.cache.buf, self.cache.capacity, self.cache.seq_start,
+                                   self.ctx_len, self.ctx, self.chunk,
+                                   self.q_rot.view(self.B, self.chunk, w.h, w.d_h), self.out if out is None else out)
+
+    def prefill_fq(self, i: int = 0):
+        self.tpa.tpa_prefill_chunk_fq(self.dims, self.cache.buf, self.cache.capacity, self.cache.seq_start,
+                                      self.ctx_len, self.ctx, self.chunk, self.A_Q, self.B_Q, self.out)
+
+    def legs(self, timer: Timer) -> dict:
+        return dict(prefill_ms=timer.median_call_ms(self.prefill, 5), append_ms=timer.median_call_ms(self.append, 5),
+                    prefill_fq_ms=timer.median_call_ms(self.prefill_fq, 5))
+
+
+def stream_probe(timer: Timer) -> dict:
+    """Achievable HBM read bandwidth: a 2 GiB buffer read once per launch by a plain streaming kernel
+    (libtpa_probe.so, built beside the library), best of two read orders x three grid sizes x two load
+    depths, median of 5 windows each."""
     import torch
-    import factorized_kv_cache_tpa_amd as tpa
-    import tpa_inputs as ti
-    from factorized_kv_cache_tpa_amd.cache import FactorCache, to_device
+    path = os.path.join(ROOT, "factorized_kv_cache_tpa_amd", "libtpa_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.tpa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    lib.tpa_probe_stream_read.restype = ctypes.c_int32
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    best, sweep = {}, []
+    for blocked in (0, 1):
+        for grid in (1024, 2048, 4096):
+            for in_flight in (8, 16):
+                sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
 
-    w = ti.get("c5")
-    dims = tpa.Dims(w.h, w.d_h, w.R_K, w.R_V, w.dtype, w.rope_base, cache_format)
-    seqs = ti.prefill_batch(w)
-    B, ctx, chunk = w.prefill_batch, w.prefill_ctx, w.prefill_chunk
-    cache = FactorCache(dims, [ctx + chunk] * B)
-    for b, s in enumerate(seqs):
-        cache.append_host(b, s.A_K, s.B_K, s.A_V, s.B_V)
-    q = to_device(np.stack([s.q for s in seqs]), dims).reshape(B * chunk, w.h, w.d_h)
-    q_pos = torch.arange(ctx, ctx + chunk, dtype=torch.int32, device="cuda").repeat(B)
-    q_rot = cache.rotate_queries(q, q_pos).reshape(B, chunk, w.h, w.d_h)
-    ctx_len = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
-    out = torch.empty(B, chunk, w.h, w.d_h, dtype=torch.float32, device="cuda")
-
-    # the same chunk with rank-6 factored query rows (full TPA), unrotated (row j is rotated at ctx + j on chip)
-    R_Q = 6
-    rng = np.random.default_rng(w.seed + 6)
-    mk = lambda shape, sig: to_device(ti.to_storage(rng.standard_normal(shape, dtype=np.float32) * sig, w.dtype),
-                                      dims)
-    A_Q = mk((B, chunk, R_Q, w.h), 1.0)
-    B_Q = mk((B, chunk, R_Q, w.d_h), 1 / np.sqrt(w.d_h))
-
-    def call():
-        tpa.tpa_prefill_chunk(dims, cache.buf, cache.capacity, cache.seq_start, ctx_len, ctx, chunk, q_rot, out)
-
-    def call_fq():
-        tpa.tpa_prefill_chunk_fq(dims, cache.buf, cache.capacity, cache.seq_start, ctx_len, ctx, chunk, A_Q, B_Q, out)
-
-    def timed(fn) -> float:
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
-            for _ in range(steps):
-                fn()
-        g.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / steps
-
-    ms = timed(call)
-    ms_fq = timed(call_fq)
-    pairs = B * sum(ctx + j + 1 for j in range(chunk))
-    flops = 4.0 * w.d_h * w.h * pairs
-    tf = flops / (ms / 1e3) / 1e12
-    return dict(workload=f"prefill_b{B}_ctx{ctx}_chunk{chunk}_h{w.h}_d{w.d_h}_r{w.R_K}_causal", ms=ms,
-                gflop=flops / 1e9, tflops=tf, mfma_frac=tf / MFMA_BF16_PEAK_TFLOPS, factored_query_rq6_ms=ms_fq)
+                def read(i, grid=grid, sink=sink, in_flight=in_flight, blocked=blocked):
+                    rc = lib.tpa_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                                   ctypes.c_void_p(sink.data_ptr()), grid, in_flight, blocked,
+                                                   ctypes.c_void_p(timer.stream.cuda_stream))
+                    if rc != 0:
+                        raise RuntimeError("stream probe launch failed")
+                ms = timer.median_call_ms(read, 4, min_calls=8)
+                gbps = nbytes / (ms / 1e3) / 1e9
+                sweep.append((blocked, grid, in_flight, round(gbps)))
+                if gbps > best.get("GBps", 0.0):
+                    best = dict(GBps=round(gbps, 1), order="blocked" if blocked else "grid-stride", grid=grid,
+                                loads_in_flight=in_flight, bytes=nbytes)
+    log(f"[stream probe] (blocked, grid, loads in flight, GB/s): {sweep}")
+    del buf
+    torch.cuda.empty_cache()
+    return best
 
 
-def cpu_baseline(name: str, budget_s: float = 12.0):
-    """The fp64 oracle on the host's cores over whole sequences of the same workload (bounded)."""
+def host_info() -> dict:
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return dict(nproc=len(os.sched_getaffinity(0)), cpu_model=model)
+
+
+def cpu_baseline(budget_decode: float = 12.0, budget_prefill: float = 8.0) -> dict:
+    """The fp64 oracle, as it stands, on the host's cores over a bounded sample of the headline workload:
+    whole decode sequences (cached-tokens/s) and whole prefill chunks (GFLOP/s of the causal-exact count).
+    Input generation is outside the timed part."""
     import oracle
     import tpa_inputs as ti
 
-    w = ti.get(name)
-    seqs = ti.decode_batch(w)
+    w = ti.get(HEADLINE)
     f = lambda a: ti.to_f64(a, w.dtype)
-    conv = [(f(s.A_K), f(s.B_K), f(s.A_V), f(s.B_V), f(s.q[0])) for s in seqs]
     threads = oracle.max_threads()
-    done_tokens, n_seq = 0, 0
-    t0 = time.perf_counter()
-    while True:
-        for args in conv:
-            oracle.decode(*args, w.rope_base, threads=threads)
-            done_tokens += args[0].shape[0]
-            n_seq += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return dict(value=done_tokens / dt, unit="cached-tokens/s", cores=threads, kind="oracle",
-                sample=f"{n_seq} decode sequences of {w.name} (4096 cached tokens each), fp64, "
-                       f"{dt:.1f}s wall")
+    done, n_seq, spent, b = 0, 0, 0.0, 0
+    while spent < budget_decode and b < w.batch:
+        s = ti.decode_sequence(w, b)
+        args = (f(s.A_K), f(s.B_K), f(s.A_V), f(s.B_V), f(s.q[0]))
+        t0 = time.perf_counter()
+        oracle.decode(*args, w.rope_base, threads=threads)
+        spent += time.perf_counter() - t0
+        done += s.n_tokens
+        n_seq += 1
+        b += 1
+    flops, n_pre, spent_p = 0.0, 0, 0.0
+    while spent_p < budget_prefill and n_pre < w.prefill_batch:
+        s = ti.prefill_sequence(w, n_pre)
+        args = (f(s.A_K), f(s.B_K), f(s.A_V), f(s.B_V), f(s.q))
+        t0 = time.perf_counter()
+        oracle.prefill(*args, w.prefill_ctx, w.rope_base, threads=threads)
+        spent_p += time.perf_counter() - t0
+        flops += 4.0 * w.d_h * w.h * sum(w.prefill_ctx + j + 1 for j in range(w.prefill_chunk))
+        n_pre += 1
+    return dict(value=round(done / spent, 1), unit="cached-tokens/s", cores=threads, kind="oracle",
+                sample=f"{n_seq} decode sequences ({done} cached tokens) of {w.name}, fp64, {spent:.1f}s",
+                prefill=dict(value=round(flops / spent_p / 1e9, 2), unit="GFLOP/s", kind="oracle",
+                             sample=f"{n_pre} prefill chunks of 512 rows over 2048 cached tokens, fp64, "
+                                    f"{spent_p:.1f}s"),
+                host=host_info())
+
+
+def run_profile_leg(leg: str, workload: str, calls: int, calibration: bool) -> None:
+    """Eager calls of one leg only, for rocprofv3 runs (kernel trace or counters)."""
+    import torch
+    if leg in ("step", "decode"):
+        b = DecodeBench(workload, min_bytes=4 * MALL_BYTES)
+        fn = b.step if leg == "step" else b.decode
+    elif leg in ("prefill", "append"):
+        p = PrefillBench()
+        fn = p.prefill if leg == "prefill" else p.append
+    else:
+        raise SystemExit(f"unknown leg {leg}")
+    for i in range(calls):
+        fn(i)
+    torch.cuda.synchronize()
+    if calibration:  # a plain 64 MiB device copy: the scale for the HBM byte counters
+        src = torch.empty(64 << 20, dtype=torch.uint8, device="cuda").fill_(7)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    log(f"profiled {calls} {leg} calls of {workload}")
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--no-extras", action="store_true", help="time only the main workload")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true", help="only the headline step and its legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--step-only", action="store_true",
-                    help="time only the fused step of the main workload (for profiled runs)")
-    ap.add_argument("--prefill-only", action="store_true",
-                    help="time only the causal prefill workload and print its own JSON line (for profiled runs)")
+    ap.add_argument("--profile-leg", choices=("step", "decode", "prefill", "append"),
+                    help="run --steps eager calls of one leg only (for rocprofv3) and exit")
+    ap.add_argument("--workload", default=HEADLINE, help="workload of --profile-leg step/decode")
     ap.add_argument("--calibration-copy", action="store_true",
-                    help="also run a plain 64 MiB device copy three times (scale reference for the HBM byte "
-                         "counters of a profiled run)")
+                    help="with --profile-leg: also run a plain 64 MiB device copy three times (the scale of "
+                         "the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the library runs on a "
-              f"single MI355X; see the sharding notes in the design document)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the library runs on a single "
+              f"MI355X; how the path would shard is described in the design notes)", file=sys.stderr)
         sys.exit(2)
 
     import torch
     import factorized_kv_cache_tpa_amd as tpa
     tpa.load()  # fails loudly when the HIP library is missing
     torch.cuda.set_device(0)
-
-    if args.prefill_only:
-        p = prefill_bench(max(5, args.steps // 10), 3)
-        print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in p.items()}), flush=True)
+    if args.profile_leg:
+        run_profile_leg(args.profile_leg, args.workload, args.steps, args.calibration_copy)
         return
 
-    main_b = DecodeBench(MAIN, min_bytes=4 * MALL_BYTES)
-    res = main_b.run(args.steps, args.warmup, step_only=args.step_only)
-    log(f"[{main_b.w.name}] fused step {res['ms_per_step'] * 1e3:.2f} us, {res['step_GBps']:.0f} GB/s")
-    extras = {}
-    if not args.step_only:
-        log(f"[{main_b.w.name}] two-call step {res['two_call_ms'] * 1e3:.2f} us, decode alone "
-            f"{res['decode_ms'] * 1e3:.2f} us, {res['decode_GBps']:.0f} GB/s, factored query (R_Q 6) "
-            f"{res['fq_ms'] * 1e3:.2f} us")
-        extras[main_b.w.name] = dict(two_call_step_us=round(res["two_call_ms"] * 1e3, 2),
-                                     decode_us=round(res["decode_ms"] * 1e3, 2),
-                                     decode_GBps=round(res["decode_GBps"], 1),
-                                     decode_hbm_frac=round(res["decode_GBps"] / HBM_PEAK_GBS, 4),
-                                     factored_query_rq6_decode_us=round(res["fq_ms"] * 1e3, 2),
-                                     factored_query_rq6_GBps=round(res["fq_GBps"], 1))
-    if not args.no_extras and not args.step_only:
-        for name in ("c3", "c4", "c5"):
-            b = DecodeBench(name, min_bytes=4 * MALL_BYTES)
-            r = b.run(max(10, args.steps // 4), max(3, args.warmup // 4))
-            extras[b.w.name] = dict(decode_us=round(r["decode_ms"] * 1e3, 2),
-                                    step_us=round(r["ms_per_step"] * 1e3, 2),
-                                    two_call_step_us=round(r["two_call_ms"] * 1e3, 2),
-                                    cached_tokens_per_s=round(r["decode_tokens_per_s"], 1),
-                                    GBps=round(r["decode_GBps"], 1),
-                                    hbm_frac=round(r["decode_GBps"] / HBM_PEAK_GBS, 4))
-            log(f"[{b.w.name}] decode {r['decode_ms'] * 1e3:.2f} us, {r['decode_GBps']:.0f} GB/s, fused step "
-                f"{r['ms_per_step'] * 1e3:.2f} us, factored query {r['fq_ms'] * 1e3:.2f} us")
-            del b
-            torch.cuda.empty_cache()
-        p = prefill_bench(max(5, args.steps // 10), 3)
-        pname = p.pop("workload")
-        extras[pname] = {k: round(v, 4) for k, v in p.items()}
-        log(f"[prefill] {p['ms'] * 1e3:.1f} us, {p['tflops']:.1f} TFLOP/s, {100 * p['mfma_frac']:.1f}% MFMA")
-        # the same workloads over an 8-bit (E4M3) factor cache: half the bytes per cached token
-        for name in (MAIN, "c3", "c4", "c5"):
-            b = DecodeBench(name, min_bytes=4 * MALL_BYTES, cache_format=tpa.TPA_CACHE_E4M3)
-            r = b.run(max(10, args.steps // 4), max(3, args.warmup // 4))
-            extras[b.w.name]["e4m3_cache"] = dict(
-                step_us=round(r["ms_per_step"] * 1e3, 2), step_cached_tokens_per_s=round(r["tokens_per_s"], 1),
-                two_call_step_us=round(r["two_call_ms"] * 1e3, 2), decode_us=round(r["decode_ms"] * 1e3, 2),
-                cached_tokens_per_s=round(r["decode_tokens_per_s"], 1), GBps=round(r["decode_GBps"], 1),
-                hbm_frac=round(r["decode_GBps"] / HBM_PEAK_GBS, 4),
-                factored_query_rq6_decode_us=round(r["fq_ms"] * 1e3, 2))
-            log(f"[{b.w.name}] E4M3 cache: fused step {r['ms_per_step'] * 1e3:.2f} us, decode "
-                f"{r['decode_ms'] * 1e3:.2f} us, {r['decode_GBps']:.0f} GB/s")
-            del b
-            torch.cuda.empty_cache()
-        p8 = prefill_bench(max(5, args.steps // 10), 3, cache_format=tpa.TPA_CACHE_E4M3)
-        extras[pname]["e4m3_cache"] = dict(ms=round(p8["ms"], 4), tflops=round(p8["tflops"], 1),
-                                           mfma_frac=round(p8["mfma_frac"], 4),
-                                           factored_query_rq6_ms=round(p8["factored_query_rq6_ms"], 4))
-        log(f"[prefill] E4M3 cache: {p8['ms'] * 1e3:.1f} us, {p8['tflops']:.1f} TFLOP/s")
+    timer = Timer()
+    dec = DecodeBench(HEADLINE, min_bytes=0)   # 5.8 GB: far beyond the last-level cache, one replica
+    pre = PrefillBench()
+    w = dec.w
 
-    achieved = res["step_GBps"]
+    def serving_step(i: int):
+        dec.step(0)
+        pre.append()
+        pre.prefill()
+
+    for _ in range(args.warmup):
+        serving_step(0)
+    torch.cuda.synchronize()
+    eager_dec, eager_pre = dec.out.clone(), pre.out.clone()
+    g = timer.capture(serving_step, 1)
+    g.replay()
+    torch.cuda.synchronize()
+    # the timed region: exactly `steps` steps, one graph replay each, events around every replay
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    with torch.cuda.stream(timer.stream):
+        ev[0].record(timer.stream)
+        for k in range(args.steps):
+            g.replay()
+            ev[k + 1].record(timer.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = ev[0].elapsed_time(ev[-1])
+    per_step = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
+    ms_step = total_ms / args.steps
+    if not (torch.equal(dec.out, eager_dec) and torch.equal(pre.out, eager_pre)):
+        raise RuntimeError("a graph replay of the serving step differs from the eager step")
+    log(f"[serving step] {ms_step * 1e3:.1f} us per step (median {np.median(per_step) * 1e3:.1f} us), "
+        f"wall {wall * 1e3:.1f} ms for {args.steps} steps")
+
+    d_legs = dec.legs(timer)
+    p_legs = pre.legs(timer)
+    step_gbps = dec.step_bytes / (d_legs["step_ms"] / 1e3) / 1e9
+    pre_tf = pre.flops / (p_legs["prefill_ms"] / 1e3) / 1e12
+    log(f"[{w.name}] decode step {d_legs['step_ms'] * 1e3:.1f} us ({step_gbps:.0f} GB/s), decode "
+        f"{d_legs['decode_ms'] * 1e3:.1f} us, two-call step {d_legs['two_call_ms'] * 1e3:.1f} us, factored query "
+        f"{d_legs['fq_ms'] * 1e3:.1f} us; append chunk {p_legs['append_ms'] * 1e3:.1f} us; prefill "
+        f"{p_legs['prefill_ms'] * 1e3:.1f} us ({pre_tf:.0f} TFLOP/s, {100 * pre_tf / MFMA_BF16_PEAK_TFLOPS:.1f}% "
+        f"MFMA), factored query {p_legs['prefill_fq_ms'] * 1e3:.1f} us")
+
+    traffic = profile_record("hbm_bytes_" + w.name, DECODE_SOURCES)
+    busy = profile_record("mfma_busy_prefill_b8_ctx2048_chunk512", PREFILL_SOURCES)
     line = {
         "metric": "factor-cache decode cached-tokens/s + HBM GB/s (% of roofline); prefill % MFMA",
-        "value": round(res["tokens_per_s"], 1),
+        "value": round(dec.tokens / (ms_step / 1e3), 1),
         "unit": "cached-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(res["ms_per_step"], 6),
+        "ms_per_step": round(ms_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded Gaussian factors; no dataset)",
-        "config": {"workload": main_b.w.name, "batch": main_b.batch, "cached_tokens_per_seq": main_b.max_len,
-                   "h": main_b.w.h, "d_h": main_b.w.d_h, "R_K": main_b.w.R_K, "R_V": main_b.w.R_V,
-                   "rope_base": main_b.w.rope_base, "cache_replicas": main_b.n_rep,
-                   "step": "tpa_decode_step: append the new token, rotate the query, attend (split + merge)"},
-        "roofline": {"kernel": "tpa_decode_step (split + merge kernels, timed back to back in a graph)",
-                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
-                     "algorithmic_bytes_per_launch": main_b.step_bytes,
-                     "avg_launch_us": round(res["ms_per_step"] * 1e3, 3)},
-        "extras": extras,
+        "config": {"workload": w.name, "decode_sequences": w.batch, "decode_cached_tokens": int(dec.tokens),
+                   "decode_len_range": [w.ragged_lo, w.ragged_hi], "prefill_sequences": w.prefill_batch,
+                   "prefill_ctx": w.prefill_ctx, "prefill_chunk": w.prefill_chunk, "h": w.h, "d_h": w.d_h,
+                   "R_K": w.R_K, "R_V": w.R_V, "rope_base": w.rope_base,
+                   "step": "tpa_decode_step (128 sequences) + tpa_cache_append (8 x 512-token chunk, query "
+                           "rows rotated) + tpa_prefill_chunk (causal)",
+                   "median_step_ms": round(float(np.median(per_step)), 6)},
+        "roofline": {"kernel": "tpa_decode_step (split + merge kernels)", "bound": "hbm",
+                     "achieved": round(step_gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(step_gbps / HBM_PEAK_GBS, 4),
+                     "traffic": traffic.get("step_call_traffic_bytes") if traffic else None,
+                     "algorithmic_bytes_per_launch": dec.step_bytes,
+                     "avg_launch_us": round(d_legs["step_ms"] * 1e3, 3)},
+        "roofline_prefill": {"kernel": "tpa_prefill_chunk (one launch)", "bound": "mfma",
+                             "achieved": round(pre_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(pre_tf / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flop_per_launch":
+                             pre.flops, "avg_launch_us": round(p_legs["prefill_ms"] * 1e3, 3),
+                             "mfma_busy_frac": busy.get("mfma_busy_frac") if busy else None},
+        "legs": {"decode_step_us": round(d_legs["step_ms"] * 1e3, 2),
+                 "decode_step_GBps": round(step_gbps, 1),
+                 "decode_us": round(d_legs["decode_ms"] * 1e3, 2),
+                 "decode_GBps": round(dec.bytes / (d_legs["decode_ms"] / 1e3) / 1e9, 1),
+                 "decode_hbm_frac": round(dec.bytes / (d_legs["decode_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "two_call_step_us": round(d_legs["two_call_ms"] * 1e3, 2),
+                 "factored_query_rq6_decode_us": round(d_legs["fq_ms"] * 1e3, 2),
+                 "append_chunk_us": round(p_legs["append_ms"] * 1e3, 2),
+                 "append_chunk_GBps": round(pre.append_bytes / (p_legs["append_ms"] / 1e3) / 1e9, 1),
+                 "prefill_us": round(p_legs["prefill_ms"] * 1e3, 2),
+                 "prefill_TFLOPs": round(pre_tf, 1),
+                 "factored_query_rq6_prefill_us": round(p_legs["prefill_fq_ms"] * 1e3, 2),
+                 "timing": f"median of {REPEATS} windows of graph replays, events on the replay stream"},
     }
-    del main_b
-    if args.calibration_copy:
-        src = torch.empty(64 << 20, dtype=torch.uint8, device="cuda").fill_(7)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+    del dec, pre, g
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        line["stream_probe_GBps"] = stream_probe(timer)
+        log(f"[stream probe] {line['stream_probe_GBps']}")
+        extras = {}
+        for name in ("c2", "c3", "c4"):
+            b = DecodeBench(name, min_bytes=4 * MALL_BYTES)
+            r = b.legs(timer)
+            tr = profile_record("hbm_bytes_" + b.w.name, DECODE_SOURCES)
+            gbps = b.bytes / (r["decode_ms"] / 1e3) / 1e9
+            extras[b.w.name] = dict(step_us=round(r["step_ms"] * 1e3, 2),
+                                    step_GBps=round(b.step_bytes / (r["step_ms"] / 1e3) / 1e9, 1),
+                                    step_hbm_frac=round(b.step_bytes / (r["step_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                                    decode_us=round(r["decode_ms"] * 1e3, 2),
+                                    cached_tokens_per_s=round(b.tokens / (r["decode_ms"] / 1e3), 1),
+                                    decode_GBps=round(gbps, 1), decode_hbm_frac=round(gbps / HBM_PEAK_GBS, 4),
+                                    two_call_step_us=round(r["two_call_ms"] * 1e3, 2),
+                                    factored_query_rq6_decode_us=round(r["fq_ms"] * 1e3, 2),
+                                    step_traffic_bytes=tr.get("step_call_traffic_bytes") if tr else None,
+                                    algorithmic_step_bytes=b.step_bytes, cache_replicas=b.n_rep)
+            log(f"[{b.w.name}] step {r['step_ms'] * 1e3:.2f} us, decode {r['decode_ms'] * 1e3:.2f} us "
+                f"({gbps:.0f} GB/s), two-call {r['two_call_ms'] * 1e3:.2f} us, fq {r['fq_ms'] * 1e3:.2f} us")
+            del b
+            torch.cuda.empty_cache()
+        # the same workloads over an 8-bit (E4M3) factor cache: half the bytes per cached token
+        for name in ("c2", "c3", "c4", HEADLINE):
+            b = DecodeBench(name, min_bytes=4 * MALL_BYTES, cache_format=tpa.TPA_CACHE_E4M3)
+            r = b.legs(timer)
+            gbps = b.bytes / (r["decode_ms"] / 1e3) / 1e9
+            extras.setdefault(b.w.name, {})["e4m3_cache"] = dict(
+                step_us=round(r["step_ms"] * 1e3, 2), decode_us=round(r["decode_ms"] * 1e3, 2),
+                cached_tokens_per_s=round(b.tokens / (r["decode_ms"] / 1e3), 1), GBps=round(gbps, 1),
+                hbm_frac=round(gbps / HBM_PEAK_GBS, 4), two_call_step_us=round(r["two_call_ms"] * 1e3, 2),
+                factored_query_rq6_decode_us=round(r["fq_ms"] * 1e3, 2))
+            log(f"[{b.w.name}] E4M3 cache: step {r['step_ms'] * 1e3:.2f} us, decode {r['decode_ms'] * 1e3:.2f} us, "
+                f"{gbps:.0f} GB/s of stored bytes")
+            del b
+            torch.cuda.empty_cache()
+        p8 = PrefillBench(cache_format=tpa.TPA_CACHE_E4M3)
+        r = p8.legs(timer)
+        extras["prefill_b8_ctx2048_chunk512_e4m3_cache"] = dict(
+            prefill_us=round(r["prefill_ms"] * 1e3, 2),
+            TFLOPs=round(p8.flops / (r["prefill_ms"] / 1e3) / 1e12, 1),
+            mfma_frac=round(p8.flops / (r["prefill_ms"] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            factored_query_rq6_prefill_us=round(r["prefill_fq_ms"] * 1e3, 2))
+        log(f"[prefill] E4M3 cache: {r['prefill_ms'] * 1e3:.1f} us")
+        del p8
+        line["extras"] = extras
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(MAIN)
+        line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
 
 

@@ -15,6 +15,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libtpa.so")
 SOURCES = ["api.hip", "append.hip", "decode.hip", "prefill.hip"]
+# measurement helper for the benchmark (a plain streaming read), built beside the library, not part of it
+PROBE_SOURCE = "stream_probe.hip"
+PROBE_OUT = os.path.join(HERE, "libtpa_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -30,19 +33,24 @@ def _compile(src: str, obj_dir: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    obj_dir = os.path.join(HERE, "_build")
-    os.makedirs(obj_dir, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, obj_dir), SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, obj_dir), SOURCES + [PROBE_SOURCE]))
+    _link(objs[:-1], OUT)
+    _link(objs[-1:], PROBE_OUT)
     if verbose:
-        print(f"built {OUT}", file=sys.stderr)
+        print(f"built {OUT} and {PROBE_OUT}", file=sys.stderr)
     return OUT
 
 

@@ -57,59 +57,56 @@ __device__ __forceinline__ int vpos(int k) { return (k & ~15) | ((k & 4) << 1) |
 // a 32x32x16 product supplies (features 16 ks + 8 hi + e, e < 8):
 //     q[d] = (1/R_Q) sum_r A_Q[jq][r][head] B_Q[jq][r][d]    (TPA notes page, tensor product decomposition
 //                                                             applied to Q)
-// summed in fp32, then rotated to the row's position pos with the append's arithmetic (fp64 angle
-// reduction, fp32 rotation; RoPE is linear, so rotating the combined row equals combining rotated B_Q
-// rows), and rounded once to bf16.  Rows past the chunk are zeros.
+// summed in fp32, then rotated to the row's position pos (RoPE is linear, so rotating the combined row equals
+// combining rotated B_Q rows), and rounded once to bf16.  Rows past the chunk are zeros.  The angle
+// pos * theta_j is reduced in fp64 to a fraction of a turn, whose sine and cosine come from the hardware
+// v_sin_f32 / v_cos_f32 (absolute error ~1e-6, far below the bf16 rounding that follows); the library's
+// sincosf would be as exact as the append's, but 32 of them per row block overflow the register budget of
+// the wide form into scratch memory.
 template <int KS>
 __device__ __forceinline__ void factored_query_row(const PrefillParams &p, int b, int jq, int head, int hi, int pos,
                                                    bf16x8 *qf) {
-    float x[KS][8] = {};
-    if (jq < p.chunk) {
-        const int64_t row = int64_t(b) * p.chunk + jq;
-        const uint16_t *aq = reinterpret_cast<const uint16_t *>(p.a_q) + row * p.r_q * p.h + head;
-        const uint16_t *bq = reinterpret_cast<const uint16_t *>(p.q) + row * p.r_q * p.d_h;
-        for (int r = 0; r < p.r_q; ++r) {
-            const float a = bf16_to_f32(aq[r * p.h]);
+    constexpr double kInvTwoPi = 0.15915494309189535;
+    const int64_t row = int64_t(b) * p.chunk + jq;
+    const uint16_t *aq = reinterpret_cast<const uint16_t *>(p.a_q) + row * p.r_q * p.h + head;
+    const uint16_t *bq = reinterpret_cast<const uint16_t *>(p.q) + row * p.r_q * p.d_h;
+    const float inv_rq = 1.f / float(p.r_q);
+    // one 8-feature fragment at a time (summed over the rank, rotated, packed), so that only its eight sums
+    // are live next to the fragments already built
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int d0 = 16 * ks + 8 * hi;
+    for (int ks = 0; ks < KS; ++ks) {
+        const int d0 = 16 * ks + 8 * hi;
+        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (jq < p.chunk && d0 < p.d_h) {
+            for (int r = 0; r < p.r_q; ++r) {
+                const float a = bf16_to_f32(aq[r * p.h]);
                 if ((p.d_h & 7) == 0) {
-                    if (d0 < p.d_h) {
-                        const uint4 v = *reinterpret_cast<const uint4 *>(bq + r * p.d_h + d0);
-                        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+                    const uint4 v = *reinterpret_cast<const uint4 *>(bq + r * p.d_h + d0);
+                    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            x[ks][e] = fmaf(a, __uint_as_float((e & 1) ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16)),
-                                            x[ks][e]);
-                    }
+                    for (int e = 0; e < 8; ++e)
+                        x[e] = fmaf(a, __uint_as_float((e & 1) ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16)), x[e]);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        if (d0 + e < p.d_h) x[ks][e] = fmaf(a, bf16_to_f32(bq[r * p.d_h + d0 + e]), x[ks][e]);
+                        if (d0 + e < p.d_h) x[e] = fmaf(a, bf16_to_f32(bq[r * p.d_h + d0 + e]), x[e]);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const int d = d0 + e;  // even: the pair (d, d + 1)
+                if (d < p.d_h) {
+                    const double turns = double(pos) * (p.rope.theta[d >> 1] * kInvTwoPi);
+                    const float t = float(turns - rint(turns));  // in [-1/2, 1/2]
+                    const float c = __builtin_amdgcn_cosf(t), sn = __builtin_amdgcn_sinf(t);
+                    float y0, y1;
+                    rope_rotate(x[e], x[e + 1], c, sn, y0, y1);
+                    x[e] = y0 * inv_rq;
+                    x[e + 1] = y1 * inv_rq;
                 }
             }
         }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const int d = 16 * ks + 8 * hi + e;  // even: the pair (d, d + 1)
-                if (d < p.d_h) {
-                    float cs[2];
-                    rope_cos_sin<uint16_t>(cs, double(pos), p.rope.theta[d >> 1]);
-                    float y0, y1;
-                    rope_rotate(x[ks][e], x[ks][e + 1], cs[0], cs[1], y0, y1);
-                    x[ks][e] = y0;
-                    x[ks][e + 1] = y1;
-                }
-            }
-    }
-    const float inv_rq = 1.f / float(p.r_q);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[ks][e] *= inv_rq;
-        qf[ks] = pack8(x[ks]);
+        qf[ks] = pack8(x);
     }
 }
 
