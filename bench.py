@@ -297,8 +297,8 @@ class PrefillBench:
 
 def stream_probe(timer: Timer) -> dict:
     """Achievable HBM read bandwidth: a 2 GiB buffer read once per launch by a plain streaming kernel
-    (libtpa_probe.so, built beside the library), best of two read orders x three grid sizes x two load
-    depths, median of 5 windows each."""
+    (libtpa_probe.so, built beside the library), best of two read orders x three grid sizes (one to four
+    4-wave work-groups per compute unit) x two load depths, median of 5 windows each."""
     import torch
     path = os.path.join(ROOT, "factorized_kv_cache_tpa_amd", "libtpa_probe.so")
     lib = ctypes.CDLL(path)
@@ -309,7 +309,7 @@ def stream_probe(timer: Timer) -> dict:
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     best, sweep = {}, []
     for blocked in (0, 1):
-        for grid in (1024, 2048, 4096):
+        for grid in (256, 512, 1024):
             for in_flight in (8, 16):
                 sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
 
@@ -404,6 +404,163 @@ def run_profile_leg(leg: str, workload: str, calls: int, calibration: bool) -> N
     log(f"profiled {calls} {leg} calls of {workload}")
 
 
+# ---- rocprofv3 summaries (profiles/): kernel traces, HBM byte counters, matrix-core counters -------------
+
+PROFILE_COMMANDS = {
+    "kt": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/{dir} -o run --output-format csv -- "
+          "python3 bench.py --profile-leg {leg}{wl} --steps 30",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/fetch_{w} -o run --output-format csv -- "
+             "python3 bench.py --profile-leg step --workload {w} --steps 12 --calibration-copy",
+    "write": "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/write_{w} -o run --output-format csv -- "
+             "python3 bench.py --profile-leg step --workload {w} --steps 12 --calibration-copy",
+    "mfma": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+            "-d gpurun_out/prof/mfma_prefill -o run --output-format csv -- python3 bench.py --profile-leg prefill "
+            "--steps 20",
+}
+SUMMARY_COMMAND = "python3 bench.py --summarize-profiles gpurun_out/prof"
+
+
+def _kernel_label(name: str) -> str:
+    import re
+    m = re.search(r"tpa::\(anonymous namespace\)::(\w+?)_kernel(<[^()]*>)?", name)
+    return (m.group(1) + (m.group(2) or "")) if m else name.split("(")[0].replace("void ", "")[:60]
+
+
+def _rows(path):
+    import csv
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def summarize_profiles(raw: str) -> None:
+    """Turn the raw rocprofv3 CSV output of the committed commands above into the summaries under profiles/."""
+    import tpa_inputs as ti
+    os.makedirs(PROFILES, exist_ok=True)
+    header = ("Commands (from the repository root, on one MI355X; each pass a run of its own, then the "
+              f"summary):\n\n")
+    # kernel traces
+    traces = [(f"kt_step_{c}", "step", c, "decode_step_" + ti.get(c).name) for c in ("c2", "c3", "c4", "c5")]
+    traces += [("kt_prefill", "prefill", None, "prefill_b8_ctx2048_chunk512_h32_d128_r4"),
+               ("kt_append", "append", None, "append_chunk_b8x512_h32_d128_r4")]
+    for d, leg, c, label in traces:
+        path = os.path.join(raw, d, "run_kernel_stats.csv")
+        if not os.path.exists(path):
+            continue
+        cmd = PROFILE_COMMANDS["kt"].format(dir=d, leg=leg, wl=f" --workload {c}" if c else "")
+        lines = [f"# rocprofv3 kernel trace: {label}", "", header + f"    {cmd}\n    {SUMMARY_COMMAND}", "",
+                 "Every kernel the run launched under the library's name (the workload's cache build included):", "",
+                 "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for r in _rows(path):
+            if "tpa::" not in r["Name"]:
+                continue
+            lines.append(f"| `{_kernel_label(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+        with open(os.path.join(PROFILES, f"kernel_trace_{label}.md"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+    # the default benchmark command itself (all workloads; graph-launched calls are traced too)
+    path = os.path.join(raw, "kt_bench", "run_kernel_stats.csv")
+    if os.path.exists(path):
+        cmd = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof/kt_bench -o run --output-format csv -- "
+               "python3 bench.py --steps 20 --warmup 5 --no-cpu")
+        lines = ["# rocprofv3 kernel trace: the default benchmark run (every workload)", "",
+                 header + f"    {cmd}\n    {SUMMARY_COMMAND}", "",
+                 "Each decode workload has its own kernel instantiation (rank 4: the ragged workload; rank 2 with "
+                 "h=32: 4 x 131072; h=16: 64 x 8192; rank 1: 16 x 4096; `..., true>` instantiations: the E4M3 "
+                 "cache; mode 1: the fused step, 0: tpa_decode, 2: factored query).  `prefill2<32, 128, 4, false>` "
+                 "is the serving step's prefill and its timed leg.", "",
+                 "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for r in _rows(path):
+            if "tpa::" not in r["Name"]:
+                continue
+            lines.append(f"| `{_kernel_label(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+        with open(os.path.join(PROFILES, "kernel_trace_all_workloads.md"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+    # HBM bytes of the decode step, scaled by what the same counters read for a plain 64 MiB copy
+    for c in ("c2", "c3", "c4", "c5"):
+        fpath, wpath = (os.path.join(raw, f"{k}_{c}", "run_counter_collection.csv") for k in ("fetch", "write"))
+        if not (os.path.exists(fpath) and os.path.exists(wpath)):
+            continue
+        w = ti.get(c)
+        per = {}
+        scale = {}
+        for key, path, counter in (("fetch", fpath, "FETCH_SIZE"), ("write", wpath, "WRITE_SIZE")):
+            rows = [r for r in _rows(path) if r["Counter_Name"] == counter]
+            copies = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"] == "__amd_rocclr_copyBuffer"][-3:]
+            scale[key] = 65536.0 / float(np.mean(copies))
+            for r in rows:
+                if "decode_split_kernel" in r["Kernel_Name"] or "decode_merge_kernel" in r["Kernel_Name"]:
+                    per.setdefault(_kernel_label(r["Kernel_Name"]), {}).setdefault(key, []).append(
+                        float(r["Counter_Value"]))
+        kernels = {k: {"fetch_kib": float(np.mean(v["fetch"])), "write_kib": float(np.mean(v["write"])),
+                       "dispatches": len(v["fetch"]),
+                       "fetch_bytes": float(np.mean(v["fetch"])) * 1024 * scale["fetch"],
+                       "write_bytes": float(np.mean(v["write"])) * 1024 * scale["write"]} for k, v in per.items()}
+        traffic = sum(k["fetch_bytes"] + k["write_bytes"] for k in kernels.values())
+        lens = ti.decode_lengths(w)
+        alg = step_bytes(w, lens)
+        rec = {"source_hash": source_hash(DECODE_SOURCES), "workload": w.name, "step_call_traffic_bytes": traffic,
+               "algorithmic_step_bytes": alg, "fetch_scale": scale["fetch"], "write_scale": scale["write"],
+               "kernels": kernels}
+        name = "hbm_bytes_" + w.name
+        with open(os.path.join(PROFILES, name + ".json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        lines = [f"# rocprofv3 HBM byte counters: tpa_decode_step on {w.name}", "",
+                 header + "    " + PROFILE_COMMANDS["fetch"].format(w=c) + "\n    " +
+                 PROFILE_COMMANDS["write"].format(w=c) + f"\n    {SUMMARY_COMMAND}", "",
+                 f"Calibration: the same runs copy 64 MiB three times with a plain device copy; its FETCH_SIZE and "
+                 f"WRITE_SIZE give the scales {scale['fetch']:.3f} and {scale['write']:.3f} (bytes per counted "
+                 "KiB / 1024).", "",
+                 "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched MB (scaled) | written MB (scaled) |",
+                 "|---|---|---|---|---|---|"]
+        for k, v in kernels.items():
+            lines.append(f"| `{k}` | {v['dispatches']} | {v['fetch_kib']:.0f} | {v['write_kib']:.0f} | "
+                         f"{v['fetch_bytes'] / 1e6:.2f} | {v['write_bytes'] / 1e6:.2f} |")
+        lines += ["", f"Per `tpa_decode_step` call (split + merge): {traffic / 1e6:.2f} MB of HBM traffic against "
+                      f"{alg / 1e6:.2f} MB algorithmic ({traffic / alg:.3f}x).",
+                  f"Decode source hash (decode.hip + common.h + api.hip): `{rec['source_hash']}`."]
+        with open(os.path.join(PROFILES, name + ".md"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+    # matrix-core use of the prefill
+    mpath = os.path.join(raw, "mfma_prefill", "run_counter_collection.csv")
+    if os.path.exists(mpath):
+        vals, dur = {}, []
+        for r in _rows(mpath):
+            if "prefill" not in r["Kernel_Name"] or "tpa::" not in r["Kernel_Name"]:
+                continue
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                dur.append((float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-9)
+        mean = {k: float(np.mean(v)) for k, v in vals.items()}
+        xcd_cycles = mean["GRBM_GUI_ACTIVE"] / 8
+        t = float(np.mean(dur))
+        clock = xcd_cycles / t
+        busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * 1024)
+        flop = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        w = ti.get(HEADLINE)
+        alg = 4.0 * w.d_h * w.h * w.prefill_batch * sum(w.prefill_ctx + j + 1 for j in range(w.prefill_chunk))
+        rec = {"source_hash": source_hash(PREFILL_SOURCES), "mfma_busy_frac": busy, "clock_GHz": clock / 1e9,
+               "dispatch_s": t, "flop_executed": flop, "flop_algorithmic": alg, "counters": mean}
+        with open(os.path.join(PROFILES, "mfma_busy_prefill_b8_ctx2048_chunk512.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        lines = ["# rocprofv3 counters: matrix-core use of the causal prefill (8 x (2048 + 512), h=32, d_h=128, "
+                 "R=4, bf16)", "", header + "    " + PROFILE_COMMANDS["mfma"] + f"\n    {SUMMARY_COMMAND}", "",
+                 f"Kernel: the prefill's wide form, {len(dur)} dispatches; means per dispatch (chip totals):", "",
+                 "| counter | value | reading |", "|---|---|---|",
+                 f"| GRBM_GUI_ACTIVE | {mean['GRBM_GUI_ACTIVE']:.4g} (8 XCDs) | {xcd_cycles:.4g} cycles per XCD "
+                 f"over the {t * 1e6:.0f} us dispatch: clock {clock / 1e9:.2f} GHz |",
+                 f"| SQ_INSTS_VALU_MFMA_MOPS_BF16 | {mean['SQ_INSTS_VALU_MFMA_MOPS_BF16']:.4g} | x 512 flop = "
+                 f"{flop / 1e9:.1f} GFLOP executed ({alg / 1e9:.2f} causal-exact: {alg / flop:.0%} useful) |",
+                 f"| SQ_VALU_MFMA_BUSY_CYCLES | {mean['SQ_VALU_MFMA_BUSY_CYCLES']:.4g} | / ({xcd_cycles:.4g} cycles "
+                 f"x 1024 SIMDs) = **{busy:.1%} matrix-core busy** |",
+                 f"| SQ_BUSY_CU_CYCLES | {mean['SQ_BUSY_CU_CYCLES']:.4g} | |", "",
+                 f"Cross-check: {flop / 1e9:.1f} GFLOP in {t * 1e6:.0f} us = {flop / t / 1e12:.0f} TFLOP/s = "
+                 f"{flop / t / (clock * 256 * 4 * 1024):.1%} of the peak at the measured clock.",
+                 f"Prefill source hash (prefill.hip + common.h + api.hip): `{rec['source_hash']}`."]
+        with open(os.path.join(PROFILES, "mfma_busy_prefill_b8_ctx2048_chunk512.md"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -414,10 +571,15 @@ def main():
     ap.add_argument("--profile-leg", choices=("step", "decode", "prefill", "append"),
                     help="run --steps eager calls of one leg only (for rocprofv3) and exit")
     ap.add_argument("--workload", default=HEADLINE, help="workload of --profile-leg step/decode")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write the profiles/ summaries from the raw rocprofv3 output of the profiling commands")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="with --profile-leg: also run a plain 64 MiB device copy three times (the scale of "
                          "the HBM byte counters)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the library runs on a single "
               f"MI355X; how the path would shard is described in the design notes)", file=sys.stderr)

@@ -50,6 +50,8 @@ def _load():
         I64 = ctypes.POINTER(ctypes.c_int64)
         lib.tpa_oracle_rope_row.argtypes = [D, ctypes.c_int, ctypes.c_double, ctypes.c_double]
         lib.tpa_oracle_rope_row.restype = None
+        lib.tpa_oracle_rope_rows.argtypes = [D, ctypes.c_int64, ctypes.c_int, D, ctypes.c_double, ctypes.c_int]
+        lib.tpa_oracle_rope_rows.restype = None
         lib.tpa_oracle_attention.argtypes = [ctypes.c_int] * 4 + [ctypes.c_int64] + [D] * 5 + [
             ctypes.c_int64, D, D, I64, ctypes.c_double, ctypes.c_double, D, ctypes.c_int]
         lib.tpa_oracle_attention.restype = ctypes.c_int
@@ -88,6 +90,18 @@ def rope_rows(x: np.ndarray, pos: float, base: float) -> np.ndarray:
         row = np.ascontiguousarray(flat[r])
         lib.tpa_oracle_rope_row(_dp(row), int(row.shape[0]), float(pos), float(base))
         flat[r] = row
+    return y
+
+
+def rope_rows_at(x: np.ndarray, pos, base: float, threads: Optional[int] = None) -> np.ndarray:
+    """Standard RoPE of every last-axis row of x at its own position: pos has the shape of x without the last
+    axis (or broadcasts to it).  Each row is rotated exactly as rope_rows rotates it; returns a copy."""
+    y = _f64(x).copy()
+    d = y.shape[-1]
+    p = np.ascontiguousarray(np.broadcast_to(np.asarray(pos, dtype=np.float64), y.shape[:-1]))
+    n = int(np.prod(y.shape[:-1]))
+    _load().tpa_oracle_rope_rows(_dp(y), n, int(d), _dp(p), float(base),
+                                 int(threads if threads is not None else max_threads()))
     return y
 
 

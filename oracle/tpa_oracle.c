@@ -51,6 +51,14 @@ void tpa_oracle_rope_row(double *x, int d, double pos, double base) {
     }
 }
 
+/* Step 2 for many rows at once: row k of x (d values) rotated to position pos[k] in place, each row exactly as
+ * tpa_oracle_rope_row rotates it (a loop over rows, nothing shared between them). */
+void tpa_oracle_rope_rows(double *x, int64_t n_rows, int d, const double *pos, double base, int n_threads) {
+    if (n_threads < 1) n_threads = 1;
+#pragma omp parallel for schedule(static) num_threads(n_threads)
+    for (int64_t k = 0; k < n_rows; ++k) tpa_oracle_rope_row(x + k * d, d, pos[k], base);
+}
+
 /* Step 1 for one head row i of one token: row = (1/R) sum_r A[r][i] * B[r][:]. */
 static void materialize_row(double *row, int h, int d, int R, const double *A /* [R][h] */,
                             const double *B /* [R][d] */, int i) {
@@ -133,8 +141,6 @@ int tpa_oracle_attention(int h, int d, int RK, int RV, int64_t n_kv, const doubl
     return bad ? -1 : 0;
 }
 
-/* Per-token element counts the pages compare (tensor product decomposition paragraph):
- * a TPA cache holds (R_K + R_V)(h + d_h) elements per token, a dense MHA cache 2 h d_h. */
 /* Query rows from query factors (full TPA: the tensor product decomposition applied to Q, same page,
  * Key design: tensor product decomposition):  q[n][i][c] = (1/R_Q) sum_r A_Q[n][r][i] B_Q[n][r][c],
  * A_Q [n][R_Q][h], B_Q [n][R_Q][d] (unrotated), out [n][h][d].  The result is the query of step 3 above,
@@ -192,6 +198,8 @@ void tpa_oracle_e4m3_encode_n(int64_t n, const double *x, uint8_t *out) {
     for (int64_t i = 0; i < n; ++i) out[i] = tpa_oracle_e4m3_encode(x[i]);
 }
 
+/* Per-token element counts the pages compare (tensor product decomposition paragraph):
+ * a TPA cache holds (R_K + R_V)(h + d_h) elements per token, a dense MHA cache 2 h d_h. */
 int64_t tpa_oracle_factor_elems_per_token(int h, int d, int RK, int RV) {
     return (int64_t)(RK + RV) * (int64_t)(h + d);
 }

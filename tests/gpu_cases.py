@@ -198,8 +198,10 @@ def stored_factors(s: ti.Sequence, n: int, w: ti.Workload, dims: tpa.Dims):
     if dims.cache_format != tpa.TPA_CACHE_E4M3:
         return A_K, B_K, A_V, B_V
     A_K, A_V, B_V = e4m3_values(A_K, dims.scale(0)), e4m3_values(A_V, dims.scale(2)), e4m3_values(B_V, dims.scale(3))
-    B_K = np.stack([oracle.rope_rows(e4m3_values(oracle.rope_rows(B_K[t], t, w.rope_base), dims.scale(1)), -t,
-                                     w.rope_base) for t in range(n)]) if n else B_K
+    if n:
+        pos = np.arange(n, dtype=np.float64)[:, None]  # token t's rank rows sit at position t
+        B_K = oracle.rope_rows_at(e4m3_values(oracle.rope_rows_at(B_K, pos, w.rope_base), dims.scale(1)), -pos,
+                                  w.rope_base)
     return A_K, B_K, A_V, B_V
 
 

@@ -370,3 +370,28 @@ def test_step_misaligned_start_gives_nan_and_writes_nothing():
     blk = tpa.tpa_cache_bytes(st.dims, tpa.tpa_block_tokens(st.dims))
     assert changed.numel() > 0
     assert int(changed.min()) >= (40 // 32) * blk and int(changed.max()) < (40 // 32 + 1) * blk
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+def test_storage_accuracy_on_the_measured_workloads(name):
+    """What 8-bit factor storage costs in accuracy (the TPA notes page lists TPA with quantization as
+    unexplored): the E4M3 path at full size, compared (a) with the oracle on the values the cache stores
+    (parity, the usual bound) and (b) with the oracle on the unquantized bf16 factors (the storage error,
+    reported; a sanity bound only).  The ragged workload checks its first 8 sequences."""
+    w = ti.get(name)
+    only = list(range(8)) if name == "c5" else None
+    seqs = ti.decode_batch(w, only=only)
+    say(f"case: E4M3 storage accuracy on {w.name}")
+    s = DecodeSetup(w, seqs, dims=dims_of(w, E4M3))
+    got = s.run()
+    stored = np.stack([s.oracle(b) for b in range(s.batch)])
+    assert_close(got, stored, w.dtype, "against the stored values")
+    exact = np.stack([oracle.decode(*(f64(x, w.dtype) for x in (sq.A_K, sq.B_K, sq.A_V, sq.B_V, sq.q[0])),
+                                    w.rope_base) for sq in seqs])
+    max_abs = float(np.abs(got - exact).max())
+    rel = float(np.linalg.norm(got - exact) / np.linalg.norm(exact))
+    st_abs = float(np.abs(stored - exact).max())
+    st_rel = float(np.linalg.norm(stored - exact) / np.linalg.norm(exact))
+    say(f"  E4M3 storage error vs the bf16 factors: kernel max_abs={max_abs:.3e} rel_l2={rel:.3e}; "
+        f"exact attention over the stored values max_abs={st_abs:.3e} rel_l2={st_rel:.3e}")
+    assert np.isfinite(got).all() and rel < 0.1

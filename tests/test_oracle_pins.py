@@ -355,3 +355,13 @@ def test_e4m3_encode_matches_torch_in_range():
     codes = np.arange(256, dtype=np.uint8)
     tv = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
     np.testing.assert_array_equal(oracle.e4m3_decode(codes), tv)
+
+
+def test_rope_rows_at_equals_row_by_row_rotation():
+    """The batched rotation is the per-row rotation, row for row, at each row's own position."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((7, 3, 16))
+    pos = rng.integers(0, 100000, size=(7, 1)).astype(np.float64)
+    got = oracle.rope_rows_at(x, pos, 500000.0)
+    for t in range(7):
+        np.testing.assert_array_equal(got[t], oracle.rope_rows(x[t], float(pos[t, 0]), 500000.0))

@@ -56,10 +56,11 @@ def test_round_to_bf16_is_the_nearest_neighbour():
                                   torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy())
 
 
-def _stored(x: np.ndarray, pos: float, base: float) -> np.ndarray:
-    """What a bf16 buffer of x rotated to pos holds, rotated back exactly (so the oracle, which rotates
-    whole rows itself, sees exactly the stored rotated values)."""
-    return oracle.rope_rows(oracle.round_to_bf16(oracle.rope_rows(x, pos, base)), -pos, base)
+def _stored(x: np.ndarray, pos, base: float) -> np.ndarray:
+    """What a bf16 buffer of x's rows rotated to pos holds (pos: per row, broadcast), rotated back exactly, so
+    the oracle, which rotates whole rows itself, sees exactly the stored rotated values."""
+    pos = np.asarray(pos, dtype=np.float64)
+    return oracle.rope_rows_at(oracle.round_to_bf16(oracle.rope_rows_at(x, pos, base)), -pos, base)
 
 
 @pytest.mark.parametrize("h,d_h", [(32, 128), (16, 64), (64, 64)])
@@ -73,7 +74,7 @@ def test_storage_floor_of_sharp_rank1_decode(h, d_h):
     for s, n in zip(seqs, lens):
         A_K, B_K, A_V, B_V, q = (ti.to_f64(x, w.dtype) for x in (s.A_K, s.B_K, s.A_V, s.B_V, s.q[:1]))
         refs.append(oracle.attention(A_K, B_K, A_V, B_V, np.arange(n), q, [n], [n], w.rope_base)[0])
-        B_K_st = np.stack([_stored(B_K[t], t, w.rope_base) for t in range(n)])
+        B_K_st = _stored(B_K, np.arange(n, dtype=np.float64)[:, None], w.rope_base)
         q_st = _stored(q, n, w.rope_base)
         stos.append(oracle.attention(A_K, B_K_st, A_V, B_V, np.arange(n), q_st, [n], [n], w.rope_base)[0])
     ref, sto = np.stack(refs), np.stack(stos)
@@ -92,7 +93,7 @@ def test_storage_floor_is_small_on_the_measured_workloads():
         A_K, B_K, A_V, B_V, q = (ti.to_f64(x[:n] if x is not s.q else x[:1], w.dtype)
                                  for x in (s.A_K, s.B_K, s.A_V, s.B_V, s.q))
         ref = oracle.attention(A_K, B_K, A_V, B_V, np.arange(n), q, [n], [n], w.rope_base)[0]
-        B_K_st = np.stack([_stored(B_K[t], t, w.rope_base) for t in range(n)])
+        B_K_st = _stored(B_K, np.arange(n, dtype=np.float64)[:, None], w.rope_base)
         sto = oracle.attention(A_K, B_K_st, A_V, B_V, np.arange(n), _stored(q, n, w.rope_base), [n], [n],
                                w.rope_base)[0]
         assert np.abs(sto - ref).max() < 1e-3
