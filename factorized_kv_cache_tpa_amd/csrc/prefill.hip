@@ -67,46 +67,74 @@ template <int KS>
 __device__ __forceinline__ void factored_query_row(const PrefillParams &p, int b, int jq, int head, int hi, int pos,
                                                    bf16x8 *qf) {
     constexpr double kInvTwoPi = 0.15915494309189535;
-    const int64_t row = int64_t(b) * p.chunk + jq;
-    const uint16_t *aq = reinterpret_cast<const uint16_t *>(p.a_q) + row * p.r_q * p.h + head;
-    const uint16_t *bq = reinterpret_cast<const uint16_t *>(p.q) + row * p.r_q * p.d_h;
+    constexpr int KH = KS / 2;  // fragments per half
+    const bool row = jq < p.chunk;
+    const int64_t rw = int64_t(b) * p.chunk + jq;
+    const uint16_t *aq = reinterpret_cast<const uint16_t *>(p.a_q) + rw * p.r_q * p.h + head;
+    const uint16_t *bq = reinterpret_cast<const uint16_t *>(p.q) + rw * p.r_q * p.d_h;
     const float inv_rq = 1.f / float(p.r_q);
-    // one 8-feature fragment at a time (summed over the rank, rotated, packed), so that only its eight sums
-    // are live next to the fragments already built
+    const bool vec = (p.d_h & 7) == 0;
+    // Half the fragments at a time (their 8 KH sums live), two factor rows per round of loads: every load of a
+    // round is issued before any is used, so the build costs R_Q rounds of load latency in all.
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int d0 = 16 * ks + 8 * hi;
-        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (jq < p.chunk && d0 < p.d_h) {
-            for (int r = 0; r < p.r_q; ++r) {
-                const float a = bf16_to_f32(aq[r * p.h]);
-                if ((p.d_h & 7) == 0) {
-                    const uint4 v = *reinterpret_cast<const uint4 *>(bq + r * p.d_h + d0);
-                    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    for (int half = 0; half < 2; ++half) {
+        float x[KH][8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        x[e] = fmaf(a, __uint_as_float((e & 1) ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16)), x[e]);
-                } else {
+        for (int k = 0; k < KH; ++k)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (d0 + e < p.d_h) x[e] = fmaf(a, bf16_to_f32(bq[r * p.d_h + d0 + e]), x[e]);
+            for (int e = 0; e < 8; ++e) x[k][e] = 0.f;
+        if (row) {
+            for (int r = 0; r < p.r_q; r += 2) {
+                const bool two = r + 1 < p.r_q;
+                const float a0 = bf16_to_f32(aq[r * p.h]);
+                const float a1 = two ? bf16_to_f32(aq[(r + 1) * p.h]) : 0.f;
+                uint4 v0[KH], v1[KH];
+#pragma unroll
+                for (int k = 0; k < KH; ++k) {
+                    const int d0 = 16 * (half * KH + k) + 8 * hi;
+                    v0[k] = v1[k] = make_uint4(0, 0, 0, 0);
+                    if (vec && d0 < p.d_h) {
+                        v0[k] = *reinterpret_cast<const uint4 *>(bq + r * p.d_h + d0);
+                        if (two) v1[k] = *reinterpret_cast<const uint4 *>(bq + (r + 1) * p.d_h + d0);
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < KH; ++k) {
+                    const int d0 = 16 * (half * KH + k) + 8 * hi;
+                    const uint32_t w0[4] = {v0[k].x, v0[k].y, v0[k].z, v0[k].w};
+                    const uint32_t w1[4] = {v1[k].x, v1[k].y, v1[k].z, v1[k].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float b0, b1;
+                        if (vec) {
+                            b0 = __uint_as_float((e & 1) ? (w0[e >> 1] & 0xffff0000u) : (w0[e >> 1] << 16));
+                            b1 = __uint_as_float((e & 1) ? (w1[e >> 1] & 0xffff0000u) : (w1[e >> 1] << 16));
+                        } else {  // head dims that are not a multiple of 8: element by element
+                            b0 = d0 + e < p.d_h ? bf16_to_f32(bq[r * p.d_h + d0 + e]) : 0.f;
+                            b1 = two && d0 + e < p.d_h ? bf16_to_f32(bq[(r + 1) * p.d_h + d0 + e]) : 0.f;
+                        }
+                        x[k][e] = fmaf(a1, b1, fmaf(a0, b0, x[k][e]));
+                    }
                 }
             }
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const int d = d0 + e;  // even: the pair (d, d + 1)
-                if (d < p.d_h) {
-                    const double turns = double(pos) * (p.rope.theta[d >> 1] * kInvTwoPi);
-                    const float t = float(turns - rint(turns));  // in [-1/2, 1/2]
-                    const float c = __builtin_amdgcn_cosf(t), sn = __builtin_amdgcn_sinf(t);
-                    float y0, y1;
-                    rope_rotate(x[e], x[e + 1], c, sn, y0, y1);
-                    x[e] = y0 * inv_rq;
-                    x[e + 1] = y1 * inv_rq;
+            for (int k = 0; k < KH; ++k)
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const int d = 16 * (half * KH + k) + 8 * hi + e;  // even: the pair (d, d + 1)
+                    if (d < p.d_h) {
+                        const double turns = double(pos) * (p.rope.theta[d >> 1] * kInvTwoPi);
+                        const float t = float(turns - rint(turns));  // in [-1/2, 1/2]
+                        const float c = __builtin_amdgcn_cosf(t), sn = __builtin_amdgcn_sinf(t);
+                        float y0, y1;
+                        rope_rotate(x[k][e], x[k][e + 1], c, sn, y0, y1);
+                        x[k][e] = y0 * inv_rq;
+                        x[k][e + 1] = y1 * inv_rq;
+                    }
                 }
-            }
         }
-        qf[ks] = pack8(x);
+#pragma unroll
+        for (int k = 0; k < KH; ++k) qf[half * KH + k] = pack8(x[k]);
     }
 }
 
