@@ -12,7 +12,8 @@
 //   2. gate: z[s, i] = sum_r A_K[s,r,i] U^T[(s,r), i]  (in-lane: a lane's four
 //      accumulator rows hold whole tokens because the padded rank is 1, 2 or 4)
 //   3. online softmax per head (running max in log2 units, running sum)
-//   4. W[(s,r), i] = p[s,i] A_V[s,r,i], rounded once to the element type
+//   4. W[(s,r), i] = p[s,i] A_V[s,r,i], rounded once to the element type (at
+//      rank 1 with bf16 operands: as a pair hi + lo, see kSplitW)
 //   5. O^T[:, i] += B_V[(s,r), :]^T W[(s,r), i]     (M = d_h, K = token rows)
 // The cache block layout (common.h) makes the score accumulator of a lane
 // exactly the k-slice it feeds to step 5, so no data crosses lanes between
@@ -176,6 +177,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     constexpr int KBV = kRows / (4 * E);  // value K blocks
     constexpr int TOK = kRows / RH;       // tokens per cache block
     constexpr int TPL = 4 / RH;           // tokens per lane per score row block
+    // Rank 1 with bf16 operands: each token's value row carries its whole weight p A_V, so the weights go
+    // to the matrix cores as a bf16 pair hi + lo (two products with the same B_V operand; the matrix cores
+    // have slack in this memory-bound loop), which leaves the weights exact to ~2^-17.
+    constexpr bool kSplitW = RH == 1 && sizeof(T) == 2;
     constexpr int64_t BLK = 2LL * kRows * (HP + DP);
     constexpr int OFF_AV = kRows * HP, OFF_BK = 2 * kRows * HP, OFF_BV = 2 * kRows * HP + kRows * DP;
 
@@ -712,6 +717,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                 const Frag wf = M::pack(x);
 #pragma unroll
                 for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] = M::mma(bvf[mv], wf, acc[mv][nb]);
+                if constexpr (kSplitW) {  // the weights' bf16 rounding residuals, as a second product
+                    float r[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) r[e] = x[e] - M::value(wf, e);
+                    const Frag wl = M::pack(r);
+#pragma unroll
+                    for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] = M::mma(bvf[mv], wl, acc[mv][nb]);
+                }
             }
         }
     };

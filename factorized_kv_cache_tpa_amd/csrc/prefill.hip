@@ -7,14 +7,19 @@
 //     K~_i[s,:] = sum_r A_K[s,r,i] B~_K[s,r,:]      (1/R_K folded into the scale)
 //     V_i[s,:]  = sum_r A_V[s,r,i] B_V[s,r,:]       (1/R_V applied at the end)
 // in fp32 from the cached factors, rounds them once to bf16 into LDS, and
-// runs a flash-attention loop on the bf16 matrix cores (32x32x16):
+// runs a flash-attention loop on the bf16 matrix cores (32x32x16).  At rank 1
+// the rows in LDS are the cached B~_K and B_V themselves (no rounding), and the
+// gates A_K[s,0,i] and A_V[s,0,i] multiply the scores and the softmax weights in
+// fp32; the weights p A_V reach the matrix cores as a bf16 pair hi + lo (two
+// products with the same V^T operand), and the row sum takes the fp32 p, so
+// the kernel adds nothing to the rounding of the values it reads.
 //     S^T = K~_i Q~^T   (M = keys, N = queries, K = d_h)
 //     causal mask: chunk row j (position ctx + j) sees keys 0 .. ctx + j
 //     online softmax per query (a lane owns one query column)
 //     O^T += V_i^T P^T  (M = d_h, N = queries, K = keys)
 // A work-group owns 256 query rows of one head (8 waves x 32), so every
 // (key, head) pair is rebuilt at most twice per chunk of 512 rows; chunks of
-// more than 256 rows at d_h = 128 take the wide form further down (512 rows
+// more than 256 rows at d_h = 128 and rank 2 or 4 take the wide form further down (512 rows
 // per work-group, factor pieces staged in LDS by direct loads).  The LDS
 // tiles are double-buffered: the factor loads of a later tile are issued between
 // the matrix-core instructions of tile t, and the waves rebuild tile t+1 (half of
@@ -140,16 +145,21 @@ __device__ __forceinline__ void factored_query_row(const PrefillParams &p, int b
 
 // kFQ: the query rows arrive as factors (tpa_prefill_chunk_fq), a separate instantiation.
 // The double-buffered K~ and V^T tiles (row strides padded by 8 elements against bank conflicts).
-template <int DP>
+// kGate (rank 1): the tiles hold the cached B~_K and B_V rows as they are, and each key's A_K and A_V gates
+// (fp32) sit beside them, applied to the scores and to the softmax weights in fp32.  (A K~ row rebuilt as
+// A_K B~_K and rounded to bf16 would move a sharp softmax by 2^-9 of its largest value rows.)
+template <int DP, bool kGate>
 struct PrefillLds {
     uint16_t k[2][kKT * (DP + 8)];
     uint16_t v[2][DP * (kKT + 8)];
+    float gk[2][kGate ? kKT : 0];  // zero-length when unused (a clang extension)
+    float gv[2][kGate ? kKT : 0];
 };
 
 // One work-group's loop.  late: the second wave of each SIMD (waves 4..7), which rebuilds at the top of
 // its iteration instead of the end; see prefill_kernel.
 template <int HP, int DP, int RH, bool kFQ, bool late, bool kF8>
-__device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<DP> &lds) {
+__device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<DP, RH == 1> &lds) {
     auto &sK = lds.k;
     auto &sV = lds.v;
     constexpr int KS = DP / 16;  // score K steps
@@ -158,6 +168,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
     constexpr int KBS = DP / 32;  // B~_K 32-wide column blocks in the cache layout
     constexpr int MBV = DP / 16;
     constexpr int TOK = kRows / RH;
+    constexpr bool kGate = RH == 1;  // gates applied in fp32 (see PrefillLds)
     constexpr int SKS = DP + 8;   // LDS row stride of K~ (bf16 elements)
     constexpr int SVS = kKT + 8;  // LDS row stride of V^T
     constexpr int BLK = 2 * kRows * (HP + DP);
@@ -349,29 +360,31 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
             const int k = kk + u * K_STEP;
             const uint2 kgu = in_kg(raw, u);
             const uint32_t gw[2] = {kgu.x, kgu.y};
+            if constexpr (kGate) {
+                // the cached row itself; the key's gate beside it (written by the thread of its first chunk)
+                const bool dead = kPartial && key0 + k >= n_keys;
+                const uint4 row = in_kb(raw, u, 0);
+                const uint32_t a = (kv0 & 1) ? (gw[kv0 >> 1] >> 16) : (gw[kv0 >> 1] & 0xffffu);
+                if (c8 == 0) lds.gk[buf][k] = dead ? 0.f : __builtin_bit_cast(float, a << 16);
+                *reinterpret_cast<uint4 *>(&dK[k * SKS + 8 * c8]) = dead ? make_uint4(0, 0, 0, 0) : row;
+                continue;
+            }
             uint4 kbr[RH];
 #pragma unroll
             for (int r = 0; r < RH; ++r) kbr[r] = in_kb(raw, u, r);
             float kv[8];
 #pragma unroll
             for (int w2 = 0; w2 < 4; ++w2) {  // feature pairs (2 w2, 2 w2 + 1)
-                if (RH == 1) {
-                    const uint32_t a = (kv0 & 1) ? (gw[kv0 >> 1] >> 16) : (gw[kv0 >> 1] & 0xffffu);
-                    const uint32_t bw = (&kbr[0].x)[w2];
-                    kv[2 * w2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(bw & 0xffffu), 0.f, false);
-                    kv[2 * w2 + 1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(bw >> 16), 0.f, false);
-                } else {
-                    kv[2 * w2] = kv[2 * w2 + 1] = 0.f;
+                kv[2 * w2] = kv[2 * w2 + 1] = 0.f;
 #pragma unroll
-                    for (int rp = 0; rp < RH / 2; ++rp) {  // rank pairs (2 rp, 2 rp + 1)
-                        const uint32_t a = gw[(kv0 >> 1) + rp];
-                        const uint32_t b0 = (&kbr[2 * rp].x)[w2], b1 = (&kbr[2 * rp + 1].x)[w2];
-                        const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x05040100u);  // (b0[d], b1[d])
-                        const uint32_t hi2 = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // (b0[d+1], b1[d+1])
-                        kv[2 * w2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(lo), kv[2 * w2], false);
-                        kv[2 * w2 + 1] =
-                            __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(hi2), kv[2 * w2 + 1], false);
-                    }
+                for (int rp = 0; rp < RH / 2; ++rp) {  // rank pairs (2 rp, 2 rp + 1)
+                    const uint32_t a = gw[(kv0 >> 1) + rp];
+                    const uint32_t b0 = (&kbr[2 * rp].x)[w2], b1 = (&kbr[2 * rp + 1].x)[w2];
+                    const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x05040100u);  // (b0[d], b1[d])
+                    const uint32_t hi2 = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // (b0[d+1], b1[d+1])
+                    kv[2 * w2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(lo), kv[2 * w2], false);
+                    kv[2 * w2 + 1] =
+                        __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(hi2), kv[2 * w2 + 1], false);
                 }
             }
             uint4 packed = make_uint4(pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3]), pack_bf16x2(kv[4], kv[5]),
@@ -393,21 +406,31 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
                 // rows 16 m + 4 vg4 + 0..3 of the block: TPH whole tokens
                 const uint2 vgm = in_vg(raw, m);
                 const uint32_t gw[2] = {vgm.x, vgm.y};
+                if constexpr (kGate) {
+                    // four tokens' B_V values as cached (zero past n_keys), and their gates, written by the
+                    // threads of feature 0
+                    const int t0 = kbase + 16 * m + 4 * vg4;  // tile key of the first of the four
+                    uint32_t x2[2] = {xw[2 * m], xw[2 * m + 1]};
+#pragma unroll
+                    for (int tl = 0; tl < 4; ++tl) {
+                        const bool dead = kPartial && key0 + t0 + tl >= n_keys;
+                        if (dead) x2[tl >> 1] &= (tl & 1) ? 0x0000ffffu : 0xffff0000u;
+                        if (u == 0 && vmv0 == 0 && (vcl & 15) == 0) {
+                            const uint32_t a = (tl & 1) ? (gw[tl >> 1] >> 16) : (gw[tl >> 1] & 0xffffu);
+                            lds.gv[buf][t0 + tl] = dead ? 0.f : __builtin_bit_cast(float, a << 16);
+                        }
+                    }
+                    *reinterpret_cast<uint2 *>(&dV[vd * SVS + vpos(t0)]) = make_uint2(x2[0], x2[1]);
+                    continue;
+                }
                 float vt[TPH];
 #pragma unroll
                 for (int tl = 0; tl < TPH; ++tl) {
                     float acc = 0.f;
-                    if (RH == 1) {
-                        const uint32_t a = (tl & 1) ? (gw[tl >> 1] >> 16) : (gw[tl >> 1] & 0xffffu);
-                        const uint32_t x = (tl & 1) ? (xw[2 * m + (tl >> 1)] >> 16) : (xw[2 * m + (tl >> 1)] & 0xffffu);
-                        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(x), 0.f, false);
-                    } else {
 #pragma unroll
-                        for (int rp = 0; rp < RH / 2; ++rp)
-                            acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(gw[(tl * RH) / 2 + rp]),
-                                                                  as_bf16x2(xw[2 * m + (tl * RH) / 2 + rp]), acc,
-                                                                  false);
-                    }
+                    for (int rp = 0; rp < RH / 2; ++rp)
+                        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(gw[(tl * RH) / 2 + rp]),
+                                                              as_bf16x2(xw[2 * m + (tl * RH) / 2 + rp]), acc, false);
                     vt[tl] = acc;
                     if (kPartial && key0 + kbase + (16 * m + 4 * vg4) / RH + tl >= n_keys) vt[tl] = 0.f;
                 }
@@ -516,6 +539,18 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // global loads
             }
+            if constexpr (kGate) {  // score of key k: (q . B~_K[k]) A_K[k], in fp32
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const float4 a = *reinterpret_cast<const float4 *>(&lds.gk[buf][32 * kb2 + 8 * g + 4 * hi]);
+                        s[kb2][4 * g] *= a.x;
+                        s[kb2][4 * g + 1] *= a.y;
+                        s[kb2][4 * g + 2] *= a.z;
+                        s[kb2][4 * g + 3] *= a.w;
+                    }
+            }
             // ---- causal mask only where the tile crosses the diagonal (or past the chunk's end)
             if (key0 + kKT - 1 > ctx + jw || wave_last < jw + 31) {
 #pragma unroll
@@ -546,12 +581,46 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) s[kb2][v] = __builtin_amdgcn_exp2f(fmaf(s[kb2][v], sm, neg_ms));
+            if constexpr (kGate) {  // row sum of p in fp32, then the weights p A_V[k] in place
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const float4 a = *reinterpret_cast<const float4 *>(&lds.gv[buf][32 * kb2 + 8 * g + 4 * hi]);
+                        run_l += (s[kb2][4 * g] + s[kb2][4 * g + 1]) + (s[kb2][4 * g + 2] + s[kb2][4 * g + 3]);
+                        s[kb2][4 * g] *= a.x;
+                        s[kb2][4 * g + 1] *= a.y;
+                        s[kb2][4 * g + 2] *= a.z;
+                        s[kb2][4 * g + 3] *= a.w;
+                    }
+            }
             // ---- O^T += V^T P^T over four 16-key steps, with the V inputs of the next tile issued; the
             // row sum takes the same bf16-rounded P the matrix cores use, two values per v_dot2 against (1, 1)
 #pragma unroll
             for (int ks4 = 0; ks4 < 4; ++ks4) {
                 const floatx16 &sv = s[ks4 >> 1];
                 const int o8 = 8 * (ks4 & 1);
+                if constexpr (kGate) {
+                    // the fp32 weights as a bf16 pair hi + lo, two products with the same V^T operand: each
+                    // weight reaches the accumulator to ~2^-17 of itself
+                    uint32_t ph[4], pl[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float w0 = sv[o8 + 2 * i], w1 = sv[o8 + 2 * i + 1];
+                        ph[i] = pack_bf16x2(w0, w1);
+                        pl[i] = pack_bf16x2(w0 - __builtin_bit_cast(float, ph[i] << 16),
+                                            w1 - __builtin_bit_cast(float, ph[i] & 0xffff0000u));
+                    }
+                    const bf16x8 pfh = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+                    const bf16x8 pfl = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&cV[(32 * mb + col) * SVS + 16 * ks4 + 8 * hi]);
+                        acc[mb] = mma32(a, pfh, acc[mb]);
+                        acc[mb] = mma32(a, pfl, acc[mb]);
+                    }
+                    continue;
+                }
                 const uint32_t pw[4] = {pack_bf16x2(sv[o8], sv[o8 + 1]), pack_bf16x2(sv[o8 + 2], sv[o8 + 3]),
                                         pack_bf16x2(sv[o8 + 4], sv[o8 + 5]), pack_bf16x2(sv[o8 + 6], sv[o8 + 7])};
 #pragma unroll
@@ -606,7 +675,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, PrefillLds<
 // half is its own instantiation so the register allocator sees one loop shape at a time.
 template <int HP, int DP, int RH, bool kFQ, bool kF8>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams p) {
-    __shared__ __attribute__((aligned(16))) PrefillLds<DP> lds;
+    __shared__ __attribute__((aligned(16))) PrefillLds<DP, RH == 1> lds;
     if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= kPrefillWaves / 2)
         prefill_body<HP, DP, RH, kFQ, true, kF8>(p, lds);
     else
@@ -614,7 +683,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
 }
 
 // ===================================================================================================
-// Wide form (bf16 cache, d_h = 128, chunks of more than 256 rows): a work-group owns 512 query rows of
+// Wide form (bf16 cache, d_h = 128, rank 2 or 4, chunks of more than 256 rows): a work-group owns 512 query rows of
 // one head, so each (key, head) pair is rebuilt once per 512 rows and the factor bytes a work-group
 // loads per query row halve.  8 waves x 64 rows: each wave holds two 32-row blocks, w and 15 - w of the
 // tile, so every wave has the same causal extent; 32-key tiles.  The factor pieces a wave rebuilds from
@@ -654,6 +723,7 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
     constexpr int BLK = 2 * kRows * (HP + DP);
     constexpr int OFF_AV = kRows * HP, OFF_BK = 2 * kRows * HP, OFF_BV = 2 * kRows * HP + kRows * DP;
     constexpr int C8 = DP / 8;
+    static_assert(RH >= 2, "rank 1 takes the 256-row form, which keeps its gates in fp32");
     static_assert(kKT2 * C8 == kPrefillThreads, "one K~ item per thread");
     static_assert(MVG * BPT == kPrefillWaves && V_ITEMS * MVG == DP / 16, "V items must tile the group");
 
@@ -764,23 +834,16 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
             float kv[8];
 #pragma unroll
             for (int w2 = 0; w2 < 4; ++w2) {  // feature pairs (2 w2, 2 w2 + 1)
-                if (RH == 1) {
-                    const uint32_t a = (kv0_ & 1) ? (gw[kv0_ >> 1] >> 16) : (gw[kv0_ >> 1] & 0xffffu);
-                    const uint32_t bw = (&kbr[0].x)[w2];
-                    kv[2 * w2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(bw & 0xffffu), 0.f, false);
-                    kv[2 * w2 + 1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(bw >> 16), 0.f, false);
-                } else {
-                    kv[2 * w2] = kv[2 * w2 + 1] = 0.f;
+                kv[2 * w2] = kv[2 * w2 + 1] = 0.f;
 #pragma unroll
-                    for (int rp = 0; rp < RH / 2; ++rp) {  // rank pairs (2 rp, 2 rp + 1)
-                        const uint32_t a = gw[(kv0_ >> 1) + rp];
-                        const uint32_t b0 = (&kbr[2 * rp].x)[w2], b1 = (&kbr[2 * rp + 1].x)[w2];
-                        const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x05040100u);
-                        const uint32_t hi2 = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
-                        kv[2 * w2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(lo), kv[2 * w2], false);
-                        kv[2 * w2 + 1] =
-                            __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(hi2), kv[2 * w2 + 1], false);
-                    }
+                for (int rp = 0; rp < RH / 2; ++rp) {  // rank pairs (2 rp, 2 rp + 1)
+                    const uint32_t a = gw[(kv0_ >> 1) + rp];
+                    const uint32_t b0 = (&kbr[2 * rp].x)[w2], b1 = (&kbr[2 * rp + 1].x)[w2];
+                    const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x05040100u);
+                    const uint32_t hi2 = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+                    kv[2 * w2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(lo), kv[2 * w2], false);
+                    kv[2 * w2 + 1] =
+                        __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(hi2), kv[2 * w2 + 1], false);
                 }
             }
             uint4 packed = make_uint4(pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3]), pack_bf16x2(kv[4], kv[5]),
@@ -811,16 +874,10 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
 #pragma unroll
                 for (int tl = 0; tl < TPH; ++tl) {
                     float acc = 0.f;
-                    if (RH == 1) {
-                        const uint32_t a = (tl & 1) ? (gv[m][tl >> 1] >> 16) : (gv[m][tl >> 1] & 0xffffu);
-                        const uint32_t x = (tl & 1) ? (xw[2 * m + (tl >> 1)] >> 16) : (xw[2 * m + (tl >> 1)] & 0xffffu);
-                        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(x), 0.f, false);
-                    } else {
 #pragma unroll
-                        for (int rp = 0; rp < RH / 2; ++rp)
-                            acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(gv[m][(tl * RH) / 2 + rp]),
-                                                                  as_bf16x2(xw[2 * m + (tl * RH) / 2 + rp]), acc, false);
-                    }
+                    for (int rp = 0; rp < RH / 2; ++rp)
+                        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(gv[m][(tl * RH) / 2 + rp]),
+                                                              as_bf16x2(xw[2 * m + (tl * RH) / 2 + rp]), acc, false);
                     vt[tl] = acc;
                     if (kPartial && key0 + kbase + (16 * m + 4 * vg4_) / RH + tl >= n_keys) vt[tl] = 0.f;
                 }
@@ -1012,12 +1069,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill2_kernel(PrefillParams
         prefill2_body<HP, DP, RH, kFQ, false>(p, lds);
 }
 
-// The wide form pays off once a chunk fills more than one 256-row work-group.
+// The wide form pays off once a chunk fills more than one 256-row work-group.  Rank 1 stays on the
+// 256-row form, whose rebuild is a copy at that rank: the fp32 gates do not fit the wide form's registers.
 bool use_wide(const PrefillParams &p) { return p.d_h == 128 && p.chunk > kQT; }
 
 template <int HP, int DP, int RH, bool kF8>
 hipError_t launch_one(const PrefillParams &p, hipStream_t s) {
-    if constexpr (DP == 128 && !kF8) {
+    if constexpr (DP == 128 && !kF8 && RH >= 2) {
         if (use_wide(p)) {
             const dim3 grid2(unsigned(((p.chunk + kQT2 - 1) / kQT2) * p.h * p.batch));
             if (p.r_q > 0)

@@ -76,11 +76,27 @@ class Checks:
 
 
 # Causes of the known max-abs excesses (the measured figures are in each test's table).
-STORAGE_CAUSE = ("sharpened softmax over rank-1 factors (outputs up to |5..7|): the bf16 storage of the rotated "
-                 "B_K and of the rotated query alone moves the exact output by more than 1e-2 "
-                 "(tests/test_storage_rounding.py shows it on the CPU, with no kernel involved)")
-REBUILD_CAUSE = ("prefill rebuilds rank-1 K~ and V rows (|V| up to ~10) and rounds them to bf16 for the matrix "
-                 "cores: 2^-9 of the output where few tokens carry the softmax")
+STORAGE_CAUSE = ("sharpened softmax over rank-1 factors (outputs up to |5..7|): the bf16 values of the rotated "
+                 "B_K in the cache and of the rotated query row alone move the exact output by more than 1e-2 "
+                 "(tests/test_storage_rounding.py shows it on the CPU, with no kernel involved); against exact "
+                 "attention over those stored values the kernel is inside both bounds (the *_stored_values tests)")
+
+
+def stored_key_and_query(B_K: np.ndarray, q: np.ndarray, q_pos, w: ti.Workload, dims: tpa.Dims):
+    """B_K [n][R][d] and query rows q [rows][h][d] (at positions q_pos) replaced by the values the kernel
+    reads.  bf16 only: an E4M3 B_K is a stored value already (stored_factors), only the query is rounded."""
+    assert w.dtype == ti.BF16
+    if dims.cache_format != tpa.TPA_CACHE_E4M3:
+        B_K = stored_rotated(B_K, np.arange(B_K.shape[0], dtype=np.float64)[:, None], w.rope_base)
+    q = stored_rotated(q, np.asarray(q_pos, dtype=np.float64).reshape(-1, 1), w.rope_base)
+    return B_K, q
+
+
+def stored_rotated(x: np.ndarray, pos, base: float) -> np.ndarray:
+    """What a bf16 buffer of x's rows rotated to pos holds (pos: one per row, broadcast), rotated back in fp64,
+    so the oracle, which rotates whole rows itself, sees exactly the stored rotated values.  Oracle side only."""
+    pos = np.asarray(pos, dtype=np.float64)
+    return oracle.rope_rows_at(oracle.round_to_bf16(oracle.rope_rows_at(x, pos, base)), -pos, base)
 
 
 def known_max_abs_excess(request, measured: str, cause: str) -> None:
@@ -136,10 +152,16 @@ class DecodeSetup:
         """The cached factor values the oracle attends over (fp64)."""
         return stored_factors(self.seqs[b], n, self.w, self.dims)
 
-    def oracle(self, b: int, scale: Optional[float] = None) -> np.ndarray:
+    def oracle(self, b: int, scale: Optional[float] = None, as_stored: bool = False) -> np.ndarray:
+        """as_stored: over the values the kernel reads (the query rotated and rounded to bf16; in a native
+        cache also B_K rotated and rounded per token) instead of the caller's factors."""
         s, dt = self.seqs[b], self.w.dtype
         n = self.lens[b]
-        return oracle.attention(*self.factors(b, n), np.arange(n), f64(s.q[:1], dt), [self.q_positions[b]], [n],
+        A_K, B_K, A_V, B_V = self.factors(b, n)
+        q = f64(s.q[:1], dt)
+        if as_stored:
+            B_K, q = stored_key_and_query(B_K, q, self.q_positions[b], self.w, self.dims)
+        return oracle.attention(A_K, B_K, A_V, B_V, np.arange(n), q, [self.q_positions[b]], [n],
                                 self.w.rope_base, scale)[0]
 
 
@@ -177,10 +199,15 @@ class PrefillSetup:
         torch.cuda.synchronize()
         return out.cpu().numpy()
 
-    def oracle(self, b: int, rows=None) -> np.ndarray:
+    def oracle(self, b: int, rows=None, as_stored: bool = False) -> np.ndarray:
+        """as_stored: over the values the kernel reads (B_K rotated and rounded to bf16 per token, query rows
+        rotated and rounded per row) instead of the caller's factors; the other factors are exact either way."""
         s, dt = self.seqs[b], self.w.dtype
-        return oracle.prefill(*stored_factors(s, s.n_tokens, self.w, self.dims), f64(s.q, dt), self.ctx[b],
-                              self.w.rope_base, rows=rows)
+        A_K, B_K, A_V, B_V = stored_factors(s, s.n_tokens, self.w, self.dims)
+        q = f64(s.q, dt)
+        if as_stored:
+            B_K, q = stored_key_and_query(B_K, q, self.ctx[b] + np.arange(self.chunk), self.w, self.dims)
+        return oracle.prefill(A_K, B_K, A_V, B_V, q, self.ctx[b], self.w.rope_base, rows=rows)
 
 
 def e4m3_values(x: np.ndarray, scale: float) -> np.ndarray:

@@ -90,8 +90,8 @@ def test_append_saturates_at_the_largest_finite_code():
 
 # Sharpened rank-1 cases whose max-abs error exceeds 1e-2 (measured on MI355X; rel-L2 within 5e-3).  The
 # oracle already sees the stored E4M3 values; what remains is the bf16 rounding of the rotated query.
-SHARP_RANK1 = {(16, 64, 1, 1, 8.0): "max-abs 1.58e-2, rel-L2 1.6e-3",
-               (64, 64, 1, 1, 8.0): "max-abs 1.35e-2, rel-L2 1.4e-3"}
+SHARP_RANK1 = {(16, 64, 1, 1, 8.0): "max-abs 1.187e-2, rel-L2 1.3e-3",
+               (64, 64, 1, 1, 8.0): "max-abs 1.324e-2, rel-L2 1.4e-3"}
 
 
 @pytest.mark.parametrize("h,d_h,R_K,R_V", SHAPES)
@@ -105,6 +105,22 @@ def test_decode_matches_oracle(h, d_h, R_K, R_V, q_scale, request):
     say(f"case: e4m3 decode h={h} d_h={d_h} R_K={R_K} R_V={R_V} q_scale={q_scale}")
     s = DecodeSetup(w, random_sequences(w, lens, q_scale=q_scale, seed=h * 7 + d_h), dims=dims_of(w, E4M3))
     ref = np.stack([s.oracle(b) for b in range(s.batch)])
+    chk = Checks()
+    for split in (0, 64):
+        chk.close(s.run(split_tokens=split), ref, w.dtype, f"split_tokens={split}")
+    chk.done()
+
+
+@pytest.mark.parametrize("key", sorted(SHARP_RANK1, key=str))
+def test_sharp_rank1_stored_values(key):
+    """The listed cases against exact attention over the stored values, the query's bf16 rounding included:
+    inside both plain bounds."""
+    h, d_h, R_K, R_V, q_scale = key
+    w = case_workload(h, d_h, R_K, R_V)
+    say(f"case: e4m3 decode over stored values h={h} d_h={d_h} q_scale={q_scale}")
+    s = DecodeSetup(w, random_sequences(w, [1, 31, 32, 33, 300, 1000], q_scale=q_scale, seed=h * 7 + d_h),
+                    dims=dims_of(w, E4M3))
+    ref = np.stack([s.oracle(b, as_stored=True) for b in range(s.batch)])
     chk = Checks()
     for split in (0, 64):
         chk.close(s.run(split_tokens=split), ref, w.dtype, f"split_tokens={split}")

@@ -3,28 +3,40 @@ import numpy as np
 import pytest
 
 import tpa_inputs as ti
-from tests.gpu_cases import (REBUILD_CAUSE, STORAGE_CAUSE, DecodeSetup, PrefillSetup, assert_close, case_workload,
+from tests.gpu_cases import (STORAGE_CAUSE, DecodeSetup, PrefillSetup, assert_close, case_workload,
                              known_max_abs_excess, random_sequences, say)
 
 pytestmark = pytest.mark.gpu
 
-# Rank-1 prefill cases whose max-abs error exceeds 1e-2 (measured on MI355X; rel-L2 within 5e-3), keyed by
-# (h, d_h, R, ctx, chunk, q_scale).  Outputs of rows that see few tokens reach |V| ~ 10 at rank 1.
+# Rank-1 prefill cases whose max-abs error against the oracle on the caller's factors exceeds 1e-2 (measured
+# on MI355X; rel-L2 within 5e-3), keyed by (h, d_h, R, ctx, chunk, q_scale): sharpened softmax, where the
+# bf16 storage of the rotated keys and queries alone moves the output that far.  The same values, to three
+# digits, come out of exact attention over the stored values on the CPU; test_rank1_stress_stored_values
+# compares the kernel with that at the plain bounds.
 RANK1_PREFILL = {
-    (32, 128, 1, (0, 45, 300), 70, 1.0): "max-abs 1.49e-2, rel-L2 2.0e-3",
-    (64, 64, 1, (0, 45, 300), 70, 1.0): "max-abs 1.51e-2, rel-L2 2.1e-3",
-    (32, 128, 1, (64, 2), 160, 1.0): "max-abs 1.04e-2, rel-L2 2.2e-3",
-    (32, 128, 1, (0, 45, 300), 70, 10.0): "max-abs 3.43e-2, rel-L2 3.6e-3",
-    (64, 64, 1, (0, 45, 300), 70, 10.0): "max-abs 5.97e-2, rel-L2 4.2e-3",
-    (32, 128, 1, (64, 2), 160, 10.0): "max-abs 3.50e-2, rel-L2 3.9e-3",
-    (64, 64, 1, (64, 2), 160, 10.0): "max-abs 8.09e-2, rel-L2 4.3e-3",
-    (32, 128, 1, (257,), 129, 10.0): "max-abs 3.42e-2, rel-L2 4.8e-3",
-    (64, 64, 1, (257,), 129, 10.0): "max-abs 5.40e-2, rel-L2 4.9e-3",
-    (32, 128, 1, (0, 45), 300, 2.0): "max-abs 1.01e-2, rel-L2 2.2e-3",
-    (32, 128, 1, (0, 45), 300, 6.0): "max-abs 2.12e-2, rel-L2 3.1e-3",
-    (32, 128, 1, (257,), 700, 6.0): "max-abs 4.41e-2, rel-L2 4.1e-3",
-    (32, 128, 1, (64, 1000, 3), 257, 6.0): "max-abs 2.58e-2, rel-L2 3.0e-3",
+    (32, 128, 1, (0, 45, 300), 70, 10.0): "max-abs 1.913e-2, rel-L2 2.5e-3",
+    (64, 64, 1, (0, 45, 300), 70, 10.0): "max-abs 3.402e-2, rel-L2 3.1e-3",
+    (32, 128, 1, (64, 2), 160, 10.0): "max-abs 2.636e-2, rel-L2 2.8e-3",
+    (64, 64, 1, (64, 2), 160, 10.0): "max-abs 7.214e-2, rel-L2 3.2e-3",
+    (32, 128, 1, (257,), 129, 10.0): "max-abs 1.875e-2, rel-L2 3.3e-3",
+    (64, 64, 1, (257,), 129, 10.0): "max-abs 4.661e-2, rel-L2 3.7e-3",
+    (32, 128, 1, (0, 45), 300, 6.0): "max-abs 1.208e-2, rel-L2 1.8e-3",
+    (32, 128, 1, (257,), 700, 6.0): "max-abs 3.098e-2, rel-L2 2.5e-3",
+    (32, 128, 1, (64, 1000, 3), 257, 6.0): "max-abs 1.995e-2, rel-L2 1.8e-3",
 }
+
+
+@pytest.mark.parametrize("h,d_h,R,ctx,chunk,q_scale", sorted(RANK1_PREFILL, key=str))
+def test_rank1_stress_stored_values(h, d_h, R, ctx, chunk, q_scale):
+    """The listed cases against exact attention over the values the kernel reads (rotated B_K and query rows
+    as stored in bf16): inside both plain bounds, so their excess above is the storage format's alone."""
+    w = case_workload(h, d_h, R, R)
+    say(f"case: prefill over stored values h={h} d_h={d_h} R={R} ctx={ctx} chunk={chunk} q_scale={q_scale}")
+    seqs = random_sequences(w, [c + chunk for c in ctx], n_q=chunk, q_scale=q_scale, seed=h * R + chunk)
+    s = PrefillSetup(w, seqs, list(ctx))
+    out = s.run()
+    ref = np.stack([s.oracle(b, as_stored=True) for b in range(len(seqs))])
+    assert_close(out, ref, w.dtype, "all rows vs stored values")
 
 
 @pytest.mark.parametrize("h,d_h,R", [(32, 128, 4), (32, 128, 1), (16, 64, 2), (20, 48, 3), (16, 128, 2), (64, 64, 1),
@@ -34,7 +46,7 @@ RANK1_PREFILL = {
 def test_small_chunks(h, d_h, R, ctx, chunk, q_scale, request):
     known = RANK1_PREFILL.get((h, d_h, R, tuple(ctx), chunk, q_scale))
     if known:
-        known_max_abs_excess(request, known, REBUILD_CAUSE if q_scale == 1.0 else REBUILD_CAUSE + "; and " + STORAGE_CAUSE)
+        known_max_abs_excess(request, known, STORAGE_CAUSE)
     w = case_workload(h, d_h, R, R)
     say(f"case: prefill h={h} d_h={d_h} R={R} ctx={ctx} chunk={chunk} q_scale={q_scale}")
     seqs = random_sequences(w, [c + chunk for c in ctx], n_q=chunk, q_scale=q_scale, seed=h + chunk)
@@ -72,16 +84,16 @@ def test_full_size_prefill_all_rows():
     assert_close(out, ref, w.dtype, "all 8 x 512 rows")
 
 
-# Chunks of more than 256 rows at d_h = 128 run the wide form (512 query rows per work-group, factor
-# pieces staged through LDS); these cases cover it with ragged chunk ends, a second row tile, short and
-# empty contexts and every rank.
+# Chunks of more than 256 rows at d_h = 128 run the wide form at ranks 2 and 4 (512 query rows per
+# work-group, factor pieces staged through LDS); these cases cover it with ragged chunk ends, a second row
+# tile, short and empty contexts, and rank 1 (which keeps the 256-row form at every chunk length).
 @pytest.mark.parametrize("h,R,q_scale", [(32, 4, 2.0), (32, 2, 2.0), (32, 1, 2.0), (20, 4, 2.0), (16, 4, 2.0),
                                          (32, 4, 10.0), (32, 1, 6.0)])
 @pytest.mark.parametrize("ctx,chunk", [([0, 45], 300), ([257], 700), ([64, 1000, 3], 257)])
 def test_wide_chunks(h, R, q_scale, ctx, chunk, request):
     known = RANK1_PREFILL.get((h, 128, R, tuple(ctx), chunk, q_scale))
     if known:
-        known_max_abs_excess(request, known, REBUILD_CAUSE if q_scale <= 2.0 else REBUILD_CAUSE + "; and " + STORAGE_CAUSE)
+        known_max_abs_excess(request, known, STORAGE_CAUSE)
     w = case_workload(h, 128, R, R)
     say(f"case: wide prefill h={h} R={R} q_scale={q_scale} ctx={ctx} chunk={chunk}")
     seqs = random_sequences(w, [c + chunk for c in ctx], n_q=chunk, q_scale=q_scale, seed=h * R + chunk)

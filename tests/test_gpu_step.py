@@ -13,7 +13,8 @@ import factorized_kv_cache_tpa_amd as tpa
 import oracle
 import tpa_inputs as ti
 from factorized_kv_cache_tpa_amd.cache import FactorCache, to_device
-from tests.gpu_cases import assert_close, case_workload, dims_of, f64, random_sequences, say, stored_factors
+from tests.gpu_cases import (STORAGE_CAUSE, Checks, assert_close, case_workload, dims_of, f64, known_max_abs_excess,
+                             random_sequences, say, stored_factors, stored_key_and_query)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,10 +50,15 @@ class StepSetup:
                             self.A_K, self.B_K, self.A_V, self.B_V, self.q, out, ws, split_tokens=split_tokens)
         return out
 
-    def oracle(self, b: int) -> np.ndarray:
+    def oracle(self, b: int, as_stored: bool = False) -> np.ndarray:
+        """as_stored: over the values the kernel reads (B_K rotated and rounded to bf16 per token, the new
+        token's included, and the query rotated to position N and rounded) instead of the caller's factors."""
         s, n, dt = self.seqs[b], self.lens[b], self.w.dtype
-        return oracle.prefill(*stored_factors(s, n + 1, self.w, self.dims), f64(s.q[:1], dt), n,
-                              self.w.rope_base)[0]
+        A_K, B_K, A_V, B_V = stored_factors(s, n + 1, self.w, self.dims)
+        q = f64(s.q[:1], dt)
+        if as_stored:
+            B_K, q = stored_key_and_query(B_K, q, [n], self.w, self.dims)
+        return oracle.prefill(A_K, B_K, A_V, B_V, q, n, self.w.rope_base)[0]
 
 
 SHAPES = [(32, 128, 1, 1, ti.BF16, 1e4), (16, 64, 2, 2, ti.BF16, 1e4), (32, 128, 4, 4, ti.BF16, 5e5),
@@ -61,16 +67,41 @@ SHAPES = [(32, 128, 1, 1, ti.BF16, 1e4), (16, 64, 2, 2, ti.BF16, 1e4), (32, 128,
           (30, 64, 2, 1, ti.F32, 1e4)]
 
 
+STEP_LENS = [0, 1, 31, 32, 33, 300, 1000]
+# Sharpened rank-1 cases whose max-abs error exceeds 1e-2 (measured on MI355X; rel-L2 within 5e-3), keyed by
+# (h, d_h, R_K, R_V, dtype, base, q_scale).  Exact attention over the stored rotated B_K and query, on the
+# CPU, is 1.035e-2 away from the oracle for the sequence of N = 31 alone.
+SHARP_RANK1 = {(64, 64, 1, 1, ti.BF16, 1e4, 6.0): "max-abs 1.006e-2 (N = 31), rel-L2 2.6e-3"}
+
+
 @pytest.mark.parametrize("h,d_h,R_K,R_V,dtype,base", SHAPES)
 @pytest.mark.parametrize("q_scale", [1.0, 6.0])
-def test_step_matches_oracle(h, d_h, R_K, R_V, dtype, base, q_scale):
+def test_step_matches_oracle(h, d_h, R_K, R_V, dtype, base, q_scale, request):
+    known = SHARP_RANK1.get((h, d_h, R_K, R_V, dtype, base, q_scale))
+    if known:
+        known_max_abs_excess(request, known, STORAGE_CAUSE)
     w = case_workload(h, d_h, R_K, R_V, dtype, base)
-    lens = [0, 1, 31, 32, 33, 300, 1000]
-    say(f"case: step h={h} d_h={d_h} R_K={R_K} R_V={R_V} {dtype} q_scale={q_scale} lens={lens}")
-    st = StepSetup(w, lens, q_scale=q_scale, seed=h + d_h + R_K)
+    say(f"case: step h={h} d_h={d_h} R_K={R_K} R_V={R_V} {dtype} q_scale={q_scale} lens={STEP_LENS}")
+    st = StepSetup(w, STEP_LENS, q_scale=q_scale, seed=h + d_h + R_K)
     got = st.run().cpu().numpy()
+    chk = Checks()
     for b in range(st.batch):
-        assert_close(got[b], st.oracle(b), dtype, f"seq {b} (N={lens[b]})")
+        chk.close(got[b], st.oracle(b), dtype, f"seq {b} (N={STEP_LENS[b]})")
+    chk.done()
+
+
+@pytest.mark.parametrize("key", sorted(SHARP_RANK1, key=str))
+def test_step_sharp_rank1_stored_values(key):
+    """The listed cases against exact attention over the values the kernel reads: inside both plain bounds."""
+    h, d_h, R_K, R_V, dtype, base, q_scale = key
+    w = case_workload(h, d_h, R_K, R_V, dtype, base)
+    say(f"case: step over stored values {key}")
+    st = StepSetup(w, STEP_LENS, q_scale=q_scale, seed=h + d_h + R_K)
+    got = st.run().cpu().numpy()
+    chk = Checks()
+    for b in range(st.batch):
+        chk.close(got[b], st.oracle(b, as_stored=True), dtype, f"seq {b} (N={STEP_LENS[b]})")
+    chk.done()
 
 
 def test_step_with_no_cached_tokens_returns_the_new_value_row():
