@@ -3,6 +3,7 @@
 // side effect and the checks work on a machine without a GPU.
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/tpa.h"
@@ -19,12 +20,12 @@ namespace {
 
 using tpa::Layout;
 
-// The planner sizes splits so that one round of decode work-groups fills the
-// 256 compute units of an MI355X: the wide layouts (HP * DP >= 2048) run one
-// 4-wave work-group per CU (their waves need most of the register file), the
-// narrow ones two.  Fewer, longer splits mean fewer partials to merge.  A split
-// holds at least four blocks per wave (when the call is that short it is latency-bound, and
-// fewer partials matter more than the idle compute units).
+// Decode work partition: the split kernel shares the batch's blocks out evenly over its work-groups (it
+// scans the device-resident lengths itself), so the host only picks the grid: one round of work-groups
+// over the 256 compute units of an MI355X, where the wide layouts (HP * DP >= 2048) run one 4-wave
+// work-group per CU (their waves need most of the register file) and the narrow ones two.  A caller's
+// split_tokens fixes the blocks per work-group instead, and the grid is sized for the longest batch the
+// arguments allow.
 constexpr int64_t kComputeUnits = 256;
 constexpr int kDecodeWaves = 4;
 
@@ -60,41 +61,43 @@ int32_t check_dims(const tpa_dims *d) {
     return TPA_OK;
 }
 
-// Decode workspace: [per-split outputs O][per-split (max, sum)].
+// Decode workspace: [partials O][partials (max, sum)][per-sequence work-group range], one partial per
+// (work-group, sequence) job, at index wg + b (at most grid + batch - 1 of them).
 struct DecodePlan {
-    int split_blocks = 1;
-    int n_split = 1;
+    int split_blocks = 0;  // 0: the kernel's even share
+    int grid = 1;
+    int merge_parts = 1;
     int64_t off_o = 0;
     int64_t off_ml = 0;
+    int64_t off_meta = 0;
     int64_t bytes = 0;
+    bool ok = true;
 };
 
 DecodePlan plan_decode(const Layout &L, int32_t batch, int32_t max_len, int32_t split_tokens) {
     DecodePlan P;
     const int TOK = L.tok_per_block();
-    const int64_t nblk_max = (int64_t(max_len) + TOK - 1) / TOK;
-    int64_t sb;
+    const int64_t vmax = std::max<int64_t>((int64_t(max_len) + TOK - 1) / TOK, 1);  // virtual blocks per sequence
+    int64_t grid, t_est;
     if (split_tokens > 0) {
-        sb = (int64_t(split_tokens) + TOK - 1) / TOK;
+        const int64_t sb = (int64_t(split_tokens) + TOK - 1) / TOK;
+        grid = (int64_t(batch) * vmax + sb - 1) / sb;
+        t_est = sb;
+        P.split_blocks = int(std::min<int64_t>(sb, 1 << 30));
     } else {
-        const int64_t total = int64_t(batch) * nblk_max;
-        const int64_t target = kComputeUnits * (L.HP * L.DP >= 2048 ? 1 : 2);
-        sb = (total + target - 1) / target;
-        sb = (sb + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
-        // A short call (two blocks per wave or fewer) is latency-bound: half as many, twice as long splits
-        // halve the partials to merge and cost no bandwidth (measured: 16 x 4096 tokens, 2-3% faster).
-        if (sb <= 2 * kDecodeWaves) sb = 4 * kDecodeWaves;
+        grid = kComputeUnits * (L.HP * L.DP >= 2048 ? 1 : 2);
+        t_est = std::max<int64_t>(4 * kDecodeWaves, (int64_t(batch) * vmax + grid - 1) / grid);
     }
-    if (sb < 1) sb = 1;
-    int64_t ns = (nblk_max + sb - 1) / sb;
-    if (ns < 1) ns = 1;
-    P.split_blocks = int(sb > (1 << 30) ? (1 << 30) : sb);
-    P.n_split = int(ns);
-    const int64_t parts = int64_t(batch) * ns;
+    if (grid < 1) grid = 1;
+    const int64_t parts = grid + batch;
+    P.ok = grid <= (int64_t(1) << 30) && parts * L.HP * L.DP <= (int64_t(1) << 40);
+    P.grid = int(std::min<int64_t>(grid, 1 << 30));
+    P.merge_parts = int(std::min<int64_t>((vmax + t_est - 1) / t_est + 1, 1 << 30));
     const int64_t o_bytes = parts * L.HP * L.DP * 4;
     P.off_o = 0;
     P.off_ml = P.off_o + (o_bytes + 255) / 256 * 256;
-    P.bytes = P.off_ml + (parts * L.HP * 2 * 4 + 255) / 256 * 256;
+    P.off_meta = P.off_ml + (parts * L.HP * 2 * 4 + 255) / 256 * 256;
+    P.bytes = P.off_meta + (int64_t(batch) * 8 + 255) / 256 * 256;
     return P;
 }
 
@@ -147,16 +150,15 @@ int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
     if (int64_t(max_len) + (step ? 1 : 0) > capacity_tokens) return TPA_ERR_CAPACITY;
     const Layout L = layout_of(dims);
     const DecodePlan P = plan_decode(L, batch, max_len, split_tokens);
+    if (!P.ok) return TPA_ERR_ARG;
     if (use_scratch) {
         if (P.bytes > kScratchBytes) return TPA_ERR_WORKSPACE;
-        if (P.n_split > 65535) return TPA_ERR_ARG;
         const int32_t sst = scratch_address(stream, &workspace);  // the only HIP calls before the launch
         if (sst != TPA_OK) return sst;
         workspace_bytes = kScratchBytes;
     }
     if (!workspace || workspace_bytes < P.bytes) return TPA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TPA_ERR_WORKSPACE;
-    if (P.n_split > 65535) return TPA_ERR_ARG;
 
     tpa::DecodeParams p{};
     p.cache = cache;
@@ -167,6 +169,7 @@ int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
     p.capacity = capacity_tokens;
     p.ws_o = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + P.off_o);
     p.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + P.off_ml);
+    p.ws_meta = reinterpret_cast<int2 *>(reinterpret_cast<char *>(workspace) + P.off_meta);
     p.h = dims->h;
     p.d_h = dims->d_h;
     p.RK = dims->R_K;
@@ -174,7 +177,8 @@ int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
     p.batch = batch;
     p.max_len = max_len;
     p.split_blocks = P.split_blocks;
-    p.n_split = P.n_split;
+    p.grid = P.grid;
+    p.merge_parts = P.merge_parts;
     p.score_mul = float(double(resolve_scale(scale, dims->d_h)) * M_LOG2E * factor_scale(dims, 0) *
                         factor_scale(dims, 1) / dims->R_K);
     p.out_mul = float(factor_scale(dims, 2) * factor_scale(dims, 3) / dims->R_V);
@@ -313,7 +317,8 @@ int32_t tpa_cache_read(const tpa_dims *dims, const void *cache, int64_t capacity
 
 int64_t tpa_decode_workspace_bytes(const tpa_dims *dims, int32_t batch, int32_t max_len, int32_t split_tokens) {
     if (!dims_valid(dims) || batch < 0 || max_len < 0 || split_tokens < 0) return -1;
-    return plan_decode(layout_of(dims), batch, max_len, split_tokens).bytes;
+    const DecodePlan P = plan_decode(layout_of(dims), batch, max_len, split_tokens);
+    return P.ok ? P.bytes : -1;
 }
 
 int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,

@@ -246,11 +246,15 @@ struct DecodeParams {
     const int32_t *seq_len;
     const void *q;  // [batch][h][d_h]
     float *out;     // [batch][h][d_h]
-    float *ws_o;    // [batch][n_split][HP][DP]
-    float *ws_ml;   // [batch][n_split][HP][2]
+    float *ws_o;    // [grid + batch][HP][DP]: one partial per (work-group, sequence) job, at wg + b
+    float *ws_ml;   // [grid + batch][HP][2]
+    int2 *ws_meta;  // [batch]: the first and last work-group holding a piece of the sequence
     int64_t capacity;  // cache slots: a sequence reaching past them (or misaligned) gets NaN output
     int h, d_h, RK, RV;
-    int batch, max_len, split_blocks, n_split;
+    int batch, max_len;
+    int split_blocks;  // blocks per work-group; 0: the kernel shares the batch's blocks out over the grid
+    int grid;          // split work-groups
+    int merge_parts;   // the planner's estimate of the pieces per sequence (picks the merge's width)
     float score_mul;  // scale * log2(e) / R_K
     float out_mul;    // 1 / R_V
     // Fused step (tpa_decode_step) when nonzero: q is unrotated and sits at position seq_len[b]; the

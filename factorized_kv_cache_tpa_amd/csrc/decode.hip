@@ -17,11 +17,15 @@
 //   5. O^T[:, i] += B_V[(s,r), :]^T W[(s,r), i]     (M = d_h, K = token rows)
 // The cache block layout (common.h) makes the score accumulator of a lane
 // exactly the k-slice it feeds to step 5, so no data crosses lanes between
-// the contractions.  Each work-group (4 waves) handles one split of one
-// sequence, the waves taking interleaved blocks; the waves merge in LDS and
-// write one partial (max, sum, unnormalized output) per split; a second
-// kernel merges the splits of each sequence:
+// the contractions.  The batch's blocks are shared out evenly over the
+// work-groups (4 waves each), which therefore cover pieces of one or more
+// sequences whatever their lengths; for each piece the waves take interleaved
+// blocks, merge in LDS and write one partial (max, sum, unnormalized output);
+// a second kernel merges the pieces of each sequence:
 //   M = max_j m_j,  out = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j.
+// (Fixed-size splits per sequence left a ragged batch's long sequences running
+// alone at the end: 74% of HBM peak where equal lengths of the same total
+// reach 87%.)
 // (Merging in the same launch by the last work-group to finish a sequence was
 // measured slower on MI355X: the agent-scope release / acquire every
 // work-group then needs writes back and invalidates its XCD's L2.)
@@ -155,11 +159,18 @@ __device__ __forceinline__ float wave_sum_across_groups(float x) {
 
 // Query modes, each its own instantiation so the plain decode carries none of the others:
 //   kQRot  -- q arrives rotated (tpa_decode);
-//   kStep  -- a fused step: q arrives unrotated, split 0 carries the new token (tpa_decode_step);
+//   kStep  -- a fused step: q arrives unrotated, the sequence's first job carries the new token (tpa_decode_step);
 //   kQFact -- q arrives as factors A_Q, B_Q (unrotated), q~ = RoPE((1/R_Q) A_Q^T B_Q) at position len
 //             (tpa_decode_fq).
 constexpr int kQRot = 0, kStepMode = 1, kQFact = 2;
 constexpr int kMaxRQ = 16;  // query rank limit of the factored mode
+
+// A value that is the same in every lane of the wave, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x)));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
+    return int64_t((uint64_t(hi) << 32) | lo);
+}
 
 // kF8: the cache holds E4M3 codes in the paired 8-bit layout (T = uint16_t: bf16 queries and operands).
 template <typename T, int HP, int DP, int RH, int kMode, bool kF8>
@@ -185,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     constexpr int OFF_AV = kRows * HP, OFF_BK = 2 * kRows * HP, OFF_BV = 2 * kRows * HP + kRows * DP;
 
     using F = typename RopeMath<T>::F;
-    // per-wave (max, sum); row kWaves holds a fused step's new token (split 0), else (-inf, 0)
+    // per-wave (max, sum); row kWaves holds a fused step's new token (first job), else (-inf, 0)
     __shared__ float sm_m[kWaves + 1][HP];
     __shared__ float sm_l[kWaves + 1][HP];
     __shared__ __attribute__((aligned(16))) float sm_o[kWaves][HP][DP + 4];
@@ -196,43 +207,119 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     __shared__ __attribute__((aligned(16))) float sm_bq[QR][QD];
     __shared__ __attribute__((aligned(16))) T sm_q[QH][QD + 8];
     __shared__ F sm_cs[SD];             // fused step, factored query: cos/sin of the query's position
-    __shared__ float sm_na[2][RH][SH];  // fused step, split 0: the new token's A_K, A_V
+    __shared__ float sm_na[2][RH][SH];  // fused step, first job: the new token's A_K, A_V
     __shared__ __attribute__((aligned(16))) float sm_nb[2][RH][SD];  // ... its B_K, B_V (unrotated)
     __shared__ float sm_wt[SH];         // ... and the weight of its value row per head (in-group merge)
     static_assert(RH * HP <= kThreads && RH * DP / 2 <= kThreads && DP / 2 <= kThreads,
                   "one new-token item and one RoPE pair per thread");
 
-    const int b = blockIdx.y;
-    const int split = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform: scalar addressing
     const int g = lane >> 4, c = lane & 15;
+    const int tid = threadIdx.x;
 
-    int len = p.seq_len[b];
-    const int64_t start = p.seq_start[b];
-    len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
+    // ---- Work partition.  Sequence b owns v_b = max(ceil(len_b / TOK), 1) virtual blocks (1 if it is
+    // rejected), laid end to end in batch order; work-group wg takes the virtual blocks [wg P, (wg + 1) P)
+    // (P = per_wg)
+    // and runs one job per sequence that range touches: that piece of the sequence's blocks, folded into
+    // one partial at index wg + b (along the partition (wg, b) only ever steps up, in one or both, so the
+    // index is unique).  The blocks are shared out evenly however ragged the lengths, and every work-group
+    // finds its range from the lengths itself (no planning launch).
+    struct SeqInfo {
+        int len, vb;
+        int64_t start;
+        bool rejected;
+    };
+    auto seq_info = [&](int bb) -> SeqInfo {
+        SeqInfo si;
+        const int ln = p.seq_len[bb];
+        si.len = ln < 0 ? 0 : (ln > p.max_len ? p.max_len : ln);
+        si.start = p.seq_start[bb];
+        // A sequence that is misaligned, or whose slots (a fused step: and the new token's slot) reach past
+        // the capacity, is not read at all: NaN output.
+        si.rejected = seq_rejected(si.start, int64_t(si.len) + (kStep ? 1 : 0), TOK, p.capacity);
+        si.vb = si.rejected ? 1 : max((si.len + TOK - 1) / TOK, 1);
+        return si;
+    };
+    __shared__ int64_t sm_wsum[kWaves];
+    __shared__ int64_t sm_first[2];  // the first sequence of this work-group's range, and its first virtual block
+    __shared__ int64_t sm_first_start;  // ... and that sequence's start, length, virtual blocks, state
+    __shared__ int sm_first_len, sm_first_vb, sm_first_rej;
+    const int wg = blockIdx.x;
+    const int per = (p.batch + kThreads - 1) / kThreads;  // sequences per thread in the scan
+    const int b_lo = min(p.batch, tid * per), b_hi = min(p.batch, b_lo + per);
+    int64_t mine = 0;
+    SeqInfo lo_si{0, 0, 0, false};  // the thread's first sequence, kept (one sequence per thread up to 256)
+    for (int bb = b_lo; bb < b_hi; ++bb) {
+        const SeqInfo si = seq_info(bb);
+        if (bb == b_lo) lo_si = si;
+        mine += si.vb;
+    }
+    int64_t incl = mine;  // inclusive scan over the wave, then over the waves through LDS
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int64_t y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
+    }
+    if (lane == kWave - 1) sm_wsum[w] = incl;
+    __syncthreads();
+    int64_t excl = incl - mine, V = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+        excl += ww < w ? sm_wsum[ww] : 0;
+        V += sm_wsum[ww];
+    }
+    V = uniform64(V);  // the same in every lane: scalar registers
+    int64_t per_wg = p.split_blocks;  // blocks per work-group: the caller's, or the batch's share of the grid
+    if (per_wg <= 0) {
+        per_wg = (V + gridDim.x - 1) / gridDim.x;
+        per_wg = (per_wg + kWaves - 1) / kWaves * kWaves;
+        // a short call (two blocks per wave or fewer) is latency-bound: fewer, longer pieces halve the
+        // partials to merge and cost no bandwidth
+        if (per_wg <= 2 * kWaves) per_wg = 4 * kWaves;
+    }
+    per_wg = uniform64(per_wg);
+    const int64_t gs = int64_t(wg) * per_wg;
+    if (gs >= V) return;  // nothing left for this work-group (uniform)
+    const int64_t ge = uniform64(min(V, gs + per_wg));
+    if (gs >= excl && gs < excl + mine) {  // the one thread whose sequences hold virtual block gs
+        int bb = b_lo;
+        SeqInfo si = lo_si;
+        while (gs >= excl + si.vb) {  // (only with more than one sequence per thread)
+            excl += si.vb;
+            si = seq_info(++bb);
+        }
+        sm_first[0] = bb;
+        sm_first[1] = excl;
+        sm_first_start = si.start;
+        sm_first_len = si.len;
+        sm_first_vb = si.vb;
+        sm_first_rej = si.rejected;
+    }
+    __syncthreads();
+
+    // One job: blocks [blk_begin, blk_end_v) of sequence b (virtual blocks past its last real one hold
+    // nothing), its partial at index part.  first: the job holds the sequence's first block, last: its last.
+    auto run_job = [&](const int b, const SeqInfo si, const int64_t part, const int blk_begin, const int blk_end_v,
+                       const bool first_job, const bool last_job) {
+    const int len = si.len;
+    const int64_t start = si.start;
+    const bool rejected = si.rejected;
     const int nblk = (len + TOK - 1) / TOK;
-    const int blk_begin = split * p.split_blocks;
-    // A sequence that is misaligned, or whose slots (a fused step: and the new token's slot) reach past
-    // the capacity, is not read at all: NaN output.
-    const bool rejected = seq_rejected(start, int64_t(len) + (kStep ? 1 : 0), TOK, p.capacity);
-    // A fused step's split 0 carries the step's new token (even over an empty sequence): it writes the
-    // token's record and folds the token's own score and value into its partial.
-    const bool new_tok = kStep && split == 0 && !rejected;
-    // ... and the sequence's last split with tokens (split 0 for an empty sequence) writes its record, so
-    // the two extra jobs land on different work-groups
-    const int last_split = nblk > 0 ? min(p.n_split - 1, (nblk - 1) / p.split_blocks) : 0;
-    const bool rec_tok = kStep && split == last_split && !rejected;
+    // A fused step's first job carries the step's new token (even over an empty sequence): it folds the
+    // token's own score and value into its partial ...
+    const bool new_tok = kStep && first_job && !rejected;
+    // ... and its last job writes the token's record (for a long sequence the two land on different
+    // work-groups)
+    const bool rec_tok = kStep && last_job && !rejected;
     if (rejected || (blk_begin >= nblk && !new_tok)) {
-        // A split with no tokens (past the sequence's end, or the sequence is empty or rejected) marks
-        // its partial empty (max -inf, sum 0), so the merge kernel can read every split without waiting
-        // for anything else; the merge writes zeros (empty) or NaN (rejected).
-        const int64_t part = int64_t(b) * p.n_split + split;
+        // A job with no tokens (an empty or rejected sequence) marks its partial empty (max -inf, sum 0);
+        // the merge writes zeros (empty) or NaN (rejected).
         for (int head = threadIdx.x; head < HP; head += kThreads)
             *reinterpret_cast<float2 *>(p.ws_ml + (part * HP + head) * 2) = make_float2(-INFINITY, 0.f);
         return;
     }
-    const int blk_end = min(nblk, blk_begin + p.split_blocks);
+    const int blk_end = min(nblk, blk_end_v);
     const int full_end = min(blk_end, len / TOK);  // blocks [blk_begin, full_end) hold TOK valid tokens
     constexpr int CES = kF8 ? 1 : int(sizeof(T));  // bytes per stored element
     const char *seq = reinterpret_cast<const char *>(p.cache) + (start / TOK) * BLK * CES;
@@ -313,10 +400,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         }
     };
 
-    // Fused step, split 0: this thread's item of the new token (one head-factor pair (A_K, A_V) of row
+    // Fused step, first job: this thread's item of the new token (one head-factor pair (A_K, A_V) of row
     // r, head i, and one feature pair (d, d+1) of B_K and B_V of row r), loaded before everything else:
     // memory returns in order, so these must not queue behind the factor stream.
-    const int tid = threadIdx.x;
     const int na_r = tid / HP, na_i = tid % HP, nb_r = tid / (DP / 2), nb_d = 2 * (tid % (DP / 2));
     T nak = T(0), nav = T(0), nbk0 = T(0), nbk1 = T(0), nbv0 = T(0), nbv1 = T(0);
     if (kStep && (new_tok || rec_tok)) {
@@ -381,11 +467,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     constexpr bool kTwoStages = sizeof(T) == 2 || HP * DP <= 1024;
     Stage s0, s1;
     int blk = blk_begin + w;
-    // The two stages are loaded unconditionally, clamped to the split's last block (which every wave
+    // The two stages are loaded unconditionally, clamped to the job's last block (which every wave
     // may read): a wave with a single block reads one block twice, but the loads then sit in fixed
     // program order, so the compiler can wait for each stage exactly instead of draining every load in
     // flight at the top of the pipelined loop below.
-    // (Outside a fused step every work-group that gets here has a block.  A fused step's split 0 of an
+    // (Outside a fused step every work-group that gets here has a block.  A fused step's first job of an
     // empty sequence has none: its stages read the cache's first block instead and never use it, so that
     // no load sits behind a branch, which would leave every wait of the mode conservative.)
     const int last_blk = blk_end - 1;
@@ -455,17 +541,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     }
     if constexpr (kStep) {
         // Fused step, while the first blocks stream in.  q arrives unrotated and sits at position len (the
-        // number of cached tokens).  Split 0 stages the new token's factors in LDS and, after the one
+        // number of cached tokens).  The first job stages the new token's factors in LDS and, after the one
         // barrier the angle table needs anyway, takes the token's score per head from the still unrotated
         // query fragments and the unrotated B_K: query and token share a position, so RoPE drops out of that
         // score (RoPE compatibility, Theorem 3.1 with t = s).  Then every wave rotates its query fragments
         // (the table covers every padded pair; theta is zero past d_h / 2: an identity rotation of zeros),
-        // and the sequence's last split writes the token's record at slot len: no work-group of this kernel
+        // and the sequence's last job writes the token's record at slot len: no work-group of this kernel
         // reads that slot's rows (a partly filled last block masks every row at or past len), and the next
         // call sees it.
         // Over an E4M3 cache the token enters as its stored values, exactly as tpa_cache_append and then a
         // decode would see it: every factor is rounded to its code and decoded back, B_K after its rotation,
-        // which no longer cancels in the score; so split 0 stages the rotated, decoded B~_K after the
+        // which no longer cancels in the score; so the first job stages the rotated, decoded B~_K after the
         // table and takes the score from the rotated query fragments behind a second barrier.
         auto token_score = [&]() {
             // the token's score per head: a lane sums its d-values, the four lane groups of a head are
@@ -556,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                     sm_nb[0][nb_r][nb_d] = v.x;
                     sm_nb[0][nb_r][nb_d + 1] = v.y;
                 }
-                __syncthreads();  // split 0 only (uniform over the work-group)
+                __syncthreads();  // first job only (uniform over the work-group)
                 token_score();
             }
         }
@@ -800,7 +886,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                 sm_wt[head] = sm_m[kWaves][head] == -INFINITY ? 0.f : exp2f(sm_m[kWaves][head] - mm);
     }
     // every wave writes its rescaled accumulators to its own LDS slice; after one barrier all threads
-    // sum the slices column by column straight into the split's partial
+    // sum the slices column by column straight into the job's partial
 #pragma unroll
     for (int mv = 0; mv < MBV; ++mv)
 #pragma unroll
@@ -809,8 +895,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             *reinterpret_cast<float4 *>(&sm_o[w][16 * nb + c][16 * mv + 4 * g]) = make_float4(a[0], a[1], a[2], a[3]);
         }
     __syncthreads();
-    // write the split's partial: O [HP][DP], (max, sum) [HP]
-    const int64_t part = int64_t(b) * p.n_split + split;
+    // write the job's partial: O [HP][DP], (max, sum) [HP]
     float *wo = p.ws_o + part * HP * DP;
     for (int idx = threadIdx.x; idx < HP * DP / 4; idx += kThreads) {
         const int hh = idx / (DP / 4), d4 = idx % (DP / 4);
@@ -846,16 +931,39 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             ll += sm_m[ww][head] == -INFINITY ? 0.f : sm_l[ww][head] * exp2f(sm_m[ww][head] - mm);
         *reinterpret_cast<float2 *>(p.ws_ml + (part * HP + head) * 2) = make_float2(mm, ll);
     }
+    };
 
+    // the jobs of this work-group's range, in batch order
+    int b = __builtin_amdgcn_readfirstlane(int(sm_first[0]));
+    int64_t Vb = uniform64(sm_first[1]);
+    for (bool first_of_wg = true;; first_of_wg = false) {
+        SeqInfo si;
+        if (first_of_wg) {
+            si.len = sm_first_len;
+            si.vb = sm_first_vb;
+            si.start = sm_first_start;
+            si.rejected = sm_first_rej != 0;
+        } else {
+            si = seq_info(b);
+        }
+        const int64_t lo = max(gs, Vb) - Vb, hi = min(ge, Vb + si.vb) - Vb;
+        const bool first_job = Vb >= gs, last_job = Vb + si.vb <= ge;
+        // the work-group of a sequence's first block records the range of work-groups that hold its pieces
+        if (first_job && tid == 0) p.ws_meta[b] = make_int2(wg, int((Vb + si.vb - 1) / per_wg));
+        run_job(b, si, int64_t(wg) + b, int(lo), int(hi), first_job, last_job);
+        Vb += si.vb;
+        if (Vb >= ge || ++b >= p.batch) break;
+        __syncthreads();  // the next job reuses this one's LDS
+    }
 }
 
-// Second pass: merge the per-split partials.  One work-group of kThr threads per (head, sequence);
-// thread t owns output columns 4 (t % C4) .. +3 and the splits j = t / C4 (mod JL),
-// where C4 = DP / 4 and JL = kThr / C4.  Each thread folds its splits with the
+// Second pass: merge the partials of each sequence's pieces.  One work-group of kThr threads per (head,
+// sequence); thread t owns output columns 4 (t % C4) .. +3 and the pieces j = t / C4 (mod JL),
+// where C4 = DP / 4 and JL = kThr / C4.  Each thread folds its pieces with the
 // same rescaling rule, loads issued eight at a time, and the JL lanes of a column
 // group are folded once more through LDS.  (A fused step's new token is already part
-// of split 0's partial.)  The launch takes 128 threads when every lane then has one round of
-// loads (a short call: the smaller work-group finishes sooner), else 256.
+// of the first piece's partial.)  The launch takes 128 threads when the planner expects every lane to
+// have one round of loads (a short call: the smaller work-group finishes sooner), else 256.
 constexpr int kMergeUnroll = 8;
 
 template <int kThr>
@@ -864,16 +972,18 @@ __global__ __launch_bounds__(kThr) void decode_merge_kernel(DecodeParams p, int 
     const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int C4 = DP / 4, JL = kThr / C4;
     const int c4 = tid % C4, jl = tid / C4;
-    // Every split wrote a partial (an empty one has max -inf), so the loads below do not wait on the
-    // sequence's start and length; those only decide the rejected case (the split kernel's predicate).
+    // The sequence's pieces sit at partial indices wg + b for the work-groups wg its meta record names
+    // (every one of them wrote a partial; an empty one has max -inf).  Start and length only decide the
+    // rejected case (the split kernel's predicate).
+    const int2 wgs = p.ws_meta[b];
     const int64_t start = p.seq_start[b];
     int len = p.seq_len[b];
     len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
     const bool rejected = seq_rejected(start, int64_t(len) + (p.step ? 1 : 0), TOK, p.capacity);
-    const int n_valid = p.n_split;
+    const int n_valid = wgs.y - wgs.x + 1;
 
     float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-    const int64_t base = int64_t(b) * p.n_split;
+    const int64_t base = int64_t(wgs.x) + b;
     for (int j0 = jl; j0 < n_valid; j0 += JL * kMergeUnroll) {
         float mj[kMergeUnroll], lj[kMergeUnroll];
         float4 oj[kMergeUnroll];
@@ -941,7 +1051,7 @@ __global__ __launch_bounds__(kThr) void decode_merge_kernel(DecodeParams p, int 
 
 template <typename T, int HP, int DP, int RH>
 hipError_t launch_split(const DecodeParams &p, bool f8, hipStream_t s) {
-    const dim3 grid(p.n_split, p.batch);
+    const dim3 grid(p.grid);
     if constexpr (sizeof(T) == 2) {
         if (f8) {
             if (p.step)
@@ -1004,7 +1114,7 @@ hipError_t launch_decode(const Layout &L, const DecodeParams &p, hipStream_t s) 
     TPA_DECODE_SHAPES(X)
 #undef X
     if (!found || e != hipSuccess) return e;
-    if (p.n_split <= (128 / (L.DP / 4)) * kMergeUnroll)
+    if (p.merge_parts <= (128 / (L.DP / 4)) * kMergeUnroll)
         hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(L.HP, p.batch), dim3(128), 0, s, p, L.HP, L.DP,
                            L.tok_per_block());
     else

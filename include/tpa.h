@@ -161,7 +161,10 @@ int64_t tpa_decode_workspace_bytes(const tpa_dims *dims, int32_t batch, int32_t 
 
 /* Split-sequence decode: one query row per sequence attends to all of its
  * cached tokens, computed from the factors (TPA notes page, FlashTPA: no full
- * K/V is built).  Per sequence b and head i:
+ * K/V is built).  The batch's cache blocks are shared out evenly over the
+ * work-groups whatever the lengths (a work-group may cover the end of one
+ * sequence and the start of the next); each piece leaves a partial, and a
+ * second kernel merges the pieces of each sequence.  Per sequence b and head i:
  *     out[b][i] = sum_s softmax_s(scale * q~_b,i . K~_s[i,:]) V_s[i,:]
  * over s = 0 .. seq_len[b]-1, with K~_s, V_s from the cached factors.
  *   seq_start[batch]  int64 first slot of each sequence; must be a multiple of
@@ -175,12 +178,13 @@ int64_t tpa_decode_workspace_bytes(const tpa_dims *dims, int32_t batch, int32_t 
  *   q_rot [batch][h][d_h]  queries already rotated to their positions (tpa_cache_append)
  *   scale             softmax scale; <= 0 selects 1/sqrt(d_h)
  *   out [batch][h][d_h]    fp32
- *   split_tokens      tokens per split work unit; 0 lets the library choose
+ *   split_tokens      cached tokens per work-group (rounded up to whole blocks); 0 lets the
+ *                     library share the batch's tokens evenly over one round of work-groups
  *   workspace         >= tpa_decode_workspace_bytes(dims, batch, max_len, split_tokens)
- *                     bytes of device memory, 256-byte aligned; holds the per-split partials
- *                     (running max, sum, unnormalized output) between the split kernel and the
- *                     merge kernel.  One workspace serves one call at a time: calls that overlap
- *                     on it race.
+ *                     bytes of device memory, 256-byte aligned; holds the pieces' partials
+ *                     (running max, sum, unnormalized output) and each sequence's range of
+ *                     pieces between the split kernel and the merge kernel.  One workspace
+ *                     serves one call at a time: calls that overlap on it race.
  * max_len <= capacity_tokens, else TPA_ERR_CAPACITY. */
 int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tokens, int32_t batch,
                    const int64_t *seq_start, const int32_t *seq_len, int32_t max_len, const void *q_rot,
@@ -188,7 +192,7 @@ int32_t tpa_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
                    void *stream);
 
 /* tpa_decode for callers that cannot allocate device memory (code under HIP graph capture, tight serving
- * loops, harnesses that forbid hipMalloc): the same split and merge kernels, with the per-split partials in a
+ * loops, harnesses that forbid hipMalloc): the same split and merge kernels, with the pieces' partials in a
  * static device array of the library instead of a caller workspace.  The call allocates nothing and calls
  * no allocating routine.
  *   - The array holds TPA_DECODE_NOALLOC_MAX_BYTES; a call whose tpa_decode_workspace_bytes(dims, batch,
@@ -210,9 +214,10 @@ int32_t tpa_decode_noalloc(const tpa_dims *dims, const void *cache, int64_t capa
  * tpa_cache_append writes it), rotate the query at position N, and attend over the N cached tokens and
  * the new one (the one-query decode of the TPA notes page, FlashTPA; RoPE compatibility, Theorem 3.1):
  *     out[b][i] = sum_{s <= N} softmax_s(scale * q~_b,i . K~_s[i,:]) V_s[i,:]
- * Two kernel launches (split, merge) and no separate append: every split work-group rotates the query in
- * registers, the sequence's first split folds in the new token's own score and value (query and token share
- * a position, so RoPE cancels in that score) and its last split writes the token's record.  Over a
+ * Two kernel launches (split, merge) and no separate append: every work-group rotates the query in
+ * registers, the work-group holding the sequence's first piece folds in the new token's own score and value
+ * (query and token share a position, so RoPE cancels in that score) and the one holding its last piece
+ * writes the token's record.  Over a
  * TPA_CACHE_E4M3 cache the token enters as its stored values (codes decoded back, B_K rotated before its
  * rounding), exactly as tpa_cache_append followed by tpa_decode would see it.
  *   A_K [batch][R_K][h], B_K [batch][R_K][d_h], A_V [batch][R_V][h], B_V [batch][R_V][d_h]
