@@ -9,6 +9,8 @@ One step = one serving iteration of the largest workload,
   2. tpa_cache_append of a 512-token chunk for each of 8 more sequences holding 2048 cached
      tokens, which also rotates the chunk's 512 query rows;
   3. tpa_prefill_chunk: row j of each chunk attends causally over tokens 0 .. 2048 + j.
+  Parts 2-3 serve other sequences than part 1 and run on a second stream beside it (fork and join
+  inside the step's graph).
 Every input is resident in device memory before the timed region.  value = cached tokens the
 decode attends to (the sum of the 128 lengths) per second of whole-step time.
 
@@ -565,7 +567,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20, help="untimed replays of the step before the timed ones")
     ap.add_argument("--no-extras", action="store_true", help="only the headline step and its legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--profile-leg", choices=("step", "decode", "prefill", "append"),
@@ -598,17 +600,32 @@ def main():
     pre = PrefillBench()
     w = dec.w
 
-    def serving_step(i: int):
-        dec.step(0)
-        pre.append()
-        pre.prefill()
+    # The decode and the prefill serve different sequences, so the step forks: the append and the prefill
+    # run on a second stream beside the decode step (the decode streams HBM on most CUs, the prefill keeps
+    # the matrix cores of the others busy), and the step ends when both have.  Default stream priorities.
+    side = torch.cuda.Stream()
 
-    for _ in range(args.warmup):
-        serving_step(0)
+    def serving_step(i: int):
+        cur = torch.cuda.current_stream()
+        fork = torch.cuda.Event()
+        fork.record(cur)
+        side.wait_event(fork)
+        with torch.cuda.stream(side):
+            pre.append()
+            pre.prefill()
+        dec.step(0)
+        join = torch.cuda.Event()
+        join.record(side)
+        cur.wait_event(join)
+
+    serving_step(0)
     torch.cuda.synchronize()
     eager_dec, eager_pre = dec.out.clone(), pre.out.clone()
     g = timer.capture(serving_step, 1)
-    g.replay()
+    # warmup: replays of the step's graph (the first few after a capture run measurably slower)
+    with torch.cuda.stream(timer.stream):
+        for _ in range(args.warmup):
+            g.replay()
     torch.cuda.synchronize()
     # the timed region: exactly `steps` steps, one graph replay each, events around every replay
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]

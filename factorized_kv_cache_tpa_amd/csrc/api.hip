@@ -21,12 +21,14 @@ namespace {
 using tpa::Layout;
 
 // Decode work partition: the split kernel shares the batch's blocks out evenly over its work-groups (it
-// scans the device-resident lengths itself), so the host only picks the grid: one round of work-groups
-// over the 256 compute units of an MI355X, where the wide layouts (HP * DP >= 2048) run one 4-wave
-// work-group per CU (their waves need most of the register file) and the narrow ones two.  A caller's
-// split_tokens fixes the blocks per work-group instead, and the grid is sized for the longest batch the
-// arguments allow.
+// scans the device-resident lengths itself), so the host only picks the grid: at most one work-group per
+// compute unit of an MI355X (256), and for the wide layouts (HP * DP >= 2048, whose waves need most of
+// the register file) 192 of them, which measured faster on the ragged 128-sequence workload (831 vs 851
+// us) and leaves a quarter of the CUs to work on another stream; never more than pieces of 16 blocks
+// would fill.  A caller's split_tokens fixes the blocks per work-group instead, and the grid is sized for
+// the longest batch the arguments allow.
 constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kWideDecodeGroups = 192;
 constexpr int kDecodeWaves = 4;
 
 bool dims_valid(const tpa_dims *d) {
@@ -85,7 +87,8 @@ DecodePlan plan_decode(const Layout &L, int32_t batch, int32_t max_len, int32_t 
         t_est = sb;
         P.split_blocks = int(std::min<int64_t>(sb, 1 << 30));
     } else {
-        grid = kComputeUnits * (L.HP * L.DP >= 2048 ? 1 : 2);
+        const int64_t target = L.HP * L.DP >= 2048 ? kWideDecodeGroups : kComputeUnits;
+        grid = std::min<int64_t>(target, (int64_t(batch) * vmax + 4 * kDecodeWaves - 1) / (4 * kDecodeWaves));
         t_est = std::max<int64_t>(4 * kDecodeWaves, (int64_t(batch) * vmax + grid - 1) / grid);
     }
     if (grid < 1) grid = 1;

@@ -29,6 +29,7 @@
 // (Merging in the same launch by the last work-group to finish a sequence was
 // measured slower on MI355X: the agent-scope release / acquire every
 // work-group then needs writes back and invalidates its XCD's L2.)
+#include <climits>
 #include <type_traits>
 
 #include "common.h"
@@ -242,6 +243,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         return si;
     };
     __shared__ int64_t sm_wsum[kWaves];
+    __shared__ int sm_wmin[kWaves], sm_wmax[kWaves];
     __shared__ int64_t sm_first[2];  // the first sequence of this work-group's range, and its first virtual block
     __shared__ int64_t sm_first_start;  // ... and that sequence's start, length, virtual blocks, state
     __shared__ int sm_first_len, sm_first_vb, sm_first_rej;
@@ -249,40 +251,77 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     const int per = (p.batch + kThreads - 1) / kThreads;  // sequences per thread in the scan
     const int b_lo = min(p.batch, tid * per), b_hi = min(p.batch, b_lo + per);
     int64_t mine = 0;
+    int vmin = INT_MAX, vmax = 0;
     SeqInfo lo_si{0, 0, 0, false};  // the thread's first sequence, kept (one sequence per thread up to 256)
     for (int bb = b_lo; bb < b_hi; ++bb) {
         const SeqInfo si = seq_info(bb);
         if (bb == b_lo) lo_si = si;
         mine += si.vb;
+        vmin = min(vmin, si.vb);
+        vmax = max(vmax, si.vb);
     }
     int64_t incl = mine;  // inclusive scan over the wave, then over the waves through LDS
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
         const int64_t y = __shfl_up(incl, o, kWave);
         if (lane >= o) incl += y;
+        vmin = min(vmin, __shfl_xor(vmin, o, kWave));
+        vmax = max(vmax, __shfl_xor(vmax, o, kWave));
     }
     if (lane == kWave - 1) sm_wsum[w] = incl;
+    if (lane == 0) {
+        sm_wmin[w] = vmin;
+        sm_wmax[w] = vmax;
+    }
     __syncthreads();
     int64_t excl = incl - mine, V = 0;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
         excl += ww < w ? sm_wsum[ww] : 0;
         V += sm_wsum[ww];
+        vmin = min(vmin, sm_wmin[ww]);
+        vmax = max(vmax, sm_wmax[ww]);
     }
     V = uniform64(V);  // the same in every lane: scalar registers
-    int64_t per_wg = p.split_blocks;  // blocks per work-group: the caller's, or the batch's share of the grid
+    vmax = __builtin_amdgcn_readfirstlane(vmax);
+    // Blocks per work-group: the caller's, or the batch's share of the grid.  When every sequence has the
+    // same number of blocks (and the grid has a work-group for each), each is cut into k equal pieces
+    // instead, k work-groups per sequence and none straddling two sequences (for short pieces a second job
+    // costs more than the imbalance it removes): the same partition with every sequence padded to k pieces.
+    int64_t per_wg = p.split_blocks, stride = 0;  // stride: virtual blocks per sequence when padded
     if (per_wg <= 0) {
-        per_wg = (V + gridDim.x - 1) / gridDim.x;
-        per_wg = (per_wg + kWaves - 1) / kWaves * kWaves;
-        // a short call (two blocks per wave or fewer) is latency-bound: fewer, longer pieces halve the
-        // partials to merge and cost no bandwidth
-        if (per_wg <= 2 * kWaves) per_wg = 4 * kWaves;
+        auto round_up = [&](int64_t x) {
+            x = (x + kWaves - 1) / kWaves * kWaves;
+            // a short piece (two blocks per wave or fewer) is latency-bound: fewer, longer pieces halve
+            // the partials to merge and cost no bandwidth
+            return x <= 2 * kWaves ? int64_t(4 * kWaves) : x;
+        };
+        if (__builtin_amdgcn_readfirstlane(vmin) == vmax && int64_t(gridDim.x) >= p.batch) {
+            const int64_t k0 = max<int64_t>(1, int64_t(gridDim.x) / p.batch);
+            per_wg = round_up((vmax + k0 - 1) / k0);
+            stride = (vmax + per_wg - 1) / per_wg * per_wg;
+            V = stride * p.batch;
+        } else {
+            per_wg = round_up((V + gridDim.x - 1) / gridDim.x);
+        }
     }
     per_wg = uniform64(per_wg);
+    stride = uniform64(stride);
     const int64_t gs = int64_t(wg) * per_wg;
     if (gs >= V) return;  // nothing left for this work-group (uniform)
     const int64_t ge = uniform64(min(V, gs + per_wg));
-    if (gs >= excl && gs < excl + mine) {  // the one thread whose sequences hold virtual block gs
+    if (stride > 0) {  // padded: the first sequence is gs / stride
+        const int64_t b0 = gs / stride;
+        if (b0 >= b_lo && b0 < b_hi) {
+            const SeqInfo si = b0 == b_lo ? lo_si : seq_info(int(b0));
+            sm_first[0] = b0;
+            sm_first[1] = b0 * stride;
+            sm_first_start = si.start;
+            sm_first_len = si.len;
+            sm_first_vb = si.vb;
+            sm_first_rej = si.rejected;
+        }
+    } else if (gs >= excl && gs < excl + mine) {  // the one thread whose sequences hold virtual block gs
         int bb = b_lo;
         SeqInfo si = lo_si;
         while (gs >= excl + si.vb) {  // (only with more than one sequence per thread)
@@ -946,12 +985,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         } else {
             si = seq_info(b);
         }
-        const int64_t lo = max(gs, Vb) - Vb, hi = min(ge, Vb + si.vb) - Vb;
-        const bool first_job = Vb >= gs, last_job = Vb + si.vb <= ge;
+        const int64_t vb = stride > 0 ? stride : si.vb;  // the sequence's share of the partition
+        const int64_t lo = max(gs, Vb) - Vb, hi = min(ge, Vb + vb) - Vb;
+        const bool first_job = Vb >= gs, last_job = Vb + vb <= ge;
         // the work-group of a sequence's first block records the range of work-groups that hold its pieces
-        if (first_job && tid == 0) p.ws_meta[b] = make_int2(wg, int((Vb + si.vb - 1) / per_wg));
+        if (first_job && tid == 0) p.ws_meta[b] = make_int2(wg, int((Vb + vb - 1) / per_wg));
         run_job(b, si, int64_t(wg) + b, int(lo), int(hi), first_job, last_job);
-        Vb += si.vb;
+        Vb += vb;
         if (Vb >= ge || ++b >= p.batch) break;
         __syncthreads();  // the next job reuses this one's LDS
     }
