@@ -469,7 +469,9 @@ def summarize_profiles(raw: str) -> None:
                  "Each decode workload has its own kernel instantiation (rank 4: the ragged workload; rank 2 with "
                  "h=32: 4 x 131072; h=16: 64 x 8192; rank 1: 16 x 4096; `..., true>` instantiations: the E4M3 "
                  "cache; mode 1: the fused step, 0: tpa_decode, 2: factored query).  `prefill2<32, 128, 4, false>` "
-                 "is the serving step's prefill and its timed leg.", "",
+                 "is the serving step's prefill and its timed leg: in the serving step it runs on a second stream beside the "
+                 "decode step, so those dispatches span most of the step (the maximum column), while the timed leg runs it "
+                 "alone (the minimum column; kernel_trace_prefill_* has it alone).", "",
                  "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
         for r in _rows(path):
             if "tpa::" not in r["Name"]:
