@@ -93,7 +93,10 @@ DecodePlan plan_decode(const Layout &L, int32_t batch, int32_t max_len, int32_t 
     }
     if (grid < 1) grid = 1;
     const int64_t parts = grid + batch;
-    P.ok = grid <= (int64_t(1) << 30) && parts * L.HP * L.DP <= (int64_t(1) << 40);
+    // the kernel partitions the batch's virtual blocks in 32-bit arithmetic: keep every count it forms
+    // (padded sequences included) below 2^31
+    const int64_t vblocks = int64_t(batch) * (2 * vmax + 4 * kDecodeWaves) + t_est;
+    P.ok = grid <= (int64_t(1) << 30) && parts * L.HP * L.DP <= (int64_t(1) << 40) && vblocks < (int64_t(1) << 31);
     P.grid = int(std::min<int64_t>(grid, 1 << 30));
     P.merge_parts = int(std::min<int64_t>((vmax + t_est - 1) / t_est + 1, 1 << 30));
     const int64_t o_bytes = parts * L.HP * L.DP * 4;

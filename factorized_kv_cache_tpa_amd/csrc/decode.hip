@@ -166,13 +166,6 @@ __device__ __forceinline__ float wave_sum_across_groups(float x) {
 constexpr int kQRot = 0, kStepMode = 1, kQFact = 2;
 constexpr int kMaxRQ = 16;  // query rank limit of the factored mode
 
-// A value that is the same in every lane of the wave, moved to scalar registers.
-__device__ __forceinline__ int64_t uniform64(int64_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x)));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
-    return int64_t((uint64_t(hi) << 32) | lo);
-}
-
 // kF8: the cache holds E4M3 codes in the paired 8-bit layout (T = uint16_t: bf16 queries and operands).
 template <typename T, int HP, int DP, int RH, int kMode, bool kF8>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
@@ -242,15 +235,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         si.vb = si.rejected ? 1 : max((si.len + TOK - 1) / TOK, 1);
         return si;
     };
-    __shared__ int64_t sm_wsum[kWaves];
+    __shared__ int sm_wsum[kWaves];
     __shared__ int sm_wmin[kWaves], sm_wmax[kWaves];
-    __shared__ int64_t sm_first[2];  // the first sequence of this work-group's range, and its first virtual block
+    __shared__ int sm_first[2];  // the first sequence of this work-group's range, and its first virtual block
     __shared__ int64_t sm_first_start;  // ... and that sequence's start, length, virtual blocks, state
     __shared__ int sm_first_len, sm_first_vb, sm_first_rej;
     const int wg = blockIdx.x;
     const int per = (p.batch + kThreads - 1) / kThreads;  // sequences per thread in the scan
     const int b_lo = min(p.batch, tid * per), b_hi = min(p.batch, b_lo + per);
-    int64_t mine = 0;
+    int mine = 0;  // (the host bounds the batch's virtual blocks below 2^31)
     int vmin = INT_MAX, vmax = 0;
     SeqInfo lo_si{0, 0, 0, false};  // the thread's first sequence, kept (one sequence per thread up to 256)
     for (int bb = b_lo; bb < b_hi; ++bb) {
@@ -260,10 +253,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         vmin = min(vmin, si.vb);
         vmax = max(vmax, si.vb);
     }
-    int64_t incl = mine;  // inclusive scan over the wave, then over the waves through LDS
+    int incl = mine;  // inclusive scan over the wave, then over the waves through LDS
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
-        const int64_t y = __shfl_up(incl, o, kWave);
+        const int y = __shfl_up(incl, o, kWave);
         if (lane >= o) incl += y;
         vmin = min(vmin, __shfl_xor(vmin, o, kWave));
         vmax = max(vmax, __shfl_xor(vmax, o, kWave));
@@ -274,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         sm_wmax[w] = vmax;
     }
     __syncthreads();
-    int64_t excl = incl - mine, V = 0;
+    int excl = incl - mine, V = 0;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
         excl += ww < w ? sm_wsum[ww] : 0;
@@ -282,38 +275,38 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         vmin = min(vmin, sm_wmin[ww]);
         vmax = max(vmax, sm_wmax[ww]);
     }
-    V = uniform64(V);  // the same in every lane: scalar registers
+    V = __builtin_amdgcn_readfirstlane(V);  // the same in every lane: scalar registers
     vmax = __builtin_amdgcn_readfirstlane(vmax);
     // Blocks per work-group: the caller's, or the batch's share of the grid.  When every sequence has the
     // same number of blocks (and the grid has a work-group for each), each is cut into k equal pieces
     // instead, k work-groups per sequence and none straddling two sequences (for short pieces a second job
     // costs more than the imbalance it removes): the same partition with every sequence padded to k pieces.
-    int64_t per_wg = p.split_blocks, stride = 0;  // stride: virtual blocks per sequence when padded
+    int per_wg = p.split_blocks, stride = 0;  // stride: virtual blocks per sequence when padded
     if (per_wg <= 0) {
-        auto round_up = [&](int64_t x) {
+        auto round_up = [&](int x) {
             x = (x + kWaves - 1) / kWaves * kWaves;
             // a short piece (two blocks per wave or fewer) is latency-bound: fewer, longer pieces halve
             // the partials to merge and cost no bandwidth
-            return x <= 2 * kWaves ? int64_t(4 * kWaves) : x;
+            return x <= 2 * kWaves ? 4 * kWaves : x;
         };
         if (__builtin_amdgcn_readfirstlane(vmin) == vmax && int64_t(gridDim.x) >= p.batch) {
-            const int64_t k0 = max<int64_t>(1, int64_t(gridDim.x) / p.batch);
+            const int k0 = max(1, int(gridDim.x) / p.batch);
             per_wg = round_up((vmax + k0 - 1) / k0);
             stride = (vmax + per_wg - 1) / per_wg * per_wg;
             V = stride * p.batch;
         } else {
-            per_wg = round_up((V + gridDim.x - 1) / gridDim.x);
+            per_wg = round_up((V + int(gridDim.x) - 1) / int(gridDim.x));
         }
     }
-    per_wg = uniform64(per_wg);
-    stride = uniform64(stride);
-    const int64_t gs = int64_t(wg) * per_wg;
+    per_wg = __builtin_amdgcn_readfirstlane(per_wg);
+    stride = __builtin_amdgcn_readfirstlane(stride);
+    const int gs = wg * per_wg;
     if (gs >= V) return;  // nothing left for this work-group (uniform)
-    const int64_t ge = uniform64(min(V, gs + per_wg));
+    const int ge = __builtin_amdgcn_readfirstlane(min(V, gs + per_wg));
     if (stride > 0) {  // padded: the first sequence is gs / stride
-        const int64_t b0 = gs / stride;
+        const int b0 = gs / stride;
         if (b0 >= b_lo && b0 < b_hi) {
-            const SeqInfo si = b0 == b_lo ? lo_si : seq_info(int(b0));
+            const SeqInfo si = b0 == b_lo ? lo_si : seq_info(b0);
             sm_first[0] = b0;
             sm_first[1] = b0 * stride;
             sm_first_start = si.start;
@@ -341,6 +334,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     // nothing), its partial at index part.  first: the job holds the sequence's first block, last: its last.
     auto run_job = [&](const int b, const SeqInfo si, const int64_t part, const int blk_begin, const int blk_end_v,
                        const bool first_job, const bool last_job) {
+    // lane and wave indices through opaque copies, so that nothing derived from them is hoisted out of the
+    // job loop and held across the whole job (the body was written as straight-line code)
+    int lane_o = lane, tid_o = tid, w_o = w;
+    asm volatile("" : "+v"(lane_o), "+v"(tid_o), "+s"(w_o));
+    const int lane = lane_o, tid = tid_o, w = w_o;
+    const int g = lane >> 4, c = lane & 15;
     const int len = si.len;
     const int64_t start = si.start;
     const bool rejected = si.rejected;
@@ -973,8 +972,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     };
 
     // the jobs of this work-group's range, in batch order
-    int b = __builtin_amdgcn_readfirstlane(int(sm_first[0]));
-    int64_t Vb = uniform64(sm_first[1]);
+    int b = __builtin_amdgcn_readfirstlane(sm_first[0]);
+    int Vb = __builtin_amdgcn_readfirstlane(sm_first[1]);
     for (bool first_of_wg = true;; first_of_wg = false) {
         SeqInfo si;
         if (first_of_wg) {
@@ -985,12 +984,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         } else {
             si = seq_info(b);
         }
-        const int64_t vb = stride > 0 ? stride : si.vb;  // the sequence's share of the partition
-        const int64_t lo = max(gs, Vb) - Vb, hi = min(ge, Vb + vb) - Vb;
+        const int vb = stride > 0 ? stride : si.vb;  // the sequence's share of the partition
+        const int lo = max(gs, Vb) - Vb, hi = min(ge, Vb + vb) - Vb;
         const bool first_job = Vb >= gs, last_job = Vb + vb <= ge;
         // the work-group of a sequence's first block records the range of work-groups that hold its pieces
         if (first_job && tid == 0) p.ws_meta[b] = make_int2(wg, int((Vb + vb - 1) / per_wg));
-        run_job(b, si, int64_t(wg) + b, int(lo), int(hi), first_job, last_job);
+        run_job(b, si, int64_t(wg) + b, lo, hi, first_job, last_job);
         Vb += vb;
         if (Vb >= ge || ++b >= p.batch) break;
         __syncthreads();  // the next job reuses this one's LDS
