@@ -4,6 +4,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 #include <mutex>
 
 #include "../../include/tpa.h"
@@ -108,6 +110,13 @@ DecodePlan plan_decode(const Layout &L, int32_t batch, int32_t max_len, int32_t 
 }
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// TPA_LOG set (and not "0"), checked on every call: each decode and prefill call prints its launch plan to
+// stderr before launching.
+bool log_on() {
+    const char *e = getenv("TPA_LOG");
+    return e && e[0] && !(e[0] == '0' && e[1] == 0);
+}
 inline bool aligned16(const void *ptr) { return reinterpret_cast<uintptr_t>(ptr) % 16 == 0; }
 
 float resolve_scale(float scale, int d_h) { return scale > 0.f ? scale : float(1.0 / sqrt(double(d_h))); }
@@ -197,6 +206,14 @@ int32_t run_decode(const tpa_dims *dims, const void *cache, int64_t capacity_tok
     if (step || r_q > 0) p.rope = tpa::make_rope_table(dims->d_h, dims->rope_base);
     p.r_q = r_q;
     p.a_q = a_q;
+    if (log_on())
+        fprintf(stderr,
+                "[tpa] %s: batch %d, max_len %d, heads %d->%d, d_h %d->%d, rank %d%s | %d work-groups, %s, "
+                "merge work-groups of %d threads, workspace %lld B%s\n",
+                step ? "decode step" : (r_q > 0 ? "factored-query decode" : "decode"), batch, max_len, dims->h, L.HP,
+                dims->d_h, L.DP, L.RH, L.f8 ? ", E4M3 cache" : "", P.grid,
+                P.split_blocks > 0 ? "fixed pieces of split_tokens" : "the batch's blocks shared out evenly",
+                tpa::decode_merge_threads(L, p), (long long)P.bytes, use_scratch ? " (static array)" : "");
     const hipError_t e = tpa::launch_decode(L, p, as_stream(stream));
     return e == hipSuccess ? TPA_OK : TPA_ERR_HIP;
 }
@@ -238,6 +255,13 @@ int32_t run_prefill(const tpa_dims *dims, const void *cache, int64_t capacity_to
     p.r_q = r_q;
     p.a_q = a_q;
     if (r_q > 0) p.rope = tpa::make_rope_table(dims->d_h, dims->rope_base);
+    if (log_on()) {
+        const int rows = tpa::prefill_rows_per_group(L, p);
+        fprintf(stderr, "[tpa] %s: batch %d, chunk %d, max_ctx %d, heads %d, d_h %d->%d, rank %d%s | %lld work-groups "
+                        "of %d query rows\n", r_q > 0 ? "factored-query prefill" : "prefill", batch, chunk_len, max_ctx,
+                dims->h, dims->d_h, L.DP, L.RH, L.f8 ? ", E4M3 cache" : "",
+                (long long)((int64_t(chunk_len) + rows - 1) / rows * dims->h * batch), rows);
+    }
     const hipError_t e = tpa::launch_prefill(L, p, as_stream(stream));
     return e == hipSuccess ? TPA_OK : TPA_ERR_HIP;
 }

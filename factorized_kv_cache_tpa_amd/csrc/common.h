@@ -311,7 +311,9 @@ hipError_t launch_read(const Layout &L, int h, int d_h, int RK, int RV, const vo
                        hipStream_t s);
 bool decode_supported(const Layout &L);
 hipError_t launch_decode(const Layout &L, const DecodeParams &p, hipStream_t s);
+int decode_merge_threads(const Layout &L, const DecodeParams &p);  // the merge kernel's work-group size
 bool prefill_supported(const Layout &L);
 hipError_t launch_prefill(const Layout &L, const PrefillParams &p, hipStream_t s);
+int prefill_rows_per_group(const Layout &L, const PrefillParams &p);  // query rows per prefill work-group
 
 }  // namespace tpa

@@ -1131,6 +1131,10 @@ hipError_t launch_split_rank(int RH, const DecodeParams &p, bool f8, hipStream_t
 
 }  // namespace
 
+int decode_merge_threads(const Layout &L, const DecodeParams &p) {
+    return p.merge_parts <= (128 / (L.DP / 4)) * kMergeUnroll ? 128 : 256;
+}
+
 // An E4M3 cache runs the bf16 shapes (its operands are bf16 after decoding).
 bool decode_supported(const Layout &L) {
     const int es = L.f8 ? 2 : L.es;
@@ -1153,7 +1157,7 @@ hipError_t launch_decode(const Layout &L, const DecodeParams &p, hipStream_t s) 
     TPA_DECODE_SHAPES(X)
 #undef X
     if (!found || e != hipSuccess) return e;
-    if (p.merge_parts <= (128 / (L.DP / 4)) * kMergeUnroll)
+    if (decode_merge_threads(L, p) == 128)
         hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(L.HP, p.batch), dim3(128), 0, s, p, L.HP, L.DP,
                            L.tok_per_block());
     else

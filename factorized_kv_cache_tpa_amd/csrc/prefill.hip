@@ -1118,6 +1118,10 @@ bool prefill_supported(const Layout &L) {
     return false;
 }
 
+int prefill_rows_per_group(const Layout &L, const PrefillParams &p) {
+    return L.DP == 128 && !L.f8 && L.RH >= 2 && use_wide(p) ? kQT2 : kQT;
+}
+
 hipError_t launch_prefill(const Layout &L, const PrefillParams &p, hipStream_t s) {
 #define X(HP_, DP_)                                                                   \
     if (L.f8 && L.HP == HP_ && L.DP == DP_) return launch_rank<HP_, DP_, true>(L.RH, p, s); \

@@ -209,3 +209,21 @@ def test_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), eager), f"replay {k}"
+
+
+def test_tpa_log_prints_the_launch_plan(capfd, monkeypatch):
+    """TPA_LOG=1: each call prints its launch plan (grid, partition, merge width, workspace) to stderr; unset
+    (or "0"), nothing."""
+    w = case_workload(32, 128, 4, 4)
+    s = DecodeSetup(w, random_sequences(w, [100, 3000], seed=4))
+    capfd.readouterr()
+    monkeypatch.setenv("TPA_LOG", "0")
+    s.run()
+    assert "[tpa]" not in capfd.readouterr().err
+    monkeypatch.setenv("TPA_LOG", "1")
+    s.run()
+    err = capfd.readouterr().err
+    say(err.strip())
+    assert "[tpa] decode: batch 2, max_len 3000" in err and "work-groups" in err and "workspace" in err
+    s.run(split_tokens=256)
+    assert "fixed pieces of split_tokens" in capfd.readouterr().err

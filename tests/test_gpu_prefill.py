@@ -185,3 +185,16 @@ def test_graph_replay_matches_eager(chunk):
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), eager), f"replay {k}"
+
+
+def test_tpa_log_prints_the_prefill_plan(capfd, monkeypatch):
+    """TPA_LOG=1: a prefill call prints its form (query rows per work-group) and grid."""
+    w = case_workload(32, 128, 4, 4)
+    seqs = random_sequences(w, [40 + 300], n_q=300, seed=2)
+    s = PrefillSetup(w, seqs, [40])
+    capfd.readouterr()
+    monkeypatch.setenv("TPA_LOG", "1")
+    s.run()
+    err = capfd.readouterr().err
+    say(err.strip())
+    assert "[tpa] prefill: batch 1, chunk 300, max_ctx 40" in err and "32 work-groups of 512 query rows" in err
