@@ -245,10 +245,22 @@ def test_workspace_grows_with_splits(lib):
     a = lib.tpa_decode_workspace_bytes(ref, 4, 131072, 4096)
     b = lib.tpa_decode_workspace_bytes(ref, 4, 131072, 1024)
     assert 0 < a < b
-    # per split: 32 heads x (128 outputs + max + sum) fp32, 256-byte aligned regions
-    n_split = 131072 // 1024
-    assert b >= 4 * n_split * 32 * (128 + 2) * 4
+    # one partial per piece: 32 heads x (128 outputs + max + sum) fp32, 256-byte aligned regions, plus a
+    # (first, last) work-group record per sequence
+    n_pieces = 4 * 131072 // 1024
+    assert b >= n_pieces * 32 * (128 + 2) * 4 + 4 * 8
     assert lib.tpa_decode_workspace_bytes(ref, -1, 10, 0) == -1
+
+
+def test_decode_batches_the_partition_cannot_count_are_refused(lib):
+    """The kernel partitions the batch's cache blocks in 32-bit arithmetic: a batch whose blocks could reach
+    2^31 gets -1 from the size query and TPA_ERR_ARG from the call, before any launch."""
+    d = _d(R_K=4, R_V=4)  # 8 tokens per block
+    ref = ctypes.byref(d)
+    assert lib.tpa_decode_workspace_bytes(ref, 1024, 1 << 20, 0) > 0  # a billion tokens: fine
+    assert lib.tpa_decode_workspace_bytes(ref, 65535, (1 << 31) - 1, 0) == -1
+    assert lib.tpa_decode(ref, FAKE, 1 << 40, 65535, FAKE, FAKE, (1 << 31) - 1, FAKE, 0.0, FAKE, 0, FAKE, 1 << 40,
+                          None) == 1
 
 
 def test_prefill_argument_checks(lib):
