@@ -227,3 +227,21 @@ def test_tpa_log_prints_the_launch_plan(capfd, monkeypatch):
     assert "[tpa] decode: batch 2, max_len 3000" in err and "work-groups" in err and "workspace" in err
     s.run(split_tokens=256)
     assert "fixed pieces of split_tokens" in capfd.readouterr().err
+
+
+@pytest.mark.parametrize("lens_kind", ["ragged", "uniform"])
+def test_batches_over_256_sequences(lens_kind):
+    """More sequences than the split kernel has threads (each thread of the partition's scan then covers
+    several): 600 ragged short sequences (empty ones included) or 300 equal ones, every output against the
+    oracle, at the default partition and at a fixed piece size (with more work-groups than sequences at
+    the fixed size, fewer at the default)."""
+    w = case_workload(16, 64, 2, 2)
+    rng = np.random.default_rng(7 if lens_kind == "ragged" else 8)
+    lens = [int(x) for x in rng.integers(0, 60, 600)] if lens_kind == "ragged" else [37] * 300
+    say(f"case: decode over {len(lens)} {lens_kind} sequences")
+    s = DecodeSetup(w, random_sequences(w, lens, seed=len(lens)))
+    ref = np.stack([s.oracle(b) for b in range(s.batch)])
+    chk = Checks()
+    for split in (0, 48):
+        chk.close(s.run(split_tokens=split), ref, w.dtype, f"split_tokens={split}")
+    chk.done()

@@ -236,3 +236,18 @@ def test_step_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i}"
         del junk
+
+
+def test_step_over_more_than_256_sequences():
+    """A fused step over 400 short ragged sequences (empty ones included): every output and every written
+    record against the oracle and the append."""
+    w = case_workload(32, 128, 1, 1, ti.BF16, 1e4)
+    lens = [int(x) for x in np.random.default_rng(11).integers(0, 40, 400)]
+    say(f"case: step over {len(lens)} sequences")
+    st = StepSetup(w, lens, seed=400)
+    got = st.run().cpu().numpy()
+    chk = Checks()
+    for b in range(st.batch):
+        chk.close(got[b], st.oracle(b), w.dtype, f"seq {b} (N={lens[b]})")
+    chk.done()
+    check_record_is_what_append_writes(st, lens)
