@@ -11,10 +11,10 @@
 #include "../../include/tpa.h"
 #include "common.h"
 
-// tpa_decode_noalloc keeps the per-split partials (the workspace of tpa_decode) in this array instead of
-// a caller's buffer.  Each GPU the library runs on holds its own copy until the process ends; in host code
-// the name is only a stand-in, so its device address is looked up per device (scratch_address below) and
-// only that address is ever passed on.
+// tpa_decode_noalloc keeps the pieces' partials and range records (the workspace of tpa_decode) in this
+// array instead of a caller's buffer.  Each GPU the library runs on holds its own copy until the process
+// ends; in host code the name is only a stand-in, so its device address is looked up per device
+// (scratch_address below) and only that address is ever passed on.
 constexpr int64_t kScratchBytes = TPA_DECODE_NOALLOC_MAX_BYTES;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 

@@ -34,7 +34,7 @@ def test_tiny_fp32_workload():
     (24, 32, 2, 1, ti.F32), (12, 128, 1, 1, ti.F32), (30, 64, 2, 2, ti.F32)])
 @pytest.mark.parametrize("q_scale", [1.0, 12.0])
 def test_small_shapes_ragged(h, d_h, R_K, R_V, dtype, q_scale, request):
-    """Several blocks per split and a ragged tail; q_scale 12 sharpens the softmax."""
+    """Several blocks per work-group and a ragged tail; q_scale 12 sharpens the softmax."""
     w = case_workload(h, d_h, R_K, R_V, dtype)
     lens = [1, 7, 33, 100, 257, 600]
     known = SHARP_RANK1.get((h, d_h, R_K, R_V, dtype, q_scale))

@@ -1,5 +1,5 @@
-"""tpa_decode_noalloc, the decode whose per-split partials live in the library's static device array,
-against tpa_decode with a caller workspace: the same kernels and the same split plan, so the outputs agree bit
+"""tpa_decode_noalloc, the decode whose partials live in the library's static device array,
+against tpa_decode with a caller workspace: the same kernels and the same work plan, so the outputs agree bit
 for bit, and both meet the oracle bound.  Two calls in a row, the second with a smaller input (fewer and
 shorter sequences, another shape), so the second runs over the array the first left filled."""
 import numpy as np
