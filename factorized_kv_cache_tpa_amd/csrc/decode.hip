@@ -334,641 +334,645 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     // nothing), its partial at index part.  first: the job holds the sequence's first block, last: its last.
     auto run_job = [&](const int b, const SeqInfo si, const int64_t part, const int blk_begin, const int blk_end_v,
                        const bool first_job, const bool last_job) {
-    // lane and wave indices through opaque copies, so that nothing derived from them is hoisted out of the
-    // job loop and held across the whole job (the body was written as straight-line code)
-    int lane_o = lane, tid_o = tid, w_o = w;
-    asm volatile("" : "+v"(lane_o), "+v"(tid_o), "+s"(w_o));
-    const int lane = lane_o, tid = tid_o, w = w_o;
-    const int g = lane >> 4, c = lane & 15;
-    const int len = si.len;
-    const int64_t start = si.start;
-    const bool rejected = si.rejected;
-    const int nblk = (len + TOK - 1) / TOK;
-    // A fused step's first job carries the step's new token (even over an empty sequence): it folds the
-    // token's own score and value into its partial ...
-    const bool new_tok = kStep && first_job && !rejected;
-    // ... and its last job writes the token's record (for a long sequence the two land on different
-    // work-groups)
-    const bool rec_tok = kStep && last_job && !rejected;
-    if (rejected || (blk_begin >= nblk && !new_tok)) {
-        // A job with no tokens (an empty or rejected sequence) marks its partial empty (max -inf, sum 0);
-        // the merge writes zeros (empty) or NaN (rejected).
-        for (int head = threadIdx.x; head < HP; head += kThreads)
-            *reinterpret_cast<float2 *>(p.ws_ml + (part * HP + head) * 2) = make_float2(-INFINITY, 0.f);
-        return;
-    }
-    const int blk_end = min(nblk, blk_end_v);
-    const int full_end = min(blk_end, len / TOK);  // blocks [blk_begin, full_end) hold TOK valid tokens
-    constexpr int CES = kF8 ? 1 : int(sizeof(T));  // bytes per stored element
-    const char *seq = reinterpret_cast<const char *>(p.cache) + (start / TOK) * BLK * CES;
+        // lane and wave indices through opaque copies, so that nothing derived from them is hoisted out of the
+        // job loop and held across the whole job (the body was written as straight-line code)
+        int lane_o = lane, tid_o = tid, w_o = w;
+        asm volatile("" : "+v"(lane_o), "+v"(tid_o), "+s"(w_o));
+        const int lane = lane_o, tid = tid_o, w = w_o;
+        const int g = lane >> 4, c = lane & 15;
+        const int len = si.len;
+        const int64_t start = si.start;
+        const bool rejected = si.rejected;
+        const int nblk = (len + TOK - 1) / TOK;
+        // A fused step's first job carries the step's new token (even over an empty sequence): it folds the
+        // token's own score and value into its partial ...
+        const bool new_tok = kStep && first_job && !rejected;
+        // ... and its last job writes the token's record (for a long sequence the two land on different
+        // work-groups)
+        const bool rec_tok = kStep && last_job && !rejected;
+        if (rejected || (blk_begin >= nblk && !new_tok)) {
+            // A job with no tokens (an empty or rejected sequence) marks its partial empty (max -inf, sum 0);
+            // the merge writes zeros (empty) or NaN (rejected).
+            for (int head = threadIdx.x; head < HP; head += kThreads)
+                *reinterpret_cast<float2 *>(p.ws_ml + (part * HP + head) * 2) = make_float2(-INFINITY, 0.f);
+            return;
+        }
+        const int blk_end = min(nblk, blk_end_v);
+        const int full_end = min(blk_end, len / TOK);  // blocks [blk_begin, full_end) hold TOK valid tokens
+        constexpr int CES = kF8 ? 1 : int(sizeof(T));  // bytes per stored element
+        const char *seq = reinterpret_cast<const char *>(p.cache) + (start / TOK) * BLK * CES;
 
-    // One block's operands, loaded straight from the cache in MFMA lane order: a scalar block base
-    // plus one per-lane offset, so every load is one instruction with an immediate region offset.
-    struct StageNative {
-        GateRaw ak[2][NB], av[2][NB];
-        Frag bk[2][KBS], bv[MBV][KBV];
-    };
-    // E4M3: a lane's 16 bytes hold its codes for both row blocks of a k-block (B~_K) or for value blocks
-    // 2j and 2j+1 (B_V); its 8 gate bytes hold both row blocks of a head block.  Decoded at use.
-    struct StageF8 {
-        u32x2 ak[NB], av[NB];
-        u32x4 bk[KBS], bv[MBV / 2];
-    };
-    using Stage = std::conditional_t<kF8, StageF8, StageNative>;
-    const uint32_t off_op = uint32_t(lane * E * sizeof(T));  // operand lane offset, bytes (native)
-    const uint32_t off_gt = uint32_t(lane * 4 * sizeof(T));  // gate lane offset, bytes (native)
-    auto load = [&](Stage &st, int blk, bool real = true) {
-        const char *bp = real ? seq + int64_t(blk) * BLK * CES : reinterpret_cast<const char *>(p.cache);
-        if constexpr (kF8) {
-            const char *op = bp + lane * 16;
-            const char *gt = bp + lane * 8;
+        // One block's operands, loaded straight from the cache in MFMA lane order: a scalar block base
+        // plus one per-lane offset, so every load is one instruction with an immediate region offset.
+        struct StageNative {
+            GateRaw ak[2][NB], av[2][NB];
+            Frag bk[2][KBS], bv[MBV][KBV];
+        };
+        // E4M3: a lane's 16 bytes hold its codes for both row blocks of a k-block (B~_K) or for value blocks
+        // 2j and 2j+1 (B_V); its 8 gate bytes hold both row blocks of a head block.  Decoded at use.
+        struct StageF8 {
+            u32x2 ak[NB], av[NB];
+            u32x4 bk[KBS], bv[MBV / 2];
+        };
+        using Stage = std::conditional_t<kF8, StageF8, StageNative>;
+        const uint32_t off_op = uint32_t(lane * E * sizeof(T));  // operand lane offset, bytes (native)
+        const uint32_t off_gt = uint32_t(lane * 4 * sizeof(T));  // gate lane offset, bytes (native)
+        auto load = [&](Stage &st, int blk, bool real = true) {
+            const char *bp = real ? seq + int64_t(blk) * BLK * CES : reinterpret_cast<const char *>(p.cache);
+            if constexpr (kF8) {
+                const char *op = bp + lane * 16;
+                const char *gt = bp + lane * 8;
 #pragma unroll
-            for (int kb = 0; kb < KBS; ++kb) st.bk[kb] = stream_load16(op + OFF_BK + kb * kWave * 16);
+                for (int kb = 0; kb < KBS; ++kb) st.bk[kb] = stream_load16(op + OFF_BK + kb * kWave * 16);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                st.ak[nb] = stream_load8(gt + nb * kWave * 8);
-                st.av[nb] = stream_load8(gt + OFF_AV + nb * kWave * 8);
+                for (int nb = 0; nb < NB; ++nb) {
+                    st.ak[nb] = stream_load8(gt + nb * kWave * 8);
+                    st.av[nb] = stream_load8(gt + OFF_AV + nb * kWave * 8);
+                }
+#pragma unroll
+                for (int j = 0; j < MBV / 2; ++j) st.bv[j] = stream_load16(op + OFF_BV + j * kWave * 16);
+            } else {
+                const T *op = reinterpret_cast<const T *>(bp + off_op);
+                const T *gt = reinterpret_cast<const T *>(bp + off_gt);
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int kb = 0; kb < KBS; ++kb)
+                        st.bk[mb][kb] = M::stream(op + OFF_BK + (mb * KBS + kb) * kWave * E);
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        st.ak[mb][nb] = M::load_gates(gt + (mb * NB + nb) * kWave * 4);
+                        st.av[mb][nb] = M::load_gates(gt + OFF_AV + (mb * NB + nb) * kWave * 4);
+                    }
+#pragma unroll
+                for (int mv = 0; mv < MBV; ++mv)
+#pragma unroll
+                    for (int q = 0; q < KBV; ++q) st.bv[mv][q] = M::stream(op + OFF_BV + (mv * KBV + q) * kWave * E);
+            }
+        };
+        // The operands of a loaded stage: B~_K fragment (row block mb, k-block kb), the 4 gates of row block
+        // mb and head block nb, and the B_V fragment of value block mv (k-block q).
+        auto frag_bk = [&](const Stage &st, int mb, int kb) -> Frag {
+            if constexpr (kF8) {
+                const u32x4 r = st.bk[kb];
+                return __builtin_bit_cast(Frag, mb ? e4m3x8_to_bf16x8(r.z, r.w) : e4m3x8_to_bf16x8(r.x, r.y));
+            } else {
+                return st.bk[mb][kb];
+            }
+        };
+        auto gates = [&](const Stage &st, bool value, int mb, int nb, float *gv) {
+            if constexpr (kF8) {
+                const u32x2 r = value ? st.av[nb] : st.ak[nb];
+                e4m3x4_to_f32(mb ? r.y : r.x, gv);
+            } else {
+                M::unpack_gates(value ? st.av[mb][nb] : st.ak[mb][nb], gv);
+            }
+        };
+        auto frag_bv = [&](const Stage &st, int mv, int q) -> Frag {
+            if constexpr (kF8) {
+                const u32x4 r = st.bv[mv >> 1];
+                return __builtin_bit_cast(Frag, (mv & 1) ? e4m3x8_to_bf16x8(r.z, r.w) : e4m3x8_to_bf16x8(r.x, r.y));
+            } else {
+                return st.bv[mv][q];
+            }
+        };
+
+        // Fused step, first job: this thread's item of the new token (one head-factor pair (A_K, A_V) of row
+        // r, head i, and one feature pair (d, d+1) of B_K and B_V of row r), loaded before everything else:
+        // memory returns in order, so these must not queue behind the factor stream.
+        const int na_r = tid / HP, na_i = tid % HP, nb_r = tid / (DP / 2), nb_d = 2 * (tid % (DP / 2));
+        T nak = T(0), nav = T(0), nbk0 = T(0), nbk1 = T(0), nbv0 = T(0), nbv1 = T(0);
+        if (kStep && (new_tok || rec_tok)) {
+            const T *AK = reinterpret_cast<const T *>(p.st.A_K) + int64_t(b) * p.RK * p.h;
+            const T *AV = reinterpret_cast<const T *>(p.st.A_V) + int64_t(b) * p.RV * p.h;
+            const T *BK = reinterpret_cast<const T *>(p.st.B_K) + int64_t(b) * p.RK * p.d_h;
+            const T *BV = reinterpret_cast<const T *>(p.st.B_V) + int64_t(b) * p.RV * p.d_h;
+            if (na_r < p.RK && na_i < p.h) nak = AK[na_r * p.h + na_i];
+            if (na_r < p.RV && na_i < p.h) nav = AV[na_r * p.h + na_i];
+            if (nb_r < p.RK && nb_d < p.d_h) {
+                nbk0 = BK[nb_r * p.d_h + nb_d];
+                nbk1 = BK[nb_r * p.d_h + nb_d + 1];
+            }
+            if (nb_r < p.RV && nb_d < p.d_h) {
+                nbv0 = BV[nb_r * p.d_h + nb_d];
+                nbv1 = BV[nb_r * p.d_h + nb_d + 1];
+            }
+        }
+        for (int head = tid; head < HP; head += kThreads) {
+            sm_m[kWaves][head] = -INFINITY;
+            sm_l[kWaves][head] = 0.f;
+        }
+        // fused step, factored query: this thread's RoPE frequency (pair j = tid), read now for the same reason
+        const double theta_j = (kStep || kFact) && tid < DP / 2 ? p.rope.theta[tid] : 0.0;
+
+        // Factored query: this thread's share of A_Q (row-major [R_Q][h]) and B_Q ([R_Q][d_h], unrotated),
+        // loaded before the stream for the same reason; elements past the real sizes are zeros.
+        constexpr int QA_PER = kFact ? (kMaxRQ * HP + kThreads - 1) / kThreads : 1;
+        constexpr int QB_PER = kFact ? (kMaxRQ * DP + kThreads - 1) / kThreads : 1;
+        float qa_raw[QA_PER], qb_raw[QB_PER];
+        if constexpr (kFact) {
+            const T *AQ = reinterpret_cast<const T *>(p.a_q) + int64_t(b) * p.r_q * p.h;
+            const T *BQ = reinterpret_cast<const T *>(p.q) + int64_t(b) * p.r_q * p.d_h;
+#pragma unroll
+            for (int k = 0; k < QA_PER; ++k) {
+                const int idx = tid + k * kThreads, r = idx / HP, i = idx % HP;
+                qa_raw[k] = r < p.r_q && i < p.h ? Elem<T>::to_f32(AQ[r * p.h + i]) : 0.f;
             }
 #pragma unroll
-            for (int j = 0; j < MBV / 2; ++j) st.bv[j] = stream_load16(op + OFF_BV + j * kWave * 16);
-        } else {
-            const T *op = reinterpret_cast<const T *>(bp + off_op);
-            const T *gt = reinterpret_cast<const T *>(bp + off_gt);
+            for (int k = 0; k < QB_PER; ++k) {
+                const int idx = tid + k * kThreads, r = idx / DP, d = idx % DP;
+                qb_raw[k] = r < p.r_q && d < p.d_h ? Elem<T>::to_f32(BQ[r * p.d_h + d]) : 0.f;
+            }
+        }
+
+        // query operand (B of the score contraction; loaded first: memory returns in order, so the first
+        // block can start as soon as its own loads land): lane holds q~[16 nb + c][4E kb + E g + e]
+        Frag qf[KBS][NB];
+        if constexpr (!kFact) {
+            const T *qb = reinterpret_cast<const T *>(p.q) + int64_t(b) * p.h * p.d_h;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int kb = 0; kb < KBS; ++kb)
 #pragma unroll
-                for (int kb = 0; kb < KBS; ++kb) st.bk[mb][kb] = M::stream(op + OFF_BK + (mb * KBS + kb) * kWave * E);
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int head = 16 * nb + c;
+                    const int d0 = 4 * E * kb + E * g;
+                    qf[kb][nb] = M::load_q(qb, head, d0, p.h, p.d_h);
+                }
+        }
+        // Two register stages (the next block's loads in flight while one is consumed) wherever they
+        // fit in the register file; wide fp32 operands use one stage.
+        constexpr bool kTwoStages = sizeof(T) == 2 || HP * DP <= 1024;
+        Stage s0, s1;
+        int blk = blk_begin + w;
+        // The two stages are loaded unconditionally, clamped to the job's last block (which every wave
+        // may read): a wave with a single block reads one block twice, but the loads then sit in fixed
+        // program order, so the compiler can wait for each stage exactly instead of draining every load in
+        // flight at the top of the pipelined loop below.
+        // (Outside a fused step every work-group that gets here has a block.  A fused step's first job of an
+        // empty sequence has none: its stages read the cache's first block instead and never use it, so that
+        // no load sits behind a branch, which would leave every wait of the mode conservative.)
+        const int last_blk = blk_end - 1;
+        const bool any_blk = !kStep || blk_end > blk_begin;
+        auto load_clamped = [&](Stage &st, int b) { load(st, b < last_blk ? b : last_blk, any_blk); };
+        if (kTwoStages) {  // start streaming the first two blocks before anything else (a fused step issues
+                           // the second after its own set-up: a wave cannot pass its loads' issue until most of
+                           // them have landed, so work placed behind both stages would wait for the stream)
+            load_clamped(s0, blk);
+            if (kMode == kQRot) load_clamped(s1, blk + kWaves);
+        }
+        if constexpr (kFact) {
+            // Factored query, while the first blocks stream in: q[i][d] = (1/R_Q) sum_r A_Q[r][i] B_Q[r][d]
+            // (TPA notes page, tensor product decomposition applied to Q), computed once per work-group in
+            // 4 x 4 register tiles from LDS, then rotated to the query's position len (RoPE is linear, so
+            // rotating the combined row equals combining rotated B_Q rows: RoPE compatibility), all in fp32
+            // (fp64 for fp32 queries), rounded once to the element type, and read back as this lane's
+            // fragments.
+            if (tid < DP / 2) rope_cos_sin<T>(sm_cs + 2 * tid, double(len), theta_j);
+#pragma unroll
+            for (int k = 0; k < QA_PER; ++k) {
+                const int idx = tid + k * kThreads;
+                if (idx < kMaxRQ * HP) sm_aq[idx / HP][idx % HP] = qa_raw[k];
+            }
+#pragma unroll
+            for (int k = 0; k < QB_PER; ++k) {
+                const int idx = tid + k * kThreads;
+                if (idx < kMaxRQ * DP) sm_bq[idx / DP][idx % DP] = qb_raw[k];
+            }
+            __syncthreads();
+            const float inv_rq = 1.f / float(p.r_q);
+            for (int t = tid; t < (HP / 4) * (DP / 4); t += kThreads) {
+                const int h0 = 4 * (t / (DP / 4)), d0 = 4 * (t % (DP / 4));
+                float a4[4][4] = {};
+                for (int r = 0; r < p.r_q; ++r) {
+                    const float4 av = *reinterpret_cast<const float4 *>(&sm_aq[r][h0]);
+                    const float4 bv = *reinterpret_cast<const float4 *>(&sm_bq[r][d0]);
+                    const float ar[4] = {av.x, av.y, av.z, av.w}, br[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) a4[i][j] = fmaf(ar[i], br[j], a4[i][j]);
+                }
+                // features d0 .. d0 + 3 are the rotary pairs d0 / 2 and d0 / 2 + 1
+                const F c0 = sm_cs[d0], s0 = sm_cs[d0 + 1], c1 = sm_cs[d0 + 2], s1 = sm_cs[d0 + 3];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    F y[4];
+                    rope_rotate(F(a4[i][0]), F(a4[i][1]), c0, s0, y[0], y[1]);
+                    rope_rotate(F(a4[i][2]), F(a4[i][3]), c1, s1, y[2], y[3]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float x = float(y[j] * F(inv_rq));
+                        if constexpr (sizeof(T) == 2)
+                            sm_q[h0 + i][d0 + j] = uint16_t(pack_bf16x2(x, 0.f) & 0xffffu);
+                        else
+                            sm_q[h0 + i][d0 + j] = x;
+                    }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int kb = 0; kb < KBS; ++kb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) qf[kb][nb] = M::load(&sm_q[16 * nb + c][4 * E * kb + E * g]);
+            if (kTwoStages) load_clamped(s1, blk + kWaves);
+        }
+        if constexpr (kStep) {
+            // Fused step, while the first blocks stream in.  q arrives unrotated and sits at position len (the
+            // number of cached tokens).  The first job stages the new token's factors in LDS and, after the one
+            // barrier the angle table needs anyway, takes the token's score per head from the still unrotated
+            // query fragments and the unrotated B_K: query and token share a position, so RoPE drops out of that
+            // score (RoPE compatibility, Theorem 3.1 with t = s).  Then every wave rotates its query fragments
+            // (the table covers every padded pair; theta is zero past d_h / 2: an identity rotation of zeros),
+            // and the sequence's last job writes the token's record at slot len: no work-group of this kernel
+            // reads that slot's rows (a partly filled last block masks every row at or past len), and the next
+            // call sees it.
+            // Over an E4M3 cache the token enters as its stored values, exactly as tpa_cache_append and then a
+            // decode would see it: every factor is rounded to its code and decoded back, B_K after its rotation,
+            // which no longer cancels in the score; so the first job stages the rotated, decoded B~_K after the
+            // table and takes the score from the rotated query fragments behind a second barrier.
+            auto token_score = [&]() {
+                // the token's score per head: a lane sums its d-values, the four lane groups of a head are
+                // summed across (the same contraction as the cached tokens'); head block nb is taken by wave
+                // nb % kWaves, so the waves share the work
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    if (nb % kWaves != w) continue;  // wave-uniform; static register indexing
+                    float dot[RH];
+#pragma unroll
+                    for (int r = 0; r < RH; ++r) {
+                        float x = 0.f;
+#pragma unroll
+                        for (int kb = 0; kb < KBS; ++kb) {
+                            float bk[E];
+                            if constexpr (E == 8) {
+                                const float4 lo = *reinterpret_cast<const float4 *>(&sm_nb[0][r][4 * E * kb + E * g]);
+                                const float4 hi =
+                                    *reinterpret_cast<const float4 *>(&sm_nb[0][r][4 * E * kb + E * g + 4]);
+                                bk[0] = lo.x; bk[1] = lo.y; bk[2] = lo.z; bk[3] = lo.w;
+                                bk[4] = hi.x; bk[5] = hi.y; bk[6] = hi.z; bk[7] = hi.w;
+                            } else {
+                                bk[0] = sm_nb[0][r][4 * E * kb + E * g];
+                            }
+#pragma unroll
+                            for (int e = 0; e < E; ++e) x = fmaf(M::value(qf[kb][nb], e), bk[e], x);
+                        }
+                        dot[r] = wave_sum_across_groups(x);
+                    }
+                    if (g == 0) {
+                        const int head = 16 * nb + c;
+                        float z = 0.f;
+#pragma unroll
+                        for (int r = 0; r < RH; ++r) z = fmaf(sm_na[0][r][head], dot[r], z);
+                        sm_m[kWaves][head] = head < p.h ? z * p.score_mul : -INFINITY;
+                        sm_l[kWaves][head] = head < p.h ? 1.f : 0.f;
+                    }
+                }
+            };
+            // E4M3 codes of the token's items (A_K, A_V of this thread's head-factor item; B_V of its pair)
+            uint32_t ak8 = 0, av8 = 0, bv8 = 0;
+            if constexpr (kF8) {
+                ak8 = e4m3_one(Elem<T>::to_f32(nak) * p.st.inv_scale[0]);
+                av8 = e4m3_one(Elem<T>::to_f32(nav) * p.st.inv_scale[2]);
+                bv8 = e4m3_pair(Elem<T>::to_f32(nbv0) * p.st.inv_scale[3], Elem<T>::to_f32(nbv1) * p.st.inv_scale[3]);
+            }
+            if (new_tok) {
+                if (na_r < RH) {
+                    if constexpr (kF8) {
+                        sm_na[0][na_r][na_i] = __builtin_amdgcn_cvt_f32_fp8(int(ak8), 0);
+                        sm_na[1][na_r][na_i] = __builtin_amdgcn_cvt_f32_fp8(int(av8), 0);
+                    } else {
+                        sm_na[0][na_r][na_i] = Elem<T>::to_f32(nak);
+                        sm_na[1][na_r][na_i] = Elem<T>::to_f32(nav);
+                    }
+                }
+                if (nb_r < RH) {
+                    if constexpr (kF8) {
+                        const floatx2 v = __builtin_amdgcn_cvt_pk_f32_fp8(int(bv8), false);
+                        sm_nb[1][nb_r][nb_d] = v.x;
+                        sm_nb[1][nb_r][nb_d + 1] = v.y;
+                    } else {
+                        sm_nb[0][nb_r][nb_d] = Elem<T>::to_f32(nbk0);
+                        sm_nb[0][nb_r][nb_d + 1] = Elem<T>::to_f32(nbk1);
+                        sm_nb[1][nb_r][nb_d] = Elem<T>::to_f32(nbv0);
+                        sm_nb[1][nb_r][nb_d + 1] = Elem<T>::to_f32(nbv1);
+                    }
+                }
+            }
+            if (tid < DP / 2) rope_cos_sin<T>(sm_cs + 2 * tid, double(len), theta_j);
+            __syncthreads();
+            if constexpr (!kF8)
+                if (new_tok) token_score();
+#pragma unroll
+            for (int kb = 0; kb < KBS; ++kb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) qf[kb][nb] = M::rotate_q(qf[kb][nb], 4 * E * kb + E * g, sm_cs);
+            const int64_t slot = start + len;
+            // the token's B~_K pair, rotated as tpa_cache_append rotates it
+            F y0 = F(0), y1 = F(0);
+            if ((kF8 ? (new_tok || rec_tok) : rec_tok) && nb_r < p.RK && nb_d < p.d_h)
+                rope_rotate(F(Elem<T>::to_f32(nbk0)), F(Elem<T>::to_f32(nbk1)), sm_cs[nb_d], sm_cs[nb_d + 1], y0, y1);
+            uint32_t bk8 = 0;
+            if constexpr (kF8) {
+                bk8 = e4m3_pair(float(y0) * p.st.inv_scale[1], float(y1) * p.st.inv_scale[1]);
+                if (new_tok) {
+                    if (nb_r < RH) {
+                        const floatx2 v = __builtin_amdgcn_cvt_pk_f32_fp8(int(bk8), false);
+                        sm_nb[0][nb_r][nb_d] = v.x;
+                        sm_nb[0][nb_r][nb_d + 1] = v.y;
+                    }
+                    __syncthreads();  // first job only (uniform over the work-group)
+                    token_score();
+                }
+            }
+            if (rec_tok && slot < p.st.capacity) {
+                const int row0 = int(slot % TOK) * RH;
+                if constexpr (kF8) {
+                    // the E4M3 record: the same codes tpa_cache_append writes, in the paired 8-bit layout
+                    uint8_t *rec = reinterpret_cast<uint8_t *>(p.st.cache) + (slot / TOK) * BLK;
+                    const Layout Lay = make_layout(p.h, p.d_h, p.RK, p.RV, Elem<T>::dtype, 1);
+                    if (na_r < RH) {
+                        rec[Lay.gate(row0 + na_r, na_i)] = uint8_t(ak8);
+                        rec[OFF_AV + Lay.gate(row0 + na_r, na_i)] = uint8_t(av8);
+                    }
+                    if (nb_r < RH) {
+                        *reinterpret_cast<uint16_t *>(rec + OFF_BK + Lay.bk(row0 + nb_r, nb_d)) = uint16_t(bk8);
+                        rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d)] = uint8_t(bv8 & 0xffu);
+                        rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d + 1)] = uint8_t(bv8 >> 8);
+                    }
+                } else {
+                    // the record, B_K rotated and rounded exactly as tpa_cache_append stores it
+                    T k0 = nbk0, k1 = nbk1;
+                    if (nb_r < p.RK && nb_d < p.d_h) {
+                        if constexpr (sizeof(T) == 2) {
+                            const uint32_t pk = pack_bf16x2(y0, y1);
+                            k0 = T(pk & 0xffffu);
+                            k1 = T(pk >> 16);
+                        } else {
+                            k0 = T(y0);
+                            k1 = T(y1);
+                        }
+                    }
+                    T *rec = reinterpret_cast<T *>(p.st.cache) + (slot / TOK) * BLK;
+                    const Layout Lay = make_layout(p.h, p.d_h, p.RK, p.RV, Elem<T>::dtype);
+                    if (na_r < RH) {
+                        rec[Lay.gate(row0 + na_r, na_i)] = nak;
+                        rec[OFF_AV + Lay.gate(row0 + na_r, na_i)] = nav;
+                    }
+                    if (nb_r < RH) {
+                        rec[OFF_BK + Lay.bk(row0 + nb_r, nb_d)] = k0;
+                        rec[OFF_BK + Lay.bk(row0 + nb_r, nb_d + 1)] = k1;
+                        rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d)] = nbv0;
+                        rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d + 1)] = nbv1;
+                    }
+                }
+            }
+            if (kTwoStages) load_clamped(s1, blk + kWaves);
+        }
+
+
+        floatx4 acc[MBV][NB];
+#pragma unroll
+        for (int mv = 0; mv < MBV; ++mv)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[mv][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        // Scores are kept in raw units z = sum_r A_K U (the scale is applied inside the exponent);
+        // run_m is the lazy reference max in raw units, neg_ms = -run_m * score_mul.
+        float run_m[NB], neg_ms[NB], run_l[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            run_m[nb] = -INFINITY;
+            neg_ms[nb] = INFINITY;
+            run_l[nb] = 0.f;
+        }
+        const float sm = p.score_mul;
+        const float lazy_raw = kLazy / sm;
+
+        // Process one block.  kTail: the block may hold rows beyond the sequence (valid < TOK tokens);
+        // only the last block of a sequence can, and it takes this slower masked path.
+        auto process = [&](Stage &st, auto tail_tag, int valid) {
+            constexpr bool kTail = decltype(tail_tag)::value;
+            // ---- 1. score contraction
+            floatx4 u[2][NB];
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    st.ak[mb][nb] = M::load_gates(gt + (mb * NB + nb) * kWave * 4);
-                    st.av[mb][nb] = M::load_gates(gt + OFF_AV + (mb * NB + nb) * kWave * 4);
+                    floatx4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < KBS; ++kb) a = M::mma(frag_bk(st, mb, kb), qf[kb][nb], a);
+                    u[mb][nb] = a;
                 }
-#pragma unroll
-            for (int mv = 0; mv < MBV; ++mv)
-#pragma unroll
-                for (int q = 0; q < KBV; ++q) st.bv[mv][q] = M::stream(op + OFF_BV + (mv * KBV + q) * kWave * E);
-        }
-    };
-    // The operands of a loaded stage: B~_K fragment (row block mb, k-block kb), the 4 gates of row block
-    // mb and head block nb, and the B_V fragment of value block mv (k-block q).
-    auto frag_bk = [&](const Stage &st, int mb, int kb) -> Frag {
-        if constexpr (kF8) {
-            const u32x4 r = st.bk[kb];
-            return __builtin_bit_cast(Frag, mb ? e4m3x8_to_bf16x8(r.z, r.w) : e4m3x8_to_bf16x8(r.x, r.y));
-        } else {
-            return st.bk[mb][kb];
-        }
-    };
-    auto gates = [&](const Stage &st, bool value, int mb, int nb, float *gv) {
-        if constexpr (kF8) {
-            const u32x2 r = value ? st.av[nb] : st.ak[nb];
-            e4m3x4_to_f32(mb ? r.y : r.x, gv);
-        } else {
-            M::unpack_gates(value ? st.av[mb][nb] : st.ak[mb][nb], gv);
-        }
-    };
-    auto frag_bv = [&](const Stage &st, int mv, int q) -> Frag {
-        if constexpr (kF8) {
-            const u32x4 r = st.bv[mv >> 1];
-            return __builtin_bit_cast(Frag, (mv & 1) ? e4m3x8_to_bf16x8(r.z, r.w) : e4m3x8_to_bf16x8(r.x, r.y));
-        } else {
-            return st.bv[mv][q];
-        }
-    };
 
-    // Fused step, first job: this thread's item of the new token (one head-factor pair (A_K, A_V) of row
-    // r, head i, and one feature pair (d, d+1) of B_K and B_V of row r), loaded before everything else:
-    // memory returns in order, so these must not queue behind the factor stream.
-    const int na_r = tid / HP, na_i = tid % HP, nb_r = tid / (DP / 2), nb_d = 2 * (tid % (DP / 2));
-    T nak = T(0), nav = T(0), nbk0 = T(0), nbk1 = T(0), nbv0 = T(0), nbv1 = T(0);
-    if (kStep && (new_tok || rec_tok)) {
-        const T *AK = reinterpret_cast<const T *>(p.st.A_K) + int64_t(b) * p.RK * p.h;
-        const T *AV = reinterpret_cast<const T *>(p.st.A_V) + int64_t(b) * p.RV * p.h;
-        const T *BK = reinterpret_cast<const T *>(p.st.B_K) + int64_t(b) * p.RK * p.d_h;
-        const T *BV = reinterpret_cast<const T *>(p.st.B_V) + int64_t(b) * p.RV * p.d_h;
-        if (na_r < p.RK && na_i < p.h) nak = AK[na_r * p.h + na_i];
-        if (na_r < p.RV && na_i < p.h) nav = AV[na_r * p.h + na_i];
-        if (nb_r < p.RK && nb_d < p.d_h) {
-            nbk0 = BK[nb_r * p.d_h + nb_d];
-            nbk1 = BK[nb_r * p.d_h + nb_d + 1];
-        }
-        if (nb_r < p.RV && nb_d < p.d_h) {
-            nbv0 = BV[nb_r * p.d_h + nb_d];
-            nbv1 = BV[nb_r * p.d_h + nb_d + 1];
-        }
-    }
-    for (int head = tid; head < HP; head += kThreads) {
-        sm_m[kWaves][head] = -INFINITY;
-        sm_l[kWaves][head] = 0.f;
-    }
-    // fused step, factored query: this thread's RoPE frequency (pair j = tid), read now for the same reason
-    const double theta_j = (kStep || kFact) && tid < DP / 2 ? p.rope.theta[tid] : 0.0;
-
-    // Factored query: this thread's share of A_Q (row-major [R_Q][h]) and B_Q ([R_Q][d_h], unrotated),
-    // loaded before the stream for the same reason; elements past the real sizes are zeros.
-    constexpr int QA_PER = kFact ? (kMaxRQ * HP + kThreads - 1) / kThreads : 1;
-    constexpr int QB_PER = kFact ? (kMaxRQ * DP + kThreads - 1) / kThreads : 1;
-    float qa_raw[QA_PER], qb_raw[QB_PER];
-    if constexpr (kFact) {
-        const T *AQ = reinterpret_cast<const T *>(p.a_q) + int64_t(b) * p.r_q * p.h;
-        const T *BQ = reinterpret_cast<const T *>(p.q) + int64_t(b) * p.r_q * p.d_h;
-#pragma unroll
-        for (int k = 0; k < QA_PER; ++k) {
-            const int idx = tid + k * kThreads, r = idx / HP, i = idx % HP;
-            qa_raw[k] = r < p.r_q && i < p.h ? Elem<T>::to_f32(AQ[r * p.h + i]) : 0.f;
-        }
-#pragma unroll
-        for (int k = 0; k < QB_PER; ++k) {
-            const int idx = tid + k * kThreads, r = idx / DP, d = idx % DP;
-            qb_raw[k] = r < p.r_q && d < p.d_h ? Elem<T>::to_f32(BQ[r * p.d_h + d]) : 0.f;
-        }
-    }
-
-    // query operand (B of the score contraction; loaded first: memory returns in order, so the first
-    // block can start as soon as its own loads land): lane holds q~[16 nb + c][4E kb + E g + e]
-    Frag qf[KBS][NB];
-    if constexpr (!kFact) {
-        const T *qb = reinterpret_cast<const T *>(p.q) + int64_t(b) * p.h * p.d_h;
-#pragma unroll
-        for (int kb = 0; kb < KBS; ++kb)
+            // ---- 2.-4. gates, online softmax, value weights
+            float wv[2][NB][4];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const int head = 16 * nb + c;
-                const int d0 = 4 * E * kb + E * g;
-                qf[kb][nb] = M::load_q(qb, head, d0, p.h, p.d_h);
-            }
-    }
-    // Two register stages (the next block's loads in flight while one is consumed) wherever they
-    // fit in the register file; wide fp32 operands use one stage.
-    constexpr bool kTwoStages = sizeof(T) == 2 || HP * DP <= 1024;
-    Stage s0, s1;
-    int blk = blk_begin + w;
-    // The two stages are loaded unconditionally, clamped to the job's last block (which every wave
-    // may read): a wave with a single block reads one block twice, but the loads then sit in fixed
-    // program order, so the compiler can wait for each stage exactly instead of draining every load in
-    // flight at the top of the pipelined loop below.
-    // (Outside a fused step every work-group that gets here has a block.  A fused step's first job of an
-    // empty sequence has none: its stages read the cache's first block instead and never use it, so that
-    // no load sits behind a branch, which would leave every wait of the mode conservative.)
-    const int last_blk = blk_end - 1;
-    const bool any_blk = !kStep || blk_end > blk_begin;
-    auto load_clamped = [&](Stage &st, int b) { load(st, b < last_blk ? b : last_blk, any_blk); };
-    if (kTwoStages) {  // start streaming the first two blocks before anything else (a fused step issues
-                       // the second after its own set-up: a wave cannot pass its loads' issue until most of
-                       // them have landed, so work placed behind both stages would wait for the stream)
-        load_clamped(s0, blk);
-        if (kMode == kQRot) load_clamped(s1, blk + kWaves);
-    }
-    if constexpr (kFact) {
-        // Factored query, while the first blocks stream in: q[i][d] = (1/R_Q) sum_r A_Q[r][i] B_Q[r][d]
-        // (TPA notes page, tensor product decomposition applied to Q), computed once per work-group in
-        // 4 x 4 register tiles from LDS, then rotated to the query's position len (RoPE is linear, so
-        // rotating the combined row equals combining rotated B_Q rows: RoPE compatibility), all in fp32
-        // (fp64 for fp32 queries), rounded once to the element type, and read back as this lane's
-        // fragments.
-        if (tid < DP / 2) rope_cos_sin<T>(sm_cs + 2 * tid, double(len), theta_j);
+                float ak[2][4], av[2][4];
 #pragma unroll
-        for (int k = 0; k < QA_PER; ++k) {
-            const int idx = tid + k * kThreads;
-            if (idx < kMaxRQ * HP) sm_aq[idx / HP][idx % HP] = qa_raw[k];
-        }
-#pragma unroll
-        for (int k = 0; k < QB_PER; ++k) {
-            const int idx = tid + k * kThreads;
-            if (idx < kMaxRQ * DP) sm_bq[idx / DP][idx % DP] = qb_raw[k];
-        }
-        __syncthreads();
-        const float inv_rq = 1.f / float(p.r_q);
-        for (int t = tid; t < (HP / 4) * (DP / 4); t += kThreads) {
-            const int h0 = 4 * (t / (DP / 4)), d0 = 4 * (t % (DP / 4));
-            float a4[4][4] = {};
-            for (int r = 0; r < p.r_q; ++r) {
-                const float4 av = *reinterpret_cast<const float4 *>(&sm_aq[r][h0]);
-                const float4 bv = *reinterpret_cast<const float4 *>(&sm_bq[r][d0]);
-                const float ar[4] = {av.x, av.y, av.z, av.w}, br[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) a4[i][j] = fmaf(ar[i], br[j], a4[i][j]);
-            }
-            // features d0 .. d0 + 3 are the rotary pairs d0 / 2 and d0 / 2 + 1
-            const F c0 = sm_cs[d0], s0 = sm_cs[d0 + 1], c1 = sm_cs[d0 + 2], s1 = sm_cs[d0 + 3];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                F y[4];
-                rope_rotate(F(a4[i][0]), F(a4[i][1]), c0, s0, y[0], y[1]);
-                rope_rotate(F(a4[i][2]), F(a4[i][3]), c1, s1, y[2], y[3]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float x = float(y[j] * F(inv_rq));
-                    if constexpr (sizeof(T) == 2)
-                        sm_q[h0 + i][d0 + j] = uint16_t(pack_bf16x2(x, 0.f) & 0xffffu);
-                    else
-                        sm_q[h0 + i][d0 + j] = x;
+                for (int mb = 0; mb < 2; ++mb) {
+                    gates(st, false, mb, nb, ak[mb]);
+                    gates(st, true, mb, nb, av[mb]);
                 }
-            }
-        }
-        __syncthreads();
+                float z[2][TPL];
+                float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < KBS; ++kb)
+                for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) qf[kb][nb] = M::load(&sm_q[16 * nb + c][4 * E * kb + E * g]);
-        if (kTwoStages) load_clamped(s1, blk + kWaves);
-    }
-    if constexpr (kStep) {
-        // Fused step, while the first blocks stream in.  q arrives unrotated and sits at position len (the
-        // number of cached tokens).  The first job stages the new token's factors in LDS and, after the one
-        // barrier the angle table needs anyway, takes the token's score per head from the still unrotated
-        // query fragments and the unrotated B_K: query and token share a position, so RoPE drops out of that
-        // score (RoPE compatibility, Theorem 3.1 with t = s).  Then every wave rotates its query fragments
-        // (the table covers every padded pair; theta is zero past d_h / 2: an identity rotation of zeros),
-        // and the sequence's last job writes the token's record at slot len: no work-group of this kernel
-        // reads that slot's rows (a partly filled last block masks every row at or past len), and the next
-        // call sees it.
-        // Over an E4M3 cache the token enters as its stored values, exactly as tpa_cache_append and then a
-        // decode would see it: every factor is rounded to its code and decoded back, B_K after its rotation,
-        // which no longer cancels in the score; so the first job stages the rotated, decoded B~_K after the
-        // table and takes the score from the rotated query fragments behind a second barrier.
-        auto token_score = [&]() {
-            // the token's score per head: a lane sums its d-values, the four lane groups of a head are
-            // summed across (the same contraction as the cached tokens'); head block nb is taken by wave
-            // nb % kWaves, so the waves share the work
+                    for (int t = 0; t < TPL; ++t) {
+                        float sc = ak[mb][t * RH] * u[mb][nb][t * RH];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                if (nb % kWaves != w) continue;  // wave-uniform; static register indexing
-                float dot[RH];
-#pragma unroll
-                for (int r = 0; r < RH; ++r) {
-                    float x = 0.f;
-#pragma unroll
-                    for (int kb = 0; kb < KBS; ++kb) {
-                        float bk[E];
-                        if constexpr (E == 8) {
-                            const float4 lo = *reinterpret_cast<const float4 *>(&sm_nb[0][r][4 * E * kb + E * g]);
-                            const float4 hi = *reinterpret_cast<const float4 *>(&sm_nb[0][r][4 * E * kb + E * g + 4]);
-                            bk[0] = lo.x; bk[1] = lo.y; bk[2] = lo.z; bk[3] = lo.w;
-                            bk[4] = hi.x; bk[5] = hi.y; bk[6] = hi.z; bk[7] = hi.w;
-                        } else {
-                            bk[0] = sm_nb[0][r][4 * E * kb + E * g];
-                        }
-#pragma unroll
-                        for (int e = 0; e < E; ++e) x = fmaf(M::value(qf[kb][nb], e), bk[e], x);
+                        for (int r = 1; r < RH; ++r) sc = fmaf(ak[mb][t * RH + r], u[mb][nb][t * RH + r], sc);
+                        if (kTail) sc = (16 * mb + 4 * g) / RH + t < valid ? sc : -INFINITY;
+                        z[mb][t] = sc;
+                        mx = fmaxf(mx, sc);
                     }
-                    dot[r] = wave_sum_across_groups(x);
-                }
-                if (g == 0) {
-                    const int head = 16 * nb + c;
-                    float z = 0.f;
+                // Lazy reference max: the weights are taken relative to run_m, which only moves (with a
+                // cross-lane max and a rescale of the accumulators) when some score exceeds it by more than
+                // kLazy in log2 units, so p <= 2^kLazy and the common block needs no cross-lane traffic.
+                if (__any(mx > run_m[nb] + lazy_raw)) {
+                    const float mn = fmaxf(run_m[nb], wave_max_across_groups(mx));
+                    const float alpha = __builtin_amdgcn_exp2f((run_m[nb] - mn) * sm);
+                    run_m[nb] = mn;
+                    neg_ms[nb] = -mn * sm;
+                    run_l[nb] *= alpha;
 #pragma unroll
-                    for (int r = 0; r < RH; ++r) z = fmaf(sm_na[0][r][head], dot[r], z);
-                    sm_m[kWaves][head] = head < p.h ? z * p.score_mul : -INFINITY;
-                    sm_l[kWaves][head] = head < p.h ? 1.f : 0.f;
+                    for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] *= alpha;
+                }
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int t = 0; t < TPL; ++t) {
+                        const float pr = __builtin_amdgcn_exp2f(fmaf(z[mb][t], sm, neg_ms[nb]));
+                        run_l[nb] += pr;
+#pragma unroll
+                        for (int r = 0; r < RH; ++r) {
+                            float wgt = pr * av[mb][t * RH + r];
+                            // rows beyond the sequence: p is 0 but the stored A_V may be anything
+                            if (kTail) wgt = (16 * mb + 4 * g) / RH + t < valid ? wgt : 0.f;
+                            wv[mb][nb][t * RH + r] = wgt;
+                        }
+                    }
+            }
+
+            // ---- 5. value contraction (in a tail block, rows beyond the sequence have arbitrary stored B_V:
+            // their slots are zeroed in the operand)
+#pragma unroll
+            for (int q = 0; q < KBV; ++q) {
+                unsigned bits = 0;
+                if (kTail) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const int t = E * q + e;
+                        const int row = 16 * (t / 4) + 4 * g + (t % 4);
+                        if (row / RH >= valid) bits |= 1u << e;
+                    }
+                }
+                Frag bvf[MBV];
+#pragma unroll
+                for (int mv = 0; mv < MBV; ++mv)
+                    bvf[mv] = kTail ? M::mask(frag_bv(st, mv, q), bits) : frag_bv(st, mv, q);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    float x[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const int t = E * q + e;
+                        x[e] = wv[t / 4][nb][t % 4];
+                    }
+                    const Frag wf = M::pack(x);
+#pragma unroll
+                    for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] = M::mma(bvf[mv], wf, acc[mv][nb]);
+                    if constexpr (kSplitW) {  // the weights' bf16 rounding residuals, as a second product
+                        float r[E];
+#pragma unroll
+                        for (int e = 0; e < E; ++e) r[e] = x[e] - M::value(wf, e);
+                        const Frag wl = M::pack(r);
+#pragma unroll
+                        for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] = M::mma(bvf[mv], wl, acc[mv][nb]);
+                    }
                 }
             }
         };
-        // E4M3 codes of the token's items (A_K, A_V of this thread's head-factor item; B_V of its pair)
-        uint32_t ak8 = 0, av8 = 0, bv8 = 0;
-        if constexpr (kF8) {
-            ak8 = e4m3_one(Elem<T>::to_f32(nak) * p.st.inv_scale[0]);
-            av8 = e4m3_one(Elem<T>::to_f32(nav) * p.st.inv_scale[2]);
-            bv8 = e4m3_pair(Elem<T>::to_f32(nbv0) * p.st.inv_scale[3], Elem<T>::to_f32(nbv1) * p.st.inv_scale[3]);
-        }
-        if (new_tok) {
-            if (na_r < RH) {
-                if constexpr (kF8) {
-                    sm_na[0][na_r][na_i] = __builtin_amdgcn_cvt_f32_fp8(int(ak8), 0);
-                    sm_na[1][na_r][na_i] = __builtin_amdgcn_cvt_f32_fp8(int(av8), 0);
-                } else {
-                    sm_na[0][na_r][na_i] = Elem<T>::to_f32(nak);
-                    sm_na[1][na_r][na_i] = Elem<T>::to_f32(nav);
-                }
-            }
-            if (nb_r < RH) {
-                if constexpr (kF8) {
-                    const floatx2 v = __builtin_amdgcn_cvt_pk_f32_fp8(int(bv8), false);
-                    sm_nb[1][nb_r][nb_d] = v.x;
-                    sm_nb[1][nb_r][nb_d + 1] = v.y;
-                } else {
-                    sm_nb[0][nb_r][nb_d] = Elem<T>::to_f32(nbk0);
-                    sm_nb[0][nb_r][nb_d + 1] = Elem<T>::to_f32(nbk1);
-                    sm_nb[1][nb_r][nb_d] = Elem<T>::to_f32(nbv0);
-                    sm_nb[1][nb_r][nb_d + 1] = Elem<T>::to_f32(nbv1);
-                }
-            }
-        }
-        if (tid < DP / 2) rope_cos_sin<T>(sm_cs + 2 * tid, double(len), theta_j);
-        __syncthreads();
-        if constexpr (!kF8)
-            if (new_tok) token_score();
-#pragma unroll
-        for (int kb = 0; kb < KBS; ++kb)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) qf[kb][nb] = M::rotate_q(qf[kb][nb], 4 * E * kb + E * g, sm_cs);
-        const int64_t slot = start + len;
-        // the token's B~_K pair, rotated as tpa_cache_append rotates it
-        F y0 = F(0), y1 = F(0);
-        if ((kF8 ? (new_tok || rec_tok) : rec_tok) && nb_r < p.RK && nb_d < p.d_h)
-            rope_rotate(F(Elem<T>::to_f32(nbk0)), F(Elem<T>::to_f32(nbk1)), sm_cs[nb_d], sm_cs[nb_d + 1], y0, y1);
-        uint32_t bk8 = 0;
-        if constexpr (kF8) {
-            bk8 = e4m3_pair(float(y0) * p.st.inv_scale[1], float(y1) * p.st.inv_scale[1]);
-            if (new_tok) {
-                if (nb_r < RH) {
-                    const floatx2 v = __builtin_amdgcn_cvt_pk_f32_fp8(int(bk8), false);
-                    sm_nb[0][nb_r][nb_d] = v.x;
-                    sm_nb[0][nb_r][nb_d + 1] = v.y;
-                }
-                __syncthreads();  // first job only (uniform over the work-group)
-                token_score();
-            }
-        }
-        if (rec_tok && slot < p.st.capacity) {
-            const int row0 = int(slot % TOK) * RH;
-            if constexpr (kF8) {
-                // the E4M3 record: the same codes tpa_cache_append writes, in the paired 8-bit layout
-                uint8_t *rec = reinterpret_cast<uint8_t *>(p.st.cache) + (slot / TOK) * BLK;
-                const Layout Lay = make_layout(p.h, p.d_h, p.RK, p.RV, Elem<T>::dtype, 1);
-                if (na_r < RH) {
-                    rec[Lay.gate(row0 + na_r, na_i)] = uint8_t(ak8);
-                    rec[OFF_AV + Lay.gate(row0 + na_r, na_i)] = uint8_t(av8);
-                }
-                if (nb_r < RH) {
-                    *reinterpret_cast<uint16_t *>(rec + OFF_BK + Lay.bk(row0 + nb_r, nb_d)) = uint16_t(bk8);
-                    rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d)] = uint8_t(bv8 & 0xffu);
-                    rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d + 1)] = uint8_t(bv8 >> 8);
-                }
-            } else {
-                // the record, B_K rotated and rounded exactly as tpa_cache_append stores it
-                T k0 = nbk0, k1 = nbk1;
-                if (nb_r < p.RK && nb_d < p.d_h) {
-                    if constexpr (sizeof(T) == 2) {
-                        const uint32_t pk = pack_bf16x2(y0, y1);
-                        k0 = T(pk & 0xffffu);
-                        k1 = T(pk >> 16);
-                    } else {
-                        k0 = T(y0);
-                        k1 = T(y1);
-                    }
-                }
-                T *rec = reinterpret_cast<T *>(p.st.cache) + (slot / TOK) * BLK;
-                const Layout Lay = make_layout(p.h, p.d_h, p.RK, p.RV, Elem<T>::dtype);
-                if (na_r < RH) {
-                    rec[Lay.gate(row0 + na_r, na_i)] = nak;
-                    rec[OFF_AV + Lay.gate(row0 + na_r, na_i)] = nav;
-                }
-                if (nb_r < RH) {
-                    rec[OFF_BK + Lay.bk(row0 + nb_r, nb_d)] = k0;
-                    rec[OFF_BK + Lay.bk(row0 + nb_r, nb_d + 1)] = k1;
-                    rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d)] = nbv0;
-                    rec[OFF_BV + Lay.bv(row0 + nb_r, nb_d + 1)] = nbv1;
-                }
-            }
-        }
-        if (kTwoStages) load_clamped(s1, blk + kWaves);
-    }
+        using Full = std::integral_constant<bool, false>;
+        using Tail = std::integral_constant<bool, true>;
 
-
-    floatx4 acc[MBV][NB];
-#pragma unroll
-    for (int mv = 0; mv < MBV; ++mv)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mv][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // Scores are kept in raw units z = sum_r A_K U (the scale is applied inside the exponent);
-    // run_m is the lazy reference max in raw units, neg_ms = -run_m * score_mul.
-    float run_m[NB], neg_ms[NB], run_l[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        run_m[nb] = -INFINITY;
-        neg_ms[nb] = INFINITY;
-        run_l[nb] = 0.f;
-    }
-    const float sm = p.score_mul;
-    const float lazy_raw = kLazy / sm;
-
-    // Process one block.  kTail: the block may hold rows beyond the sequence (valid < TOK tokens);
-    // only the last block of a sequence can, and it takes this slower masked path.
-    auto process = [&](Stage &st, auto tail_tag, int valid) {
-        constexpr bool kTail = decltype(tail_tag)::value;
-        // ---- 1. score contraction
-        floatx4 u[2][NB];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                floatx4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < KBS; ++kb) a = M::mma(frag_bk(st, mb, kb), qf[kb][nb], a);
-                u[mb][nb] = a;
-            }
-
-        // ---- 2.-4. gates, online softmax, value weights
-        float wv[2][NB][4];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            float ak[2][4], av[2][4];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                gates(st, false, mb, nb, ak[mb]);
-                gates(st, true, mb, nb, av[mb]);
-            }
-            float z[2][TPL];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int t = 0; t < TPL; ++t) {
-                    float sc = ak[mb][t * RH] * u[mb][nb][t * RH];
-#pragma unroll
-                    for (int r = 1; r < RH; ++r) sc = fmaf(ak[mb][t * RH + r], u[mb][nb][t * RH + r], sc);
-                    if (kTail) sc = (16 * mb + 4 * g) / RH + t < valid ? sc : -INFINITY;
-                    z[mb][t] = sc;
-                    mx = fmaxf(mx, sc);
-                }
-            // Lazy reference max: the weights are taken relative to run_m, which only moves (with a
-            // cross-lane max and a rescale of the accumulators) when some score exceeds it by more than
-            // kLazy in log2 units, so p <= 2^kLazy and the common block needs no cross-lane traffic.
-            if (__any(mx > run_m[nb] + lazy_raw)) {
-                const float mn = fmaxf(run_m[nb], wave_max_across_groups(mx));
-                const float alpha = __builtin_amdgcn_exp2f((run_m[nb] - mn) * sm);
-                run_m[nb] = mn;
-                neg_ms[nb] = -mn * sm;
-                run_l[nb] *= alpha;
-#pragma unroll
-                for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] *= alpha;
-            }
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int t = 0; t < TPL; ++t) {
-                    const float pr = __builtin_amdgcn_exp2f(fmaf(z[mb][t], sm, neg_ms[nb]));
-                    run_l[nb] += pr;
-#pragma unroll
-                    for (int r = 0; r < RH; ++r) {
-                        float wgt = pr * av[mb][t * RH + r];
-                        // rows beyond the sequence: p is 0 but the stored A_V may be anything
-                        if (kTail) wgt = (16 * mb + 4 * g) / RH + t < valid ? wgt : 0.f;
-                        wv[mb][nb][t * RH + r] = wgt;
-                    }
-                }
-        }
-
-        // ---- 5. value contraction (in a tail block, rows beyond the sequence have arbitrary stored B_V:
-        // their slots are zeroed in the operand)
-#pragma unroll
-        for (int q = 0; q < KBV; ++q) {
-            unsigned bits = 0;
-            if (kTail) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const int t = E * q + e;
-                    const int row = 16 * (t / 4) + 4 * g + (t % 4);
-                    if (row / RH >= valid) bits |= 1u << e;
-                }
-            }
-            Frag bvf[MBV];
-#pragma unroll
-            for (int mv = 0; mv < MBV; ++mv) bvf[mv] = kTail ? M::mask(frag_bv(st, mv, q), bits) : frag_bv(st, mv, q);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                float x[E];
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const int t = E * q + e;
-                    x[e] = wv[t / 4][nb][t % 4];
-                }
-                const Frag wf = M::pack(x);
-#pragma unroll
-                for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] = M::mma(bvf[mv], wf, acc[mv][nb]);
-                if constexpr (kSplitW) {  // the weights' bf16 rounding residuals, as a second product
-                    float r[E];
-#pragma unroll
-                    for (int e = 0; e < E; ++e) r[e] = x[e] - M::value(wf, e);
-                    const Frag wl = M::pack(r);
-#pragma unroll
-                    for (int mv = 0; mv < MBV; ++mv) acc[mv][nb] = M::mma(bvf[mv], wl, acc[mv][nb]);
-                }
-            }
-        }
-    };
-    using Full = std::integral_constant<bool, false>;
-    using Tail = std::integral_constant<bool, true>;
-
-    // Steady state: stage k holds block blk + k * kWaves and both refills are real blocks, so the loop
-    // issues the same loads in the same order every iteration and each stage waits for exactly its own
-    // loads (with a conditional refill the compiler cannot count the loads issued after a stage and
-    // drains everything in flight at the top of every iteration).
-    if (kTwoStages) {
-        while (blk + 3 * kWaves < full_end) {
-            process(s0, Full{}, TOK);
-            load(s0, blk + 2 * kWaves);
-            process(s1, Full{}, TOK);
-            load(s1, blk + 3 * kWaves);
-            blk += 2 * kWaves;
-        }
-    }
-    if (kTwoStages) {
-        // The last (at most three) full blocks of the wave, in straight-line code so that the first one
-        // still waits only for its own stage: blk in s0, blk + kWaves in s1, blk + 2 kWaves refilled
-        // into s0.
-        if (blk < full_end) {
-            process(s0, Full{}, TOK);
-            if (blk + 2 * kWaves < full_end) load(s0, blk + 2 * kWaves);
-            blk += kWaves;
-            if (blk < full_end) {
+        // Steady state: stage k holds block blk + k * kWaves and both refills are real blocks, so the loop
+        // issues the same loads in the same order every iteration and each stage waits for exactly its own
+        // loads (with a conditional refill the compiler cannot count the loads issued after a stage and
+        // drains everything in flight at the top of every iteration).
+        if (kTwoStages) {
+            while (blk + 3 * kWaves < full_end) {
+                process(s0, Full{}, TOK);
+                load(s0, blk + 2 * kWaves);
                 process(s1, Full{}, TOK);
+                load(s1, blk + 3 * kWaves);
+                blk += 2 * kWaves;
+            }
+        }
+        if (kTwoStages) {
+            // The last (at most three) full blocks of the wave, in straight-line code so that the first one
+            // still waits only for its own stage: blk in s0, blk + kWaves in s1, blk + 2 kWaves refilled
+            // into s0.
+            if (blk < full_end) {
+                process(s0, Full{}, TOK);
+                if (blk + 2 * kWaves < full_end) load(s0, blk + 2 * kWaves);
                 blk += kWaves;
                 if (blk < full_end) {
-                    process(s0, Full{}, TOK);
+                    process(s1, Full{}, TOK);
                     blk += kWaves;
+                    if (blk < full_end) {
+                        process(s0, Full{}, TOK);
+                        blk += kWaves;
+                    }
                 }
             }
-        }
-    } else {
-        for (; blk < full_end; blk += kWaves) {
-            load(s0, blk);
-            process(s0, Full{}, TOK);
-        }
-    }
-    // the sequence's last, partly filled block, if it falls to this wave
-    if (blk < blk_end) {
-        load(s0, blk);
-        process(s0, Tail{}, len - blk * TOK);
-    }
-    // back to log2 units for the merges
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) run_m[nb] = run_m[nb] * sm;
-
-    // ---- merge the waves of this work-group
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) run_l[nb] = wave_sum_across_groups(run_l[nb]);
-    if (g == 0) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            sm_m[w][16 * nb + c] = run_m[nb];
-            sm_l[w][16 * nb + c] = run_l[nb];
-        }
-    }
-    __syncthreads();
-    float wscale[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int head = 16 * nb + c;
-        float mm = sm_m[0][head];
-#pragma unroll
-        for (int ww = 1; ww <= kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][head]);
-        wscale[nb] = run_m[nb] == -INFINITY ? 0.f : exp2f(run_m[nb] - mm);
-        if constexpr (kStep)
-            if (new_tok && w == 0 && g == 0)  // the new token's weight, once per head
-                sm_wt[head] = sm_m[kWaves][head] == -INFINITY ? 0.f : exp2f(sm_m[kWaves][head] - mm);
-    }
-    // every wave writes its rescaled accumulators to its own LDS slice; after one barrier all threads
-    // sum the slices column by column straight into the job's partial
-#pragma unroll
-    for (int mv = 0; mv < MBV; ++mv)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const floatx4 a = acc[mv][nb] * wscale[nb];
-            *reinterpret_cast<float4 *>(&sm_o[w][16 * nb + c][16 * mv + 4 * g]) = make_float4(a[0], a[1], a[2], a[3]);
-        }
-    __syncthreads();
-    // write the job's partial: O [HP][DP], (max, sum) [HP]
-    float *wo = p.ws_o + part * HP * DP;
-    for (int idx = threadIdx.x; idx < HP * DP / 4; idx += kThreads) {
-        const int hh = idx / (DP / 4), d4 = idx % (DP / 4);
-        float4 o = *reinterpret_cast<const float4 *>(&sm_o[0][hh][4 * d4]);
-#pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) {
-            const float4 x = *reinterpret_cast<const float4 *>(&sm_o[ww][hh][4 * d4]);
-            o.x += x.x;
-            o.y += x.y;
-            o.z += x.z;
-            o.w += x.w;
-        }
-        if constexpr (kStep) {
-            if (new_tok) {  // the new token's value row, at its own weight
-                const float wt = sm_wt[hh];
-                float v[4] = {0.f, 0.f, 0.f, 0.f};
-                for (int r = 0; r < RH; ++r)
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) v[k] = fmaf(sm_na[1][r][hh], sm_nb[1][r][4 * d4 + k], v[k]);
-                o.x = fmaf(v[0], wt, o.x);
-                o.y = fmaf(v[1], wt, o.y);
-                o.z = fmaf(v[2], wt, o.z);
-                o.w = fmaf(v[3], wt, o.w);
+        } else {
+            for (; blk < full_end; blk += kWaves) {
+                load(s0, blk);
+                process(s0, Full{}, TOK);
             }
         }
-        *reinterpret_cast<float4 *>(wo + hh * DP + 4 * d4) = o;
-    }
-    for (int head = threadIdx.x; head < HP; head += kThreads) {
-        float mm = sm_m[0][head];
-        for (int ww = 1; ww <= kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][head]);
-        float ll = 0.f;
-        for (int ww = 0; ww <= kWaves; ++ww)
-            ll += sm_m[ww][head] == -INFINITY ? 0.f : sm_l[ww][head] * exp2f(sm_m[ww][head] - mm);
-        *reinterpret_cast<float2 *>(p.ws_ml + (part * HP + head) * 2) = make_float2(mm, ll);
-    }
+        // the sequence's last, partly filled block, if it falls to this wave
+        if (blk < blk_end) {
+            load(s0, blk);
+            process(s0, Tail{}, len - blk * TOK);
+        }
+        // back to log2 units for the merges
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) run_m[nb] = run_m[nb] * sm;
+
+        // ---- merge the waves of this work-group
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) run_l[nb] = wave_sum_across_groups(run_l[nb]);
+        if (g == 0) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                sm_m[w][16 * nb + c] = run_m[nb];
+                sm_l[w][16 * nb + c] = run_l[nb];
+            }
+        }
+        __syncthreads();
+        float wscale[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int head = 16 * nb + c;
+            float mm = sm_m[0][head];
+#pragma unroll
+            for (int ww = 1; ww <= kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][head]);
+            wscale[nb] = run_m[nb] == -INFINITY ? 0.f : exp2f(run_m[nb] - mm);
+            if constexpr (kStep)
+                if (new_tok && w == 0 && g == 0)  // the new token's weight, once per head
+                    sm_wt[head] = sm_m[kWaves][head] == -INFINITY ? 0.f : exp2f(sm_m[kWaves][head] - mm);
+        }
+        // every wave writes its rescaled accumulators to its own LDS slice; after one barrier all threads
+        // sum the slices column by column straight into the job's partial
+#pragma unroll
+        for (int mv = 0; mv < MBV; ++mv)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const floatx4 a = acc[mv][nb] * wscale[nb];
+                *reinterpret_cast<float4 *>(&sm_o[w][16 * nb + c][16 * mv + 4 * g]) =
+                    make_float4(a[0], a[1], a[2], a[3]);
+            }
+        __syncthreads();
+        // write the job's partial: O [HP][DP], (max, sum) [HP]
+        float *wo = p.ws_o + part * HP * DP;
+        for (int idx = threadIdx.x; idx < HP * DP / 4; idx += kThreads) {
+            const int hh = idx / (DP / 4), d4 = idx % (DP / 4);
+            float4 o = *reinterpret_cast<const float4 *>(&sm_o[0][hh][4 * d4]);
+#pragma unroll
+            for (int ww = 1; ww < kWaves; ++ww) {
+                const float4 x = *reinterpret_cast<const float4 *>(&sm_o[ww][hh][4 * d4]);
+                o.x += x.x;
+                o.y += x.y;
+                o.z += x.z;
+                o.w += x.w;
+            }
+            if constexpr (kStep) {
+                if (new_tok) {  // the new token's value row, at its own weight
+                    const float wt = sm_wt[hh];
+                    float v[4] = {0.f, 0.f, 0.f, 0.f};
+                    for (int r = 0; r < RH; ++r)
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) v[k] = fmaf(sm_na[1][r][hh], sm_nb[1][r][4 * d4 + k], v[k]);
+                    o.x = fmaf(v[0], wt, o.x);
+                    o.y = fmaf(v[1], wt, o.y);
+                    o.z = fmaf(v[2], wt, o.z);
+                    o.w = fmaf(v[3], wt, o.w);
+                }
+            }
+            *reinterpret_cast<float4 *>(wo + hh * DP + 4 * d4) = o;
+        }
+        for (int head = threadIdx.x; head < HP; head += kThreads) {
+            float mm = sm_m[0][head];
+            for (int ww = 1; ww <= kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][head]);
+            float ll = 0.f;
+            for (int ww = 0; ww <= kWaves; ++ww)
+                ll += sm_m[ww][head] == -INFINITY ? 0.f : sm_l[ww][head] * exp2f(sm_m[ww][head] - mm);
+            *reinterpret_cast<float2 *>(p.ws_ml + (part * HP + head) * 2) = make_float2(mm, ll);
+        }
     };
 
     // the jobs of this work-group's range, in batch order
