@@ -48,7 +48,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
 MALL_BYTES = 256 << 20
-HEADLINE = "c5"
+HEADLINE = "ragged"
+DECODE_WORKLOADS = ("rank1", "h16", "longctx", HEADLINE)   # every decode workload with a profile
 REPEATS = 5
 CSRC = os.path.join(ROOT, "factorized_kv_cache_tpa_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -441,7 +442,7 @@ def summarize_profiles(raw: str) -> None:
     header = ("Commands (from the repository root, on one MI355X; each pass a run of its own, then the "
               f"summary):\n\n")
     # kernel traces
-    traces = [(f"kt_step_{c}", "step", c, "decode_step_" + ti.get(c).name) for c in ("c2", "c3", "c4", "c5")]
+    traces = [(f"kt_step_{c}", "step", c, "decode_step_" + ti.get(c).name) for c in DECODE_WORKLOADS]
     traces += [("kt_prefill", "prefill", None, "prefill_b8_ctx2048_chunk512_h32_d128_r4"),
                ("kt_append", "append", None, "append_chunk_b8x512_h32_d128_r4")]
     for d, leg, c, label in traces:
@@ -481,7 +482,7 @@ def summarize_profiles(raw: str) -> None:
         with open(os.path.join(PROFILES, "kernel_trace_all_workloads.md"), "w") as fh:
             fh.write("\n".join(lines) + "\n")
     # HBM bytes of the decode step, scaled by what the same counters read for a plain 64 MiB copy
-    for c in ("c2", "c3", "c4", "c5"):
+    for c in DECODE_WORKLOADS:
         fpath, wpath = (os.path.join(raw, f"{k}_{c}", "run_counter_collection.csv") for k in ("fetch", "write"))
         if not (os.path.exists(fpath) and os.path.exists(wpath)):
             continue
@@ -712,7 +713,7 @@ def main():
         line["stream_probe_GBps"] = stream_probe(timer)
         log(f"[stream probe] {line['stream_probe_GBps']}")
         extras = {}
-        for name in ("c2", "c3", "c4"):
+        for name in ("rank1", "h16", "longctx"):
             b = DecodeBench(name, min_bytes=4 * MALL_BYTES)
             r = b.legs(timer)
             tr = profile_record("hbm_bytes_" + b.w.name, DECODE_SOURCES)
@@ -732,7 +733,7 @@ def main():
             del b
             torch.cuda.empty_cache()
         # the same workloads over an 8-bit (E4M3) factor cache: half the bytes per cached token
-        for name in ("c2", "c3", "c4", HEADLINE):
+        for name in ("rank1", "h16", "longctx", HEADLINE):
             b = DecodeBench(name, min_bytes=4 * MALL_BYTES, cache_format=tpa.TPA_CACHE_E4M3)
             r = b.legs(timer)
             gbps = b.bytes / (r["decode_ms"] / 1e3) / 1e9

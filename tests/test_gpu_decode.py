@@ -18,7 +18,7 @@ def _check_all(setup: DecodeSetup, out: np.ndarray, what: str, scale=None):
 
 def test_tiny_fp32_workload():
     """h=4, d_h=16, R=1, 64 cached tokens, query at position 64, fp32: tolerance 1e-5."""
-    w = ti.get("c1")
+    w = ti.get("tiny")
     say("case: tiny fp32 decode workload")
     s = DecodeSetup(w, ti.decode_batch(w))
     _check_all(s, s.run(), "tiny fp32")
@@ -154,7 +154,7 @@ def test_cache_tail_garbage_is_ignored():
 
 # ---- the measured workloads at full size ------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["c2", "c3"])
+@pytest.mark.parametrize("name", ["rank1", "h16"])
 def test_full_size_decode_all_sequences(name):
     w = ti.get(name)
     say(f"case: full-size {w.name}")
@@ -163,7 +163,7 @@ def test_full_size_decode_all_sequences(name):
 
 
 def test_full_size_long_context():
-    w = ti.get("c4")
+    w = ti.get("longctx")
     say(f"case: full-size {w.name}")
     s = DecodeSetup(w, ti.decode_batch(w))
     _check_all(s, s.run(), w.name)
@@ -173,7 +173,7 @@ def test_full_size_ragged_decode_all_sequences():
     """128 ragged sequences (lengths uniform in [1024, 32768]) in the benchmark's launch configuration; the
     whole output is compared with the oracle (every sequence, every head)."""
     import time
-    w = ti.get("c5")
+    w = ti.get("ragged")
     say(f"case: full-size ragged decode {w.name}")
     s = DecodeSetup(w, ti.decode_batch(w))
     out = s.run()

@@ -153,7 +153,7 @@ def test_decode_saturated_cache():
 
 def test_full_size_decode_b16_h32_d128_r1_n4096():
     """The 16 x 4096-token, h=32, d_h=128, R=1 workload over an E4M3 cache, every sequence checked."""
-    w = ti.get("c2")
+    w = ti.get("rank1")
     say(f"case: e4m3 full size {w.name}")
     s = DecodeSetup(w, ti.decode_batch(w), lens=list(ti.decode_lengths(w)), dims=dims_of(w, E4M3))
     got = s.run()
@@ -288,7 +288,7 @@ def test_decode_after_step_sees_the_written_token():
 
 
 def test_step_full_size_decode_b16_h32_d128_r1_n4096():
-    w = ti.get("c2")
+    w = ti.get("rank1")
     say(f"case: e4m3 step full size {w.name}")
     lens = list(ti.decode_lengths(w))
     seqs = [ti.draw_sequence(np.random.SeedSequence([w.seed, 77, b]), lens[b] + 1, 1, w) for b in range(w.batch)]
@@ -388,14 +388,14 @@ def test_step_misaligned_start_gives_nan_and_writes_nothing():
     assert int(changed.min()) >= (40 // 32) * blk and int(changed.max()) < (40 // 32 + 1) * blk
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["rank1", "h16", "longctx", "ragged"])
 def test_storage_accuracy_on_the_measured_workloads(name):
     """What 8-bit factor storage costs in accuracy (the TPA notes page lists TPA with quantization as
     unexplored): the E4M3 path at full size, compared (a) with the oracle on the values the cache stores
     (parity, the usual bound) and (b) with the oracle on the unquantized bf16 factors (the storage error,
     reported; a sanity bound only).  The ragged workload checks its first 8 sequences."""
     w = ti.get(name)
-    only = list(range(8)) if name == "c5" else None
+    only = list(range(8)) if name == "ragged" else None
     seqs = ti.decode_batch(w, only=only)
     say(f"case: E4M3 storage accuracy on {w.name}")
     s = DecodeSetup(w, seqs, dims=dims_of(w, E4M3))

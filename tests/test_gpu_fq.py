@@ -120,7 +120,7 @@ def test_fq_split_sizes(split_tokens):
 def test_fq_full_size_decode_b16_h32_d128_r1_n4096_rq6():
     """The metric's cache (16 x 4096 cached tokens, h=32, d_h=128, R=1) with a rank-6 factored query,
     every sequence checked."""
-    w = ti.get("c2")
+    w = ti.get("rank1")
     say(f"case: fq full size {w.name} R_Q=6")
     lens = list(ti.decode_lengths(w))
     st = FQSetup(w, lens, R_Q=6, seqs=ti.decode_batch(w), seed=w.seed)

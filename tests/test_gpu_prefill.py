@@ -73,7 +73,7 @@ def test_full_size_prefill_all_rows():
     """8 sequences x (2048 cached + 512-row causal chunk), h=32, d_h=128, R=4: every row of every sequence
     compared with the oracle."""
     import time
-    w = ti.get("c5")
+    w = ti.get("ragged")
     say(f"case: full-size prefill of {w.name}")
     seqs = ti.prefill_batch(w)
     s = PrefillSetup(w, seqs, [w.prefill_ctx] * w.prefill_batch)

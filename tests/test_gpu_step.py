@@ -170,7 +170,7 @@ def test_step_split_sizes(split_tokens):
 
 def test_step_full_size_decode_b16_h32_d128_r1_n4096():
     """The metric's workload: 16 sequences of 4096 cached tokens, every sequence checked."""
-    w = ti.get("c2")
+    w = ti.get("rank1")
     say(f"case: step full size {w.name}")
     lens = list(ti.decode_lengths(w))
     seqs = []

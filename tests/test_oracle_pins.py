@@ -231,7 +231,7 @@ def test_brute_force_agreement(h, d, RK, RV, n):
 
 def test_brute_force_on_tiny_fp32_workload():
     """The tiny fp32 decode workload itself (h=4, d_h=16, R=1, 64 cached tokens, query at 64)."""
-    w = ti.get("c1")
+    w = ti.get("tiny")
     s = ti.decode_sequence(w, 0)
     f = lambda a: ti.to_f64(a, w.dtype)
     A_K, B_K, A_V, B_V, q = map(f, (s.A_K, s.B_K, s.A_V, s.B_V, s.q))

@@ -80,7 +80,7 @@ def test_storage_floor_of_sharp_rank1_decode(h, d_h):
 
 def test_storage_floor_is_small_on_the_measured_workloads():
     """The same floor on a sample of the 16 x 4096 workload (unsharpened query) is far inside both bounds."""
-    w = ti.get("c2")
+    w = ti.get("rank1")
     for b in (0, 7):
         s = ti.decode_sequence(w, b)
         n = 512  # the first 512 tokens keep it quick; the query sits at position n

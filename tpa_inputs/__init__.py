@@ -75,8 +75,15 @@ WORKLOADS: Dict[str, Workload] = {
     ]
 }
 
-# short aliases in the order the workloads are listed
-ALIASES = {f"c{i + 1}": name for i, name in enumerate(WORKLOADS)}
+# short names: what sets each workload apart
+ALIASES = {
+    "tiny": "tiny_decode_b1_h4_d16_r1_n64_f32",
+    "rank1": "decode_b16_h32_d128_r1_n4096",
+    "h16": "decode_b64_h16_d64_r2_n8192",
+    "longctx": "longctx_decode_b4_h32_d128_r2_n131072",
+    "ragged": "ragged_decode_b128_h32_d128_r4_plus_prefill_b8_ctx2048_chunk512",
+}
+assert set(ALIASES.values()) == set(WORKLOADS)
 
 
 def get(name: str) -> Workload:
