@@ -700,8 +700,9 @@ struct Prefill2Lds {
     static constexpr int BPT = kKT2 / TOK;                   // cache blocks per tile
     static constexpr int MVG = kPrefillWaves / BPT;          // waves sharing one block's value chunks
     static constexpr int V_ITEMS = (DP / 16) / MVG;          // value chunks per lane
-    static constexpr int PIECES = RH + V_ITEMS;              // 16-byte pieces per lane
-    static constexpr int GATE_OFF = PIECES * 1024;           // then 3 gate slots (12 bytes used of 16 per lane)
+    static constexpr int K_STRIDE = 1024 + 16;               // K~ pieces, each one bank group after the last
+    static constexpr int V_OFF = RH * K_STRIDE;              // then the value chunks
+    static constexpr int GATE_OFF = V_OFF + V_ITEMS * 1024;  // then 3 gate slots (12 bytes used of 16 per lane)
     static constexpr int RAW_BYTES = GATE_OFF + 3 * 1024;
     uint16_t k[2][kKT2 * (DP + 8)];
     uint16_t v[2][DP * (kKT2 + 8)];
@@ -768,12 +769,18 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
     // over RH of the 4 32-feature column blocks, so each of its RH fetches is one whole, contiguous 1 KB
     // piece of the cache block; lane (key kl, chunk) then reads the RH rank pieces of its key from the
     // staging area.  V: V_ITEMS contiguous value chunks of one cache block.
+    // A K~ piece's 64 chunks are (sub, row): features 8 sub .. 8 sub + 7 of factor row `row` of the group, at
+    // chunk 16 sub + row of the cache block.  Staged in that order, the 16 lanes that read one rank row at a
+    // time (one key, four pieces x four subs) would hit chunks 256 bytes apart: the same four LDS banks.  So
+    // chunk (sub, row) goes to slot 16 sub + (row ^ 4 sub) (the rows of a sub stay in its 256 bytes), and
+    // piece q starts 16 q bytes past a 1 KB boundary: the 16 lanes' reads then fall in 16 different bank groups.
     constexpr int WPG = 4 / RH;                       // waves per 16-row group
     const int gi = w / WPG;                           // the wave's 16-row group inside the tile
     const int kbw0 = (w % WPG) * RH;                  // its first 32-feature column block
     const int kl = lane / (4 * RH);                   // this lane's key inside the group
     const int k_blk = gi / 2, k_mb = gi % 2;          // cache block (tile-relative) and row group in it
-    const uint32_t k_off_b = uint32_t(k_blk * BLK + OFF_BK + ((k_mb * KBS + kbw0) * kWave + lane) * 8) * 2u;
+    const int lane_sw = lane ^ ((lane >> 4) << 2);   // the cache chunk this lane stages into its slot
+    const uint32_t k_off_b = uint32_t(k_blk * BLK + OFF_BK + ((k_mb * KBS + kbw0) * kWave + lane_sw) * 8) * 2u;
     const int k_gl = 16 * ((kl * RH) >> 2) + gate_lane;
     const uint32_t k_off_gate = uint32_t(k_blk * BLK + ((k_mb * NB + gate_nb) * kWave + k_gl) * 4) * 2u;
     const int vrow = w, vcl = lane, vg4 = vcl >> 4;
@@ -801,11 +808,13 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
         asm volatile("" : "+v"(ko), "+v"(kg), "+v"(vo), "+v"(vg));
 #pragma unroll
         for (int q = 0; q < RH; ++q)
-            __builtin_amdgcn_global_load_lds(tb + uint32_t(ko + q * kWave * 16), (lds_ptr)(rw + q * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(tb + uint32_t(ko + q * kWave * 16), (lds_ptr)(rw + q * LD::K_STRIDE), 16,
+                                             0, 0);
         __builtin_amdgcn_global_load_lds(tb + uint32_t(ko + kg), (lds_ptr)(rw + LD::GATE_OFF), 12, 0, 0);
 #pragma unroll
         for (int u = 0; u < V_ITEMS; ++u)
-            __builtin_amdgcn_global_load_lds(tb + uint32_t(vo + u * kWave * 16), (lds_ptr)(rw + (RH + u) * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(tb + uint32_t(vo + u * kWave * 16), (lds_ptr)(rw + LD::V_OFF + u * 1024), 16,
+                                             0, 0);
 #pragma unroll
         for (int m = 0; m < 2; ++m)
             __builtin_amdgcn_global_load_lds(tb + uint32_t(vo + vg + m * NB * kWave * 8),
@@ -826,8 +835,9 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
         {
             const uint32_t *gp = reinterpret_cast<const uint32_t *>(rl + LD::GATE_OFF);
             const uint32_t gw[2] = {gp[0], gp[1]};
-            // rank pieces of this lane's key: position 16 sub + kl RH + r of column block kb
-            const char *kp = rw + (kb_ - kbw0) * 1024 + 16 * (16 * sub_ + kl_ * RH);
+            // rank pieces of this lane's key: row kl RH + r of sub `sub` in piece kb - kbw0, in slot
+            // 16 sub + ((kl RH) ^ 4 sub) + r (r only occupies the row's low bits)
+            const char *kp = rw + (kb_ - kbw0) * LD::K_STRIDE + 16 * (16 * sub_ + ((kl_ * RH) ^ (4 * sub_)));
             uint4 kbr[RH];
 #pragma unroll
             for (int r = 0; r < RH; ++r) kbr[r] = *reinterpret_cast<const uint4 *>(kp + 16 * r);
@@ -865,7 +875,7 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
         uint16_t *dV = &lds.v[buf][(16 * vmv0 + (ln & 15)) * SVS];
 #pragma unroll
         for (int u = 0; u < V_ITEMS; ++u) {
-            const uint4 vxu = *reinterpret_cast<const uint4 *>(rl + (RH + u) * 1024);
+            const uint4 vxu = *reinterpret_cast<const uint4 *>(rl + LD::V_OFF + u * 1024);
             const uint32_t xw[4] = {vxu.x, vxu.y, vxu.z, vxu.w};
             float v_one[2];
 #pragma unroll
