@@ -22,7 +22,7 @@ The line carries:
                     (profiles/), or null when the kernels changed since the counters were taken;
   roofline_prefill  the prefill kernel: causal-exact flops over its median duration against the
                     2.5 PFLOP/s dense bf16 matrix-core peak, with the counters' busy fraction;
-  legs              each part of the step timed alone (median of 5 windows);
+  legs              each part of the step timed alone (median of 5 windows after 0.3 s of warm-up replays);
   stream_probe_GBps a plain streaming read of 2 GiB with the decode's load width and hint;
   extras            the other decode workloads (16 x 4096, 64 x 8192, 4 x 131072) and the same
                     workloads over an 8-bit E4M3 factor cache;
@@ -51,6 +51,7 @@ MALL_BYTES = 256 << 20
 HEADLINE = "ragged"
 DECODE_WORKLOADS = ("rank1", "h16", "longctx", HEADLINE)   # every decode workload with a profile
 REPEATS = 5
+LEG_WARM_S = 0.3                # warm-up replays before each leg's windows (seconds)
 CSRC = os.path.join(ROOT, "factorized_kv_cache_tpa_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -130,9 +131,14 @@ class Timer:
 
     def median_call_ms(self, fn, n_calls: int, min_calls: int = 20) -> float:
         """Median over REPEATS windows of the milliseconds per call; a window replays a graph of n_calls
-        calls as often as needed to reach min_calls calls."""
+        calls as often as needed to reach min_calls calls.  Before the windows the graph is replayed for
+        LEG_WARM_S seconds (at most 2000 replays), so that a short leg is timed at the clocks the GPU holds
+        under sustained work rather than while they are still ramping up."""
         g = self.capture(fn, n_calls)
-        self.window_ms(g, 1)  # warm replay
+        t0, warm = time.perf_counter(), 0
+        while warm < 2000 and time.perf_counter() - t0 < LEG_WARM_S:
+            self.window_ms(g, 1)
+            warm += 1
         replays = max(1, -(-min_calls // n_calls))
         ms = [self.window_ms(g, replays) / (replays * n_calls) for _ in range(REPEATS)]
         return float(np.median(ms))
@@ -395,6 +401,14 @@ def run_profile_leg(leg: str, workload: str, calls: int, calibration: bool) -> N
         fn = p.prefill if leg == "prefill" else p.append
     else:
         raise SystemExit(f"unknown leg {leg}")
+    if leg in ("prefill", "append"):
+        # calls for LEG_WARM_S seconds first (in the trace too), as the timed legs do: these short, compute-bound
+        # calls otherwise run while the clocks are still ramping up
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < LEG_WARM_S:
+            for _ in range(10):
+                fn(0)
+            torch.cuda.synchronize()
     for i in range(calls):
         fn(i)
     torch.cuda.synchronize()
@@ -704,7 +718,8 @@ def main():
                  "prefill_us": round(p_legs["prefill_ms"] * 1e3, 2),
                  "prefill_TFLOPs": round(pre_tf, 1),
                  "factored_query_rq6_prefill_us": round(p_legs["prefill_fq_ms"] * 1e3, 2),
-                 "timing": f"median of {REPEATS} windows of graph replays, events on the replay stream"},
+                 "timing": f"median of {REPEATS} windows of graph replays after {LEG_WARM_S} s of warm-up replays, "
+                           "events on the replay stream"},
     }
     del dec, pre, g
     torch.cuda.empty_cache()
