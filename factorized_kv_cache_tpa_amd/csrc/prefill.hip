@@ -824,20 +824,20 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
     // Its per-lane addresses are derived from an opaque copy of the lane index, so they live only here.
     auto rebuild = [&](int kt, int buf, auto partial_tag) {
         constexpr bool kPartial = decltype(partial_tag)::value;
-        int ln = lane;
+        uint32_t ln = lane;  // unsigned: the divisions and remainders below are shifts and masks
         asm volatile("" : "+v"(ln));
         const int key0 = kt * kKT2;
         const char *rl = rw + 16 * ln;  // this lane's 16-byte slot of each staged piece
-        const int kl_ = ln / (4 * RH), cl_ = ln % (4 * RH);
-        const int kb_ = kbw0 + cl_ / 4, sub_ = cl_ % 4;
-        const int kk_ = (16 * gi) / RH + kl_;
-        const int kv0_ = (kl_ * RH) & 3;
+        const uint32_t kl_ = ln / (4 * RH), cl_ = ln % (4 * RH);
+        const int kb_ = kbw0 + int(cl_ / 4), sub_ = int(cl_ % 4);
+        const int kk_ = (16 * gi) / RH + int(kl_);
+        const int kv0_ = int(kl_ * RH) & 3;
         {
             const uint32_t *gp = reinterpret_cast<const uint32_t *>(rl + LD::GATE_OFF);
             const uint32_t gw[2] = {gp[0], gp[1]};
             // rank pieces of this lane's key: row kl RH + r of sub `sub` in piece kb - kbw0, in slot
             // 16 sub + ((kl RH) ^ 4 sub) + r (r only occupies the row's low bits)
-            const char *kp = rw + (kb_ - kbw0) * LD::K_STRIDE + 16 * (16 * sub_ + ((kl_ * RH) ^ (4 * sub_)));
+            const char *kp = rw + (kb_ - kbw0) * LD::K_STRIDE + 16 * (16 * sub_ + (int(kl_ * RH) ^ (4 * sub_)));
             uint4 kbr[RH];
 #pragma unroll
             for (int r = 0; r < RH; ++r) kbr[r] = *reinterpret_cast<const uint4 *>(kp + 16 * r);
@@ -862,7 +862,7 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
             *reinterpret_cast<uint4 *>(&lds.k[buf][kk_ * SKS + 32 * kb_ + 8 * sub_]) = packed;
         }
         __builtin_amdgcn_sched_barrier(0);
-        const int vg4_ = ln >> 4;
+        const int vg4_ = int(ln >> 4);
         const int kbase = vbi * TOK;
         constexpr int TPH = 4 / RH;
         uint32_t gv[2][2];
@@ -872,7 +872,7 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
             gv[m][0] = gp[0];
             gv[m][1] = gp[1];
         }
-        uint16_t *dV = &lds.v[buf][(16 * vmv0 + (ln & 15)) * SVS];
+        uint16_t *dV = &lds.v[buf][(16 * vmv0 + int(ln & 15)) * SVS];
 #pragma unroll
         for (int u = 0; u < V_ITEMS; ++u) {
             const uint4 vxu = *reinterpret_cast<const uint4 *>(rl + LD::V_OFF + u * 1024);
