@@ -826,6 +826,7 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
         constexpr bool kPartial = decltype(partial_tag)::value;
         uint32_t ln = lane;  // unsigned: the divisions and remainders below are shifts and masks
         asm volatile("" : "+v"(ln));
+        __builtin_assume(ln < 64u);  // and the products below fit 24-bit multiplies
         const int key0 = kt * kKT2;
         const char *rl = rw + 16 * ln;  // this lane's 16-byte slot of each staged piece
         const uint32_t kl_ = ln / (4 * RH), cl_ = ln % (4 * RH);
@@ -859,7 +860,8 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
             uint4 packed = make_uint4(pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3]), pack_bf16x2(kv[4], kv[5]),
                                       pack_bf16x2(kv[6], kv[7]));
             if (kPartial && key0 + kk_ >= n_keys) packed = make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4 *>(&lds.k[buf][kk_ * SKS + 32 * kb_ + 8 * sub_]) = packed;
+            const uint32_t k_at = uint32_t(kk_) * SKS + uint32_t(32 * kb_ + 8 * sub_);  // 32-bit LDS index math
+            *reinterpret_cast<uint4 *>(&lds.k[buf][k_at]) = packed;
         }
         __builtin_amdgcn_sched_barrier(0);
         const int vg4_ = int(ln >> 4);
@@ -872,7 +874,7 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
             gv[m][0] = gp[0];
             gv[m][1] = gp[1];
         }
-        uint16_t *dV = &lds.v[buf][(16 * vmv0 + int(ln & 15)) * SVS];
+        uint16_t *dV = &lds.v[buf][uint32_t(16 * vmv0 * SVS) + (ln & 15u) * SVS];
 #pragma unroll
         for (int u = 0; u < V_ITEMS; ++u) {
             const uint4 vxu = *reinterpret_cast<const uint4 *>(rl + LD::V_OFF + u * 1024);
