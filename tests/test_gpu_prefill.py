@@ -85,10 +85,11 @@ def test_full_size_prefill_all_rows():
 
 
 # Chunks of more than 256 rows at d_h = 128 run the wide form at ranks 2 and 4 (512 query rows per
-# work-group, factor pieces staged through LDS); these cases cover it with ragged chunk ends, a second row
-# tile, short and empty contexts, and rank 1 (which keeps the 256-row form at every chunk length).
+# work-group, factor pieces staged through LDS); these cases cover each of its instantiations (16 and 32
+# padded heads, ranks 2 and 4) with ragged chunk ends, a second row tile, short and empty contexts, and rank 1
+# (which keeps the 256-row form at every chunk length).
 @pytest.mark.parametrize("h,R,q_scale", [(32, 4, 2.0), (32, 2, 2.0), (32, 1, 2.0), (20, 4, 2.0), (16, 4, 2.0),
-                                         (32, 4, 10.0), (32, 1, 6.0)])
+                                         (16, 2, 2.0), (32, 4, 10.0), (32, 1, 6.0)])
 @pytest.mark.parametrize("ctx,chunk", [([0, 45], 300), ([257], 700), ([64, 1000, 3], 257)])
 def test_wide_chunks(h, R, q_scale, ctx, chunk, request):
     known = RANK1_PREFILL.get((h, 128, R, tuple(ctx), chunk, q_scale))
