@@ -770,8 +770,9 @@ __device__ __forceinline__ void prefill2_body(const PrefillParams &p, Prefill2Ld
     // piece of the cache block; lane (key kl, chunk) then reads the RH rank pieces of its key from the
     // staging area.  V: V_ITEMS contiguous value chunks of one cache block.
     // A K~ piece's 64 chunks are (sub, row): features 8 sub .. 8 sub + 7 of factor row `row` of the group, at
-    // chunk 16 sub + row of the cache block.  Staged in that order, the 16 lanes that read one rank row at a
-    // time (one key, four pieces x four subs) would hit chunks 256 bytes apart: the same four LDS banks.  So
+    // chunk 16 sub + row of the cache block.  Staged in that order, the 16 lanes that read one rank at a time
+    // (rank 4: one key over four pieces and four subs; rank 2: two keys over two pieces and four subs) would hit
+    // chunks that are multiples of 256 bytes apart, i.e. the same four LDS banks or two groups of them.  So
     // chunk (sub, row) goes to slot 16 sub + (row ^ 4 sub) (the rows of a sub stay in its 256 bytes), and
     // piece q starts 16 q bytes past a 1 KB boundary: the 16 lanes' reads then fall in 16 different bank groups.
     constexpr int WPG = 4 / RH;                       // waves per 16-row group
