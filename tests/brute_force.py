@@ -58,3 +58,19 @@ def query_from_factors(A_Q, B_Q):
     """q[i][c] = (1/R_Q) sum_r A_Q[r][i] B_Q[r][c] for one query token, as fsum loops."""
     RQ, h, d = len(A_Q), len(A_Q[0]), len(B_Q[0])
     return [[math.fsum(A_Q[r][i] * B_Q[r][c] for r in range(RQ)) / RQ for c in range(d)] for i in range(h)]
+
+
+def scores(A_K, B_K, kv_pos, q_head, q_pos, head, base, scale=None):
+    """Scores z_s = scale * rope(q_head, q_pos) . rope(K_s[head], kv_pos[s]) of one query head over every cached
+    token, K_s[head][c] = (1/R) sum_r A_K[s][r][head] B_K[s][r][c], as fsum loops."""
+    d = len(q_head)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    qt = rope_complex(list(q_head), q_pos, base)
+    z = []
+    for s in range(len(A_K)):
+        R = len(A_K[s])
+        k = [math.fsum(A_K[s][r][head] * B_K[s][r][c] for r in range(R)) / R for c in range(d)]
+        kt = rope_complex(k, kv_pos[s], base)
+        z.append(scale * math.fsum(qt[c] * kt[c] for c in range(d)))
+    return z

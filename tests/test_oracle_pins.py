@@ -365,3 +365,43 @@ def test_rope_rows_at_equals_row_by_row_rotation():
     got = oracle.rope_rows_at(x, pos, 500000.0)
     for t in range(7):
         np.testing.assert_array_equal(got[t], oracle.rope_rows(x[t], float(pos[t, 0]), 500000.0))
+
+
+@pytest.mark.parametrize("cuts", [[0, 40], [0, 1, 40], [0, 13, 14, 29, 40], list(range(0, 41, 5)),
+                                  [0, 39, 40], "random"])
+def test_split_merge_algebra_equals_one_pass(cuts):
+    """Pin O7: cut the cached tokens into contiguous pieces; per piece j and head, m_j = max score, l_j = sum of
+    exp(score - m_j) (scores from the independent brute force) and O_j = the piece's normalized attention
+    output (the oracle over that piece alone, tokens at their own positions).  The textbook merge
+    M = max m_j, out = sum_j e^(m_j - M) l_j O_j / sum_j e^(m_j - M) l_j must give the one-pass output: the rule
+    the split-sequence decode applies to its partials.  Sharpened query, so the pieces' masses differ widely."""
+    rng = np.random.default_rng(707)
+    h, d, RK, RV, N, base = 3, 8, 2, 3, 40, 1e4
+    A_K = rng.standard_normal((N, RK, h)) / np.sqrt(RK)
+    B_K = rng.standard_normal((N, RK, d)) / np.sqrt(RK)
+    A_V = rng.standard_normal((N, RV, h)) / np.sqrt(RV)
+    B_V = rng.standard_normal((N, RV, d)) / np.sqrt(RV)
+    q = 4.0 * rng.standard_normal((h, d))
+    if cuts == "random":
+        cuts = [0] + sorted(int(c) for c in rng.choice(np.arange(1, N), 6, replace=False)) + [N]
+    full = oracle.decode(A_K, B_K, A_V, B_V, q, base)
+    z_all = [brute_force.scores(A_K.tolist(), B_K.tolist(), list(range(N)), q[i].tolist(), N, i, base)
+             for i in range(h)]
+    pieces = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        O = oracle.attention(A_K[a:b], B_K[a:b], A_V[a:b], B_V[a:b], np.arange(a, b), q[None], [N], [b - a],
+                             base)[0]
+        ml = []
+        for i in range(h):
+            z = z_all[i][a:b]
+            m = max(z)
+            ml.append((m, math.fsum(math.exp(x - m) for x in z)))
+        pieces.append((ml, O))
+    for i in range(h):
+        M = max(ml[i][0] for ml, _ in pieces)
+        w = [math.exp(ml[i][0] - M) * ml[i][1] for ml, _ in pieces]
+        merged = sum(wj * O[i] for wj, (_, O) in zip(w, pieces)) / math.fsum(w)
+        np.testing.assert_allclose(merged, full[i], rtol=0, atol=1e-12)
+    if len(cuts) > 2:  # a wrong rule (the pieces' outputs averaged, masses ignored) is far off
+        avg = np.mean([O for _, O in pieces], axis=0)
+        assert np.abs(avg - full).max() > 1e-3
