@@ -405,3 +405,27 @@ def test_split_merge_algebra_equals_one_pass(cuts):
     if len(cuts) > 2:  # a wrong rule (the pieces' outputs averaged, masses ignored) is far off
         avg = np.mean([O for _, O in pieces], axis=0)
         assert np.abs(avg - full).max() > 1e-3
+
+
+@pytest.mark.parametrize("d,pos,base", [(8, 3.0, 1e4), (16, 1000.0, 1e4), (128, 131071.0, 5e5)])
+def test_half_split_rotation_is_a_channel_permutation_of_the_pair_rotation(d, pos, base):
+    """Pin O2b (reading R2: pairs (2j, 2j+1)).  The half-split convention rotates (x_j, x_{j+d/2}) by the same
+    angle pos * base^(-2j/d); with P the permutation taking channel 2j to j and 2j+1 to j + d/2, the half-split
+    rotation of P x equals P times the oracle's rotation of x.  The oracle does not itself equal the half-split
+    form, so the convention is fixed, and a half-split caller permutes its channels once."""
+    rng = np.random.default_rng(int(d + pos) % 2**32)
+    x = rng.standard_normal((5, d))
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])  # (P x)[k] = x[perm[k]]
+    half = d // 2
+    ang = pos * base ** (-2.0 * np.arange(half) / d)
+    c, s = np.cos(ang), np.sin(ang)
+
+    def half_split(v):
+        a, b = v[:, :half], v[:, half:]
+        return np.concatenate([a * c - b * s, b * c + a * s], axis=1)
+
+    ours = oracle.rope_rows(x, pos, base)
+    # the two sides form and reduce the angle (up to pos rad) separately: a few fp64 ulps of it apart
+    tol = 1e-12 + 16 * pos * 2.0**-52 * np.abs(x).max()
+    np.testing.assert_allclose(half_split(x[:, perm]), ours[:, perm], rtol=0, atol=tol)
+    assert np.abs(half_split(x) - ours).max() > 1e-3
